@@ -1,0 +1,296 @@
+// Kernels around the split-KV attention core:
+//   plan_items        - per query item: request, visible key range, tile count,
+//                       and the exclusive prefix sum of tile counts (the
+//                       split plan; computed on the device from context_lens,
+//                       so there is no host synchronisation)
+//   combine_segments  - log-sum-exp merge of the partial results of items whose
+//                       tiles were cut across workgroups
+//   dense_combine     - the general LSE merge of [S][rows][dim] partials
+//   absorb            - q_lat[i,h,:] = W_UK[h]^T q_nope[i,h,:]  (bf16 out)
+//   up_project        - out[i,h,:] = W_UV[h] o_lat[i,h,:]        (bf16 out)
+//
+// Decode positions and context lengths follow "feat(serving): DeepSeek-V2/V3
+// paged-attention shim (MLA)", Root causes items 2 and 4 (the newest token is
+// written first and sits at position n - 1).  Prefill rows follow "[Attention]
+// MLA with chunked prefill" (row i of an m-token chunk sits at n - m + i).  The
+// window follows "[Models] Support MLA_SWA functionality", Motivation, with the
+// boundary p - w < t <= p (the pages give none).  The weight-absorption
+// reading of kv_b_proj (k_nope = W_UK c, v = W_UV c) is this library's.
+#include <math.h>
+
+#include "device_utils.h"
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void plan_items_kernel(
+    int mode, int32_t B, int32_t Nq, const int32_t* __restrict__ ctx,
+    const int32_t* __restrict__ qsl, int32_t window, int32_t max_ctx, int32_t* __restrict__ item_b,
+    int32_t* __restrict__ item_lo, int32_t* __restrict__ item_hi,
+    int32_t* __restrict__ tile_start) {
+  __shared__ int32_t buf[kPlanThreads];
+  __shared__ int32_t carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < Nq; base += kPlanThreads) {
+    const int i = base + tid;
+    int32_t nt = 0;
+    if (i < Nq) {
+      int b, p;
+      if (mode == kPlanDecode) {
+        b = i;
+        const int n = min(max(ctx[b], 0), max_ctx);
+        p = n - 1;
+      } else {
+        int lo = 0, hi = B;  // largest b < B with qsl[b] <= i
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (qsl[mid] <= i) lo = mid; else hi = mid;
+        }
+        b = lo;
+        const int n = min(max(ctx[b], 0), max_ctx);
+        const int m = qsl[b + 1] - qsl[b];
+        p = min(n - m + (i - qsl[b]), n - 1);
+      }
+      int lo_t = 0, hi_t = 0;
+      if (p >= 0) {
+        hi_t = p + 1;
+        lo_t = window > 0 ? max(0, p - window + 1) : 0;
+      }
+      item_b[i] = b;
+      item_lo[i] = lo_t;
+      item_hi[i] = hi_t;
+      nt = hi_t > lo_t ? (hi_t + kTile - 1) / kTile - lo_t / kTile : 0;
+    }
+    // inclusive scan over the block (Hillis-Steele)
+    buf[tid] = nt;
+    __syncthreads();
+    for (int off = 1; off < kPlanThreads; off <<= 1) {
+      const int32_t add = tid >= off ? buf[tid - off] : 0;
+      __syncthreads();
+      buf[tid] += add;
+      __syncthreads();
+    }
+    if (i < Nq) tile_start[i] = carry + buf[tid] - nt;
+    __syncthreads();
+    if (tid == kPlanThreads - 1) carry += buf[tid];
+    __syncthreads();
+  }
+  if (tid == 0) tile_start[Nq] = carry;
+}
+
+// One block per item.  Items whose tiles all fell to one workgroup were
+// finished by the attention kernel; empty items get o = 0, lse = -inf; cut
+// items are merged from the partial slots of the workgroups that cover them
+// (slot 2g+1 for the first, which the item starts in, slot 2g after it).
+__global__ __launch_bounds__(256) void combine_segments_kernel(AttnArgs a) {
+  const int i = blockIdx.x;
+  const int64_t ts = a.tile_start[i], te = a.tile_start[i + 1];
+  const int H = a.H, R = a.kv.R;
+  const int tid = threadIdx.x;
+  if (ts == te) {
+    for (int idx = tid; idx < H * R; idx += blockDim.x) a.o_lat[static_cast<int64_t>(i) * H * R + idx] = 0.f;
+    for (int h = tid; h < H; h += blockDim.x) a.lse[static_cast<int64_t>(i) * H + h] = -INFINITY;
+    return;
+  }
+  const int64_t W = a.tile_start[a.num_items];
+  const int64_t G = a.G;
+  const int64_t g0 = wg_of_tile(ts, W, G), g1 = wg_of_tile(te - 1, W, G);
+  if (g0 == g1) return;
+  for (int h = 0; h < H; ++h) {
+    // every thread computes the head's merged lse (few segments, cheap)
+    float mx = -INFINITY;
+    for (int64_t g = g0; g <= g1; ++g) {
+      if (wg_tile_begin(g, W, G) == wg_tile_begin(g + 1, W, G)) continue;
+      const int64_t slot = (g == g0) ? 2 * g + 1 : 2 * g;
+      mx = fmaxf(mx, a.part_lse[slot * H + h]);
+    }
+    float tot = 0.f;
+    for (int64_t g = g0; g <= g1; ++g) {
+      if (wg_tile_begin(g, W, G) == wg_tile_begin(g + 1, W, G)) continue;
+      const int64_t slot = (g == g0) ? 2 * g + 1 : 2 * g;
+      const float l = a.part_lse[slot * H + h];
+      tot += (l == -INFINITY) ? 0.f : expf(l - mx);
+    }
+    float* dst = a.o_lat + (static_cast<int64_t>(i) * H + h) * R;
+    for (int r = tid; r < R; r += blockDim.x) {
+      float acc = 0.f;
+      for (int64_t g = g0; g <= g1; ++g) {
+        if (wg_tile_begin(g, W, G) == wg_tile_begin(g + 1, W, G)) continue;
+        const int64_t slot = (g == g0) ? 2 * g + 1 : 2 * g;
+        const float l = a.part_lse[slot * H + h];
+        if (l == -INFINITY) continue;
+        acc += expf(l - mx) * a.part_o[(slot * H + h) * R + r];
+      }
+      dst[r] = acc / tot;
+    }
+    if (tid == 0) a.lse[static_cast<int64_t>(i) * H + h] = mx + logf(tot);
+  }
+}
+
+__global__ __launch_bounds__(256) void dense_combine_kernel(const float* __restrict__ o_part,
+                                                             const float* __restrict__ lse_part,
+                                                             int32_t S, int32_t rows, int32_t dim,
+                                                             float* __restrict__ o,
+                                                             float* __restrict__ lse) {
+  const int64_t row = blockIdx.x;
+  float mx = -INFINITY;
+  for (int s = 0; s < S; ++s) mx = fmaxf(mx, lse_part[static_cast<int64_t>(s) * rows + row]);
+  float tot = 0.f;
+  if (mx != -INFINITY) {
+    for (int s = 0; s < S; ++s) {
+      const float l = lse_part[static_cast<int64_t>(s) * rows + row];
+      tot += (l == -INFINITY) ? 0.f : expf(l - mx);
+    }
+  }
+  for (int d = threadIdx.x; d < dim; d += blockDim.x) {
+    float acc = 0.f;
+    if (mx != -INFINITY) {
+      for (int s = 0; s < S; ++s) {
+        const float l = lse_part[static_cast<int64_t>(s) * rows + row];
+        if (l == -INFINITY) continue;
+        acc += expf(l - mx) * o_part[(static_cast<int64_t>(s) * rows + row) * dim + d];
+      }
+      acc /= tot;
+    }
+    o[row * dim + d] = acc;
+  }
+  if (threadIdx.x == 0) lse[row] = (mx == -INFINITY) ? -INFINITY : mx + logf(tot);
+}
+
+// q_lat[i,h,r] = sum_d q_nope[i,h,d] * W_UK[h,d,r]; fp32 accumulation, bf16 out.
+// Block: one head, 16 items; thread t owns columns r = t + 256k.
+constexpr int kGemmItems = 16;
+
+__global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict__ q_nope,
+                                                      int64_t st, int64_t sh,
+                                                      const uint16_t* __restrict__ w_uk,
+                                                      int32_t Nq, int32_t H, int32_t Dn, int32_t R,
+                                                      uint16_t* __restrict__ q_lat) {
+  extern __shared__ float qs[];  // [kGemmItems][Dn]
+  const int h = blockIdx.y;
+  const int i0 = blockIdx.x * kGemmItems;
+  const int ni = min(kGemmItems, Nq - i0);
+  for (int idx = threadIdx.x; idx < kGemmItems * Dn; idx += blockDim.x) {
+    const int it = idx / Dn, d = idx % Dn;
+    qs[idx] = it < ni ? bf16_to_f32(q_nope[(i0 + it) * st + h * sh + d]) : 0.f;
+  }
+  __syncthreads();
+  const uint16_t* w = w_uk + static_cast<int64_t>(h) * Dn * R;
+  for (int r0 = 0; r0 < R; r0 += 256) {
+    const int r = r0 + threadIdx.x;
+    if (r >= R) break;
+    float acc[kGemmItems];
+#pragma unroll
+    for (int it = 0; it < kGemmItems; ++it) acc[it] = 0.f;
+    for (int d = 0; d < Dn; ++d) {
+      const float wv = bf16_to_f32(w[static_cast<int64_t>(d) * R + r]);
+#pragma unroll
+      for (int it = 0; it < kGemmItems; ++it) acc[it] = fmaf(qs[it * Dn + d], wv, acc[it]);
+    }
+    for (int it = 0; it < ni; ++it)
+      q_lat[(static_cast<int64_t>(i0 + it) * H + h) * R + r] = f32_to_bf16(acc[it]);
+  }
+}
+
+// out[i,h,v] = sum_r W_UV[h,v,r] * o_lat[i,h,r]; fp32 accumulation, bf16 out.
+// Block: one head, 16 items; a wave handles one output column v at a time,
+// its lanes splitting r.
+__global__ __launch_bounds__(256) void up_project_kernel(const float* __restrict__ o_lat,
+                                                          const uint16_t* __restrict__ w_uv,
+                                                          int32_t Nq, int32_t H, int32_t R,
+                                                          int32_t Dv, uint16_t* __restrict__ out) {
+  extern __shared__ float os[];  // [kGemmItems][R]
+  const int h = blockIdx.y;
+  const int i0 = blockIdx.x * kGemmItems;
+  const int ni = min(kGemmItems, Nq - i0);
+  for (int idx = threadIdx.x; idx < kGemmItems * R; idx += blockDim.x) {
+    const int it = idx / R, r = idx % R;
+    os[idx] = it < ni ? o_lat[(static_cast<int64_t>(i0 + it) * H + h) * R + r] : 0.f;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint16_t* w = w_uv + static_cast<int64_t>(h) * Dv * R;
+  for (int v = wave; v < Dv; v += 4) {
+    float acc[kGemmItems];
+#pragma unroll
+    for (int it = 0; it < kGemmItems; ++it) acc[it] = 0.f;
+    for (int r = lane; r < R; r += 64) {
+      const float wv = bf16_to_f32(w[static_cast<int64_t>(v) * R + r]);
+#pragma unroll
+      for (int it = 0; it < kGemmItems; ++it) acc[it] = fmaf(os[it * R + r], wv, acc[it]);
+    }
+#pragma unroll
+    for (int it = 0; it < kGemmItems; ++it) acc[it] = wave_sum(acc[it]);
+    if (lane < ni) {
+      float mine = 0.f;
+#pragma unroll
+      for (int it = 0; it < kGemmItems; ++it) mine = (it == lane) ? acc[it] : mine;
+      out[(static_cast<int64_t>(i0 + lane) * H + h) * Dv + v] = f32_to_bf16(mine);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void latent_out_kernel(const float* __restrict__ o_lat,
+                                                          int64_t count,
+                                                          uint16_t* __restrict__ out) {
+  for (int64_t k = blockIdx.x * 256ll + threadIdx.x; k < count; k += 256ll * gridDim.x)
+    out[k] = f32_to_bf16(o_lat[k]);
+}
+
+}  // namespace
+
+hipError_t launch_plan(int mode, int32_t batch, int32_t num_items, const int32_t* context_lens,
+                       const int32_t* query_start_loc, int32_t window, int32_t max_ctx,
+                       const Plan& plan, hipStream_t s) {
+  hipLaunchKernelGGL(plan_items_kernel, dim3(1), dim3(kPlanThreads), 0, s, mode, batch, num_items,
+                     context_lens, query_start_loc, window, max_ctx, plan.item_b, plan.item_lo,
+                     plan.item_hi, plan.tile_start);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_segments(const AttnArgs& a, hipStream_t s) {
+  if (a.num_items == 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_segments_kernel, dim3(a.num_items), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_combine(const float* o_part, const float* lse_part, int32_t num_splits,
+                                int32_t rows, int32_t dim, float* o, float* lse, hipStream_t s) {
+  hipLaunchKernelGGL(dense_combine_kernel, dim3(rows), dim3(256), 0, s, o_part, lse_part,
+                     num_splits, rows, dim, o, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_absorb(const uint16_t* q_nope, int64_t st, int64_t sh, const uint16_t* w_uk,
+                         int32_t num_items, int32_t H, int32_t Dn, int32_t R, uint16_t* q_lat,
+                         hipStream_t s) {
+  const dim3 grid((num_items + kGemmItems - 1) / kGemmItems, H);
+  const size_t smem = sizeof(float) * kGemmItems * Dn;
+  hipLaunchKernelGGL(absorb_kernel, grid, dim3(256), smem, s, q_nope, st, sh, w_uk, num_items, H,
+                     Dn, R, q_lat);
+  return hipGetLastError();
+}
+
+hipError_t launch_up_project(const float* o_lat, const uint16_t* w_uv, int32_t num_items, int32_t H,
+                             int32_t R, int32_t Dv, uint16_t* out, hipStream_t s) {
+  const dim3 grid((num_items + kGemmItems - 1) / kGemmItems, H);
+  const size_t smem = sizeof(float) * kGemmItems * R;
+  hipLaunchKernelGGL(up_project_kernel, grid, dim3(256), smem, s, o_lat, w_uv, num_items, H, R, Dv,
+                     out);
+  return hipGetLastError();
+}
+
+hipError_t launch_latent_out(const float* o_lat, int64_t count, uint16_t* out, hipStream_t s) {
+  if (count == 0) return hipSuccess;
+  const int64_t blocks = (count + 255) / 256;
+  hipLaunchKernelGGL(latent_out_kernel, dim3(static_cast<unsigned>(blocks < 65536 ? blocks : 65536)),
+                     dim3(256), 0, s, o_lat, count, out);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,316 @@
+// Host side of the C ABI: argument validation, workspace carving and launch
+// sequencing.  No device memory is allocated here and nothing synchronises
+// with the host; every launch goes to the caller's stream.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/mla.h"
+#include "mla_internal.h"
+
+namespace {
+
+using mla::AttnArgs;
+using mla::CacheView;
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxDevices = 64;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Compute units of the current device (cached per device id).
+int current_cu_count() {
+  static int cached[kMaxDevices] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < kMaxDevices && cached[dev] > 0) return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return -1;
+  if (dev < kMaxDevices) cached[dev] = n;
+  return n;
+}
+
+bool page_size_ok(int ps) { return ps == 16 || ps == 32 || ps == 64 || ps == 128; }
+
+mla_status check_cache(const mla_cache* c) {
+  if (!c || !c->data) return MLA_ERR_INVALID_ARGUMENT;
+  if (c->num_layers <= 0 || c->num_pages <= 0 || c->page_size <= 0 || c->kv_lora_rank <= 0 ||
+      c->qk_rope_dim < 0)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (c->dtype != MLA_KV_BF16 && c->dtype != MLA_KV_FP8_E4M3) return MLA_ERR_INVALID_ARGUMENT;
+  if (c->dtype == MLA_KV_FP8_E4M3 && !c->scale) return MLA_ERR_INVALID_ARGUMENT;
+  if (!page_size_ok(c->page_size)) return MLA_ERR_UNSUPPORTED;
+  const int D = c->kv_lora_rank + c->qk_rope_dim;
+  if (c->kv_lora_rank % 8 != 0 || c->qk_rope_dim % 8 != 0 || D < 8 || D > 1024)
+    return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+mla_status check_attn(const mla_attn* a) {
+  if (!a) return MLA_ERR_INVALID_ARGUMENT;
+  if (a->num_heads <= 0 || a->num_heads > 1024) return MLA_ERR_INVALID_ARGUMENT;
+  if (a->w_uk && (a->qk_nope_dim <= 0 || a->qk_nope_dim > 1024)) return MLA_ERR_INVALID_ARGUMENT;
+  if (a->w_uv && (a->v_head_dim <= 0 || a->v_head_dim > 1024)) return MLA_ERR_INVALID_ARGUMENT;
+  if (!isfinite(a->scale)) return MLA_ERR_INVALID_ARGUMENT;
+  if (a->num_workgroups < 0) return MLA_ERR_INVALID_ARGUMENT;
+  return MLA_OK;
+}
+
+size_t elem_bytes(int dtype) { return dtype == MLA_KV_BF16 ? 2 : 1; }
+
+// Workspace regions (byte offsets from the workspace base).
+struct Layout {
+  int G = 0;
+  size_t q_lat = 0, o_lat = 0, lse = 0, item_b = 0, item_lo = 0, item_hi = 0, tile_start = 0,
+         part_o = 0, part_lse = 0, total = 0;
+};
+
+// Returns false when the number of workgroups cannot be determined.
+bool make_layout(const mla_cache* c, const mla_attn* a, int64_t num_items, Layout* L) {
+  int G = a->num_workgroups;
+  if (G <= 0) {
+    G = current_cu_count();
+    if (G <= 0) return false;
+  }
+  const int64_t H = a->num_heads, R = c->kv_lora_rank;
+  size_t off = 0;
+  L->G = G;
+  L->q_lat = off;
+  if (a->w_uk) off = align_up(off + sizeof(uint16_t) * num_items * H * R);
+  L->o_lat = off;
+  off = align_up(off + sizeof(float) * num_items * H * R);
+  L->lse = off;
+  off = align_up(off + sizeof(float) * num_items * H);
+  L->item_b = off;
+  off = align_up(off + sizeof(int32_t) * num_items);
+  L->item_lo = off;
+  off = align_up(off + sizeof(int32_t) * num_items);
+  L->item_hi = off;
+  off = align_up(off + sizeof(int32_t) * num_items);
+  L->tile_start = off;
+  off = align_up(off + sizeof(int32_t) * (num_items + 1));
+  L->part_o = off;
+  off = align_up(off + sizeof(float) * 2 * G * H * R);
+  L->part_lse = off;
+  off = align_up(off + sizeof(float) * 2 * G * H);
+  L->total = off;
+  return true;
+}
+
+template <typename T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+mla_status to_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+// Shared by decode (one item per request) and prefill (one item per query row).
+mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, const mla_attn* attn,
+                         const void* q_nope, int64_t qn_st, int64_t qn_sh, const void* q_pe,
+                         int64_t qp_st, int64_t qp_sh, const int32_t* qsl, int32_t num_items,
+                         const int32_t* block_tables, int32_t max_blocks,
+                         const int32_t* context_lens, int32_t batch, void* out,
+                         float* lse_or_null, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  mla_status st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if ((st = check_attn(attn)) != MLA_OK) return st;
+  if (layer_idx < 0 || layer_idx >= cache->num_layers) return MLA_ERR_INVALID_ARGUMENT;
+  if (batch < 0 || num_items < 0 || max_blocks <= 0) return MLA_ERR_INVALID_ARGUMENT;
+  if (batch == 0 || num_items == 0) return MLA_OK;
+  if (!q_nope || !q_pe || !block_tables || !context_lens || !out) return MLA_ERR_INVALID_ARGUMENT;
+  if (mode == mla::kPlanPrefill && !qsl) return MLA_ERR_INVALID_ARGUMENT;
+  const int64_t max_ctx64 = static_cast<int64_t>(max_blocks) * cache->page_size;
+  if (max_ctx64 > (1ll << 30)) return MLA_ERR_UNSUPPORTED;
+  // the tile counts are int32 on the device
+  if (static_cast<int64_t>(num_items) * (max_ctx64 / mla::kTile + 1) >= (1ll << 31))
+    return MLA_ERR_UNSUPPORTED;
+
+  Layout L;
+  if (!make_layout(cache, attn, num_items, &L)) return MLA_ERR_HIP;
+  if (!workspace || workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MLA_ERR_WORKSPACE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int H = attn->num_heads, R = cache->kv_lora_rank;
+
+  const int64_t layer_elems =
+      static_cast<int64_t>(cache->num_pages) * cache->page_size * (R + cache->qk_rope_dim);
+  CacheView kv;
+  kv.data = static_cast<const char*>(cache->data) + layer_idx * layer_elems * elem_bytes(cache->dtype);
+  kv.scale = cache->dtype == MLA_KV_FP8_E4M3
+                 ? cache->scale + static_cast<int64_t>(layer_idx) * cache->num_pages * cache->page_size
+                 : nullptr;
+  kv.dtype = cache->dtype == MLA_KV_BF16 ? mla::kKvBf16 : mla::kKvFp8;
+  kv.num_pages = cache->num_pages;
+  kv.page_size = cache->page_size;
+  kv.R = R;
+  kv.Dr = cache->qk_rope_dim;
+  kv.D = R + cache->qk_rope_dim;
+
+  hipError_t e;
+  const uint16_t* q_lat = static_cast<const uint16_t*>(q_nope);
+  int64_t ql_st = qn_st, ql_sh = qn_sh;
+  if (attn->w_uk) {
+    uint16_t* ql = at<uint16_t>(workspace, L.q_lat);
+    e = mla::launch_absorb(static_cast<const uint16_t*>(q_nope), qn_st, qn_sh,
+                           static_cast<const uint16_t*>(attn->w_uk), num_items, H,
+                           attn->qk_nope_dim, R, ql, s);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    q_lat = ql;
+    ql_st = static_cast<int64_t>(H) * R;
+    ql_sh = R;
+  }
+
+  mla::Plan plan;
+  plan.item_b = at<int32_t>(workspace, L.item_b);
+  plan.item_lo = at<int32_t>(workspace, L.item_lo);
+  plan.item_hi = at<int32_t>(workspace, L.item_hi);
+  plan.tile_start = at<int32_t>(workspace, L.tile_start);
+  e = mla::launch_plan(mode, batch, num_items, context_lens, qsl, attn->window,
+                       static_cast<int32_t>(max_ctx64), plan, s);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.kv = kv;
+  a.q_lat = q_lat;
+  a.q_lat_st = ql_st;
+  a.q_lat_sh = ql_sh;
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.q_pe_st = qp_st;
+  a.q_pe_sh = qp_sh;
+  a.block_tables = block_tables;
+  a.max_blocks = max_blocks;
+  a.item_b = plan.item_b;
+  a.item_lo = plan.item_lo;
+  a.item_hi = plan.item_hi;
+  a.tile_start = plan.tile_start;
+  a.num_items = num_items;
+  a.H = H;
+  a.G = L.G;
+  a.scale_log2 = attn->scale * 1.4426950408889634f;
+  a.o_lat = at<float>(workspace, L.o_lat);
+  a.lse = lse_or_null ? lse_or_null : at<float>(workspace, L.lse);
+  a.part_o = at<float>(workspace, L.part_o);
+  a.part_lse = at<float>(workspace, L.part_lse);
+
+  const bool use_mfma = !(attn->flags & MLA_FLAG_GENERIC_KERNELS) && mla::mfma_attn_supported(kv, H);
+  e = use_mfma ? mla::launch_attn_mfma(a, s) : mla::launch_attn_generic(a, s);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  e = mla::launch_combine_segments(a, s);
+  if (e != hipSuccess) return MLA_ERR_HIP;
+
+  if (attn->w_uv) {
+    e = mla::launch_up_project(a.o_lat, static_cast<const uint16_t*>(attn->w_uv), num_items, H, R,
+                               attn->v_head_dim, static_cast<uint16_t*>(out), s);
+  } else {
+    e = mla::launch_latent_out(a.o_lat, static_cast<int64_t>(num_items) * H * R,
+                               static_cast<uint16_t*>(out), s);
+  }
+  return to_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARGUMENT: return "MLA_ERR_INVALID_ARGUMENT";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+  }
+  return "MLA_ERR_UNKNOWN";
+}
+
+const char* mla_version(void) { return "paged-mla-gfx950 0.1"; }
+
+mla_status mla_write_kv(const mla_cache* cache, int32_t layer_idx, const void* c_kv,
+                        int64_t c_kv_row_stride, const void* k_pe, int64_t k_pe_row_stride,
+                        const int64_t* slot_mapping, int32_t num_tokens, void* stream) {
+  mla_status st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if (layer_idx < 0 || layer_idx >= cache->num_layers || num_tokens < 0)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (num_tokens == 0) return MLA_OK;
+  if (!c_kv || !slot_mapping || (cache->qk_rope_dim > 0 && !k_pe)) return MLA_ERR_INVALID_ARGUMENT;
+  if (c_kv_row_stride < cache->kv_lora_rank || k_pe_row_stride < cache->qk_rope_dim)
+    return MLA_ERR_INVALID_ARGUMENT;
+  const int64_t slots = static_cast<int64_t>(cache->num_pages) * cache->page_size;
+  const int64_t D = cache->kv_lora_rank + cache->qk_rope_dim;
+  void* layer = static_cast<char*>(cache->data) + layer_idx * slots * D * elem_bytes(cache->dtype);
+  float* scale = cache->dtype == MLA_KV_FP8_E4M3 ? cache->scale + layer_idx * slots : nullptr;
+  const hipError_t e = mla::launch_write_kv(
+      layer, scale, cache->dtype == MLA_KV_BF16 ? mla::kKvBf16 : mla::kKvFp8, slots,
+      cache->kv_lora_rank, cache->qk_rope_dim, static_cast<const uint16_t*>(c_kv), c_kv_row_stride,
+      static_cast<const uint16_t*>(k_pe), k_pe_row_stride, slot_mapping, num_tokens,
+      static_cast<hipStream_t>(stream));
+  return to_status(e);
+}
+
+size_t mla_decode_workspace_size(const mla_cache* cache, const mla_attn* attn, int32_t batch,
+                                 int32_t max_blocks_per_seq) {
+  if (check_cache(cache) != MLA_OK || check_attn(attn) != MLA_OK || batch < 0 ||
+      max_blocks_per_seq <= 0)
+    return 0;
+  Layout L;
+  if (!make_layout(cache, attn, batch, &L)) return 0;
+  return L.total;
+}
+
+size_t mla_prefill_workspace_size(const mla_cache* cache, const mla_attn* attn, int32_t batch,
+                                  int32_t total_q_tokens, int32_t max_blocks_per_seq) {
+  if (check_cache(cache) != MLA_OK || check_attn(attn) != MLA_OK || batch < 0 ||
+      total_q_tokens < 0 || max_blocks_per_seq <= 0)
+    return 0;
+  Layout L;
+  if (!make_layout(cache, attn, total_q_tokens, &L)) return 0;
+  return L.total;
+}
+
+mla_status mla_decode(const mla_cache* cache, int32_t layer_idx, const mla_attn* attn,
+                      const void* q_nope, int64_t q_nope_stride_b, int64_t q_nope_stride_h,
+                      const void* q_pe, int64_t q_pe_stride_b, int64_t q_pe_stride_h,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, int32_t batch, void* out, float* lse_or_null,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return run_attention(mla::kPlanDecode, cache, layer_idx, attn, q_nope, q_nope_stride_b,
+                       q_nope_stride_h, q_pe, q_pe_stride_b, q_pe_stride_h, nullptr, batch,
+                       block_tables, max_blocks_per_seq, context_lens, batch, out, lse_or_null,
+                       workspace, workspace_bytes, stream);
+}
+
+mla_status mla_prefill_chunk(const mla_cache* cache, int32_t layer_idx, const mla_attn* attn,
+                             const void* q_nope, int64_t q_nope_stride_t, int64_t q_nope_stride_h,
+                             const void* q_pe, int64_t q_pe_stride_t, int64_t q_pe_stride_h,
+                             const int32_t* query_start_loc, int32_t total_q_tokens,
+                             int32_t max_q_len, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             int32_t batch, void* out, float* lse_or_null, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  if (total_q_tokens < 0 || max_q_len < 0) return MLA_ERR_INVALID_ARGUMENT;
+  return run_attention(mla::kPlanPrefill, cache, layer_idx, attn, q_nope, q_nope_stride_t,
+                       q_nope_stride_h, q_pe, q_pe_stride_t, q_pe_stride_h, query_start_loc,
+                       total_q_tokens, block_tables, max_blocks_per_seq, context_lens, batch, out,
+                       lse_or_null, workspace, workspace_bytes, stream);
+}
+
+mla_status mla_decode_combine(const float* o_part, const float* lse_part, int32_t num_splits,
+                              int32_t batch, int32_t num_heads, int32_t dim, float* o, float* lse,
+                              void* stream) {
+  if (num_splits < 0 || batch < 0 || num_heads < 0 || dim < 0) return MLA_ERR_INVALID_ARGUMENT;
+  const int64_t rows = static_cast<int64_t>(batch) * num_heads;
+  if (rows == 0) return MLA_OK;
+  if (!o || !lse || (num_splits > 0 && (!o_part || !lse_part))) return MLA_ERR_INVALID_ARGUMENT;
+  if (rows > (1ll << 31) - 1) return MLA_ERR_UNSUPPORTED;
+  return to_status(mla::launch_dense_combine(o_part, lse_part, num_splits,
+                                             static_cast<int32_t>(rows), dim, o, lse,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

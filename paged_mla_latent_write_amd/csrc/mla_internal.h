@@ -1,0 +1,91 @@
+// Internal declarations shared by the host layer (mla_api.cpp) and the HIP
+// kernel files.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// Split-KV work unit: 32 consecutive token positions of one query item's
+// visible key range, aligned to absolute token position (tile k covers
+// positions [32k, 32k + 32)).
+constexpr int kTile = 32;
+
+enum PlanMode { kPlanDecode = 0, kPlanPrefill = 1 };
+enum KvDtype { kKvBf16 = 0, kKvFp8 = 1 };
+
+// One layer of the latent cache.
+struct CacheView {
+  const void* data;      // layer base: [num_pages][page_size][D]
+  const float* scale;    // layer base: [num_pages][page_size] (fp8), else null
+  int32_t dtype;         // KvDtype
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t R;             // kv_lora_rank
+  int32_t Dr;            // qk_rope_dim
+  int32_t D;             // R + Dr
+};
+
+// Per-item plan produced on the device (see plan_items in attn_common.hip).
+// An item is one query token: a decode request, or one prefill row.
+struct Plan {
+  int32_t* item_b;       // [Nq] request of the item
+  int32_t* item_lo;      // [Nq] first visible key position
+  int32_t* item_hi;      // [Nq] one past the last visible key position
+  int32_t* tile_start;   // [Nq + 1] exclusive prefix sum of the items' tile counts
+};
+
+struct AttnArgs {
+  CacheView kv;
+  const uint16_t* q_lat;  // bf16 latent query rows [.., H, R]
+  int64_t q_lat_st, q_lat_sh;
+  const uint16_t* q_pe;   // bf16 rope query rows [.., H, Dr]
+  int64_t q_pe_st, q_pe_sh;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  const int32_t* item_b;
+  const int32_t* item_lo;
+  const int32_t* item_hi;
+  const int32_t* tile_start;
+  int32_t num_items;
+  int32_t H;
+  int32_t G;              // workgroups the tile stream is divided over
+  float scale_log2;       // softmax scale * log2(e)
+  float* o_lat;           // [Nq][H][R] fp32, normalised (complete items)
+  float* lse;             // [Nq][H] fp32 natural log (complete items)
+  float* part_o;          // [2G][H][R] fp32 partials (cut items)
+  float* part_lse;        // [2G][H]
+};
+
+// ---- launchers (each returns the launch's hipGetLastError) ----
+hipError_t launch_write_kv(void* cache_layer, float* scale_layer, int32_t dtype, int64_t num_slots,
+                           int32_t R, int32_t Dr, const uint16_t* c_kv, int64_t c_stride,
+                           const uint16_t* k_pe, int64_t k_stride, const int64_t* slots,
+                           int32_t num_tokens, hipStream_t s);
+
+hipError_t launch_plan(int mode, int32_t batch, int32_t num_items, const int32_t* context_lens,
+                       const int32_t* query_start_loc, int32_t window, int32_t max_ctx,
+                       const Plan& plan, hipStream_t s);
+
+hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t s);
+
+// True when the MFMA split-KV kernel handles this shape (R 512, Dr 64, H <= 128).
+bool mfma_attn_supported(const CacheView& kv, int32_t H);
+hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
+
+hipError_t launch_combine_segments(const AttnArgs& a, hipStream_t s);
+
+hipError_t launch_absorb(const uint16_t* q_nope, int64_t st, int64_t sh, const uint16_t* w_uk,
+                         int32_t num_items, int32_t H, int32_t Dn, int32_t R, uint16_t* q_lat,
+                         hipStream_t s);
+
+hipError_t launch_up_project(const float* o_lat, const uint16_t* w_uv, int32_t num_items, int32_t H,
+                             int32_t R, int32_t Dv, uint16_t* out, hipStream_t s);
+
+hipError_t launch_latent_out(const float* o_lat, int64_t count, uint16_t* out, hipStream_t s);
+
+hipError_t launch_dense_combine(const float* o_part, const float* lse_part, int32_t num_splits,
+                                int32_t rows, int32_t dim, float* o, float* lse, hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,268 @@
+"""Thin ctypes binding over libmla.so (argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels; this module
+only turns torch tensors into pointers, sizes and strides, allocates outputs
+and workspaces with torch on the tensors' device, and raises on a non-OK
+status.  Importing it without a built libmla.so raises ImportError: there is
+no CPU fallback.
+
+The names follow the C ABI in include/mla.h: write_kv, decode, decode_combine,
+prefill_chunk, decode_workspace_size, prefill_workspace_size.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run paged_mla_latent_write_amd.build.build() "
+                      "(hipcc, gfx950).  There is no CPU fallback.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+MLA_OK = 0
+MLA_ERR_INVALID_ARGUMENT = 1
+MLA_ERR_UNSUPPORTED = 2
+MLA_ERR_WORKSPACE = 3
+MLA_ERR_HIP = 4
+MLA_KV_BF16 = 0
+MLA_KV_FP8_E4M3 = 1
+MLA_FLAG_GENERIC_KERNELS = 1
+
+EXPORTED = ("mla_write_kv", "mla_decode_workspace_size", "mla_decode", "mla_decode_combine",
+            "mla_prefill_workspace_size", "mla_prefill_chunk", "mla_status_string", "mla_version")
+
+
+class MlaCacheStruct(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("num_layers", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("kv_lora_rank", ctypes.c_int32),
+                ("qk_rope_dim", ctypes.c_int32)]
+
+
+class MlaAttnStruct(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("qk_nope_dim", ctypes.c_int32),
+                ("v_head_dim", ctypes.c_int32), ("w_uk", ctypes.c_void_p), ("w_uv", ctypes.c_void_p),
+                ("scale", ctypes.c_float), ("window", ctypes.c_int32),
+                ("num_workgroups", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_CP = ctypes.POINTER(MlaCacheStruct)
+_AP = ctypes.POINTER(MlaAttnStruct)
+
+
+def _sig(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_write_kv = _sig("mla_write_kv", _I32, _CP, _I32, _P, _I64, _P, _I64, _P, _I32, _P)
+_decode_ws = _sig("mla_decode_workspace_size", _SZ, _CP, _AP, _I32, _I32)
+_decode = _sig("mla_decode", _I32, _CP, _I32, _AP, _P, _I64, _I64, _P, _I64, _I64, _P, _I32, _P,
+               _I32, _P, _P, _P, _SZ, _P)
+_combine = _sig("mla_decode_combine", _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P)
+_prefill_ws = _sig("mla_prefill_workspace_size", _SZ, _CP, _AP, _I32, _I32, _I32)
+_prefill = _sig("mla_prefill_chunk", _I32, _CP, _I32, _AP, _P, _I64, _I64, _P, _I64, _I64, _P, _I32,
+                _I32, _P, _I32, _P, _I32, _P, _P, _P, _SZ, _P)
+_status_string = _sig("mla_status_string", ctypes.c_char_p, _I32)
+_version = _sig("mla_version", ctypes.c_char_p)
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {_status_string(status).decode()}")
+
+
+def _check(status, where):
+    if status != MLA_OK:
+        raise MlaError(status, where)
+
+
+def version() -> str:
+    return _version().decode()
+
+
+def status_string(status: int) -> str:
+    return _status_string(status).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+@dataclass
+class KVCache:
+    """Caller-owned latent cache: data [L, P, ps, R + Dr] (bfloat16, or uint8
+    E4M3 codes) and, for fp8, scale [L, P, ps] float32."""
+    data: torch.Tensor
+    scale: torch.Tensor | None
+    kv_lora_rank: int
+    qk_rope_dim: int
+
+    @classmethod
+    def empty(cls, num_layers, num_pages, page_size, kv_lora_rank, qk_rope_dim, fp8=False,
+              device="cuda"):
+        D = kv_lora_rank + qk_rope_dim
+        if fp8:
+            data = torch.empty((num_layers, num_pages, page_size, D), dtype=torch.uint8, device=device)
+            scale = torch.empty((num_layers, num_pages, page_size), dtype=torch.float32, device=device)
+        else:
+            data = torch.empty((num_layers, num_pages, page_size, D), dtype=torch.bfloat16, device=device)
+            scale = None
+        return cls(data, scale, kv_lora_rank, qk_rope_dim)
+
+    @property
+    def fp8(self):
+        return self.data.dtype == torch.uint8
+
+    @property
+    def page_size(self):
+        return int(self.data.shape[2])
+
+    def struct(self) -> MlaCacheStruct:
+        assert self.data.is_contiguous()
+        L, P, ps, D = self.data.shape
+        assert D == self.kv_lora_rank + self.qk_rope_dim
+        return MlaCacheStruct(self.data.data_ptr(), self.scale.data_ptr() if self.fp8 else None,
+                              MLA_KV_FP8_E4M3 if self.fp8 else MLA_KV_BF16, L, P, ps,
+                              self.kv_lora_rank, self.qk_rope_dim)
+
+
+def _attn_struct(num_heads, qk_nope_dim, v_head_dim, w_uk, w_uv, scale, window, num_workgroups,
+                 flags):
+    for w in (w_uk, w_uv):
+        assert w is None or (w.is_contiguous() and w.dtype == torch.bfloat16)
+    return MlaAttnStruct(num_heads, qk_nope_dim, v_head_dim, _ptr(w_uk), _ptr(w_uv), float(scale),
+                         int(window), int(num_workgroups), int(flags))
+
+
+def _row_strides(q):
+    assert q.dim() == 3 and q.stride(2) == 1 and q.dtype == torch.bfloat16
+    return q.stride(0), q.stride(1)
+
+
+def write_kv(cache: KVCache, layer_idx: int, c_kv: torch.Tensor, k_pe: torch.Tensor,
+             slot_mapping: torch.Tensor, stream=None):
+    """Scatter rows [c_kv | k_pe] (bf16 [T, R], [T, Dr], unit inner stride)
+    into layer `layer_idx` at slot_mapping (int64 [T]; negative = pad row)."""
+    assert c_kv.dtype == torch.bfloat16 and k_pe.dtype == torch.bfloat16
+    assert c_kv.stride(-1) == 1 and k_pe.stride(-1) == 1 and slot_mapping.dtype == torch.int64
+    st = cache.struct()
+    T = int(c_kv.shape[0])
+    _check(_write_kv(ctypes.byref(st), layer_idx, _ptr(c_kv), c_kv.stride(0), _ptr(k_pe),
+                     k_pe.stride(0), _ptr(slot_mapping), T, _stream(stream)), "mla_write_kv")
+
+
+def decode_workspace_size(cache: KVCache, attn: MlaAttnStruct, batch: int, max_blocks: int) -> int:
+    return int(_decode_ws(ctypes.byref(cache.struct()), ctypes.byref(attn), batch, max_blocks))
+
+
+def prefill_workspace_size(cache: KVCache, attn: MlaAttnStruct, batch: int, total_q: int,
+                           max_blocks: int) -> int:
+    return int(_prefill_ws(ctypes.byref(cache.struct()), ctypes.byref(attn), batch, total_q,
+                           max_blocks))
+
+
+class Workspace:
+    """A reusable device workspace that grows on demand (torch-allocated)."""
+
+    def __init__(self):
+        self.buf = None
+
+    def get(self, nbytes, device):
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        return self.buf
+
+
+def decode(cache: KVCache, layer_idx: int, q_nope, q_pe, block_tables, context_lens, *, scale,
+           w_uk=None, w_uv=None, window=0, out=None, lse=None, want_lse=True, workspace=None,
+           num_workgroups=0, flags=0, stream=None):
+    """Absorbed split-KV decode.  q_nope bf16 [B, H, Dn] (or [B, H, R] latent when
+    w_uk is None), q_pe bf16 [B, H, Dr]; block_tables int32 [B, max_blocks];
+    context_lens int32 [B].  Returns (out bf16 [B, H, Dv or R], lse fp32 [B, H])."""
+    B, H = int(q_nope.shape[0]), int(q_nope.shape[1])
+    dn = int(w_uk.shape[1]) if w_uk is not None else 0
+    dv = int(w_uv.shape[1]) if w_uv is not None else cache.kv_lora_rank
+    attn = _attn_struct(H, dn, dv, w_uk, w_uv, scale, window, num_workgroups, flags)
+    st = cache.struct()
+    assert block_tables.dtype == torch.int32 and block_tables.is_contiguous()
+    assert context_lens.dtype == torch.int32 and context_lens.is_contiguous()
+    max_blocks = int(block_tables.shape[1])
+    dev = q_nope.device
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=torch.bfloat16, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    nbytes = int(_decode_ws(ctypes.byref(st), ctypes.byref(attn), B, max_blocks))
+    if nbytes == 0 and B > 0:
+        raise MlaError(MLA_ERR_INVALID_ARGUMENT, "mla_decode_workspace_size")
+    ws = (workspace or Workspace()).get(nbytes, dev)
+    qs_b, qs_h = _row_strides(q_nope)
+    ps_b, ps_h = _row_strides(q_pe)
+    _check(_decode(ctypes.byref(st), layer_idx, ctypes.byref(attn), _ptr(q_nope), qs_b, qs_h,
+                   _ptr(q_pe), ps_b, ps_h, _ptr(block_tables), max_blocks, _ptr(context_lens), B,
+                   _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)), "mla_decode")
+    return out, lse
+
+
+def prefill_chunk(cache: KVCache, layer_idx: int, q_nope, q_pe, query_start_loc, max_q_len,
+                  block_tables, context_lens, *, scale, w_uk=None, w_uv=None, window=0, out=None,
+                  lse=None, want_lse=True, workspace=None, num_workgroups=0, flags=0, stream=None):
+    """Causal chunked prefill.  q_nope bf16 [Tq, H, Dn], q_pe bf16 [Tq, H, Dr];
+    query_start_loc int32 [B + 1]; context_lens int32 [B] (chunk included)."""
+    Tq, H = int(q_nope.shape[0]), int(q_nope.shape[1])
+    B = int(context_lens.shape[0])
+    dn = int(w_uk.shape[1]) if w_uk is not None else 0
+    dv = int(w_uv.shape[1]) if w_uv is not None else cache.kv_lora_rank
+    attn = _attn_struct(H, dn, dv, w_uk, w_uv, scale, window, num_workgroups, flags)
+    st = cache.struct()
+    assert query_start_loc.dtype == torch.int32 and query_start_loc.numel() == B + 1
+    max_blocks = int(block_tables.shape[1])
+    dev = q_nope.device
+    if out is None:
+        out = torch.empty((Tq, H, dv), dtype=torch.bfloat16, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((Tq, H), dtype=torch.float32, device=dev)
+    nbytes = int(_prefill_ws(ctypes.byref(st), ctypes.byref(attn), B, Tq, max_blocks))
+    if nbytes == 0 and Tq > 0:
+        raise MlaError(MLA_ERR_INVALID_ARGUMENT, "mla_prefill_workspace_size")
+    ws = (workspace or Workspace()).get(nbytes, dev)
+    qs_t, qs_h = _row_strides(q_nope)
+    ps_t, ps_h = _row_strides(q_pe)
+    _check(_prefill(ctypes.byref(st), layer_idx, ctypes.byref(attn), _ptr(q_nope), qs_t, qs_h,
+                    _ptr(q_pe), ps_t, ps_h, _ptr(query_start_loc), Tq, int(max_q_len),
+                    _ptr(block_tables), max_blocks, _ptr(context_lens), B, _ptr(out), _ptr(lse),
+                    _ptr(ws), ws.numel(), _stream(stream)), "mla_prefill_chunk")
+    return out, lse
+
+
+def decode_combine(o_part, lse_part, stream=None):
+    """LSE merge: o_part fp32 [S, B, H, D], lse_part fp32 [S, B, H] -> (o [B, H, D], lse [B, H])."""
+    S, B, H, D = (int(x) for x in o_part.shape)
+    assert o_part.dtype == torch.float32 and lse_part.dtype == torch.float32
+    assert o_part.is_contiguous() and lse_part.is_contiguous()
+    o = torch.empty((B, H, D), dtype=torch.float32, device=o_part.device)
+    lse = torch.empty((B, H), dtype=torch.float32, device=o_part.device)
+    _check(_combine(_ptr(o_part), _ptr(lse_part), S, B, H, D, _ptr(o), _ptr(lse), _stream(stream)),
+           "mla_decode_combine")
+    return o, lse

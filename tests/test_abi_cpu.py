@@ -1,0 +1,125 @@
+"""Host-side checks of the C ABI that need no GPU: the library builds and loads,
+it exports every function include/mla.h declares, and argument errors are
+reported before anything is enqueued."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+LIB = os.path.join(ROOT, "paged_mla_latent_write_amd", "libmla.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from paged_mla_latent_write_amd.build import build
+        build()
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    for want in ("mla_write_kv", "mla_decode", "mla_decode_combine", "mla_prefill_chunk",
+                 "mla_decode_workspace_size", "mla_prefill_workspace_size", "mla_status_string"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (mla_\w+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        assert getattr(lib, n) is not None
+
+
+def test_header_compiles_as_c():
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c", HEADER],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_status_strings_and_version():
+    from paged_mla_latent_write_amd import mla
+    assert mla.status_string(0) == "MLA_OK"
+    assert mla.status_string(3) == "MLA_ERR_WORKSPACE"
+    assert mla.status_string(99) == "MLA_ERR_UNKNOWN"
+    assert "gfx950" in mla.version()
+
+
+def _cache(mla, **kw):
+    base = dict(data=0x1000, scale=None, dtype=0, num_layers=2, num_pages=8, page_size=64,
+                kv_lora_rank=512, qk_rope_dim=64)
+    base.update(kw)
+    return mla.MlaCacheStruct(**base)
+
+
+def _attn(mla, **kw):
+    base = dict(num_heads=16, qk_nope_dim=128, v_head_dim=128, w_uk=0x2000, w_uv=0x3000,
+                scale=0.07, window=0, num_workgroups=4, flags=0)
+    base.update(kw)
+    return mla.MlaAttnStruct(**base)
+
+
+def test_argument_validation_without_device():
+    """Every error here is found on the host before any HIP call."""
+    from paged_mla_latent_write_amd import mla
+    byref = ctypes.byref
+    c, a = _cache(mla), _attn(mla)
+    P = ctypes.c_void_p
+    # write_kv
+    assert mla._write_kv(None, 0, P(1), 512, P(1), 64, P(1), 4, None) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert mla._write_kv(byref(c), 2, P(1), 512, P(1), 64, P(1), 4, None) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert mla._write_kv(byref(c), 0, P(1), 512, P(1), 64, P(1), 0, None) == mla.MLA_OK
+    assert mla._write_kv(byref(c), 0, None, 512, P(1), 64, P(1), 4, None) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert mla._write_kv(byref(c), 0, P(1), 100, P(1), 64, P(1), 4, None) == mla.MLA_ERR_INVALID_ARGUMENT
+    bad_ps = _cache(mla, page_size=48)
+    assert mla._write_kv(byref(bad_ps), 0, P(1), 512, P(1), 64, P(1), 4, None) == mla.MLA_ERR_UNSUPPORTED
+    fp8_no_scale = _cache(mla, dtype=1)
+    assert mla._write_kv(byref(fp8_no_scale), 0, P(1), 512, P(1), 64, P(1), 4, None) == mla.MLA_ERR_INVALID_ARGUMENT
+    odd = _cache(mla, kv_lora_rank=500)
+    assert mla._write_kv(byref(odd), 0, P(1), 512, P(1), 64, P(1), 4, None) == mla.MLA_ERR_UNSUPPORTED
+
+    def dec(cache=c, attn=a, layer=0, batch=4, ws=None, ws_bytes=0, q=P(1), bt=P(1), ctx=P(1), out=P(1)):
+        return mla._decode(byref(cache), layer, byref(attn), q, 128 * 16, 128, P(1), 64 * 16, 64, bt,
+                           4, ctx, batch, out, None, ws, ws_bytes, None)
+
+    assert dec(layer=-1) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert dec(batch=0) == mla.MLA_OK
+    assert dec(q=None) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert dec(bt=None) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert dec(out=None) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert dec(attn=_attn(mla, num_heads=0)) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert dec(attn=_attn(mla, scale=float("nan"))) == mla.MLA_ERR_INVALID_ARGUMENT
+    # forced workgroup count: the workspace size needs no device
+    need = mla._decode_ws(byref(c), byref(a), 4, 4)
+    assert need > 0
+    assert dec(ws=None) == mla.MLA_ERR_WORKSPACE
+    assert dec(ws=P(0x10000), ws_bytes=need - 1) == mla.MLA_ERR_WORKSPACE
+    assert dec(ws=P(0x10001), ws_bytes=need + 1024) == mla.MLA_ERR_WORKSPACE  # misaligned
+    # workspace grows with batch and with the forced workgroup count
+    assert mla._decode_ws(byref(c), byref(a), 8, 4) > need
+    assert mla._decode_ws(byref(c), byref(_attn(mla, num_workgroups=64)), 4, 4) > need
+    # no W_UK: no q_lat region
+    assert mla._decode_ws(byref(c), byref(_attn(mla, w_uk=None)), 4, 4) < need
+    assert mla._decode_ws(byref(c), byref(a), -1, 4) == 0
+    # prefill
+    assert mla._prefill_ws(byref(c), byref(a), 2, 100, 4) > 0
+    assert mla._prefill(byref(c), 0, byref(a), P(1), 1, 1, P(1), 1, 1, None, 10, 5, P(1), 4, P(1), 2,
+                        P(1), None, P(0x10000), 1 << 30, None) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert mla._prefill(byref(c), 0, byref(a), P(1), 1, 1, P(1), 1, 1, P(1), -1, 5, P(1), 4, P(1), 2,
+                        P(1), None, P(0x10000), 1 << 30, None) == mla.MLA_ERR_INVALID_ARGUMENT
+    # combine
+    assert mla._combine(P(1), P(1), 2, 0, 4, 8, P(1), P(1), None) == mla.MLA_OK
+    assert mla._combine(None, P(1), 2, 1, 4, 8, P(1), P(1), None) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert mla._combine(P(1), P(1), -1, 1, 4, 8, P(1), P(1), None) == mla.MLA_ERR_INVALID_ARGUMENT

@@ -1,0 +1,371 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the
+same seeded inputs.  Writes are compared bit for bit; attention outputs within
+max-abs 2e-2 / rel-L2 5e-3 (bf16 cache) or 0.1 / 3e-2 (fp8 cache), over the
+call's output tensor (or, at full sizes, over sampled requests and rows)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mla_oracle as O
+from paged_mla_latent_write_amd import workloads as W
+
+from gpu_support import (BF16_TOL, FP8_TOL, assert_close, assert_lse_close, bf16_host_bits,
+                         bf16_host_f64, dev, dev_bf16, gpu_decode, host_cache, new_device_cache,
+                         oracle_decode, populate_device, say, weights)
+
+pytestmark = pytest.mark.gpu
+
+# lse has no stated tolerance; these are about 8 standard deviations of the
+# error that rounding q_lat to bf16 puts into the scores in the sharp regime.
+LSE_ATOL = {O.KV_BF16: 2e-2, O.KV_FP8: 5e-2}
+
+
+@pytest.fixture(scope="module")
+def mla():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from paged_mla_latent_write_amd import mla as m
+    return m
+
+
+def tol_for(case):
+    return FP8_TOL if case.kv_dtype == O.KV_FP8 else BF16_TOL
+
+
+# ---------------------------------------------------------------------------
+# mla_write_kv: bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kv_dtype", [O.KV_BF16, O.KV_FP8])
+def test_write_kv_bit_exact_with_pads_layers_and_overwrite(mla, kv_dtype):
+    say(f"write_kv bit-exact {kv_dtype}")
+    d = W.Dims(H=4, R=512, Dr=64, Dn=128, Dv=128, page_size=16)
+    case = W.custom(d, [5, 40, 77], seed=101, kv_dtype=kv_dtype, num_layers=3, layer=1)
+    # pad rows interleaved with real ones
+    T = case.ctx_slots.size
+    slots = case.ctx_slots.copy()
+    slots[::7] = -1
+    cache = new_device_cache(mla, 3, case.num_pages, d, kv_dtype)
+    mla.write_kv(cache, 1, dev_bf16(case.ctx_c_kv), dev_bf16(case.ctx_k_pe), dev(slots))
+    # overwrite the first few live tokens with new values
+    rng = np.random.default_rng(5)
+    new_c = W.bf16_normal(rng, (4, d.R), 0.3)
+    new_r = W.bf16_normal(rng, (4, d.Dr), 0.3)
+    live = np.nonzero(slots >= 0)[0][:4]
+    mla.write_kv(cache, 1, dev_bf16(new_c), dev_bf16(new_r), dev(slots[live]))
+    torch.cuda.synchronize()
+
+    fill = W.BF16_NAN if kv_dtype == O.KV_BF16 else W.E4M3_NAN
+    dt = np.uint16 if kv_dtype == O.KV_BF16 else np.uint8
+    hc = np.full((3, case.num_pages, d.page_size, d.D), fill, dtype=dt)
+    hs = np.full((3, case.num_pages, d.page_size), np.nan, dtype=np.float32)
+    O.write_kv(hc, hs, 1, case.ctx_c_kv, case.ctx_k_pe, slots, kv_dtype)
+    O.write_kv(hc, hs, 1, new_c, new_r, slots[live], kv_dtype)
+    if kv_dtype == O.KV_BF16:
+        got = bf16_host_bits(cache.data)
+    else:
+        got = cache.data.cpu().numpy()
+        gs = cache.scale.cpu().numpy()
+        assert np.array_equal(gs.view(np.uint32), hs.view(np.uint32)), "fp8 scales differ"
+    assert got.shape == hc.shape
+    assert np.array_equal(got, hc), f"{int((got != hc).sum())} cache elements differ"
+    assert T > 0
+
+
+def test_write_fp8_full_size_sampled_rows(mla):
+    """fp8 quantisation at the V3 fp8 workload's size: every token written, a
+    sample of 1/16 of them compared byte for byte (codes and scales)."""
+    say("write_kv fp8 v3fp8 population")
+    case = W.v3fp8()
+    cache = populate_device(mla, case)
+    idx = np.arange(0, case.ctx_slots.size, 16)
+    codes, scl = O.fp8_quantize_tokens(np.concatenate([case.ctx_c_kv[idx], case.ctx_k_pe[idx]], axis=1))
+    s = torch.from_numpy(case.ctx_slots[idx]).cuda()
+    ps = case.dims.page_size
+    got = cache.data[0].view(-1, case.dims.D)[s].cpu().numpy()
+    gs = cache.scale[0].reshape(-1)[s].cpu().numpy()
+    assert np.array_equal(got, codes)
+    assert np.array_equal(gs.view(np.uint32), scl.view(np.uint32))
+    assert ps == 64
+
+
+def test_write_fp8_codec_edges(mla):
+    """Values at every E4M3 midpoint, the saturation bound and zeros, written
+    through the fp8 cache (one token per row, scale forced to 1 by amax 448)."""
+    say("write_kv fp8 codec edges")
+    mags = O.E4M3_TABLE[:0x7F]
+    mids = ((mags[:-1] + mags[1:]) / 2).astype(np.float32)
+    vals = np.concatenate([mids, -mids, O.E4M3_TABLE[:0x7F].astype(np.float32), [0.0, -0.0]])
+    # only bf16-representable values survive the bf16 input; keep those
+    bits = W.f32_to_bf16_bits(vals)
+    keep = O.bf16_bits_to_f32(bits) == vals
+    vals = vals[keep]
+    D = 64
+    n_val = (len(vals) + D - 2) // (D - 1)
+    n_tok = n_val + 2
+    rows = np.zeros((n_tok, D), dtype=np.float32)
+    flat = np.concatenate([vals, np.zeros(n_val * (D - 1) - len(vals), np.float32)])
+    rows[2:, 1:] = flat.reshape(n_val, D - 1)
+    rows[2:, 0] = 448.0  # amax 448 -> scale exactly 1
+    rows[1, 0] = 448.0
+    rows[1, 1:] = -0.0   # signed zeros keep their sign
+    # row 0 stays all zero: scale 1.0, codes 0
+    row_bits = W.f32_to_bf16_bits(rows)
+    d = W.Dims(H=1, R=48, Dr=16, Dn=8, Dv=8, page_size=16)
+    cache = new_device_cache(mla, 1, (n_tok + 15) // 16 + 1, d, O.KV_FP8)
+    slots = np.arange(n_tok, dtype=np.int64)
+    mla.write_kv(cache, 0, dev_bf16(row_bits[:, :48]), dev_bf16(row_bits[:, 48:]), dev(slots))
+    torch.cuda.synchronize()
+    codes, scl = O.fp8_quantize_tokens(row_bits)
+    got = cache.data[0].view(-1, D)[:n_tok].cpu().numpy()
+    gs = cache.scale[0].reshape(-1)[:n_tok].cpu().numpy()
+    assert np.array_equal(gs.view(np.uint32), scl.view(np.uint32))
+    assert np.array_equal(got, codes)
+
+
+# ---------------------------------------------------------------------------
+# Decode
+# ---------------------------------------------------------------------------
+
+def check_decode(mla, case, requests=None, flags=0, num_workgroups=0, tol=None, label=""):
+    cache = populate_device(mla, case)
+    out, lse = gpu_decode(mla, case, cache, flags=flags, num_workgroups=num_workgroups)
+    hc = host_cache(case)
+    ref, ref_lse = oracle_decode(case, hc, requests=requests)
+    sel = slice(None) if requests is None else list(requests)
+    got = bf16_host_f64(out)[sel]
+    assert_close(got, ref[sel], tol or tol_for(case), f"{case.name}{label} out")
+    assert_lse_close(lse.cpu().numpy()[sel], ref_lse[sel], LSE_ATOL[case.kv_dtype], f"{case.name}{label} lse")
+    return cache, out, lse
+
+
+@pytest.mark.parametrize("sharp", [False, True])
+def test_decode_tiny(mla, sharp):
+    say(f"decode tiny sharp={sharp}")
+    check_decode(mla, W.tiny(sharp=sharp))
+
+
+@pytest.mark.parametrize("flags", [0, 1])
+@pytest.mark.parametrize("sharp", [False, True])
+def test_decode_v2lite(mla, sharp, flags):
+    say(f"decode v2lite sharp={sharp} flags={flags}")
+    check_decode(mla, W.v2lite(sharp=sharp), flags=flags)
+
+
+def v3_sample(case):
+    ctx = case.context_lens
+    return sorted({0, int(np.argmax(ctx)), int(np.argmin(ctx)), 17, 33, case.batch - 1})
+
+
+@pytest.mark.parametrize("sharp", [False, True])
+def test_decode_v3_full_size(mla, sharp):
+    say(f"decode v3 sharp={sharp}")
+    case = W.v3(sharp=sharp)
+    check_decode(mla, case, requests=v3_sample(case))
+
+
+def test_decode_v3fp8_full_size(mla):
+    say("decode v3fp8 sharp")
+    case = W.v3fp8(sharp=True)
+    check_decode(mla, case, requests=[0, 5, 64, 127])
+
+
+@pytest.mark.parametrize("G", [1, 3, 7, 1000])
+def test_decode_forced_partitions(mla, G):
+    """The split plan: any workgroup count gives the oracle's answer."""
+    say(f"decode forced G={G}")
+    d = W.Dims(H=16, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
+    case = W.custom(d, [1, 31, 32, 33, 64, 65, 700, 2049], seed=201, sharp=True)
+    check_decode(mla, case, num_workgroups=G, label=f" G={G}")
+
+
+@pytest.mark.parametrize("window", [1, 2, 31, 32, 33, 128, 5000])
+def test_decode_windows(mla, window):
+    say(f"decode window={window}")
+    d = W.Dims(H=16, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
+    case = W.custom(d, [1, 2, 100, 129, 1000, 4097], seed=300 + window, sharp=True, window=window)
+    check_decode(mla, case)
+
+
+@pytest.mark.parametrize("ps", [16, 32, 128])
+def test_decode_page_sizes(mla, ps):
+    say(f"decode page size {ps}")
+    d = W.Dims(H=32, R=512, Dr=64, Dn=128, Dv=128, page_size=ps)
+    case = W.custom(d, [3, 200, 1111], seed=400 + ps, sharp=True)
+    check_decode(mla, case)
+
+
+def test_decode_edge_contexts(mla):
+    """n = 0 (out 0, lse -inf), n = 1 (the token's value), mixed in one batch."""
+    say("decode edge contexts")
+    d = W.Dims(H=16, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
+    case = W.custom(d, [0, 1, 2, 0, 64], seed=500, sharp=True)
+    cache, out, lse = check_decode(mla, case)
+    o = bf16_host_f64(out)
+    assert (o[0] == 0).all() and (o[3] == 0).all()
+    assert np.isneginf(lse.cpu().numpy()[[0, 3]]).all()
+
+
+def test_decode_page_permutation_bitwise(mla):
+    """Physical page placement does not change a single output bit."""
+    say("decode page permutation")
+    d = W.Dims(H=128, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
+    base = W.custom(d, [100, 3000, 777], seed=600, sharp=True)
+    outs = []
+    for perm_seed in (1, 2):
+        rng = np.random.default_rng(perm_seed)
+        bt, npg, _ = W.assign_pages(rng, base.context_lens, 64, num_pages=base.num_pages + 5)
+        c = W.Case(**{**base.__dict__, "block_tables": bt, "num_pages": npg,
+                      "ctx_slots": W.slots_for(bt, base.context_lens, 64)})
+        cache = populate_device(mla, c)
+        out, lse = gpu_decode(mla, c, cache)
+        outs.append((bf16_host_bits(out), lse.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0])
+    assert np.array_equal(outs[0][1], outs[1][1])
+
+
+def test_decode_latent_io_and_needle(mla):
+    """No W_UK / W_UV (latent query in, latent output out) and a needle query:
+    the output is the needle token's latent."""
+    say("decode latent io + needle")
+    d = W.Dims(H=32, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
+    case = W.custom(d, [300, 41], seed=700)
+    cache = populate_device(mla, case)
+    j = 123
+    c_j = O.bf16_bits_to_f64(case.ctx_c_kv[j])
+    q_lat = np.zeros((2, d.H, d.R))
+    q_lat[0] = 40.0 / (case.scale * (c_j @ c_j)) * c_j  # score gap >> 30 against the others
+    q_bits = W.f32_to_bf16_bits(q_lat.astype(np.float32))
+    out, lse = mla.decode(cache, 0, dev_bf16(q_bits), dev_bf16(case.q_pe), dev(case.block_tables),
+                          dev(case.context_lens), scale=case.scale)
+    torch.cuda.synchronize()
+    hc = host_cache(case)
+    ref, _ = O.decode(hc[0], hc[1], case.kv_dtype, 0, q_bits, case.q_pe, case.block_tables,
+                      case.context_lens, None, None, case.scale, 0)
+    assert_close(bf16_host_f64(out), ref, BF16_TOL, "latent io")
+    assert np.max(np.abs(bf16_host_f64(out)[0] - c_j[None, :])) < 2e-2
+
+
+# ---------------------------------------------------------------------------
+# Combine
+# ---------------------------------------------------------------------------
+
+def test_decode_combine_abi(mla):
+    say("decode_combine")
+    rng = np.random.default_rng(9)
+    S, B, H, D = 5, 3, 4, 64
+    o = rng.normal(size=(S, B, H, D)).astype(np.float32)
+    lse = rng.normal(scale=3, size=(S, B, H)).astype(np.float32)
+    lse[1, 0, :] = -np.inf
+    o[1, 0, :] = np.nan          # empty partials are not read
+    lse[:, 2, 1] = -np.inf       # a row with nothing at all
+    go, gl = mla.decode_combine(dev(o), dev(lse))
+    torch.cuda.synchronize()
+    ro, rl = O.combine(o, lse)
+    assert np.max(np.abs(go.cpu().numpy() - ro)) < 1e-5
+    gl = gl.cpu().numpy()
+    assert np.isneginf(gl[2, 1]) and np.isneginf(rl[2, 1])
+    m = ~np.isneginf(rl)
+    assert np.max(np.abs(gl[m] - rl[m])) < 1e-5
+    assert (go.cpu().numpy()[2, 1] == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# Prefill
+# ---------------------------------------------------------------------------
+
+def check_prefill(mla, case, rows=None, flags=0, num_workgroups=0, label=""):
+    cache = populate_device(mla, case)
+    w_uk, w_uv = weights(case)
+    out, lse = mla.prefill_chunk(cache, case.layer, dev_bf16(case.q_nope), dev_bf16(case.q_pe),
+                                 dev(case.query_start_loc),
+                                 int(np.max(np.diff(case.query_start_loc))), dev(case.block_tables),
+                                 dev(case.context_lens), scale=case.scale, w_uk=w_uk, w_uv=w_uv,
+                                 window=case.window, flags=flags, num_workgroups=num_workgroups)
+    torch.cuda.synchronize()
+    hc, hs = host_cache(case)
+    ref, ref_lse = O.prefill_chunk(hc, hs, case.kv_dtype, 0, case.q_nope, case.q_pe,
+                                   case.query_start_loc, case.block_tables, case.context_lens,
+                                   case.w_uk, case.w_uv, case.scale, case.window, rows=rows)
+    sel = slice(None) if rows is None else list(rows)
+    assert_close(bf16_host_f64(out)[sel], ref[sel], tol_for(case), f"prefill{label}")
+    assert_lse_close(lse.cpu().numpy()[sel], ref_lse[sel], LSE_ATOL[case.kv_dtype], f"prefill{label} lse")
+    return out, lse
+
+
+@pytest.mark.parametrize("window", [0, 3, 64])
+@pytest.mark.parametrize("flags", [0, 1])
+def test_prefill_small(mla, window, flags):
+    say(f"prefill small window={window} flags={flags}")
+    d = W.Dims(H=16, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
+    case = W.prefill_case(d, [0, 5, 100, 64], [7, 1, 70, 33], seed=800 + window, window=window,
+                          sharp=True)
+    check_prefill(mla, case, flags=flags, label=f" w={window}")
+
+
+def test_prefill_tiny_dims(mla):
+    say("prefill tiny dims")
+    case = W.prefill_case(W.TINY_DIMS, [10, 0], [27, 5], seed=810, sharp=True,
+                          stds=W.Stds(0.5, 0.5, 0.5, 0.5, 0.5), scale=1 / math.sqrt(48))
+    check_prefill(mla, case)
+
+
+def test_prefill_rows_match_decode_on_gpu(mla):
+    """A prefill row and the decode of the same position agree to the tolerance."""
+    say("prefill row vs decode")
+    d = W.Dims(H=128, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
+    case = W.prefill_case(d, [300], [40], seed=820, sharp=True)
+    out, _ = check_prefill(mla, case)
+    cache = populate_device(mla, case)
+    w_uk, w_uv = weights(case)
+    r = 17
+    dout, _ = mla.decode(cache, 0, dev_bf16(case.q_nope[[r]]), dev_bf16(case.q_pe[[r]]),
+                         dev(case.block_tables), dev(np.array([300 + r + 1], np.int32)),
+                         scale=case.scale, w_uk=w_uk, w_uv=w_uv)
+    torch.cuda.synchronize()
+    a, b = bf16_host_f64(out)[r], bf16_host_f64(dout)[0]
+    assert np.max(np.abs(a - b)) < 2e-2
+
+
+# ---------------------------------------------------------------------------
+# Mixed batch with sliding window (4-layer cache)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("layer", [0, 1])
+def test_mixed_step_full_size(mla, layer):
+    """Per layer: write the step's 4216 new tokens, prefill the 8 chunks, decode
+    the 120 single-token requests.  Sampled rows against the oracle."""
+    say(f"mixed step layer {layer}")
+    ml = W.mixed(layer, sharp=True)
+    d = ml.dims
+    cache = new_device_cache(mla, ml.num_layers, ml.num_pages, d, O.KV_BF16)
+    mla.write_kv(cache, layer, dev_bf16(ml.pre_c_kv), dev_bf16(ml.pre_k_pe), dev(ml.pre_slots))
+    mla.write_kv(cache, layer, dev_bf16(ml.new_c_kv), dev_bf16(ml.new_k_pe), dev(ml.new_slots))
+    w_uk, w_uv = dev_bf16(ml.w_uk), dev_bf16(ml.w_uv)
+    P = ml.n_prefill
+    bt = dev(ml.block_tables)
+    ctx = dev(ml.context_lens)
+    pout, plse = mla.prefill_chunk(cache, layer, dev_bf16(ml.q_nope_p), dev_bf16(ml.q_pe_p),
+                                   dev(ml.query_start_loc), 512, bt[:P], ctx[:P], scale=ml.scale,
+                                   w_uk=w_uk, w_uv=w_uv, window=ml.window)
+    dout, dlse = mla.decode(cache, layer, dev_bf16(ml.q_nope_d), dev_bf16(ml.q_pe_d), bt[P:], ctx[P:],
+                            scale=ml.scale, w_uk=w_uk, w_uv=w_uv, window=ml.window)
+    torch.cuda.synchronize()
+    hc = np.full((1, ml.num_pages, 64, d.D), W.BF16_NAN, dtype=np.uint16)
+    hs = np.full((1, ml.num_pages, 64), np.nan, dtype=np.float32)
+    O.write_kv(hc, hs, 0, ml.pre_c_kv, ml.pre_k_pe, ml.pre_slots)
+    O.write_kv(hc, hs, 0, ml.new_c_kv, ml.new_k_pe, ml.new_slots)
+    rows = sorted({0, 1, 255, 511, 512, 1500, 2047, 3000, 4095})
+    ref, ref_lse = O.prefill_chunk(hc, hs, O.KV_BF16, 0, ml.q_nope_p, ml.q_pe_p, ml.query_start_loc,
+                                   ml.block_tables[:P], ml.context_lens[:P], ml.w_uk, ml.w_uv,
+                                   ml.scale, ml.window, rows=rows)
+    assert_close(bf16_host_f64(pout)[rows], ref[rows], BF16_TOL, f"mixed L{layer} prefill")
+    assert_lse_close(plse.cpu().numpy()[rows], ref_lse[rows], LSE_ATOL[O.KV_BF16])
+    reqs = [0, 7, 50, 119]
+    dref, dref_lse = O.decode(hc, hs, O.KV_BF16, 0, ml.q_nope_d, ml.q_pe_d, ml.block_tables[P:],
+                              ml.context_lens[P:], ml.w_uk, ml.w_uv, ml.scale, ml.window,
+                              requests=reqs)
+    assert_close(bf16_host_f64(dout)[reqs], dref[reqs], BF16_TOL, f"mixed L{layer} decode")
+    assert_lse_close(dlse.cpu().numpy()[reqs], dref_lse[reqs], LSE_ATOL[O.KV_BF16])
