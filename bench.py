@@ -1,0 +1,207 @@
+"""Benchmark: paged MLA decode on one MI355X, DeepSeek-V3 shape, bf16 cache.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3]
+
+A step is one decode step of the whole hot path for a batch: mla_write_kv of
+the batch's newest tokens (write-then-attend) followed by mla_decode (absorb,
+device-side split plan, split-KV attention, combine, up-projection).  Inputs
+are seeded synthetic data with the V3 shape (128 heads, kv_lora_rank 512 +
+qk_rope 64, page size 64, batch 64, contexts uniform in [1024, 32768],
+shuffled block tables), resident in HBM before the timed region.  K steps are
+timed back to back between two device synchronisations; the KV working set
+(about 1.25 GB) is five times the 256 MB Infinity Cache, so no cache flush is
+needed between steps.
+
+One JSON line is printed.  `value` is attended KV tokens per second for the
+whole job.  `roofline` is for the dominant kernel (the split-KV attention
+kernel), timed live with HIP events recorded around it on the call's stream:
+achieved = algorithmic bytes per launch (attended tokens x (R + Dr) x 2 B) /
+mean launch time, against the 8 TB/s HBM peak.  `cpu_baseline` times the fp64
+oracle (numpy, absorbed form) on a bounded sample of the same requests; its
+outputs are also compared with the GPU's.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+METRIC = "paged MLA decode attended-KV-tokens/s + HBM GB/s % peak, V3 shape bf16"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="v3", choices=["v3", "v3fp8", "v2lite"])
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="CPU time budget for the oracle baseline sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--generic", action="store_true", help="force the plain (non-MFMA) kernels")
+    return p.parse_args()
+
+
+def cpu_baseline(case, budget_s, gpu_out_f64):
+    """Time the oracle on requests taken in order until the budget is spent."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import mla_oracle as O
+
+    ps, D = case.dims.page_size, case.dims.D
+    hc = np.full((1, case.num_pages, ps, D), 0, dtype=np.uint16 if case.kv_dtype == "bf16" else np.uint8)
+    hs = np.ones((1, case.num_pages, ps), dtype=np.float32)
+    t0 = time.perf_counter()
+    O.write_kv(hc, hs, 0, case.ctx_c_kv, case.ctx_k_pe, case.ctx_slots, case.kv_dtype)
+    write_s = time.perf_counter() - t0
+    done, tokens, elapsed = [], 0, 0.0
+    outs = []
+    while len(done) < case.batch and (elapsed < budget_s or len(done) < 1):
+        b = len(done)
+        t0 = time.perf_counter()
+        out, _ = O.decode(hc, hs, case.kv_dtype, 0, case.q_nope, case.q_pe, case.block_tables,
+                          case.context_lens, case.w_uk, case.w_uv, case.scale, case.window,
+                          requests=[b])
+        elapsed += time.perf_counter() - t0
+        outs.append(out[b])
+        done.append(b)
+        tokens += int(case.context_lens[b])
+    threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] + [1])
+    ref = np.stack(outs)
+    got = gpu_out_f64[done]
+    err = {"max_abs": float(np.max(np.abs(got - ref))),
+           "rel_l2": float(np.linalg.norm(got - ref) / np.linalg.norm(ref))}
+    return {"value": tokens / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 numpy oracle (absorbed form) on the first {len(done)} of {case.batch} "
+                      f"requests ({tokens} attended tokens, {elapsed:.1f} s); cache write "
+                      f"{write_s:.1f} s untimed"}, err
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(multi-GPU sharding is described, not built)"}))
+        sys.exit(2)
+    import torch
+
+    from paged_mla_latent_write_amd import mla
+    from paged_mla_latent_write_amd import workloads as W
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    case = {"v3": W.v3, "v3fp8": W.v3fp8, "v2lite": W.v2lite}[args.workload]()
+    d = case.dims
+    B = case.batch
+
+    def bf16(u16):
+        return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    fp8 = case.kv_dtype != "bf16"
+    cache = mla.KVCache.empty(case.num_layers, case.num_pages, d.page_size, d.R, d.Dr, fp8=fp8)
+    if fp8:
+        cache.data.fill_(0x7F)
+        cache.scale.fill_(float("nan"))
+    else:
+        cache.data.view(torch.int16).fill_(0x7FC0)
+    mla.write_kv(cache, case.layer, bf16(case.ctx_c_kv), bf16(case.ctx_k_pe),
+                 torch.from_numpy(case.ctx_slots).to(dev))
+    newest = case.new_token_rows()
+    new_c, new_r = bf16(case.ctx_c_kv[newest]), bf16(case.ctx_k_pe[newest])
+    new_slots = torch.from_numpy(case.ctx_slots[newest]).to(dev)
+    q_nope, q_pe = bf16(case.q_nope), bf16(case.q_pe)
+    w_uk, w_uv = bf16(case.w_uk), bf16(case.w_uv)
+    bt = torch.from_numpy(case.block_tables).to(dev)
+    ctx = torch.from_numpy(case.context_lens).to(dev)
+    out = torch.empty((B, d.H, d.Dv), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, d.H), dtype=torch.float32, device=dev)
+    ws = mla.Workspace()
+    flags = mla.MLA_FLAG_GENERIC_KERNELS if args.generic else 0
+    K = args.steps
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(K)]
+    for a, b in events:  # torch creates its events lazily, at the first record
+        a.record()
+        b.record()
+
+    def step(ev=None):
+        mla.write_kv(cache, case.layer, new_c, new_r, new_slots)
+        mla.decode(cache, case.layer, q_nope, q_pe, bt, ctx, scale=case.scale, w_uk=w_uk, w_uv=w_uv,
+                   window=case.window, out=out, lse=lse, workspace=ws, flags=flags,
+                   kernel_events=ev)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] {args.workload}: warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    print(f"[bench] timed {K} steps: {wall * 1e3 / K:.3f} ms/step, attention kernel {kern_ms:.3f} ms",
+          file=sys.stderr, flush=True)
+
+    tokens = int(case.context_lens.astype(np.int64).sum())
+    per_tok_bytes = d.D * (1 if fp8 else 2) + (4 if fp8 else 0)
+    kv_bytes = tokens * per_tok_bytes
+    flops = tokens * 2 * d.H * (2 * d.R + d.Dr)
+    fixed_bytes = 2 * d.H * d.Dn * d.R * 2 + B * d.H * (d.Dn + d.Dr + d.Dv) * 2
+    step_s = wall / K
+    achieved = kv_bytes / (kern_ms * 1e-3) / 1e9
+    gpu_out = None
+    from oracle import mla_oracle as O  # noqa: E402  (CPU-baseline leg only)
+    gpu_out = O.bf16_bits_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16))
+    line = {
+        "metric": METRIC,
+        "value": tokens * K / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if not fp8 else "fp8_e4m3 cache, bf16 compute",
+        "data": "synthetic (seeded; N(0,1)/sqrt(dim) latents and queries, random-init W_UK/W_UV)",
+        "config": {
+            "workload": {"v3": "DeepSeek-V3-shape MLA decode, one GPU's full head set",
+                         "v3fp8": "V3-shape MLA decode with fp8 e4m3 latent cache",
+                         "v2lite": "DeepSeek-V2-Lite-shape MLA decode"}[args.workload],
+            "batch": B, "heads": d.H, "kv_lora_rank": d.R, "qk_rope": d.Dr, "qk_nope": d.Dn,
+            "v_head": d.Dv, "page_size": d.page_size,
+            "context_lens": f"{int(case.context_lens.min())}..{int(case.context_lens.max())}",
+            "attended_tokens": tokens, "kv_cache": case.kv_dtype,
+            "step": "mla_write_kv(batch newest tokens) + mla_decode",
+            "kernels": "generic" if args.generic else "default",
+        },
+        "step_hbm_gbs": (kv_bytes + fixed_bytes) / step_s / 1e9,
+        "step_tflops": flops / step_s / 1e12,
+        "step_frac_of_hbm_roofline": (kv_bytes + fixed_bytes) / step_s / 1e9 / HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "split-KV attention", "kernel_ms": kern_ms,
+                     "alg_bytes_per_launch": kv_bytes,
+                     "mfma_tflops": flops / (kern_ms * 1e-3) / 1e12},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        base, err = cpu_baseline(case, args.cpu_seconds, gpu_out)
+        line["cpu_baseline"] = base
+        line["parity_sample"] = err
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -94,6 +94,10 @@ typedef struct {
  *          convention, this one keeps exactly min(w, p + 1) keys).
  *   num_workgroups: 0 = one workgroup per compute unit for the split-KV work
  *          partition; > 0 forces that many (testing).
+ *   kernel_events: optional pair of hipEvent_t (either may be NULL).  When
+ *          set, [0] is recorded on the call's stream just before the split-KV
+ *          attention kernel and [1] just after it, so a caller can time that
+ *          kernel alone (profiling).
  */
 typedef struct {
   int32_t num_heads;
@@ -105,6 +109,7 @@ typedef struct {
   int32_t window;
   int32_t num_workgroups;
   uint32_t flags;
+  void* kernel_events[2];
 } mla_attn;
 
 /*

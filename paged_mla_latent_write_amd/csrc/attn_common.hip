@@ -83,52 +83,62 @@ __global__ __launch_bounds__(kPlanThreads) void plan_items_kernel(
   if (tid == 0) tile_start[Nq] = carry;
 }
 
-// One block per item.  Items whose tiles all fell to one workgroup were
+// One wave per (item, head).  Items whose tiles all fell to one workgroup were
 // finished by the attention kernel; empty items get o = 0, lse = -inf; cut
 // items are merged from the partial slots of the workgroups that cover them
-// (slot 2g+1 for the first, which the item starts in, slot 2g after it).
+// (slot 2g+1 for the first, which the item starts in, slot 2g after it).  The
+// merged row is written normalised (its o_scale set to 1).
 __global__ __launch_bounds__(256) void combine_segments_kernel(AttnArgs a) {
   const int i = blockIdx.x;
-  const int64_t ts = a.tile_start[i], te = a.tile_start[i + 1];
+  const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   const int H = a.H, R = a.kv.R;
-  const int tid = threadIdx.x;
+  if (h >= H) return;
+  const int64_t ts = a.tile_start[i], te = a.tile_start[i + 1];
+  const int64_t row = static_cast<int64_t>(i) * H + h;
+  float* dst = a.o_lat + row * R;
   if (ts == te) {
-    for (int idx = tid; idx < H * R; idx += blockDim.x) a.o_lat[static_cast<int64_t>(i) * H * R + idx] = 0.f;
-    for (int h = tid; h < H; h += blockDim.x) a.lse[static_cast<int64_t>(i) * H + h] = -INFINITY;
+    for (int r = lane; r < R; r += 64) dst[r] = 0.f;
+    if (lane == 0) {
+      a.lse[row] = -INFINITY;
+      a.o_scale[row] = 1.f;
+    }
     return;
   }
   const int64_t W = a.tile_start[a.num_items];
   const int64_t G = a.G;
   const int64_t g0 = wg_of_tile(ts, W, G), g1 = wg_of_tile(te - 1, W, G);
   if (g0 == g1) return;
-  for (int h = 0; h < H; ++h) {
-    // every thread computes the head's merged lse (few segments, cheap)
-    float mx = -INFINITY;
-    for (int64_t g = g0; g <= g1; ++g) {
-      if (wg_tile_begin(g, W, G) == wg_tile_begin(g + 1, W, G)) continue;
-      const int64_t slot = (g == g0) ? 2 * g + 1 : 2 * g;
-      mx = fmaxf(mx, a.part_lse[slot * H + h]);
-    }
-    float tot = 0.f;
+  float mx = -INFINITY;
+  for (int64_t g = g0; g <= g1; ++g) {
+    if (wg_tile_begin(g, W, G) == wg_tile_begin(g + 1, W, G)) continue;
+    const int64_t slot = (g == g0) ? 2 * g + 1 : 2 * g;
+    mx = fmaxf(mx, a.part_lse[slot * H + h]);
+  }
+  float tot = 0.f;
+  for (int64_t g = g0; g <= g1; ++g) {
+    if (wg_tile_begin(g, W, G) == wg_tile_begin(g + 1, W, G)) continue;
+    const int64_t slot = (g == g0) ? 2 * g + 1 : 2 * g;
+    const float l = a.part_lse[slot * H + h];
+    tot += (l == -INFINITY) ? 0.f : expf(l - mx);
+  }
+  const float inv_tot = 1.f / tot;
+  for (int r0 = 0; r0 < R; r0 += 64) {
+    const int r = r0 + lane;
+    if (r >= R) break;
+    float acc = 0.f;
     for (int64_t g = g0; g <= g1; ++g) {
       if (wg_tile_begin(g, W, G) == wg_tile_begin(g + 1, W, G)) continue;
       const int64_t slot = (g == g0) ? 2 * g + 1 : 2 * g;
       const float l = a.part_lse[slot * H + h];
-      tot += (l == -INFINITY) ? 0.f : expf(l - mx);
+      if (l == -INFINITY) continue;
+      acc += expf(l - mx) * a.part_scale[slot * H + h] * a.part_o[(slot * H + h) * R + r];
     }
-    float* dst = a.o_lat + (static_cast<int64_t>(i) * H + h) * R;
-    for (int r = tid; r < R; r += blockDim.x) {
-      float acc = 0.f;
-      for (int64_t g = g0; g <= g1; ++g) {
-        if (wg_tile_begin(g, W, G) == wg_tile_begin(g + 1, W, G)) continue;
-        const int64_t slot = (g == g0) ? 2 * g + 1 : 2 * g;
-        const float l = a.part_lse[slot * H + h];
-        if (l == -INFINITY) continue;
-        acc += expf(l - mx) * a.part_o[(slot * H + h) * R + r];
-      }
-      dst[r] = acc / tot;
-    }
-    if (tid == 0) a.lse[static_cast<int64_t>(i) * H + h] = mx + logf(tot);
+    dst[r] = acc * inv_tot;
+  }
+  if (lane == 0) {
+    a.lse[row] = mx + logf(tot);
+    a.o_scale[row] = 1.f;
   }
 }
 
@@ -201,6 +211,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
 // Block: one head, 16 items; a wave handles one output column v at a time,
 // its lanes splitting r.
 __global__ __launch_bounds__(256) void up_project_kernel(const float* __restrict__ o_lat,
+                                                          const float* __restrict__ o_scale,
                                                           const uint16_t* __restrict__ w_uv,
                                                           int32_t Nq, int32_t H, int32_t R,
                                                           int32_t Dv, uint16_t* __restrict__ out) {
@@ -210,7 +221,8 @@ __global__ __launch_bounds__(256) void up_project_kernel(const float* __restrict
   const int ni = min(kGemmItems, Nq - i0);
   for (int idx = threadIdx.x; idx < kGemmItems * R; idx += blockDim.x) {
     const int it = idx / R, r = idx % R;
-    os[idx] = it < ni ? o_lat[(static_cast<int64_t>(i0 + it) * H + h) * R + r] : 0.f;
+    const int64_t row = static_cast<int64_t>(i0 + it) * H + h;
+    os[idx] = it < ni ? o_lat[row * R + r] * o_scale[row] : 0.f;
   }
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -236,10 +248,11 @@ __global__ __launch_bounds__(256) void up_project_kernel(const float* __restrict
 }
 
 __global__ __launch_bounds__(256) void latent_out_kernel(const float* __restrict__ o_lat,
-                                                          int64_t count,
+                                                          const float* __restrict__ o_scale,
+                                                          int64_t count, int32_t R,
                                                           uint16_t* __restrict__ out) {
   for (int64_t k = blockIdx.x * 256ll + threadIdx.x; k < count; k += 256ll * gridDim.x)
-    out[k] = f32_to_bf16(o_lat[k]);
+    out[k] = f32_to_bf16(o_lat[k] * o_scale[k / R]);
 }
 
 }  // namespace
@@ -255,7 +268,7 @@ hipError_t launch_plan(int mode, int32_t batch, int32_t num_items, const int32_t
 
 hipError_t launch_combine_segments(const AttnArgs& a, hipStream_t s) {
   if (a.num_items == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_segments_kernel, dim3(a.num_items), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(combine_segments_kernel, dim3(a.num_items, (a.H + 3) / 4), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -276,20 +289,23 @@ hipError_t launch_absorb(const uint16_t* q_nope, int64_t st, int64_t sh, const u
   return hipGetLastError();
 }
 
-hipError_t launch_up_project(const float* o_lat, const uint16_t* w_uv, int32_t num_items, int32_t H,
-                             int32_t R, int32_t Dv, uint16_t* out, hipStream_t s) {
+hipError_t launch_up_project(const float* o_lat, const float* o_scale, const uint16_t* w_uv,
+                             int32_t num_items, int32_t H, int32_t R, int32_t Dv, uint16_t* out,
+                             hipStream_t s) {
   const dim3 grid((num_items + kGemmItems - 1) / kGemmItems, H);
   const size_t smem = sizeof(float) * kGemmItems * R;
-  hipLaunchKernelGGL(up_project_kernel, grid, dim3(256), smem, s, o_lat, w_uv, num_items, H, R, Dv,
-                     out);
+  hipLaunchKernelGGL(up_project_kernel, grid, dim3(256), smem, s, o_lat, o_scale, w_uv, num_items,
+                     H, R, Dv, out);
   return hipGetLastError();
 }
 
-hipError_t launch_latent_out(const float* o_lat, int64_t count, uint16_t* out, hipStream_t s) {
+hipError_t launch_latent_out(const float* o_lat, const float* o_scale, int32_t num_items, int32_t H,
+                             int32_t R, uint16_t* out, hipStream_t s) {
+  const int64_t count = static_cast<int64_t>(num_items) * H * R;
   if (count == 0) return hipSuccess;
   const int64_t blocks = (count + 255) / 256;
   hipLaunchKernelGGL(latent_out_kernel, dim3(static_cast<unsigned>(blocks < 65536 ? blocks : 65536)),
-                     dim3(256), 0, s, o_lat, count, out);
+                     dim3(256), 0, s, o_lat, o_scale, count, R, out);
   return hipGetLastError();
 }
 

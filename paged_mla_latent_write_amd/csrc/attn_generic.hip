@@ -42,6 +42,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a, int hpb) 
   float* al_s = l_s + hpb;           // [hpb]
 
   const int64_t g = blockIdx.x;
+  if (a.redo_only && a.redo_only[g] == 0) return;
   const int h0 = blockIdx.y * hpb;
   const int nh = min(hpb, a.H - h0);
   const int64_t W = a.tile_start[a.num_items];
@@ -145,20 +146,26 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a, int hpb) 
     const bool complete = (t == ts) && (seg_end == te);
     float* o_dst;
     float* lse_dst;
+    float* scl_dst;
     if (complete) {
       o_dst = a.o_lat + (static_cast<int64_t>(i) * a.H + h0) * R;
       lse_dst = a.lse + static_cast<int64_t>(i) * a.H + h0;
+      scl_dst = a.o_scale + static_cast<int64_t>(i) * a.H + h0;
     } else {
       const int64_t slot = (ts < t0) ? 2 * g : 2 * g + 1;
       o_dst = a.part_o + (slot * a.H + h0) * R;
       lse_dst = a.part_lse + slot * a.H + h0;
+      scl_dst = a.part_scale + slot * a.H + h0;
     }
 #pragma unroll
     for (int k = 0; k < kMaxAcc; ++k) {
       const int idx = tid + 256 * k;
       if (idx < nh * R) o_dst[idx] = acc[k] / l_s[idx / R];
     }
-    if (tid < nh) lse_dst[tid] = (m_s[tid] + log2f(l_s[tid])) * kLn2;
+    if (tid < nh) {
+      lse_dst[tid] = (m_s[tid] + log2f(l_s[tid])) * kLn2;
+      scl_dst[tid] = 1.0f;  // stored normalised
+    }
     __syncthreads();
     t = seg_end;
   }

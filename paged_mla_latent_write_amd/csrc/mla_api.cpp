@@ -63,8 +63,8 @@ size_t elem_bytes(int dtype) { return dtype == MLA_KV_BF16 ? 2 : 1; }
 // Workspace regions (byte offsets from the workspace base).
 struct Layout {
   int G = 0;
-  size_t q_lat = 0, o_lat = 0, lse = 0, item_b = 0, item_lo = 0, item_hi = 0, tile_start = 0,
-         part_o = 0, part_lse = 0, total = 0;
+  size_t q_lat = 0, o_lat = 0, lse = 0, o_scale = 0, item_b = 0, item_lo = 0, item_hi = 0,
+         tile_start = 0, part_o = 0, part_lse = 0, part_scale = 0, redo = 0, total = 0;
 };
 
 // Returns false when the number of workgroups cannot be determined.
@@ -83,6 +83,8 @@ bool make_layout(const mla_cache* c, const mla_attn* a, int64_t num_items, Layou
   off = align_up(off + sizeof(float) * num_items * H * R);
   L->lse = off;
   off = align_up(off + sizeof(float) * num_items * H);
+  L->o_scale = off;
+  off = align_up(off + sizeof(float) * num_items * H);
   L->item_b = off;
   off = align_up(off + sizeof(int32_t) * num_items);
   L->item_lo = off;
@@ -95,6 +97,10 @@ bool make_layout(const mla_cache* c, const mla_attn* a, int64_t num_items, Layou
   off = align_up(off + sizeof(float) * 2 * G * H * R);
   L->part_lse = off;
   off = align_up(off + sizeof(float) * 2 * G * H);
+  L->part_scale = off;
+  off = align_up(off + sizeof(float) * 2 * G * H);
+  L->redo = off;
+  off = align_up(off + sizeof(int32_t) * G);
   L->total = off;
   return true;
 }
@@ -146,6 +152,7 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
   kv.dtype = cache->dtype == MLA_KV_BF16 ? mla::kKvBf16 : mla::kKvFp8;
   kv.num_pages = cache->num_pages;
   kv.page_size = cache->page_size;
+  kv.page_shift = __builtin_ctz(static_cast<unsigned>(cache->page_size));
   kv.R = R;
   kv.Dr = cache->qk_rope_dim;
   kv.D = R + cache->qk_rope_dim;
@@ -153,11 +160,18 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
   hipError_t e;
   const uint16_t* q_lat = static_cast<const uint16_t*>(q_nope);
   int64_t ql_st = qn_st, ql_sh = qn_sh;
+  const bool generic = (attn->flags & MLA_FLAG_GENERIC_KERNELS) != 0;
+  const auto aligned16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
   if (attn->w_uk) {
     uint16_t* ql = at<uint16_t>(workspace, L.q_lat);
-    e = mla::launch_absorb(static_cast<const uint16_t*>(q_nope), qn_st, qn_sh,
-                           static_cast<const uint16_t*>(attn->w_uk), num_items, H,
-                           attn->qk_nope_dim, R, ql, s);
+    const bool mfma = !generic && mla::absorb_mfma_supported(attn->qk_nope_dim, R) &&
+                      aligned16(q_nope) && aligned16(attn->w_uk) && qn_st % 8 == 0 && qn_sh % 8 == 0;
+    e = mfma ? mla::launch_absorb_mfma(static_cast<const uint16_t*>(q_nope), qn_st, qn_sh,
+                                       static_cast<const uint16_t*>(attn->w_uk), num_items, H,
+                                       attn->qk_nope_dim, R, ql, s)
+             : mla::launch_absorb(static_cast<const uint16_t*>(q_nope), qn_st, qn_sh,
+                                  static_cast<const uint16_t*>(attn->w_uk), num_items, H,
+                                  attn->qk_nope_dim, R, ql, s);
     if (e != hipSuccess) return MLA_ERR_HIP;
     q_lat = ql;
     ql_st = static_cast<int64_t>(H) * R;
@@ -194,21 +208,46 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
   a.scale_log2 = attn->scale * 1.4426950408889634f;
   a.o_lat = at<float>(workspace, L.o_lat);
   a.lse = lse_or_null ? lse_or_null : at<float>(workspace, L.lse);
+  a.o_scale = at<float>(workspace, L.o_scale);
   a.part_o = at<float>(workspace, L.part_o);
   a.part_lse = at<float>(workspace, L.part_lse);
+  a.part_scale = at<float>(workspace, L.part_scale);
+  a.redo = at<int32_t>(workspace, L.redo);
+  a.redo_only = nullptr;
 
-  const bool use_mfma = !(attn->flags & MLA_FLAG_GENERIC_KERNELS) && mla::mfma_attn_supported(kv, H);
+  const bool use_mfma = !generic && mla::mfma_attn_supported(kv, H) &&
+                        (ql_st % 8 == 0) && (ql_sh % 8 == 0) && (qp_st % 8 == 0) &&
+                        (qp_sh % 8 == 0) && aligned16(q_lat) && aligned16(q_pe);
+  if (attn->kernel_events[0] &&
+      hipEventRecord(static_cast<hipEvent_t>(attn->kernel_events[0]), s) != hipSuccess)
+    return MLA_ERR_HIP;
   e = use_mfma ? mla::launch_attn_mfma(a, s) : mla::launch_attn_generic(a, s);
   if (e != hipSuccess) return MLA_ERR_HIP;
+  if (use_mfma) {
+    // ranges whose scores outran the MFMA kernel's fixed reference maximum
+    // (rare) are recomputed by the plain kernel; the others exit at once
+    AttnArgs fix = a;
+    fix.redo_only = a.redo;
+    e = mla::launch_attn_generic(fix, s);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+  }
+  if (attn->kernel_events[1] &&
+      hipEventRecord(static_cast<hipEvent_t>(attn->kernel_events[1]), s) != hipSuccess)
+    return MLA_ERR_HIP;
   e = mla::launch_combine_segments(a, s);
   if (e != hipSuccess) return MLA_ERR_HIP;
 
   if (attn->w_uv) {
-    e = mla::launch_up_project(a.o_lat, static_cast<const uint16_t*>(attn->w_uv), num_items, H, R,
-                               attn->v_head_dim, static_cast<uint16_t*>(out), s);
+    const bool mfma = !generic && mla::up_project_mfma_supported(R, attn->v_head_dim) &&
+                      aligned16(attn->w_uv);
+    e = mfma ? mla::launch_up_project_mfma(a.o_lat, a.o_scale,
+                                           static_cast<const uint16_t*>(attn->w_uv), num_items, H,
+                                           R, attn->v_head_dim, static_cast<uint16_t*>(out), s)
+             : mla::launch_up_project(a.o_lat, a.o_scale, static_cast<const uint16_t*>(attn->w_uv),
+                                      num_items, H, R, attn->v_head_dim,
+                                      static_cast<uint16_t*>(out), s);
   } else {
-    e = mla::launch_latent_out(a.o_lat, static_cast<int64_t>(num_items) * H * R,
-                               static_cast<uint16_t*>(out), s);
+    e = mla::launch_latent_out(a.o_lat, a.o_scale, num_items, H, R, static_cast<uint16_t*>(out), s);
   }
   return to_status(e);
 }

@@ -22,6 +22,7 @@ struct CacheView {
   int32_t dtype;         // KvDtype
   int32_t num_pages;
   int32_t page_size;
+  int32_t page_shift;    // log2(page_size)
   int32_t R;             // kv_lora_rank
   int32_t Dr;            // qk_rope_dim
   int32_t D;             // R + Dr
@@ -52,10 +53,18 @@ struct AttnArgs {
   int32_t H;
   int32_t G;              // workgroups the tile stream is divided over
   float scale_log2;       // softmax scale * log2(e)
-  float* o_lat;           // [Nq][H][R] fp32, normalised (complete items)
+  // Results.  o values are stored unnormalised together with a per-head
+  // factor (o_scale / part_scale = 1/l); the normalised row is o * factor.
+  float* o_lat;           // [Nq][H][R] fp32 (complete items)
   float* lse;             // [Nq][H] fp32 natural log (complete items)
+  float* o_scale;         // [Nq][H]
   float* part_o;          // [2G][H][R] fp32 partials (cut items)
   float* part_lse;        // [2G][H]
+  float* part_scale;      // [2G][H]
+  // Per-workgroup recompute flags: the MFMA kernel writes one per workgroup;
+  // the plain kernel, given them, only runs the flagged workgroups' ranges.
+  int32_t* redo;          // [G]
+  const int32_t* redo_only;  // null: run every range
 };
 
 // ---- launchers (each returns the launch's hipGetLastError) ----
@@ -80,10 +89,22 @@ hipError_t launch_absorb(const uint16_t* q_nope, int64_t st, int64_t sh, const u
                          int32_t num_items, int32_t H, int32_t Dn, int32_t R, uint16_t* q_lat,
                          hipStream_t s);
 
-hipError_t launch_up_project(const float* o_lat, const uint16_t* w_uv, int32_t num_items, int32_t H,
-                             int32_t R, int32_t Dv, uint16_t* out, hipStream_t s);
+hipError_t launch_up_project(const float* o_lat, const float* o_scale, const uint16_t* w_uv,
+                             int32_t num_items, int32_t H, int32_t R, int32_t Dv, uint16_t* out,
+                             hipStream_t s);
 
-hipError_t launch_latent_out(const float* o_lat, int64_t count, uint16_t* out, hipStream_t s);
+hipError_t launch_latent_out(const float* o_lat, const float* o_scale, int32_t num_items, int32_t H,
+                             int32_t R, uint16_t* out, hipStream_t s);
+
+// Matrix-core versions of the two per-head projections (head_gemm.hip).
+bool absorb_mfma_supported(int32_t Dn, int32_t R);
+bool up_project_mfma_supported(int32_t R, int32_t Dv);
+hipError_t launch_absorb_mfma(const uint16_t* q_nope, int64_t st, int64_t sh, const uint16_t* w_uk,
+                              int32_t num_items, int32_t H, int32_t Dn, int32_t R, uint16_t* q_lat,
+                              hipStream_t s);
+hipError_t launch_up_project_mfma(const float* o_lat, const float* o_scale, const uint16_t* w_uv,
+                                  int32_t num_items, int32_t H, int32_t R, int32_t Dv, uint16_t* out,
+                                  hipStream_t s);
 
 hipError_t launch_dense_combine(const float* o_part, const float* lse_part, int32_t num_splits,
                                 int32_t rows, int32_t dim, float* o, float* lse, hipStream_t s);

@@ -50,7 +50,8 @@ class MlaAttnStruct(ctypes.Structure):
     _fields_ = [("num_heads", ctypes.c_int32), ("qk_nope_dim", ctypes.c_int32),
                 ("v_head_dim", ctypes.c_int32), ("w_uk", ctypes.c_void_p), ("w_uv", ctypes.c_void_p),
                 ("scale", ctypes.c_float), ("window", ctypes.c_int32),
-                ("num_workgroups", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+                ("num_workgroups", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("kernel_events", ctypes.c_void_p * 2)]
 
 
 _P = ctypes.c_void_p
@@ -147,12 +148,17 @@ class KVCache:
                               self.kv_lora_rank, self.qk_rope_dim)
 
 
+def _event_ptr(ev):
+    return None if ev is None else ev.cuda_event
+
+
 def _attn_struct(num_heads, qk_nope_dim, v_head_dim, w_uk, w_uv, scale, window, num_workgroups,
-                 flags):
+                 flags, kernel_events=None):
     for w in (w_uk, w_uv):
         assert w is None or (w.is_contiguous() and w.dtype == torch.bfloat16)
+    ev = (ctypes.c_void_p * 2)(*(_event_ptr(e) for e in (kernel_events or (None, None))))
     return MlaAttnStruct(num_heads, qk_nope_dim, v_head_dim, _ptr(w_uk), _ptr(w_uv), float(scale),
-                         int(window), int(num_workgroups), int(flags))
+                         int(window), int(num_workgroups), int(flags), ev)
 
 
 def _row_strides(q):
@@ -196,14 +202,14 @@ class Workspace:
 
 def decode(cache: KVCache, layer_idx: int, q_nope, q_pe, block_tables, context_lens, *, scale,
            w_uk=None, w_uv=None, window=0, out=None, lse=None, want_lse=True, workspace=None,
-           num_workgroups=0, flags=0, stream=None):
+           num_workgroups=0, flags=0, kernel_events=None, stream=None):
     """Absorbed split-KV decode.  q_nope bf16 [B, H, Dn] (or [B, H, R] latent when
     w_uk is None), q_pe bf16 [B, H, Dr]; block_tables int32 [B, max_blocks];
     context_lens int32 [B].  Returns (out bf16 [B, H, Dv or R], lse fp32 [B, H])."""
     B, H = int(q_nope.shape[0]), int(q_nope.shape[1])
     dn = int(w_uk.shape[1]) if w_uk is not None else 0
     dv = int(w_uv.shape[1]) if w_uv is not None else cache.kv_lora_rank
-    attn = _attn_struct(H, dn, dv, w_uk, w_uv, scale, window, num_workgroups, flags)
+    attn = _attn_struct(H, dn, dv, w_uk, w_uv, scale, window, num_workgroups, flags, kernel_events)
     st = cache.struct()
     assert block_tables.dtype == torch.int32 and block_tables.is_contiguous()
     assert context_lens.dtype == torch.int32 and context_lens.is_contiguous()
@@ -227,14 +233,15 @@ def decode(cache: KVCache, layer_idx: int, q_nope, q_pe, block_tables, context_l
 
 def prefill_chunk(cache: KVCache, layer_idx: int, q_nope, q_pe, query_start_loc, max_q_len,
                   block_tables, context_lens, *, scale, w_uk=None, w_uv=None, window=0, out=None,
-                  lse=None, want_lse=True, workspace=None, num_workgroups=0, flags=0, stream=None):
+                  lse=None, want_lse=True, workspace=None, num_workgroups=0, flags=0,
+                  kernel_events=None, stream=None):
     """Causal chunked prefill.  q_nope bf16 [Tq, H, Dn], q_pe bf16 [Tq, H, Dr];
     query_start_loc int32 [B + 1]; context_lens int32 [B] (chunk included)."""
     Tq, H = int(q_nope.shape[0]), int(q_nope.shape[1])
     B = int(context_lens.shape[0])
     dn = int(w_uk.shape[1]) if w_uk is not None else 0
     dv = int(w_uv.shape[1]) if w_uv is not None else cache.kv_lora_rank
-    attn = _attn_struct(H, dn, dv, w_uk, w_uv, scale, window, num_workgroups, flags)
+    attn = _attn_struct(H, dn, dv, w_uk, w_uv, scale, window, num_workgroups, flags, kernel_events)
     st = cache.struct()
     assert query_start_loc.dtype == torch.int32 and query_start_loc.numel() == B + 1
     max_blocks = int(block_tables.shape[1])

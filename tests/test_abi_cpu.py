@@ -67,6 +67,7 @@ def _cache(mla, **kw):
 def _attn(mla, **kw):
     base = dict(num_heads=16, qk_nope_dim=128, v_head_dim=128, w_uk=0x2000, w_uv=0x3000,
                 scale=0.07, window=0, num_workgroups=4, flags=0)
+    kw.setdefault("kernel_events", (ctypes.c_void_p * 2)(None, None))
     base.update(kw)
     return mla.MlaAttnStruct(**base)
 
