@@ -123,18 +123,30 @@ __global__ __launch_bounds__(256) void combine_segments_kernel(AttnArgs a) {
     tot += (l == -INFINITY) ? 0.f : expf(l - mx);
   }
   const float inv_tot = 1.f / tot;
-  for (int r0 = 0; r0 < R; r0 += 64) {
-    const int r = r0 + lane;
-    if (r >= R) break;
-    float acc = 0.f;
+  // each lane owns 8 consecutive columns; the segment loop only carries the
+  // accumulators, so the loads of successive segments are issued back to back
+  for (int r0 = lane * 8; r0 < R; r0 += 512) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
     for (int64_t g = g0; g <= g1; ++g) {
       if (wg_tile_begin(g, W, G) == wg_tile_begin(g + 1, W, G)) continue;
       const int64_t slot = (g == g0) ? 2 * g + 1 : 2 * g;
       const float l = a.part_lse[slot * H + h];
-      if (l == -INFINITY) continue;
-      acc += expf(l - mx) * a.part_scale[slot * H + h] * a.part_o[(slot * H + h) * R + r];
+      const float w = (l == -INFINITY) ? 0.f : expf(l - mx) * a.part_scale[slot * H + h] * inv_tot;
+      const float4* src = reinterpret_cast<const float4*>(a.part_o + (slot * H + h) * R + r0);
+      const float4 x0 = src[0], x1 = src[1];
+      acc[0] = fmaf(w, x0.x, acc[0]);
+      acc[1] = fmaf(w, x0.y, acc[1]);
+      acc[2] = fmaf(w, x0.z, acc[2]);
+      acc[3] = fmaf(w, x0.w, acc[3]);
+      acc[4] = fmaf(w, x1.x, acc[4]);
+      acc[5] = fmaf(w, x1.y, acc[5]);
+      acc[6] = fmaf(w, x1.z, acc[6]);
+      acc[7] = fmaf(w, x1.w, acc[7]);
     }
-    dst[r] = acc * inv_tot;
+    float4* d4 = reinterpret_cast<float4*>(dst + r0);
+    d4[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    d4[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
   }
   if (lane == 0) {
     a.lse[row] = mx + logf(tot);
