@@ -61,7 +61,7 @@ def parse():
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mfma_decode_v3_bf16_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_mla_latent_write_amd", "csrc", f)
-                  for f in ("attn_mfma.hip", "device_utils.h")]
+                  for f in ("attn_mfma.hip", "attn_mfma_asm.inc", "device_utils.h")]
 
 
 def kernel_source_hash():

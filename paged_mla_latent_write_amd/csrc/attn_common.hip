@@ -30,7 +30,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_items_kernel(
     int mode, int32_t B, int32_t Nq, const int32_t* __restrict__ ctx,
     const int32_t* __restrict__ qsl, int32_t window, int32_t max_ctx, int32_t* __restrict__ item_b,
     int32_t* __restrict__ item_lo, int32_t* __restrict__ item_hi,
-    int32_t* __restrict__ tile_start) {
+    int32_t* __restrict__ tile_start, int32_t G, int32_t* __restrict__ wg_tile,
+    int32_t* __restrict__ wg_item) {
   __shared__ int32_t buf[kPlanThreads];
   __shared__ int32_t carry;
   const int tid = threadIdx.x;
@@ -81,6 +82,22 @@ __global__ __launch_bounds__(kPlanThreads) void plan_items_kernel(
     __syncthreads();
   }
   if (tid == 0) tile_start[Nq] = carry;
+  __syncthreads();
+  // Each workgroup's first tile and the item that owns it (the last item whose
+  // first tile is <= it, so items with no tiles are skipped).
+  const int64_t W = carry;
+  for (int g = tid; g <= G; g += kPlanThreads) {
+    const int32_t t = static_cast<int32_t>(wg_tile_begin(g, W, G));
+    wg_tile[g] = t;
+    if (g < G) {
+      int lo = 0, hi = Nq;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (tile_start[mid] <= t) lo = mid; else hi = mid;
+      }
+      wg_item[g] = lo;
+    }
+  }
 }
 
 // One wave per (item, head).  Items whose tiles all fell to one workgroup were
@@ -274,7 +291,7 @@ hipError_t launch_plan(int mode, int32_t batch, int32_t num_items, const int32_t
                        const Plan& plan, hipStream_t s) {
   hipLaunchKernelGGL(plan_items_kernel, dim3(1), dim3(kPlanThreads), 0, s, mode, batch, num_items,
                      context_lens, query_start_loc, window, max_ctx, plan.item_b, plan.item_lo,
-                     plan.item_hi, plan.tile_start);
+                     plan.item_hi, plan.tile_start, plan.G, plan.wg_tile, plan.wg_item);
   return hipGetLastError();
 }
 

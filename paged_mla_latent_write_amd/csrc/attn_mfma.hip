@@ -49,6 +49,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kR = 512;
 constexpr int kD = 576;
@@ -90,296 +91,12 @@ struct Meta {
   CONST_PTR(int32_t) item_hi;
   CONST_PTR(int32_t) tile_start;
   CONST_PTR(int32_t) block_tables;
+  CONST_PTR(int32_t) wg_tile;
+  CONST_PTR(int32_t) wg_item;
 };
 
-// ---- hand-scheduled inner loops (inline assembly) ----
-// With Q and O filling the register file the compiler keeps a single LDS
-// fragment in flight, so each MFMA would wait out a whole LDS latency.  These
-// two blocks keep a ring of LDS reads in flight in fixed scratch VGPRs
-// (declared clobbered: 6 K fragments for S, 6 V^T fragments for PV) and
-// wait (lgkmcnt) only for the fragment about to be used.  Hazards at the block
-// edges are covered explicitly: 2 wait states between a VALU write and an MFMA
-// source read, 21 after the last MFMA before anything else reads its results.
-#define MLA_VCLOB_S "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255"
-#define MLA_VCLOB_PV "v232", "v233", "v234", "v235", "v236", "v237", "v238", "v239", "v240", "v241", "v242", "v243", "v244", "v245", "v246", "v247", "v248", "v249", "v250", "v251", "v252", "v253", "v254", "v255"
-
-// S^T (32 tokens x 32 heads) = sum over the 36 k-steps of K_k Q_k^T, with the
-// even and odd k-steps in two accumulators (two independent MFMA chains keep
-// the matrix pipe busy; one dependent chain stalls about 20 cycles per MFMA).
-// addr[j]: LDS byte address of this lane's K row chunk for k-steps = j mod 4.
-__device__ __forceinline__ f32x16 tile_scores(const uint32_t (&addr)[4], const bf16x8 (&qf)[kKSteps]) {
-  f32x16 s, t;
-  asm volatile(
-      "ds_read_b128 v[232:235], %[a0] offset:0\n"
-      "ds_read_b128 v[236:239], %[a1] offset:0\n"
-      "ds_read_b128 v[240:243], %[a2] offset:0\n"
-      "ds_read_b128 v[244:247], %[a3] offset:0\n"
-      "ds_read_b128 v[248:251], %[a0] offset:128\n"
-      "ds_read_b128 v[252:255], %[a1] offset:128\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], v[232:235], %[q0], 0\n"
-      "ds_read_b128 v[232:235], %[a2] offset:128\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[t], v[236:239], %[q1], 0\n"
-      "ds_read_b128 v[236:239], %[a3] offset:128\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], v[240:243], %[q2], %[s]\n"
-      "ds_read_b128 v[240:243], %[a0] offset:256\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[t], v[244:247], %[q3], %[t]\n"
-      "ds_read_b128 v[244:247], %[a1] offset:256\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], v[248:251], %[q4], %[s]\n"
-      "ds_read_b128 v[248:251], %[a2] offset:256\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[t], v[252:255], %[q5], %[t]\n"
-      "ds_read_b128 v[252:255], %[a3] offset:256\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], v[232:235], %[q6], %[s]\n"
-      "ds_read_b128 v[232:235], %[a0] offset:384\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[t], v[236:239], %[q7], %[t]\n"
-      "ds_read_b128 v[236:239], %[a1] offset:384\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], v[240:243], %[q8], %[s]\n"
-      "ds_read_b128 v[240:243], %[a2] offset:384\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[t], v[244:247], %[q9], %[t]\n"
-      "ds_read_b128 v[244:247], %[a3] offset:384\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], v[248:251], %[q10], %[s]\n"
-      "ds_read_b128 v[248:251], %[a0] offset:512\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[t], v[252:255], %[q11], %[t]\n"
-      "ds_read_b128 v[252:255], %[a1] offset:512\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], v[232:235], %[q12], %[s]\n"
-      "ds_read_b128 v[232:235], %[a2] offset:512\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[t], v[236:239], %[q13], %[t]\n"
-      "ds_read_b128 v[236:239], %[a3] offset:512\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], v[240:243], %[q14], %[s]\n"
-      "ds_read_b128 v[240:243], %[a0] offset:640\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[t], v[244:247], %[q15], %[t]\n"
-      "ds_read_b128 v[244:247], %[a1] offset:640\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], v[248:251], %[q16], %[s]\n"
-      "ds_read_b128 v[248:251], %[a2] offset:640\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[t], v[252:255], %[q17], %[t]\n"
-      "ds_read_b128 v[252:255], %[a3] offset:640\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], v[232:235], %[q18], %[s]\n"
-      "ds_read_b128 v[232:235], %[a0] offset:768\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[t], v[236:239], %[q19], %[t]\n"
-      "ds_read_b128 v[236:239], %[a1] offset:768\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], v[240:243], %[q20], %[s]\n"
-      "ds_read_b128 v[240:243], %[a2] offset:768\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[t], v[244:247], %[q21], %[t]\n"
-      "ds_read_b128 v[244:247], %[a3] offset:768\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], v[248:251], %[q22], %[s]\n"
-      "ds_read_b128 v[248:251], %[a0] offset:896\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[t], v[252:255], %[q23], %[t]\n"
-      "ds_read_b128 v[252:255], %[a1] offset:896\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], v[232:235], %[q24], %[s]\n"
-      "ds_read_b128 v[232:235], %[a2] offset:896\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[t], v[236:239], %[q25], %[t]\n"
-      "ds_read_b128 v[236:239], %[a3] offset:896\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], v[240:243], %[q26], %[s]\n"
-      "ds_read_b128 v[240:243], %[a0] offset:1024\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[t], v[244:247], %[q27], %[t]\n"
-      "ds_read_b128 v[244:247], %[a1] offset:1024\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], v[248:251], %[q28], %[s]\n"
-      "ds_read_b128 v[248:251], %[a2] offset:1024\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[t], v[252:255], %[q29], %[t]\n"
-      "ds_read_b128 v[252:255], %[a3] offset:1024\n"
-      "s_waitcnt lgkmcnt(5)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], v[232:235], %[q30], %[s]\n"
-      "s_waitcnt lgkmcnt(4)\n"
-      "v_mfma_f32_32x32x16_bf16 %[t], v[236:239], %[q31], %[t]\n"
-      "s_waitcnt lgkmcnt(3)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], v[240:243], %[q32], %[s]\n"
-      "s_waitcnt lgkmcnt(2)\n"
-      "v_mfma_f32_32x32x16_bf16 %[t], v[244:247], %[q33], %[t]\n"
-      "s_waitcnt lgkmcnt(1)\n"
-      "v_mfma_f32_32x32x16_bf16 %[s], v[248:251], %[q34], %[s]\n"
-      "s_waitcnt lgkmcnt(0)\n"
-      "v_mfma_f32_32x32x16_bf16 %[t], v[252:255], %[q35], %[t]\n"
-      "s_nop 7\n"
-      "s_nop 7\n"
-      "s_nop 4\n"
-      : [s] "=&v"(s), [t] "=&v"(t)
-      : [a0] "v"(addr[0]), [a1] "v"(addr[1]), [a2] "v"(addr[2]), [a3] "v"(addr[3]),
-        [q0] "v"(qf[0]), [q1] "v"(qf[1]), [q2] "v"(qf[2]), [q3] "v"(qf[3]), [q4] "v"(qf[4]), [q5] "v"(qf[5]),
-        [q6] "v"(qf[6]), [q7] "v"(qf[7]), [q8] "v"(qf[8]), [q9] "v"(qf[9]), [q10] "v"(qf[10]), [q11] "v"(qf[11]),
-        [q12] "v"(qf[12]), [q13] "v"(qf[13]), [q14] "v"(qf[14]), [q15] "v"(qf[15]), [q16] "v"(qf[16]), [q17] "v"(qf[17]),
-        [q18] "v"(qf[18]), [q19] "v"(qf[19]), [q20] "v"(qf[20]), [q21] "v"(qf[21]), [q22] "v"(qf[22]), [q23] "v"(qf[23]),
-        [q24] "v"(qf[24]), [q25] "v"(qf[25]), [q26] "v"(qf[26]), [q27] "v"(qf[27]), [q28] "v"(qf[28]), [q29] "v"(qf[29]),
-        [q30] "v"(qf[30]), [q31] "v"(qf[31]), [q32] "v"(qf[32]), [q33] "v"(qf[33]), [q34] "v"(qf[34]), [q35] "v"(qf[35])
-      : MLA_VCLOB_S);
-  return s + t;
-}
-
-// O^T += V^T P^T over the 16 dim tiles and both 16-token steps.  ve / vo (veh /
-// voh): LDS byte addresses of this lane's transposed-read origin for even / odd
-// dim tiles, first (second) group of 8 tokens of each 16-token step.
-__device__ __forceinline__ void tile_pv(f32x16 (&acc)[kMTiles], uint32_t ve, uint32_t vo,
-                                        uint32_t veh, uint32_t voh, const bf16x8& p0,
-                                        const bf16x8& p1) {
-  asm volatile(
-      "s_nop 1\n"
-      "ds_read_b64_tr_b16 v[232:233], %[ve] offset:0\n"
-      "ds_read_b64_tr_b16 v[234:235], %[veh] offset:0\n"
-      "ds_read_b64_tr_b16 v[236:237], %[vo] offset:0\n"
-      "ds_read_b64_tr_b16 v[238:239], %[voh] offset:0\n"
-      "ds_read_b64_tr_b16 v[240:241], %[ve] offset:128\n"
-      "ds_read_b64_tr_b16 v[242:243], %[veh] offset:128\n"
-      "ds_read_b64_tr_b16 v[244:245], %[vo] offset:128\n"
-      "ds_read_b64_tr_b16 v[246:247], %[voh] offset:128\n"
-      "ds_read_b64_tr_b16 v[248:249], %[ve] offset:256\n"
-      "ds_read_b64_tr_b16 v[250:251], %[veh] offset:256\n"
-      "ds_read_b64_tr_b16 v[252:253], %[vo] offset:256\n"
-      "ds_read_b64_tr_b16 v[254:255], %[voh] offset:256\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c0], v[232:235], %[p0], %[c0]\n"
-      "ds_read_b64_tr_b16 v[232:233], %[ve] offset:384\n"
-      "ds_read_b64_tr_b16 v[234:235], %[veh] offset:384\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c1], v[236:239], %[p0], %[c1]\n"
-      "ds_read_b64_tr_b16 v[236:237], %[vo] offset:384\n"
-      "ds_read_b64_tr_b16 v[238:239], %[voh] offset:384\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c2], v[240:243], %[p0], %[c2]\n"
-      "ds_read_b64_tr_b16 v[240:241], %[ve] offset:512\n"
-      "ds_read_b64_tr_b16 v[242:243], %[veh] offset:512\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c3], v[244:247], %[p0], %[c3]\n"
-      "ds_read_b64_tr_b16 v[244:245], %[vo] offset:512\n"
-      "ds_read_b64_tr_b16 v[246:247], %[voh] offset:512\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c4], v[248:251], %[p0], %[c4]\n"
-      "ds_read_b64_tr_b16 v[248:249], %[ve] offset:640\n"
-      "ds_read_b64_tr_b16 v[250:251], %[veh] offset:640\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c5], v[252:255], %[p0], %[c5]\n"
-      "ds_read_b64_tr_b16 v[252:253], %[vo] offset:640\n"
-      "ds_read_b64_tr_b16 v[254:255], %[voh] offset:640\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c6], v[232:235], %[p0], %[c6]\n"
-      "ds_read_b64_tr_b16 v[232:233], %[ve] offset:768\n"
-      "ds_read_b64_tr_b16 v[234:235], %[veh] offset:768\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c7], v[236:239], %[p0], %[c7]\n"
-      "ds_read_b64_tr_b16 v[236:237], %[vo] offset:768\n"
-      "ds_read_b64_tr_b16 v[238:239], %[voh] offset:768\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c8], v[240:243], %[p0], %[c8]\n"
-      "ds_read_b64_tr_b16 v[240:241], %[ve] offset:896\n"
-      "ds_read_b64_tr_b16 v[242:243], %[veh] offset:896\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c9], v[244:247], %[p0], %[c9]\n"
-      "ds_read_b64_tr_b16 v[244:245], %[vo] offset:896\n"
-      "ds_read_b64_tr_b16 v[246:247], %[voh] offset:896\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c10], v[248:251], %[p0], %[c10]\n"
-      "ds_read_b64_tr_b16 v[248:249], %[ve] offset:18432\n"
-      "ds_read_b64_tr_b16 v[250:251], %[veh] offset:18432\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c11], v[252:255], %[p0], %[c11]\n"
-      "ds_read_b64_tr_b16 v[252:253], %[vo] offset:18432\n"
-      "ds_read_b64_tr_b16 v[254:255], %[voh] offset:18432\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c12], v[232:235], %[p0], %[c12]\n"
-      "ds_read_b64_tr_b16 v[232:233], %[ve] offset:18560\n"
-      "ds_read_b64_tr_b16 v[234:235], %[veh] offset:18560\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c13], v[236:239], %[p0], %[c13]\n"
-      "ds_read_b64_tr_b16 v[236:237], %[vo] offset:18560\n"
-      "ds_read_b64_tr_b16 v[238:239], %[voh] offset:18560\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c14], v[240:243], %[p0], %[c14]\n"
-      "ds_read_b64_tr_b16 v[240:241], %[ve] offset:18688\n"
-      "ds_read_b64_tr_b16 v[242:243], %[veh] offset:18688\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c15], v[244:247], %[p0], %[c15]\n"
-      "ds_read_b64_tr_b16 v[244:245], %[vo] offset:18688\n"
-      "ds_read_b64_tr_b16 v[246:247], %[voh] offset:18688\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c0], v[248:251], %[p1], %[c0]\n"
-      "ds_read_b64_tr_b16 v[248:249], %[ve] offset:18816\n"
-      "ds_read_b64_tr_b16 v[250:251], %[veh] offset:18816\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c1], v[252:255], %[p1], %[c1]\n"
-      "ds_read_b64_tr_b16 v[252:253], %[vo] offset:18816\n"
-      "ds_read_b64_tr_b16 v[254:255], %[voh] offset:18816\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c2], v[232:235], %[p1], %[c2]\n"
-      "ds_read_b64_tr_b16 v[232:233], %[ve] offset:18944\n"
-      "ds_read_b64_tr_b16 v[234:235], %[veh] offset:18944\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c3], v[236:239], %[p1], %[c3]\n"
-      "ds_read_b64_tr_b16 v[236:237], %[vo] offset:18944\n"
-      "ds_read_b64_tr_b16 v[238:239], %[voh] offset:18944\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c4], v[240:243], %[p1], %[c4]\n"
-      "ds_read_b64_tr_b16 v[240:241], %[ve] offset:19072\n"
-      "ds_read_b64_tr_b16 v[242:243], %[veh] offset:19072\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c5], v[244:247], %[p1], %[c5]\n"
-      "ds_read_b64_tr_b16 v[244:245], %[vo] offset:19072\n"
-      "ds_read_b64_tr_b16 v[246:247], %[voh] offset:19072\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c6], v[248:251], %[p1], %[c6]\n"
-      "ds_read_b64_tr_b16 v[248:249], %[ve] offset:19200\n"
-      "ds_read_b64_tr_b16 v[250:251], %[veh] offset:19200\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c7], v[252:255], %[p1], %[c7]\n"
-      "ds_read_b64_tr_b16 v[252:253], %[vo] offset:19200\n"
-      "ds_read_b64_tr_b16 v[254:255], %[voh] offset:19200\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c8], v[232:235], %[p1], %[c8]\n"
-      "ds_read_b64_tr_b16 v[232:233], %[ve] offset:19328\n"
-      "ds_read_b64_tr_b16 v[234:235], %[veh] offset:19328\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c9], v[236:239], %[p1], %[c9]\n"
-      "ds_read_b64_tr_b16 v[236:237], %[vo] offset:19328\n"
-      "ds_read_b64_tr_b16 v[238:239], %[voh] offset:19328\n"
-      "s_waitcnt lgkmcnt(10)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c10], v[240:243], %[p1], %[c10]\n"
-      "s_waitcnt lgkmcnt(8)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c11], v[244:247], %[p1], %[c11]\n"
-      "s_waitcnt lgkmcnt(6)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c12], v[248:251], %[p1], %[c12]\n"
-      "s_waitcnt lgkmcnt(4)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c13], v[252:255], %[p1], %[c13]\n"
-      "s_waitcnt lgkmcnt(2)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c14], v[232:235], %[p1], %[c14]\n"
-      "s_waitcnt lgkmcnt(0)\n"
-      "v_mfma_f32_32x32x16_bf16 %[c15], v[236:239], %[p1], %[c15]\n"
-      "s_nop 7\n"
-      "s_nop 7\n"
-      "s_nop 4\n"
-      : [c0] "+a"(acc[0]), [c1] "+a"(acc[1]), [c2] "+a"(acc[2]), [c3] "+a"(acc[3]),
-        [c4] "+a"(acc[4]), [c5] "+a"(acc[5]), [c6] "+a"(acc[6]), [c7] "+a"(acc[7]),
-        [c8] "+a"(acc[8]), [c9] "+a"(acc[9]), [c10] "+a"(acc[10]), [c11] "+a"(acc[11]),
-        [c12] "+a"(acc[12]), [c13] "+a"(acc[13]), [c14] "+a"(acc[14]), [c15] "+a"(acc[15])
-      : [ve] "v"(ve), [vo] "v"(vo), [veh] "v"(veh), [voh] "v"(voh), [p0] "v"(p0), [p1] "v"(p1)
-      : MLA_VCLOB_PV);
-}
-
+// ---- the per-tile blocks (generated; see gen_attn_mfma_asm.py) ----
+#include "attn_mfma_asm.inc"
 
 // 16-byte copy HBM -> LDS without VGPR staging: lane i's 16 bytes land at
 // lds_base + 16 i (lds_base wave-uniform, in M0).  Issued as inline assembly
@@ -394,71 +111,105 @@ __device__ __forceinline__ void lds_dma_16(const void* gptr, uint32_t lds_base) 
                : "memory", "m0");
 }
 
-struct TileInfo {
-  int item;
-  int b;
-  int vlo, vhi;
-  int tok0;  // absolute position of the tile's first token
+// 16-byte copies HBM -> LDS addressed as a wave-uniform 64-bit base (SGPRs)
+// plus this lane's 32-bit offset: lane i's 16 bytes land at lds_base + 16 i.
+__device__ __forceinline__ void lds_dma_16_sbase(const char* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2 offset:0"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
+// The copy cursor: which tile a workgroup copies next, and where it lives.
+// Every field is wave-uniform (scalar registers).  The page ids of the next
+// tile are loaded one tile ahead, when the cursor advances, so the copy issue
+// itself never waits for a block-table read; item metadata is read once per
+// item.
+struct LoadCursor {
+  int tile;       // next tile to copy (index in the workgroup's tile stream)
+  int end;        // one past the workgroup's last tile
+  int item;       // item owning `tile`
+  int item_end;   // first tile of the next item
+  int tok;        // absolute position of `tile`'s first token
+  int vlo, vhi;   // the item's visible key range
+  CONST_PTR(int32_t) bt_row;  // block-table row of the item's request
+  int32_t pg0, pg1;           // block-table entries of `tile` (pg1: second page when ps < 32),
+                              // clamped to the cache only when used, so their loads are
+                              // waited for at the next copy, not here
 };
 
-__device__ __forceinline__ TileInfo tile_info(const Meta& m, int item, int64_t tile) {
-  TileInfo ti;
-  ti.item = item;
-  ti.b = m.item_b[item];
-  ti.vlo = m.item_lo[item];
-  ti.vhi = m.item_hi[item];
-  ti.tok0 = ((ti.vlo >> 5) + static_cast<int>(tile - m.tile_start[item])) * kTile;
-  return ti;
+// Enter the item that owns c.tile (items with no tiles are skipped).
+__device__ __forceinline__ void cursor_enter_item(LoadCursor& c, const AttnArgs& a, const Meta& m) {
+  while (c.item + 1 < a.num_items && m.tile_start[c.item + 1] <= c.tile) ++c.item;
+  c.item_end = m.tile_start[c.item + 1];
+  c.vlo = m.item_lo[c.item];
+  c.vhi = m.item_hi[c.item];
+  c.tok = ((c.vlo >> 5) + (c.tile - m.tile_start[c.item])) * kTile;
+  c.bt_row = m.block_tables + static_cast<int64_t>(m.item_b[c.item]) * a.max_blocks;
 }
 
-// Next item owning `tile` (items with no tiles are skipped).
-__device__ __forceinline__ int advance_item(const Meta& m, int num_items, int item, int64_t tile) {
-  while (item + 1 < num_items && m.tile_start[item + 1] <= tile) ++item;
-  return item;
+// Read the page ids of c.tile.  Only block-table entries below ceil(vhi / ps)
+// are read: the tile's first token is < vhi, and the second page is read only
+// if it holds a visible token.
+__device__ __forceinline__ void cursor_fetch_pages(LoadCursor& c, const AttnArgs& a) {
+  const int blk = c.tok >> a.kv.page_shift;
+  const bool two = a.kv.page_size < kTile && c.tok + a.kv.page_size < c.vhi;
+  c.pg0 = c.bt_row[blk];
+  c.pg1 = c.bt_row[blk + (two ? 1 : 0)];  // (no dependence on pg0's value: not waited for here)
 }
 
-// Copy one 32-token tile into an LDS buffer: 2304 chunks of 16 B, NW waves x
-// (36 / NW) global_load_lds instructions of 64 lanes each.  Tokens outside the
-// item's visible range load a clamped (valid, finite) token; their scores are
-// masked later, so they contribute exactly zero.
+// True when c.tile is wholly visible and inside one page: its 36 KB are then
+// contiguous in HBM and every lane's source is a fixed offset from one base.
+__device__ __forceinline__ bool cursor_contiguous(const LoadCursor& c, const AttnArgs& a) {
+  return a.kv.page_size >= kTile && c.tok >= c.vlo && c.tok + kTile <= c.vhi;
+}
+
+// HBM address of c.tile's first row (contiguous tiles).
+__device__ __forceinline__ const char* cursor_src(const LoadCursor& c, const AttnArgs& a) {
+  const int psh = a.kv.page_shift;
+  const unsigned pg0 = min(static_cast<unsigned>(c.pg0), static_cast<unsigned>(a.kv.num_pages - 1));
+  const int blk0 = c.tok >> psh;
+  return static_cast<const char*>(a.kv.data) +
+         ((static_cast<int64_t>(pg0) << psh) + (c.tok - (blk0 << psh))) * kRowBytes;
+}
+
+// Copy tile c.tile into an LDS buffer (2304 chunks of 16 B: kLoads copies of
+// 64 lanes per wave).  Tokens outside the visible range load a clamped (valid,
+// finite) token; their scores are masked, so they contribute exactly zero.
 template <int NW>
-__device__ __forceinline__ void issue_tile(const AttnArgs& a, const Meta& m, const TileInfo& ti,
-                                           LDS_PTR(char) buf, int wave, int lane,
-                                           const uint32_t (&lofs)[(kChunksPerTile / 64 / NW + 1) / 2]) {
+__device__ __forceinline__ void cursor_copy(const LoadCursor& c, const AttnArgs& a, uint32_t lds0,
+                                            const uint32_t (&lofs_in)[(kChunksPerTile / 64 / NW + 1) / 2]) {
   constexpr int kPerWave = kChunksPerTile / 64 / NW;
-  CONST_PTR(int32_t) bt = m.block_tables + static_cast<int64_t>(ti.b) * a.max_blocks;
+  // Opaque copies: keeps the compiler from hoisting the per-copy address
+  // arithmetic out of the tile loop (it would hold ~30 registers for it).
+  uint32_t lofs[(kPerWave + 1) / 2];
+#pragma unroll
+  for (int i = 0; i < (kPerWave + 1) / 2; ++i) {
+    lofs[i] = lofs_in[i];
+    asm volatile("" : "+v"(lofs[i]));
+  }
   const int ps = a.kv.page_size;
   const int psh = a.kv.page_shift;
-  const unsigned last_page = static_cast<unsigned>(a.kv.num_pages - 1);
-  const char* base = static_cast<const char*>(a.kv.data);
-  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(buf)) + wave * kPerWave * 1024;
-  // The tile's page ids are wave-uniform (scalar loads, so the vector-memory
-  // counter only tracks the tile copies).
-  const int blk0 = ti.tok0 >> psh;
-  const unsigned pg0 = min(static_cast<unsigned>(bt[blk0]), last_page);
-  if (ps >= kTile && ti.tok0 >= ti.vlo && ti.tok0 + kTile <= ti.vhi) {
-    // whole tile visible and inside one page: 36 KB contiguous in HBM, so
-    // each lane's source is a fixed offset from the tile's first row
-    const char* src = base + ((static_cast<int64_t>(pg0) << psh) + (ti.tok0 - (blk0 << psh))) * kRowBytes;
+  if (cursor_contiguous(c, a)) {
+    const char* src = cursor_src(c, a);
 #pragma unroll
-    for (int k = 0; k < kPerWave; ++k) lds_dma_16(src + ((lofs[k >> 1] >> (16 * (k & 1))) & 0xFFFF), lds0 + k * 1024);
+    for (int k = 0; k < kPerWave; ++k)
+      lds_dma_16_sbase(src, (lofs[k >> 1] >> (16 * (k & 1))) & 0xFFFF, lds0 + k * 1024);
     return;
   }
-  // Partial tile (first or last of an item) or two 16-token pages.  Tokens
-  // outside the visible range load a clamped (valid, finite) token; their
-  // scores are masked, so they contribute exactly zero.  The second page is
-  // read only if it holds a visible token (the block table is read up to
-  // ceil(n / ps) entries only).
-  unsigned pg1 = pg0;
-  if (ps < kTile && ti.tok0 + ps < ti.vhi) pg1 = min(static_cast<unsigned>(bt[blk0 + 1]), last_page);
+  const char* base = static_cast<const char*>(a.kv.data);
+  const int blk0 = c.tok >> psh;
+  const unsigned last_page = static_cast<unsigned>(a.kv.num_pages - 1);
+  const unsigned pg0 = min(static_cast<unsigned>(c.pg0), last_page);
+  const unsigned pg1 = min(static_cast<unsigned>(c.pg1), last_page);
 #pragma unroll
   for (int k = 0; k < kPerWave; ++k) {
     const int lo = static_cast<int>((lofs[k >> 1] >> (16 * (k & 1))) & 0xFFFF);
     const int t = lo / kRowBytes;           // token row of this lane's chunk
     const int cbyte = lo - t * kRowBytes;   // its (swizzled-source) byte offset in the row
-    int pos = ti.tok0 + t;
-    pos = pos < ti.vlo ? ti.vlo : pos;
-    pos = pos >= ti.vhi ? ti.vhi - 1 : pos;
+    int pos = c.tok + t;
+    pos = pos < c.vlo ? c.vlo : pos;
+    pos = pos >= c.vhi ? c.vhi - 1 : pos;
     const int in_page = pos - (blk0 << psh);  // 0 .. 2 * ps - 1
     const unsigned pg = in_page >= ps ? pg1 : pg0;
     const int off = in_page >= ps ? in_page - ps : in_page;
@@ -467,17 +218,39 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, const Meta& m, con
   }
 }
 
+// Move the cursor to the next tile and start reading its page ids (they are
+// waited for only when that tile is copied).
+__device__ __forceinline__ void cursor_advance(LoadCursor& c, const AttnArgs& a, const Meta& m) {
+  ++c.tile;
+  c.tok += kTile;
+  if (c.tile < c.end) {
+    if (c.tile >= c.item_end) {
+      ++c.item;
+      cursor_enter_item(c, a, m);
+    }
+    cursor_fetch_pages(c, a);
+  }
+}
+
+// Next item owning `tile` (items with no tiles are skipped).
+__device__ __forceinline__ int advance_item(const Meta& m, int num_items, int item, int tile) {
+  while (item + 1 < num_items && m.tile_start[item + 1] <= tile) ++item;
+  return item;
+}
+
 template <int NW>
-__global__ __launch_bounds__(NW * 64, 1) void attn_mfma_kernel(
+__global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompilerVgprs))) void attn_mfma_kernel(
     AttnArgs a, const int32_t* __restrict__ item_b, const int32_t* __restrict__ item_lo,
     const int32_t* __restrict__ item_hi, const int32_t* __restrict__ tile_start,
-    const int32_t* __restrict__ block_tables) {
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ wg_tile,
+    const int32_t* __restrict__ wg_item) {
   const Meta m{(CONST_PTR(int32_t))item_b, (CONST_PTR(int32_t))item_lo, (CONST_PTR(int32_t))item_hi,
-               (CONST_PTR(int32_t))tile_start, (CONST_PTR(int32_t))block_tables};
+               (CONST_PTR(int32_t))tile_start, (CONST_PTR(int32_t))block_tables,
+               (CONST_PTR(int32_t))wg_tile, (CONST_PTR(int32_t))wg_item};
   __shared__ __attribute__((aligned(1024))) char lds_buf[4][kTileBytes];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int g = lane >> 5;        // half of the wave
   const int n32 = lane & 31;      // head within the wave / token row for K reads
   const int head = wave * 32 + n32;
@@ -486,29 +259,18 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mfma_kernel(
   // every tile (so the copy rate does not drop) but skip the arithmetic.
   const bool wave_active = wave * 32 < a.H;
 
-  const int64_t W = m.tile_start[a.num_items];
   const int64_t wg = blockIdx.x;
   // redo[wg] is written once per launch by thread 0 (no separate memset, so
   // the call stays capturable): 1 if a score ran past the reference maximum.
   __shared__ int wg_overflow;
   if (threadIdx.x == 0) wg_overflow = 0;
-  const int64_t t0 = wg_tile_begin(wg, W, a.G), t1 = wg_tile_begin(wg + 1, W, a.G);
+  const int t0 = m.wg_tile[wg], t1 = m.wg_tile[wg + 1];
   if (t0 >= t1) {
     if (threadIdx.x == 0) a.redo[wg] = 0;
     return;
   }
-  const int ntiles = static_cast<int>(t1 - t0);
-  bool overflow = false;
-
-  int first_item;
-  {
-    int lo = 0, hi = a.num_items;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (m.tile_start[mid] <= t0) lo = mid; else hi = mid;
-    }
-    first_item = advance_item(m, a.num_items, lo, t0);
-  }
+  const int ntiles = t1 - t0;
+  const int first_item = m.wg_item[wg];
 
   LDS_PTR(char) bufs[4];
 #pragma unroll
@@ -517,9 +279,6 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mfma_kernel(
   // ---- lane-constant LDS offsets ----
   // K rows (A of S^T): token n32, chunk 2k + g.  (c & 7) ^ swz = (2k & 7) ^ (g ^ swz).
   const int y = g ^ swz(n32);
-  int koff[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) koff[j] = n32 * kRowBytes + (((2 * j) ^ y) << 4);
   // V^T (A of O^T) transposed reads: group q = lane / 16, jj = lane % 16 reads
   // token 16 j + 8 h + 4 g + rr, dims 32 mt + 16 (q & 1) + 4 c4 .. + 3; the
   // swizzle of that token is 4 (rr >> 1) ^ g ^ 2 h.
@@ -546,118 +305,103 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mfma_kernel(
     lofs[k >> 1] |= o << (16 * (k & 1));
   }
 
-  // ---- load cursor: prologue issues the first three tiles ----
-  int l_item = first_item;
-  int64_t l_tile = t0;
+  // ---- copy cursor: the prologue issues the first two tiles ----
+  // Tile n is copied while tile n - 2 is computed (buffer n % 4): step n reads
+  // buffers n % 4 (scores) and (n - 1) % 4 (values of the previous tile), so
+  // buffer (n + 2) % 4, last read in step n - 1, is free once every wave has
+  // passed step n's barrier.
+  LoadCursor cur;
+  cur.tile = t0;
+  cur.end = t1;
+  cur.item = first_item;
+  cursor_enter_item(cur, a, m);
+  cursor_fetch_pages(cur, a);
+  const uint32_t lds_wave = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(bufs[0])) + wave * kLoads * 1024;
 #pragma unroll
-  for (int p = 0; p < 3; ++p) {
+  for (int p = 0; p < 2; ++p) {
     if (p < ntiles) {
-      l_item = advance_item(m, a.num_items, l_item, l_tile);
-      issue_tile<NW>(a, m, tile_info(m, l_item, l_tile), bufs[p], wave, lane, lofs);
-      ++l_tile;
+      cursor_copy<NW>(cur, a, lds_wave + p * kTileBytes, lofs);
+      cursor_advance(cur, a, m);
     }
   }
 
-  constexpr int kLoadsPerTile = kChunksPerTile / 64 / NW;
-  bf16x8 qf[kKSteps];
-  f32x16 acc[kMTiles];
+  uint32_t koff[4], voff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) koff[j] = n32 * kRowBytes + (((2 * j) ^ y) << 4);
+  voff[0] = voff_even;
+  voff[1] = voff_odd;
+  voff[2] = voff_even_h;
+  voff[3] = voff_odd_h;
+  const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(bufs[0]));
+  const float c = a.scale_log2;
+  float ovf = 0.f;  // 1 once a score ran past its segment's reference maximum
+
+  // Q (v54-v197) and the O^T accumulators (a0-a255) live in registers the
+  // compiler does not allocate; only the blocks of attn_mfma_asm.inc touch them.
+  zero_q();
 
   int tn = 0;               // tiles consumed so far (buffer tn % 4)
   int c_item = first_item;
-  int64_t ctile = t0;
+  int ctile = t0;
   while (ctile < t1) {
     // ---- a segment: the WG's tiles of one item ----
     c_item = advance_item(m, a.num_items, c_item, ctile);
-    const int64_t item_ts = m.tile_start[c_item], item_te = m.tile_start[c_item + 1];
-    const int64_t seg_begin = ctile;
-    const int64_t seg_end = item_te < t1 ? item_te : t1;
-    if (wave_active) {
-      const uint16_t* ql = a.q_lat + c_item * a.q_lat_st + head * a.q_lat_sh;
-      const uint16_t* qp = a.q_pe + c_item * a.q_pe_st + head * a.q_pe_sh;
-#pragma unroll
-      for (int k = 0; k < kKSteps; ++k) {
-        i16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (head_ok) {
-          const uint16_t* src = k < kR / 16 ? ql + 16 * k + 8 * g : qp + 16 * (k - kR / 16) + 8 * g;
-          v = *reinterpret_cast<const i16x8*>(src);
-        }
-        qf[k] = __builtin_bit_cast(bf16x8, v);
-      }
-#pragma unroll
-      for (int mt = 0; mt < kMTiles; ++mt) acc[mt] = f32x16{};
-      // consume the query loads here, so their completion wait sits outside
-      // the tile loop (a wait inside would also drain the tile prefetch)
-#pragma unroll
-      for (int k = 0; k < kKSteps; ++k) asm volatile("" : "+v"(qf[k]));
-    }
+    const int item_ts = m.tile_start[c_item], item_te = m.tile_start[c_item + 1];
+    const int seg_begin = ctile;
+    const int seg_end = item_te < t1 ? item_te : t1;
+    // the item's queries (lanes of heads >= H keep zeros); the load block waits
+    // for them, which also drains the tile copies in flight (once per segment)
+    if (wave_active && head_ok)
+      load_q(a.q_lat + c_item * a.q_lat_st + head * a.q_lat_sh + 8 * g,
+             a.q_pe + c_item * a.q_pe_st + head * a.q_pe_sh + 8 * g);
     float m_ref = 0.f, l_sum = 0.f;
     const int vlo = m.item_lo[c_item], vhi = m.item_hi[c_item];
-    const int tok_first = ((vlo >> 5) + static_cast<int>(seg_begin - item_ts)) * kTile;
+    const int tok_first = ((vlo >> 5) + (seg_begin - item_ts)) * kTile;
 
-    for (int64_t tt = seg_begin; tt < seg_end; ++tt, ++tn) {
-      const int rem = ntiles - tn - 1;
-      if (rem >= 2) wait_vmcnt<2 * kLoadsPerTile>();
-      else if (rem == 1) wait_vmcnt<kLoadsPerTile>();
+    for (int tt = seg_begin; tt < seg_end; ++tt, ++tn) {
+      if (tn + 1 < ntiles) wait_vmcnt<kLoads>();
       else wait_vmcnt<0>();
       __syncthreads();
-      if (tn + 3 < ntiles) {
-        l_item = advance_item(m, a.num_items, l_item, l_tile);
-        issue_tile<NW>(a, m, tile_info(m, l_item, l_tile), bufs[(tn + 3) & 3], wave, lane, lofs);
-        ++l_tile;
+      // copies of tile tn + 2: inside the step block when the tile is
+      // contiguous, else issued here
+      const bool copy = tn + 2 < ntiles;
+      const uint32_t lds_copy = __builtin_amdgcn_readfirstlane(lds_wave + ((tn + 2) & 3) * kTileBytes);
+      const int tok0 = tok_first + (tt - seg_begin) * kTile;
+      const bool masked = !(tok0 >= vlo && tok0 + kTile <= vhi);
+      const bool fused_copy = copy && wave_active && tt != seg_begin && !masked && cursor_contiguous(cur, a);
+      const char* sb = nullptr;
+      if (copy) {
+        if (fused_copy) sb = cursor_src(cur, a);
+        else cursor_copy<NW>(cur, a, lds_copy, lofs);
+        cursor_advance(cur, a, m);
       }
-      LDS_PTR(char) buf = bufs[tn & 3];
-      const int tok0 = tok_first + static_cast<int>(tt - seg_begin) * kTile;
-
-      if (wave_active) {
-        // S^T = K Q^T  (32 tokens x 32 heads)
-        const uint32_t bufa = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(buf));
-        const uint32_t kaddr[4] = {bufa + koff[0], bufa + koff[1], bufa + koff[2], bufa + koff[3]};
-        f32x16 s = tile_scores(kaddr, qf);
-
-        // mask + scale (log2 domain), tile max per head; only the first and
-        // last tiles of an item hold positions outside the visible range
-        float tmax = -INFINITY;
-        if (tok0 >= vlo && tok0 + kTile <= vhi) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            s[i] *= a.scale_log2;
-            tmax = fmaxf(tmax, s[i]);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int tok = tok0 + 8 * (i >> 2) + 4 * g + (i & 3);
-            const float v = (tok >= vlo && tok < vhi) ? s[i] * a.scale_log2 : -INFINITY;
-            s[i] = v;
-            tmax = fmaxf(tmax, v);
-          }
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        // The reference maximum is fixed by the segment's first tile; later
-        // tiles may exceed it by up to kRefSlack (probabilities <= 2^kRefSlack,
-        // far inside fp32 and bf16 range).  A larger jump marks this workgroup's
-        // range for recomputation by the plain kernel (rare; never silently wrong).
-        if (tt == seg_begin) m_ref = tmax;
-        else if (tmax > m_ref + kRefSlack) overflow = true;
-        bf16x8 pb[2];
-        float psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(s[i] - m_ref);
-          psum += p;
-          pb[i >> 3][i & 7] = static_cast<__bf16>(p);
-        }
-        l_sum += psum;
-
-        // O^T += V^T P^T : 16 dim tiles x 2 token steps
-        tile_pv(acc, bufa + voff_even, bufa + voff_odd, bufa + voff_even_h, bufa + voff_odd_h, pb[0],
-                pb[1]);
+      if (!wave_active) continue;
+      const uint32_t bs = lds_base + (tn & 3) * kTileBytes;
+      const uint32_t bp = lds_base + ((tn - 1) & 3) * kTileBytes;
+      // masked tiles: element i of a lane is visible iff lo <= 8 (i / 4) + i % 4 < hi
+      const int lo = vlo - tok0 - 4 * g, hi = vhi - tok0 - 4 * g;
+      if (tt == seg_begin) {
+        if (masked) tile_first_m1(koff, bs, c, m_ref, l_sum, ovf, lo, hi);
+        else tile_first_m0(koff, bs, c, m_ref, l_sum, ovf);
+      } else if (tt - 1 == seg_begin) {  // first values step of the segment: O starts at 0
+        if (masked) tile_step_d0_f1_m1(koff, voff, bs, bp, c, m_ref, l_sum, ovf, lo, hi);
+        else if (fused_copy) tile_step_d1_f1_m0(koff, voff, bs, bp, c, m_ref, l_sum, ovf, sb, lds_copy, lofs);
+        else tile_step_d0_f1_m0(koff, voff, bs, bp, c, m_ref, l_sum, ovf);
+      } else {
+        if (masked) tile_step_d0_f0_m1(koff, voff, bs, bp, c, m_ref, l_sum, ovf, lo, hi);
+        else if (fused_copy) tile_step_d1_f0_m0(koff, voff, bs, bp, c, m_ref, l_sum, ovf, sb, lds_copy, lofs);
+        else tile_step_d0_f0_m0(koff, voff, bs, bp, c, m_ref, l_sum, ovf);
       }
     }
     ctile = seg_end;
 
-    // ---- segment done: write the unnormalised accumulator, lse and 1/l ----
-    // (no arithmetic on the accumulator registers: consumers apply 1/l)
+    // ---- segment done: last values step, then the unnormalised accumulator,
+    // lse and 1/l (no arithmetic on the accumulator registers: consumers apply 1/l)
+    if (wave_active) {
+      const uint32_t bp = lds_base + ((tn - 1) & 3) * kTileBytes;
+      if (seg_end - 1 == seg_begin) tile_pv_f1(voff, bp);
+      else tile_pv_f0(voff, bp);
+    }
     const float l_tot = wave_active ? l_sum + __shfl_xor(l_sum, 32, 64) : 1.f;
     const bool complete = (seg_begin == item_ts) && (seg_end == item_te);
     float* o_dst;
@@ -674,23 +418,14 @@ __global__ __launch_bounds__(NW * 64, 1) void attn_mfma_kernel(
       scl_dst = a.part_scale + slot * a.H;
     }
     if (wave_active && head_ok) {
-      float* orow = o_dst + static_cast<int64_t>(head) * kR;
-#pragma unroll
-      for (int mt = 0; mt < kMTiles; ++mt) {
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const f32x4 v = {acc[mt][4 * a4 + 0], acc[mt][4 * a4 + 1], acc[mt][4 * a4 + 2],
-                           acc[mt][4 * a4 + 3]};
-          *reinterpret_cast<f32x4*>(orow + 32 * mt + 8 * a4 + 4 * g) = v;
-        }
-      }
+      store_acc(o_dst + static_cast<int64_t>(head) * kR + 4 * g);
       if (g == 0) {
         lse_dst[head] = (m_ref + log2f(l_tot)) * kLn2;
         scl_dst[head] = 1.0f / l_tot;
       }
     }
   }
-  if (__any(overflow) && lane == 0) wg_overflow = 1;
+  if (__any(ovf != 0.f) && lane == 0) wg_overflow = 1;
   __syncthreads();
   if (threadIdx.x == 0) a.redo[wg] = wg_overflow;
 }
@@ -703,7 +438,7 @@ bool mfma_attn_supported(const CacheView& kv, int32_t H) {
 
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(attn_mfma_kernel<4>, dim3(a.G), dim3(256), 0, s, a, a.item_b, a.item_lo,
-                     a.item_hi, a.tile_start, a.block_tables);
+                     a.item_hi, a.tile_start, a.block_tables, a.wg_tile, a.wg_item);
   return hipGetLastError();
 }
 

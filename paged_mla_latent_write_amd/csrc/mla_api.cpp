@@ -64,7 +64,8 @@ size_t elem_bytes(int dtype) { return dtype == MLA_KV_BF16 ? 2 : 1; }
 struct Layout {
   int G = 0;
   size_t q_lat = 0, o_lat = 0, lse = 0, o_scale = 0, item_b = 0, item_lo = 0, item_hi = 0,
-         tile_start = 0, part_o = 0, part_lse = 0, part_scale = 0, redo = 0, total = 0;
+         tile_start = 0, wg_tile = 0, wg_item = 0, part_o = 0, part_lse = 0, part_scale = 0,
+         redo = 0, total = 0;
 };
 
 // Returns false when the number of workgroups cannot be determined.
@@ -93,6 +94,10 @@ bool make_layout(const mla_cache* c, const mla_attn* a, int64_t num_items, Layou
   off = align_up(off + sizeof(int32_t) * num_items);
   L->tile_start = off;
   off = align_up(off + sizeof(int32_t) * (num_items + 1));
+  L->wg_tile = off;
+  off = align_up(off + sizeof(int32_t) * (G + 1));
+  L->wg_item = off;
+  off = align_up(off + sizeof(int32_t) * G);
   L->part_o = off;
   off = align_up(off + sizeof(float) * 2 * G * H * R);
   L->part_lse = off;
@@ -183,6 +188,9 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
   plan.item_lo = at<int32_t>(workspace, L.item_lo);
   plan.item_hi = at<int32_t>(workspace, L.item_hi);
   plan.tile_start = at<int32_t>(workspace, L.tile_start);
+  plan.wg_tile = at<int32_t>(workspace, L.wg_tile);
+  plan.wg_item = at<int32_t>(workspace, L.wg_item);
+  plan.G = L.G;
   e = mla::launch_plan(mode, batch, num_items, context_lens, qsl, attn->window,
                        static_cast<int32_t>(max_ctx64), plan, s);
   if (e != hipSuccess) return MLA_ERR_HIP;
@@ -202,6 +210,8 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
   a.item_lo = plan.item_lo;
   a.item_hi = plan.item_hi;
   a.tile_start = plan.tile_start;
+  a.wg_tile = plan.wg_tile;
+  a.wg_item = plan.wg_item;
   a.num_items = num_items;
   a.H = H;
   a.G = L.G;

@@ -35,6 +35,9 @@ struct Plan {
   int32_t* item_lo;      // [Nq] first visible key position
   int32_t* item_hi;      // [Nq] one past the last visible key position
   int32_t* tile_start;   // [Nq + 1] exclusive prefix sum of the items' tile counts
+  int32_t* wg_tile;      // [G + 1] first tile of each workgroup's range (wg_tile_begin)
+  int32_t* wg_item;      // [G] item owning each workgroup's first tile
+  int32_t G;             // workgroups the tile stream is divided over
 };
 
 struct AttnArgs {
@@ -49,6 +52,8 @@ struct AttnArgs {
   const int32_t* item_lo;
   const int32_t* item_hi;
   const int32_t* tile_start;
+  const int32_t* wg_tile;  // [G + 1] (see Plan)
+  const int32_t* wg_item;  // [G]
   int32_t num_items;
   int32_t H;
   int32_t G;              // workgroups the tile stream is divided over
