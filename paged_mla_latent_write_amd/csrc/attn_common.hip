@@ -31,7 +31,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_items_kernel(
     const int32_t* __restrict__ qsl, int32_t window, int32_t max_ctx, int32_t* __restrict__ item_b,
     int32_t* __restrict__ item_lo, int32_t* __restrict__ item_hi,
     int32_t* __restrict__ tile_start, int32_t G, int32_t* __restrict__ wg_tile,
-    int32_t* __restrict__ wg_item) {
+    int32_t* __restrict__ wg_item, int32_t* __restrict__ item_wg) {
   __shared__ int32_t buf[kPlanThreads];
   __shared__ int32_t carry;
   const int tid = threadIdx.x;
@@ -98,23 +98,31 @@ __global__ __launch_bounds__(kPlanThreads) void plan_items_kernel(
       wg_item[g] = lo;
     }
   }
+  // The first and last workgroup covering each item (equal when one workgroup
+  // holds all of the item's tiles; both -1 for an item with no tiles).
+  for (int i = tid; i < Nq; i += kPlanThreads) {
+    const int64_t ts = tile_start[i], te = tile_start[i + 1];
+    item_wg[2 * i] = te > ts ? static_cast<int32_t>(wg_of_tile(ts, W, G)) : -1;
+    item_wg[2 * i + 1] = te > ts ? static_cast<int32_t>(wg_of_tile(te - 1, W, G)) : -1;
+  }
 }
 
 // One wave per (item, head).  Items whose tiles all fell to one workgroup were
 // finished by the attention kernel; empty items get o = 0, lse = -inf; cut
 // items are merged from the partial slots of the workgroups that cover them
-// (slot 2g+1 for the first, which the item starts in, slot 2g after it).  The
-// merged row is written normalised (its o_scale set to 1).
+// (slot 2g+1 for the first, which the item starts in, slot 2g after it), in
+// one pass with a running maximum.  The merged row is written normalised (its
+// o_scale set to 1).
 __global__ __launch_bounds__(256) void combine_segments_kernel(AttnArgs a) {
   const int i = blockIdx.x;
   const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int H = a.H, R = a.kv.R;
   if (h >= H) return;
-  const int64_t ts = a.tile_start[i], te = a.tile_start[i + 1];
   const int64_t row = static_cast<int64_t>(i) * H + h;
   float* dst = a.o_lat + row * R;
-  if (ts == te) {
+  const int g0 = a.item_wg[2 * i], g1 = a.item_wg[2 * i + 1];
+  if (g0 < 0) {
     for (int r = lane; r < R; r += 64) dst[r] = 0.f;
     if (lane == 0) {
       a.lse[row] = -INFINITY;
@@ -122,52 +130,65 @@ __global__ __launch_bounds__(256) void combine_segments_kernel(AttnArgs a) {
     }
     return;
   }
-  const int64_t W = a.tile_start[a.num_items];
-  const int64_t G = a.G;
-  const int64_t g0 = wg_of_tile(ts, W, G), g1 = wg_of_tile(te - 1, W, G);
   if (g0 == g1) return;
-  float mx = -INFINITY;
-  for (int64_t g = g0; g <= g1; ++g) {
-    if (wg_tile_begin(g, W, G) == wg_tile_begin(g + 1, W, G)) continue;
-    const int64_t slot = (g == g0) ? 2 * g + 1 : 2 * g;
-    mx = fmaxf(mx, a.part_lse[slot * H + h]);
-  }
-  float tot = 0.f;
-  for (int64_t g = g0; g <= g1; ++g) {
-    if (wg_tile_begin(g, W, G) == wg_tile_begin(g + 1, W, G)) continue;
-    const int64_t slot = (g == g0) ? 2 * g + 1 : 2 * g;
-    const float l = a.part_lse[slot * H + h];
-    tot += (l == -INFINITY) ? 0.f : expf(l - mx);
-  }
-  const float inv_tot = 1.f / tot;
-  // each lane owns 8 consecutive columns; the segment loop only carries the
-  // accumulators, so the loads of successive segments are issued back to back
   for (int r0 = lane * 8; r0 < R; r0 += 512) {
+    float m = -INFINITY, tot = 0.f;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int64_t g = g0; g <= g1; ++g) {
-      if (wg_tile_begin(g, W, G) == wg_tile_begin(g + 1, W, G)) continue;
-      const int64_t slot = (g == g0) ? 2 * g + 1 : 2 * g;
-      const float l = a.part_lse[slot * H + h];
-      const float w = (l == -INFINITY) ? 0.f : expf(l - mx) * a.part_scale[slot * H + h] * inv_tot;
-      const float4* src = reinterpret_cast<const float4*>(a.part_o + (slot * H + h) * R + r0);
-      const float4 x0 = src[0], x1 = src[1];
-      acc[0] = fmaf(w, x0.x, acc[0]);
-      acc[1] = fmaf(w, x0.y, acc[1]);
-      acc[2] = fmaf(w, x0.z, acc[2]);
-      acc[3] = fmaf(w, x0.w, acc[3]);
-      acc[4] = fmaf(w, x1.x, acc[4]);
-      acc[5] = fmaf(w, x1.y, acc[5]);
-      acc[6] = fmaf(w, x1.z, acc[6]);
-      acc[7] = fmaf(w, x1.w, acc[7]);
+    // segments in batches of kB: the batch's loads are issued together, then
+    // merged against the running maximum
+    constexpr int kB = 8;
+    for (int gb = g0; gb <= g1; gb += kB) {
+      float l[kB], sc[kB];
+      float4 x0[kB], x1[kB];
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        const int g = gb + j;
+        const bool live = g <= g1 && a.wg_tile[g] != a.wg_tile[g + 1];  // (no tiles: no slot)
+        const int64_t slot = (g == g0) ? 2 * g + 1 : 2 * g;
+        l[j] = live ? a.part_lse[slot * H + h] : -INFINITY;
+        sc[j] = live ? a.part_scale[slot * H + h] : 0.f;
+        if (live) {
+          const float4* src = reinterpret_cast<const float4*>(a.part_o + (slot * H + h) * R + r0);
+          x0[j] = src[0];
+          x1[j] = src[1];
+        } else {
+          x0[j] = x1[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+      float mb = m;
+#pragma unroll
+      for (int j = 0; j < kB; ++j) mb = fmaxf(mb, l[j]);
+      if (mb > m) {  // wave-uniform: rescale what was merged so far
+        const float f = expf(m - mb);
+        tot *= f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= f;
+        m = mb;
+      }
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        if (l[j] == -INFINITY) continue;
+        const float e_l = expf(l[j] - m);
+        tot += e_l;
+        const float w = e_l * sc[j];
+        acc[0] = fmaf(w, x0[j].x, acc[0]);
+        acc[1] = fmaf(w, x0[j].y, acc[1]);
+        acc[2] = fmaf(w, x0[j].z, acc[2]);
+        acc[3] = fmaf(w, x0[j].w, acc[3]);
+        acc[4] = fmaf(w, x1[j].x, acc[4]);
+        acc[5] = fmaf(w, x1[j].y, acc[5]);
+        acc[6] = fmaf(w, x1[j].z, acc[6]);
+        acc[7] = fmaf(w, x1[j].w, acc[7]);
+      }
     }
+    const float inv = tot > 0.f ? 1.f / tot : 0.f;
     float4* d4 = reinterpret_cast<float4*>(dst + r0);
-    d4[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    d4[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-  }
-  if (lane == 0) {
-    a.lse[row] = mx + logf(tot);
-    a.o_scale[row] = 1.f;
+    d4[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    d4[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+    if (lane == 0 && r0 == 0) {
+      a.lse[row] = tot > 0.f ? m + logf(tot) : -INFINITY;
+      a.o_scale[row] = 1.f;
+    }
   }
 }
 
@@ -291,7 +312,8 @@ hipError_t launch_plan(int mode, int32_t batch, int32_t num_items, const int32_t
                        const Plan& plan, hipStream_t s) {
   hipLaunchKernelGGL(plan_items_kernel, dim3(1), dim3(kPlanThreads), 0, s, mode, batch, num_items,
                      context_lens, query_start_loc, window, max_ctx, plan.item_b, plan.item_lo,
-                     plan.item_hi, plan.tile_start, plan.G, plan.wg_tile, plan.wg_item);
+                     plan.item_hi, plan.tile_start, plan.G, plan.wg_tile, plan.wg_item,
+                     plan.item_wg);
   return hipGetLastError();
 }
 

@@ -42,12 +42,13 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a, int hpb) 
   float* al_s = l_s + hpb;           // [hpb]
 
   const int64_t g = blockIdx.x;
-  if (a.redo_only && a.redo_only[g] == 0) return;
-  const int h0 = blockIdx.y * hpb;
-  const int nh = min(hpb, a.H - h0);
   const int64_t W = a.tile_start[a.num_items];
   const int64_t t0 = wg_tile_begin(g, W, a.G), t1 = wg_tile_begin(g + 1, W, a.G);
   if (t0 >= t1) return;
+  // head blocks: one per grid row (the grid may also have fewer rows)
+  for (int hb = blockIdx.y; hb * hpb < a.H; hb += gridDim.y) {
+  const int h0 = hb * hpb;
+  const int nh = min(hpb, a.H - h0);
 
   // item containing tile t0: largest i with tile_start[i] <= t0
   int lo = 0, hi = a.num_items;
@@ -168,6 +169,8 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a, int hpb) 
     }
     __syncthreads();
     t = seg_end;
+  }
+  __syncthreads();  // the next head block reuses the shared buffers
   }
 }
 

@@ -13,29 +13,31 @@
 // Design (one workgroup of four waves per compute unit):
 //  * wave w owns heads [32w, 32w + 32).  Its query block Q[32 x 576] lives in
 //    VGPRs as the B operand of S^T = K Q^T (36 fragments of 16 dims), and its
-//    accumulator O^T[512 x 32] (fp32) as 16 MFMA 32x32 tiles in AGPRs.
+//    accumulator O^T[512 x 32] (fp32) as 16 MFMA 32x32 tiles in AGPRs.  Both
+//    sit in registers the compiler is not given (see attn_mfma_asm.inc).
 //  * the key/value stream is cut into 32-token tiles (36 KB of bf16 latents).
 //    Each tile is copied HBM -> LDS with global_load_lds (16 B per lane, no
-//    VGPR staging) into one of 4 buffers, three tiles ahead of the compute, and
+//    VGPR staging) into one of 4 buffers, two tiles ahead of the compute, and
 //    is shared by all waves (so every head reads each KV byte from HBM once).
-//  * S^T (32 tokens x 32 heads) = 36 v_mfma_f32_32x32x16_bf16 with K rows read
-//    by ds_read_b128; the softmax runs in the MFMA output layout (each lane
-//    holds 16 tokens of one head; one cross-half exchange per reduction); the
-//    probabilities are rounded to bf16 in registers and used directly as the B
-//    operand of O^T += V^T P^T (32 MFMAs per tile), whose A operand is read
-//    transposed from the same LDS tile by ds_read_b64_tr_b16.  The token order
-//    inside each 16-token MFMA step is the one the MFMA output layout gives;
-//    the V^T reads use the same order, so no shuffle of P is needed.
-//  * online softmax in base 2 against a reference maximum fixed at each
-//    segment's first tile, so the accumulators are never rescaled: only MFMAs
-//    write them and only the final stores read them (any VALU work on them
-//    would not fit the register file next to Q).  Later tiles may exceed the
-//    reference by up to 2^64 in probability; a bigger jump flags the
-//    workgroup, whose range the plain kernel then recomputes.  The kernel
-//    writes the unnormalised O with lse and 1/l; consumers apply 1/l.
-//  * LDS rows are 1152 B; 16-byte chunks are XOR-swizzled per token
-//    (chunk ^ (2 (t mod 4) + (t div 4) mod 2) within groups of 8) so both the
-//    row reads and the transposed reads hit distinct banks.
+//  * tile step t (one inline-assembly block per wave): S^T(t) = 36
+//    v_mfma_f32_32x32x16_bf16 with K rows read by ds_read_b128 and the copies
+//    of tile t + 2 issued between them; then O^T += V^T P^T for tile t - 1 (32
+//    MFMAs, V^T read transposed from that tile's buffer by ds_read_b64_tr_b16)
+//    with the softmax of tile t interleaved.  The softmax runs in the MFMA
+//    output layout (each lane holds 16 tokens of one head; one cross-half
+//    exchange per reduction); P is rounded to bf16 in registers and used
+//    directly as the B operand.  The token order inside each 16-token MFMA step
+//    is the one the MFMA output layout gives; the V^T reads use the same order,
+//    so no shuffle of P is needed.
+//  * softmax in base 2 against a reference maximum set at each segment's first
+//    tile, so the accumulators are normally never rescaled.  A tile whose max
+//    passes the reference by more than 16 moves the reference up: the row sum
+//    is scaled in the block and the accumulators right after it (rare; the
+//    probabilities stay <= 2^16).  The kernel writes the unnormalised O with
+//    lse and 1/l; consumers apply 1/l.
+//  * LDS rows are 1152 B; 16-byte chunks are XOR-swizzled per token within
+//    groups of 8 (swz below, from bits 1-3 of the token index) so both the row
+//    reads and the transposed reads hit distinct banks.
 #include <math.h>
 
 #include "device_utils.h"
@@ -58,7 +60,6 @@ constexpr int kTileBytes = kTile * kRowBytes; // 36864
 constexpr int kChunksPerTile = kTile * kD / 8; // 2304 16-byte chunks
 constexpr int kKSteps = kD / 16;              // 36
 constexpr int kMTiles = kR / 32;              // 16
-constexpr float kRefSlack = 64.0f;
 
 #define LDS_PTR(T) __attribute__((address_space(3))) T*
 
@@ -260,15 +261,8 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
   const bool wave_active = wave * 32 < a.H;
 
   const int64_t wg = blockIdx.x;
-  // redo[wg] is written once per launch by thread 0 (no separate memset, so
-  // the call stays capturable): 1 if a score ran past the reference maximum.
-  __shared__ int wg_overflow;
-  if (threadIdx.x == 0) wg_overflow = 0;
   const int t0 = m.wg_tile[wg], t1 = m.wg_tile[wg + 1];
-  if (t0 >= t1) {
-    if (threadIdx.x == 0) a.redo[wg] = 0;
-    return;
-  }
+  if (t0 >= t1) return;
   const int ntiles = t1 - t0;
   const int first_item = m.wg_item[wg];
 
@@ -334,7 +328,6 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
   voff[3] = voff_odd_h;
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(bufs[0]));
   const float c = a.scale_log2;
-  float ovf = 0.f;  // 1 once a score ran past its segment's reference maximum
 
   // Q (v54-v197) and the O^T accumulators (a0-a255) live in registers the
   // compiler does not allocate; only the blocks of attn_mfma_asm.inc touch them.
@@ -359,6 +352,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
     const int tok_first = ((vlo >> 5) + (seg_begin - item_ts)) * kTile;
 
     for (int tt = seg_begin; tt < seg_end; ++tt, ++tn) {
+      // tile tn landed (the copy of tile tn + 1 may still be in flight)
       if (tn + 1 < ntiles) wait_vmcnt<kLoads>();
       else wait_vmcnt<0>();
       __syncthreads();
@@ -381,16 +375,20 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
       // masked tiles: element i of a lane is visible iff lo <= 8 (i / 4) + i % 4 < hi
       const int lo = vlo - tok0 - 4 * g, hi = vhi - tok0 - 4 * g;
       if (tt == seg_begin) {
-        if (masked) tile_first_m1(koff, bs, c, m_ref, l_sum, ovf, lo, hi);
-        else tile_first_m0(koff, bs, c, m_ref, l_sum, ovf);
-      } else if (tt - 1 == seg_begin) {  // first values step of the segment: O starts at 0
-        if (masked) tile_step_d0_f1_m1(koff, voff, bs, bp, c, m_ref, l_sum, ovf, lo, hi);
-        else if (fused_copy) tile_step_d1_f1_m0(koff, voff, bs, bp, c, m_ref, l_sum, ovf, sb, lds_copy, lofs);
-        else tile_step_d0_f1_m0(koff, voff, bs, bp, c, m_ref, l_sum, ovf);
+        if (masked) tile_first_m1(koff, bs, c, m_ref, l_sum, lo, hi);
+        else tile_first_m0(koff, bs, c, m_ref, l_sum);
       } else {
-        if (masked) tile_step_d0_f0_m1(koff, voff, bs, bp, c, m_ref, l_sum, ovf, lo, hi);
-        else if (fused_copy) tile_step_d1_f0_m0(koff, voff, bs, bp, c, m_ref, l_sum, ovf, sb, lds_copy, lofs);
-        else tile_step_d0_f0_m0(koff, voff, bs, bp, c, m_ref, l_sum, ovf);
+        float fac;  // 2^(old - new) reference when the tile moved it, else 1
+        if (tt - 1 == seg_begin) {  // first values step of the segment: O starts at 0
+          if (masked) tile_step_d0_f1_m1(koff, voff, bs, bp, c, m_ref, l_sum, fac, lo, hi);
+          else if (fused_copy) tile_step_d1_f1_m0(koff, voff, bs, bp, c, m_ref, l_sum, fac, sb, lds_copy, lofs);
+          else tile_step_d0_f1_m0(koff, voff, bs, bp, c, m_ref, l_sum, fac);
+        } else {
+          if (masked) tile_step_d0_f0_m1(koff, voff, bs, bp, c, m_ref, l_sum, fac, lo, hi);
+          else if (fused_copy) tile_step_d1_f0_m0(koff, voff, bs, bp, c, m_ref, l_sum, fac, sb, lds_copy, lofs);
+          else tile_step_d0_f0_m0(koff, voff, bs, bp, c, m_ref, l_sum, fac);
+        }
+        if (__any(fac != 1.f)) rescale_acc(fac);  // rare: a score far above the reference
       }
     }
     ctile = seg_end;
@@ -425,9 +423,6 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
       }
     }
   }
-  if (__any(ovf != 0.f) && lane == 0) wg_overflow = 1;
-  __syncthreads();
-  if (threadIdx.x == 0) a.redo[wg] = wg_overflow;
 }
 
 }  // namespace

@@ -24,9 +24,10 @@ A tile step is one inline-assembly statement of one wave:
     with the softmax of tile t interleaved between them (a wave issues VALU
     work while its own MFMAs run);
   * softmax of tile t: mask (partial tiles), scale, tile max per head (the two
-    wave halves hold the same heads: one permlane32 swap), overflow check
-    against the segment's reference maximum, exp2, row sums, and P rounded to
-    bf16 (RNE).
+    wave halves hold the same heads: one permlane32 swap), a check against the
+    segment's reference maximum (moved up, with a rescale, when the tile max
+    passes it by more than the slack), exp2, row sums, and P rounded to bf16
+    (RNE).
 """
 import sys
 
@@ -39,7 +40,7 @@ RING = 232                  # v232-v255
 NF = 6                      # LDS fragments in flight
 T0, T1 = TT + 8, TT + 9     # softmax temporaries (free after the sum)
 NEG_INF = "0xff800000"
-C64 = "0x42800000"          # 64.0f: slack of the fixed reference maximum (log2 units)
+SLACK = "0x41800000"        # 16.0f: slack of the reference maximum (log2 units)
 
 VCLOB_ALL = ", ".join(f'"v{r}"' for r in range(NC, 256))
 ACLOB_ALL = ", ".join(f'"a{r}"' for r in range(256))
@@ -96,10 +97,18 @@ def softmax_ops(first, masked):
     if first:
         ops.append(f"v_mov_b32 %[mref], v{T0}")
     else:
-        # overflow: tile max > reference + 64 (NaN compares false: no flag)
-        ops += [f"v_add_f32 v{T1}, {C64}, %[mref]",
-                f"v_cmp_ngt_f32 vcc, v{T0}, v{T1}",
-                "v_cndmask_b32 %[ovf], 1.0, %[ovf], vcc"]
+        # A tile max above reference + slack moves the reference up to it: the
+        # row sum is scaled here and fac = 2^(old - new) is returned so that the
+        # caller scales the accumulators (after this block's values step, which
+        # still used the old reference).  NaN compares false: nothing moves.
+        ops += [f"v_add_f32 v{T1}, {SLACK}, %[mref]",
+                f"v_cmp_gt_f32 vcc, v{T0}, v{T1}",
+                f"v_sub_f32 v{T1}, %[mref], v{T0}",
+                f"v_exp_f32 v{T1}, v{T1}",
+                "s_nop 0",
+                f"v_cndmask_b32 %[fac], 1.0, v{T1}, vcc",
+                f"v_cndmask_b32 %[mref], %[mref], v{T0}, vcc",
+                "v_mul_f32 %[lsum], %[lsum], %[fac]"]
     ops += [f"v_sub_f32 {s[i]}, {s[i]}, %[mref]" for i in range(16)]
     ops += [f"v_exp_f32 {s[i]}, {s[i]}" for i in range(16)]
     ops.append("s_nop 0")
@@ -194,7 +203,8 @@ def cstr(lines, indent="      "):
 
 KOFF = '[k0] "+v"(koff[0]), [k1] "+v"(koff[1]), [k2] "+v"(koff[2]), [k3] "+v"(koff[3])'
 VOFF = '[v0] "+v"(voff[0]), [v1] "+v"(voff[1]), [v2] "+v"(voff[2]), [v3] "+v"(voff[3])'
-STATS = '[mref] "+v"(mref), [lsum] "+v"(lsum), [ovf] "+v"(ovf)'
+STATS = '[mref] "+v"(mref), [lsum] "+v"(lsum)'
+FAC = '[fac] "=&v"(fac)'
 DMA_IN = ('[sb] "s"(sb), [m0] "s"(m0b), [l0] "v"(lofs[0]), [l1] "v"(lofs[1]), [l2] "v"(lofs[2]), '
           '[l3] "v"(lofs[3]), [l4] "v"(lofs[4])')
 CLOBBERS = '"vcc", "memory", MLA_VCLOBBERS, MLA_ACLOBBERS'
@@ -224,7 +234,7 @@ def emit():
                 if dma and masked:
                     continue
                 args = ["uint32_t (&koff)[4]", "uint32_t (&voff)[4]", "uint32_t bs", "uint32_t bp", "float c",
-                        "float& mref", "float& lsum", "float& ovf"]
+                        "float& mref", "float& lsum", "float& fac"]
                 ins = ['[bs] "s"(bs), [bp] "s"(bp), [c] "s"(c)']
                 if masked:
                     args += ["int lo", "int hi"]
@@ -233,11 +243,11 @@ def emit():
                     args += ["const char* sb", "uint32_t m0b", "const uint32_t (&lofs)[5]"]
                     ins.append(DMA_IN)
                 body = s_part(dma, True) + pv_part(first_pv, softmax_ops(False, masked), P_FIXED)
-                o += block(f"tile_step_d{dma}_f{first_pv}_m{masked}", args, body, [STATS, KOFF, VOFF], ins,
+                o += block(f"tile_step_d{dma}_f{first_pv}_m{masked}", args, body, [STATS, FAC, KOFF, VOFF], ins,
                            ', "m0"' if dma else "")
     # first tile of a segment: S(t) and softmax(t) (sets the reference maximum)
     for masked in (0, 1):
-        args = ["uint32_t (&koff)[4]", "uint32_t bs", "float c", "float& mref", "float& lsum", "float& ovf"]
+        args = ["uint32_t (&koff)[4]", "uint32_t bs", "float c", "float& mref", "float& lsum"]
         ins = ['[bs] "s"(bs), [c] "s"(c)']
         if masked:
             args += ["int lo", "int hi"]
@@ -266,6 +276,12 @@ def emit():
             L.append(f"global_store_dwordx4 %[orow], v[{r}:{r + 3}], off offset:{4 * (32 * mt + 8 * a4)}")
             n += 1
     o += block("store_acc", ["float* orow"], L, [], ['[orow] "v"(orow)'])
+    # scale this lane's accumulators by fac (rare: after a reference move)
+    L = ["s_nop 7", "s_nop 7", "s_nop 4"]  # the last MFMA results must have landed
+    for r in range(256):
+        t = RING + (r % 24)
+        L += [f"v_accvgpr_read_b32 v{t}, a{r}", f"v_mul_f32 v{t}, %[fac], v{t}", f"v_accvgpr_write_b32 a{r}, v{t}"]
+    o += block("rescale_acc", ["float fac"], L, [], ['[fac] "v"(fac)'])
     return "\n".join(o)
 
 

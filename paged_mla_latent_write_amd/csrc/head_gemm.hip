@@ -6,8 +6,8 @@
 // this library's, as is folding W_UK into the query and W_UV into the output.
 //
 // Both are batched (one GEMM per head) with M = query items.  A workgroup of
-// four waves owns one head and 32 * MT items; each wave computes 32 output
-// columns with v_mfma_f32_32x32x16_bf16.
+// four waves owns one head and 32 * MT items (absorb: and 128 of the R output
+// columns); each wave computes 32 output columns with v_mfma_f32_32x32x16_bf16.
 //  * absorb: the W_UK[h] column block is staged in LDS (rows padded to 288 B)
 //    and read as the B operand with ds_read_b64_tr_b16 (W_UK rows run along
 //    the output dimension, the MFMA wants runs along K).  bf16 in, fp32
@@ -41,8 +41,9 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* __rest
                                                           int32_t Nq, int32_t H, int32_t Dn,
                                                           int32_t R, uint16_t* __restrict__ q_lat) {
   __shared__ __attribute__((aligned(16))) char wt[kAbsMaxDn * kAbsPitch];
+  const int c0 = blockIdx.x * kAbsCols;  // this workgroup's 128 output columns
   const int h = blockIdx.y;
-  const int m0 = blockIdx.x * 32 * MT;
+  const int m0 = blockIdx.z * 32 * MT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, n32 = lane & 31;
   const int ksteps = Dn / 16;
@@ -66,13 +67,22 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* __rest
   const int tr_off = (8 * g + rr) * kAbsPitch + (32 * wave + 16 * (q & 1) + 4 * c4) * 2;
   const uint16_t* wh = w_uk + static_cast<int64_t>(h) * Dn * R;
 
-  for (int c0 = 0; c0 < R; c0 += kAbsCols) {
-    __syncthreads();
-    // stage W_UK[h][0:Dn][c0 : c0 + 128] (16 B per thread per step)
-    for (int idx = threadIdx.x; idx < Dn * (kAbsCols / 8); idx += 256) {
+  {
+    // stage W_UK[h][0:Dn][c0 : c0 + 128]: all loads first (16 B per thread
+    // per step), then the LDS stores
+    constexpr int kStage = kAbsMaxDn * (kAbsCols / 8) / 256;
+    i16x8 wv[kStage];
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) {
+      const int idx = threadIdx.x + 256 * j;
       const int d = idx / (kAbsCols / 8), c = idx % (kAbsCols / 8);
-      *reinterpret_cast<i16x8*>(wt + d * kAbsPitch + c * 16) =
-          *reinterpret_cast<const i16x8*>(wh + static_cast<int64_t>(d) * R + c0 + 8 * c);
+      if (d < Dn) wv[j] = *reinterpret_cast<const i16x8*>(wh + static_cast<int64_t>(d) * R + c0 + 8 * c);
+    }
+#pragma unroll
+    for (int j = 0; j < kStage; ++j) {
+      const int idx = threadIdx.x + 256 * j;
+      const int d = idx / (kAbsCols / 8), c = idx % (kAbsCols / 8);
+      if (d < Dn) *reinterpret_cast<i16x8*>(wt + d * kAbsPitch + c * 16) = wv[j];
     }
     __syncthreads();
     f32x16 acc[MT];
@@ -130,24 +140,41 @@ __global__ __launch_bounds__(256) void up_project_mfma_kernel(const float* __res
   f32x16 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
-  for (int k0 = 0; k0 < R; k0 += 16) {
-    const i16x8 b = *reinterpret_cast<const i16x8*>(wrow + k0 + 8 * g);
+  // K in chunks of kU 16-wide steps: every load of a chunk is issued before
+  // its first MFMA, so the loop waits for memory once per chunk, not per step
+  constexpr int kU = 4;
+  for (int k0 = 0; k0 < R; k0 += 16 * kU) {
+    i16x8 b[kU];
+    f32x4 x0[MT][kU], x1[MT][kU];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(orow[mt] + k0 + 8 * g);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(orow[mt] + k0 + 8 * g + 4);
-      bf16x8 hi, lo;
+    for (int u = 0; u < kU; ++u) {
+      const bool in = k0 + 16 * u < R;
+      const int k = in ? k0 + 16 * u : k0;
+      b[u] = *reinterpret_cast<const i16x8*>(wrow + k + 8 * g);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float x = (e < 4 ? x0[e] : x1[e - 4]) * sc[mt];
-        const __bf16 xh = static_cast<__bf16>(x);
-        hi[e] = xh;
-        lo[e] = static_cast<__bf16>(x - static_cast<float>(xh));
+      for (int mt = 0; mt < MT; ++mt) {
+        x0[mt][u] = *reinterpret_cast<const f32x4*>(orow[mt] + k + 8 * g);
+        x1[mt][u] = *reinterpret_cast<const f32x4*>(orow[mt] + k + 8 * g + 4);
       }
-      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, __builtin_bit_cast(bf16x8, b), acc[mt],
-                                                        0, 0, 0);
-      acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, __builtin_bit_cast(bf16x8, b), acc[mt],
-                                                        0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (k0 + 16 * u >= R) break;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        bf16x8 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = (e < 4 ? x0[mt][u][e] : x1[mt][u][e - 4]) * sc[mt];
+          const __bf16 xh = static_cast<__bf16>(x);
+          hi[e] = xh;
+          lo[e] = static_cast<__bf16>(x - static_cast<float>(xh));
+        }
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, __builtin_bit_cast(bf16x8, b[u]), acc[mt],
+                                                          0, 0, 0);
+        acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, __builtin_bit_cast(bf16x8, b[u]), acc[mt],
+                                                          0, 0, 0);
+      }
     }
   }
 #pragma unroll
@@ -161,6 +188,10 @@ __global__ __launch_bounds__(256) void up_project_mfma_kernel(const float* __res
 }
 
 int pick_mt(int Nq) { return Nq <= 32 ? 1 : (Nq <= 64 ? 2 : 4); }
+
+// The up-projection streams W_UV once per 32 * MT items; small batches take
+// one 32-item tile per workgroup so that the grid still covers the chip.
+int pick_mt_up(int Nq) { return Nq <= 128 ? 1 : (Nq <= 512 ? 2 : 4); }
 
 }  // namespace
 
@@ -176,7 +207,7 @@ hipError_t launch_absorb_mfma(const uint16_t* q_nope, int64_t st, int64_t sh, co
                               int32_t num_items, int32_t H, int32_t Dn, int32_t R, uint16_t* q_lat,
                               hipStream_t s) {
   const int mt = pick_mt(num_items);
-  const dim3 grid((num_items + 32 * mt - 1) / (32 * mt), H);
+  const dim3 grid(R / kAbsCols, H, (num_items + 32 * mt - 1) / (32 * mt));
   switch (mt) {
     case 1: hipLaunchKernelGGL(absorb_mfma_kernel<1>, grid, dim3(256), 0, s, q_nope, st, sh, w_uk, num_items, H, Dn, R, q_lat); break;
     case 2: hipLaunchKernelGGL(absorb_mfma_kernel<2>, grid, dim3(256), 0, s, q_nope, st, sh, w_uk, num_items, H, Dn, R, q_lat); break;
@@ -188,7 +219,7 @@ hipError_t launch_absorb_mfma(const uint16_t* q_nope, int64_t st, int64_t sh, co
 hipError_t launch_up_project_mfma(const float* o_lat, const float* o_scale, const uint16_t* w_uv,
                                   int32_t num_items, int32_t H, int32_t R, int32_t Dv, uint16_t* out,
                                   hipStream_t s) {
-  const int mt = pick_mt(num_items);
+  const int mt = pick_mt_up(num_items);
   const dim3 grid((num_items + 32 * mt - 1) / (32 * mt), H);
   switch (mt) {
     case 1: hipLaunchKernelGGL(up_project_mfma_kernel<1>, grid, dim3(256), 0, s, o_lat, o_scale, w_uv, num_items, H, R, Dv, out); break;

@@ -64,8 +64,9 @@ size_t elem_bytes(int dtype) { return dtype == MLA_KV_BF16 ? 2 : 1; }
 struct Layout {
   int G = 0;
   size_t q_lat = 0, o_lat = 0, lse = 0, o_scale = 0, item_b = 0, item_lo = 0, item_hi = 0,
-         tile_start = 0, wg_tile = 0, wg_item = 0, part_o = 0, part_lse = 0, part_scale = 0,
-         redo = 0, total = 0;
+         tile_start = 0, wg_tile = 0, wg_item = 0, item_wg = 0, part_o = 0, part_lse = 0,
+         part_scale = 0,
+         total = 0;
 };
 
 // Returns false when the number of workgroups cannot be determined.
@@ -98,14 +99,14 @@ bool make_layout(const mla_cache* c, const mla_attn* a, int64_t num_items, Layou
   off = align_up(off + sizeof(int32_t) * (G + 1));
   L->wg_item = off;
   off = align_up(off + sizeof(int32_t) * G);
+  L->item_wg = off;
+  off = align_up(off + sizeof(int32_t) * 2 * num_items);
   L->part_o = off;
   off = align_up(off + sizeof(float) * 2 * G * H * R);
   L->part_lse = off;
   off = align_up(off + sizeof(float) * 2 * G * H);
   L->part_scale = off;
   off = align_up(off + sizeof(float) * 2 * G * H);
-  L->redo = off;
-  off = align_up(off + sizeof(int32_t) * G);
   L->total = off;
   return true;
 }
@@ -190,6 +191,7 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
   plan.tile_start = at<int32_t>(workspace, L.tile_start);
   plan.wg_tile = at<int32_t>(workspace, L.wg_tile);
   plan.wg_item = at<int32_t>(workspace, L.wg_item);
+  plan.item_wg = at<int32_t>(workspace, L.item_wg);
   plan.G = L.G;
   e = mla::launch_plan(mode, batch, num_items, context_lens, qsl, attn->window,
                        static_cast<int32_t>(max_ctx64), plan, s);
@@ -212,6 +214,7 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
   a.tile_start = plan.tile_start;
   a.wg_tile = plan.wg_tile;
   a.wg_item = plan.wg_item;
+  a.item_wg = plan.item_wg;
   a.num_items = num_items;
   a.H = H;
   a.G = L.G;
@@ -222,8 +225,6 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
   a.part_o = at<float>(workspace, L.part_o);
   a.part_lse = at<float>(workspace, L.part_lse);
   a.part_scale = at<float>(workspace, L.part_scale);
-  a.redo = at<int32_t>(workspace, L.redo);
-  a.redo_only = nullptr;
 
   const bool use_mfma = !generic && mla::mfma_attn_supported(kv, H) &&
                         (ql_st % 8 == 0) && (ql_sh % 8 == 0) && (qp_st % 8 == 0) &&
@@ -233,14 +234,6 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
     return MLA_ERR_HIP;
   e = use_mfma ? mla::launch_attn_mfma(a, s) : mla::launch_attn_generic(a, s);
   if (e != hipSuccess) return MLA_ERR_HIP;
-  if (use_mfma) {
-    // ranges whose scores outran the MFMA kernel's fixed reference maximum
-    // (rare) are recomputed by the plain kernel; the others exit at once
-    AttnArgs fix = a;
-    fix.redo_only = a.redo;
-    e = mla::launch_attn_generic(fix, s);
-    if (e != hipSuccess) return MLA_ERR_HIP;
-  }
   if (attn->kernel_events[1] &&
       hipEventRecord(static_cast<hipEvent_t>(attn->kernel_events[1]), s) != hipSuccess)
     return MLA_ERR_HIP;

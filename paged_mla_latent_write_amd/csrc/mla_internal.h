@@ -37,6 +37,7 @@ struct Plan {
   int32_t* tile_start;   // [Nq + 1] exclusive prefix sum of the items' tile counts
   int32_t* wg_tile;      // [G + 1] first tile of each workgroup's range (wg_tile_begin)
   int32_t* wg_item;      // [G] item owning each workgroup's first tile
+  int32_t* item_wg;      // [2 Nq] first and last workgroup covering each item's tiles
   int32_t G;             // workgroups the tile stream is divided over
 };
 
@@ -54,6 +55,7 @@ struct AttnArgs {
   const int32_t* tile_start;
   const int32_t* wg_tile;  // [G + 1] (see Plan)
   const int32_t* wg_item;  // [G]
+  const int32_t* item_wg;  // [2 Nq] (see Plan)
   int32_t num_items;
   int32_t H;
   int32_t G;              // workgroups the tile stream is divided over
@@ -66,10 +68,6 @@ struct AttnArgs {
   float* part_o;          // [2G][H][R] fp32 partials (cut items)
   float* part_lse;        // [2G][H]
   float* part_scale;      // [2G][H]
-  // Per-workgroup recompute flags: the MFMA kernel writes one per workgroup;
-  // the plain kernel, given them, only runs the flagged workgroups' ranges.
-  int32_t* redo;          // [G]
-  const int32_t* redo_only;  // null: run every range
 };
 
 // ---- launchers (each returns the launch's hipGetLastError) ----
