@@ -47,7 +47,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="v3", choices=["v3", "v3fp8", "v2lite"])
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="CPU time budget for the oracle baseline sample")

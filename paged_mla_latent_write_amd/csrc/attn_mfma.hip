@@ -299,11 +299,15 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
     lofs[k >> 1] |= o << (16 * (k & 1));
   }
 
-  // ---- copy cursor: the prologue issues the first two tiles ----
+  // ---- copy cursor ----
   // Tile n is copied while tile n - 2 is computed (buffer n % 4): step n reads
-  // buffers n % 4 (scores) and (n - 1) % 4 (values of the previous tile), so
-  // buffer (n + 2) % 4, last read in step n - 1, is free once every wave has
-  // passed step n's barrier.
+  // buffers n % 4 (scores) and (n - 1) % 4 (values of the previous tile).
+  // Barrier n + 1 sits at the end of step n, after its values step and its
+  // wait for tile n + 1, so buffer (n + 2) % 4 -- last read in step n - 1 --
+  // is free for the copy that step n + 1 issues... i.e. step n copies tile
+  // n + 2 into the buffer freed before barrier n.  After barrier n + 1 the
+  // step reads the first K fragments of tile n + 1, so the next step starts
+  // on data already in registers.
   LoadCursor cur;
   cur.tile = t0;
   cur.end = t1;
@@ -319,7 +323,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
     }
   }
 
-  uint32_t koff[4], voff[4];
+  uint32_t koff[4], kcur[4], voff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) koff[j] = n32 * kRowBytes + (((2 * j) ^ y) << 4);
   voff[0] = voff_even;
@@ -329,12 +333,21 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(bufs[0]));
   const float c = a.scale_log2;
 
-  // Q (v54-v197) and the O^T accumulators (a0-a255) live in registers the
+  // Q (v58-v201) and the O^T accumulators (a0-a255) live in registers the
   // compiler does not allocate; only the blocks of attn_mfma_asm.inc touch them.
   zero_q();
+  int c_item = advance_item(m, a.num_items, first_item, t0);
+  // the first item's queries (lanes of heads >= H keep zeros); the load
+  // block waits for them, which also covers the first copies
+  if (wave_active && head_ok)
+    load_q(a.q_lat + c_item * a.q_lat_st + head * a.q_lat_sh + 8 * g,
+           a.q_pe + c_item * a.q_pe_st + head * a.q_pe_sh + 8 * g);
+  if (ntiles > 1) wait_vmcnt<kLoads>();
+  else wait_vmcnt<0>();
+  __syncthreads();  // barrier 0: tile 0 is in LDS
+  if (wave_active) tile_prefetch_k(kcur, koff, lds_base);
 
   int tn = 0;               // tiles consumed so far (buffer tn % 4)
-  int c_item = first_item;
   int ctile = t0;
   while (ctile < t1) {
     // ---- a segment: the WG's tiles of one item ----
@@ -342,64 +355,84 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
     const int item_ts = m.tile_start[c_item], item_te = m.tile_start[c_item + 1];
     const int seg_begin = ctile;
     const int seg_end = item_te < t1 ? item_te : t1;
-    // the item's queries (lanes of heads >= H keep zeros); the load block waits
-    // for them, which also drains the tile copies in flight (once per segment)
-    if (wave_active && head_ok)
-      load_q(a.q_lat + c_item * a.q_lat_st + head * a.q_lat_sh + 8 * g,
-             a.q_pe + c_item * a.q_pe_st + head * a.q_pe_sh + 8 * g);
     float m_ref = 0.f, l_sum = 0.f;
     const int vlo = m.item_lo[c_item], vhi = m.item_hi[c_item];
     const int tok_first = ((vlo >> 5) + (seg_begin - item_ts)) * kTile;
 
     for (int tt = seg_begin; tt < seg_end; ++tt, ++tn) {
-      // tile tn landed (the copy of tile tn + 1 may still be in flight)
-      if (tn + 1 < ntiles) wait_vmcnt<kLoads>();
-      else wait_vmcnt<0>();
-      __syncthreads();
       // copies of tile tn + 2: inside the step block when the tile is
       // contiguous, else issued here
       const bool copy = tn + 2 < ntiles;
       const uint32_t lds_copy = __builtin_amdgcn_readfirstlane(lds_wave + ((tn + 2) & 3) * kTileBytes);
       const int tok0 = tok_first + (tt - seg_begin) * kTile;
       const bool masked = !(tok0 >= vlo && tok0 + kTile <= vhi);
-      const bool fused_copy = copy && wave_active && tt != seg_begin && !masked && cursor_contiguous(cur, a);
+      const bool fused_copy = copy && wave_active && !masked && cursor_contiguous(cur, a);
       const char* sb = nullptr;
       if (copy) {
         if (fused_copy) sb = cursor_src(cur, a);
         else cursor_copy<NW>(cur, a, lds_copy, lofs);
         cursor_advance(cur, a, m);
       }
-      if (!wave_active) continue;
+      // the end of step tn waits for tile tn + 1 (with the copy of tile tn + 2
+      // still in flight) and passes barrier tn + 1; the last tile has neither
+      const uint32_t tail = tn + 1 < ntiles ? (copy ? 2u : 1u) : 0u;
+      if (!wave_active) {
+        if (tail == 2) wait_vmcnt<kLoads>();
+        if (tail == 1) wait_vmcnt<0>();
+        if (tail != 0) __syncthreads();
+        continue;
+      }
       const uint32_t bs = lds_base + (tn & 3) * kTileBytes;
       const uint32_t bp = lds_base + ((tn - 1) & 3) * kTileBytes;
+      const uint32_t bn = lds_base + ((tn + 1) & 3) * kTileBytes;
       // masked tiles: element i of a lane is visible iff lo <= 8 (i / 4) + i % 4 < hi
       const int lo = vlo - tok0 - 4 * g, hi = vhi - tok0 - 4 * g;
-      if (tt == seg_begin) {
-        if (masked) tile_first_m1(koff, bs, c, m_ref, l_sum, lo, hi);
-        else tile_first_m0(koff, bs, c, m_ref, l_sum);
+      const bool first = tt == seg_begin, last = tt == seg_end - 1;
+      uint32_t vn[4];  // the tile's own values addresses when it ends the segment
+      if (first) {
+        if (!last) {
+          if (masked) tile_first_tail_d0_m1(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, lo, hi);
+          else if (fused_copy) tile_first_tail_d1_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, sb, lds_copy, lofs);
+          else tile_first_tail_d0_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum);
+        } else {  // one-tile segment: its own values step follows
+          if (masked) tile_first_lastv_d0_m1(kcur, koff, voff, bs, bs, bn, tail, c, m_ref, l_sum, vn, voff, lo, hi);
+          else if (fused_copy) tile_first_lastv_d1_m0(kcur, koff, voff, bs, bs, bn, tail, c, m_ref, l_sum, vn, voff, sb, lds_copy, lofs);
+          else tile_first_lastv_d0_m0(kcur, koff, voff, bs, bs, bn, tail, c, m_ref, l_sum, vn, voff);
+          tile_last_pv_f1(kcur, koff, vn, bn, tail);
+        }
       } else {
         float fac;  // 2^(old - new) reference when the tile moved it, else 1
-        if (tt - 1 == seg_begin) {  // first values step of the segment: O starts at 0
-          if (masked) tile_step_d0_f1_m1(koff, voff, bs, bp, c, m_ref, l_sum, fac, lo, hi);
-          else if (fused_copy) tile_step_d1_f1_m0(koff, voff, bs, bp, c, m_ref, l_sum, fac, sb, lds_copy, lofs);
-          else tile_step_d0_f1_m0(koff, voff, bs, bp, c, m_ref, l_sum, fac);
+        const bool fpv = tt - 1 == seg_begin;  // first values step of the segment: O starts at 0
+        if (!last) {
+          if (fpv) {
+            if (masked) tile_step_tail_d0_f1_m1(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, lo, hi);
+            else if (fused_copy) tile_step_tail_d1_f1_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, sb, lds_copy, lofs);
+            else tile_step_tail_d0_f1_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac);
+          } else {
+            if (masked) tile_step_tail_d0_f0_m1(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, lo, hi);
+            else if (fused_copy) tile_step_tail_d1_f0_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, sb, lds_copy, lofs);
+            else tile_step_tail_d0_f0_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac);
+          }
+          if (__any(fac != 1.f)) rescale_acc(fac);  // rare: a score far above the reference
         } else {
-          if (masked) tile_step_d0_f0_m1(koff, voff, bs, bp, c, m_ref, l_sum, fac, lo, hi);
-          else if (fused_copy) tile_step_d1_f0_m0(koff, voff, bs, bp, c, m_ref, l_sum, fac, sb, lds_copy, lofs);
-          else tile_step_d0_f0_m0(koff, voff, bs, bp, c, m_ref, l_sum, fac);
+          if (fpv) {
+            if (masked) tile_step_lastv_d0_f1_m1(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, vn, voff, lo, hi);
+            else if (fused_copy) tile_step_lastv_d1_f1_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, vn, voff, sb, lds_copy, lofs);
+            else tile_step_lastv_d0_f1_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, vn, voff);
+          } else {
+            if (masked) tile_step_lastv_d0_f0_m1(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, vn, voff, lo, hi);
+            else if (fused_copy) tile_step_lastv_d1_f0_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, vn, voff, sb, lds_copy, lofs);
+            else tile_step_lastv_d0_f0_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, vn, voff);
+          }
+          if (__any(fac != 1.f)) rescale_acc(fac);  // before the tile's own values step
+          tile_last_pv_f0(kcur, koff, vn, bn, tail);
         }
-        if (__any(fac != 1.f)) rescale_acc(fac);  // rare: a score far above the reference
       }
     }
     ctile = seg_end;
 
-    // ---- segment done: last values step, then the unnormalised accumulator,
-    // lse and 1/l (no arithmetic on the accumulator registers: consumers apply 1/l)
-    if (wave_active) {
-      const uint32_t bp = lds_base + ((tn - 1) & 3) * kTileBytes;
-      if (seg_end - 1 == seg_begin) tile_pv_f1(voff, bp);
-      else tile_pv_f0(voff, bp);
-    }
+    // ---- segment done: the unnormalised accumulator, lse and 1/l
+    // (no arithmetic on the accumulator registers: consumers apply 1/l)
     const float l_tot = wave_active ? l_sum + __shfl_xor(l_sum, 32, 64) : 1.f;
     const bool complete = (seg_begin == item_ts) && (seg_end == item_te);
     float* o_dst;
@@ -421,6 +454,12 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
         lse_dst[head] = (m_ref + log2f(l_tot)) * kLn2;
         scl_dst[head] = 1.0f / l_tot;
       }
+    }
+    // the next segment's queries (its first K fragments are already read)
+    if (ctile < t1 && wave_active && head_ok) {
+      const int n_item = advance_item(m, a.num_items, c_item, ctile);
+      load_q(a.q_lat + n_item * a.q_lat_st + head * a.q_lat_sh + 8 * g,
+             a.q_pe + n_item * a.q_pe_st + head * a.q_pe_sh + 8 * g);
     }
   }
 }

@@ -1,0 +1,69 @@
+"""Static checks of the generated attention blocks (attn_mfma_asm.inc).
+
+    python check_attn_mfma_asm.py        # exit status 1 on a problem
+
+For every block it replays the instruction list and checks that
+  1. no MFMA reads a ring register whose LDS read has not been waited for
+     (lgkmcnt counts reads in issue order; reads complete in order), and
+  2. no LDS read overwrites a ring register that still holds data no MFMA has
+     read yet (a ring slot reused too early).
+Blocks that start a tile step begin with all ring registers holding data read
+by the previous block's tail.
+"""
+import re
+import sys
+from pathlib import Path
+
+HERE = Path(__file__).resolve().parent
+
+
+def ring_base():
+    src = (HERE / "gen_attn_mfma_asm.py").read_text()
+    nf = int(re.search(r"^NF = (\d+)", src, re.M).group(1))
+    return 256 - 4 * nf
+
+
+def regs(tok):
+    m = re.match(r"v\[(\d+):(\d+)\]", tok)
+    if m:
+        return set(range(int(m.group(1)), int(m.group(2)) + 1))
+    m = re.match(r"v(\d+)$", tok)
+    return {int(m.group(1))} if m else set()
+
+
+def check(text):
+    ring = ring_base()
+    problems = []
+    blocks = re.findall(r"void (\w+)\(.*?\) \{\n  asm volatile\(\n(.*?)\n      :", text, re.S)
+    for name, body in blocks:
+        lines = [ln.strip().strip('"').replace("\\n", "") for ln in body.split("\n")]
+        starts_with_ring = name.startswith(("tile_step", "tile_first", "tile_last_pv"))
+        live = set(range(ring, 256)) if starts_with_ring else set()
+        in_flight = []
+        for ln in lines:
+            op = ln.split(" ")[0]
+            if op.startswith("ds_read"):
+                dst = regs(ln.split(" ")[1].rstrip(","))
+                if dst & live:
+                    problems.append(f"{name}: LDS read overwrites unread data: {ln}")
+                in_flight.append(dst)
+                live |= dst
+            elif op == "s_waitcnt" and "lgkmcnt" in ln:
+                n = int(re.search(r"lgkmcnt\((\d+)\)", ln).group(1))
+                while len(in_flight) > n:
+                    in_flight.pop(0)
+            elif op.startswith("v_mfma"):
+                for tok in (t.rstrip(",") for t in ln.split(" ")[2:4]):
+                    r = regs(tok)
+                    if any(r & q for q in in_flight):
+                        problems.append(f"{name}: MFMA before its LDS read landed: {ln}")
+                    live -= r
+    return len(blocks), problems
+
+
+if __name__ == "__main__":
+    n, problems = check((HERE / "attn_mfma_asm.inc").read_text())
+    for p in problems:
+        print(p)
+    print(f"{n} blocks, {len(problems)} problems")
+    sys.exit(1 if problems else 0)

@@ -8,12 +8,13 @@ amdgpu_num_vgpr), so every register above is reserved and keeps its value from
 one block to the next; the blocks below own them:
 
     a0-a255    O^T accumulators of the wave's 32 heads: 16 tiles of 32 dims
-    v46-v53    P of the previous tile (bf16, B operand of O^T += V^T P^T)
-    v54-v197   Q^T fragments: 36 k-steps x 4 registers (q_lat then q_pe)
-    v198       copy-offset temporary
-    v200-v215  score chain 0; v216-v231 score chain 1 (after the softmax sum,
-               v216-v223 hold the new P and v224/v225 are temporaries)
-    v232-v255  ring of six LDS fragments in flight
+    v50-v57    P of the previous tile (bf16, B operand of O^T += V^T P^T)
+    v58-v201   Q^T fragments: 36 k-steps x 4 registers (q_lat then q_pe)
+    v202       copy-offset temporary
+    v204-v219  score chain 0; v220-v235 score chain 1 (after the softmax sum,
+               v220-v227 hold the new P, v228/v229 are temporaries and
+               v232-v235 the addresses of a segment's last values step)
+    v236-v255  ring of five LDS fragments in flight
 
 A tile step is one inline-assembly statement of one wave:
 
@@ -31,13 +32,14 @@ A tile step is one inline-assembly statement of one wave:
 """
 import sys
 
-NC = 46                     # v0..v45 for the compiler
-P_BASE = 46                 # v46-v53 (tuples start on even registers)
-Q_BASE = 54                 # v54-v197
-TMP_DMA = 198               # (v199 unused)
-SS, TT = 200, 216           # score chains
-RING = 232                  # v232-v255
-NF = 6                      # LDS fragments in flight
+NF = 5                      # LDS fragments in flight (ring of 4 NF registers)
+RING = 256 - 4 * NF         # v236-v255
+TT = RING - 16              # score chain 1: v220-v235
+SS = TT - 16                # score chain 0: v204-v219
+TMP_DMA = SS - 2            # v202 (v203 unused; tuples start on even registers)
+Q_BASE = TMP_DMA - 144      # v58-v201
+P_BASE = Q_BASE - 8         # v50-v57
+NC = P_BASE                 # v0..v49 for the compiler
 T0, T1 = TT + 8, TT + 9     # softmax temporaries (free after the sum)
 NEG_INF = "0xff800000"
 SLACK = "0x41800000"        # 16.0f: slack of the reference maximum (log2 units)
@@ -71,7 +73,7 @@ def s_chain(k):
 
 def softmax_ops(first, masked):
     """The softmax of one tile (scores in both chains) as VALU instructions;
-    leaves P (bf16 pairs) in v216-v223."""
+    leaves P (bf16 pairs) in v220-v227."""
     s = [f"v{SS + i}" for i in range(16)]
     t = [f"v{TT + i}" for i in range(16)]
     ops = [f"v_add_f32 {s[i]}, {s[i]}, {t[i]}" for i in range(16)]
@@ -119,89 +121,155 @@ def softmax_ops(first, masked):
     return ops
 
 
-def s_part(dma, copy_p):
-    """Scores of the current tile (K from LDS buffer %[bs]).  copy_p: first
-    move the previous step's P (v216-v223) to v46-v53.  dma: also issue the 9
-    copies of a later tile (HBM base %[sb], LDS rows from %[m0], lane offsets
-    packed two per register in %[l0..l4])."""
-    L = [f"v_add_u32 %[k{j}], %[bs], %[k{j}]" for j in range(4)]
-    issued = 0
-    for i in range(NF):
-        L.append(f"ds_read_b128 {ring4(i)}, %[k{i % 4}] offset:{128 * (i // 4)}")
-        issued += 1
+class Stream:
+    """Instruction list with the LDS reads in flight tracked, so that each MFMA
+    waits (lgkmcnt) only until its own operand has arrived: LDS reads complete
+    in issue order, so the wait count is the number of reads issued after it."""
+
+    def __init__(self):
+        self.lines = []
+        self.queue = []          # tags of the LDS reads in flight, oldest first
+
+    def add(self, *lines):
+        self.lines += list(lines)
+
+    def lds(self, line, tag):
+        self.lines.append(line)
+        self.queue.append(tag)
+
+    def wait_for(self, tag):
+        if tag not in self.queue:
+            return  # already known to have completed (an older wait covered it)
+        last = max(i for i, t in enumerate(self.queue) if t == tag)
+        after = len(self.queue) - last - 1
+        self.lines.append(f"s_waitcnt lgkmcnt({min(15, after)})")
+        self.queue = self.queue[last + 1:]
+
+
+PV_ORDER = [(mt, j) for j in range(2) for mt in range(16)]
+
+
+def v_reads(st, i, regs=("%[v0]", "%[v1]", "%[v2]", "%[v3]")):
+    """The two transposed reads of values fragment i (ring slot i mod NF)."""
+    mt, j = PV_ORDER[i]
+    rl = regs[0] if mt % 2 == 0 else regs[1]
+    rh = regs[2] if mt % 2 == 0 else regs[3]
+    off = 128 * (mt >> 1) + 1152 * 16 * j
+    st.lds(f"ds_read_b64_tr_b16 {ring2(i, 0)}, {rl} offset:{off}", ("V", i))
+    st.lds(f"ds_read_b64_tr_b16 {ring2(i, 1)}, {rh} offset:{off}", ("V", i))
+
+
+def k_read(st, k):
+    st.lds(f"ds_read_b128 {ring4(k)}, %[k{k % 4}] offset:{128 * (k // 4)}", ("K", k))
+
+
+def s_part(st, dma, copy_p, prefetch_v):
+    """Scores of the current tile.  Its first NF K fragments are already in the
+    ring (read by the previous block's tail, addresses %[k0..k3] = this lane's
+    K row offsets within the tile's LDS buffer).  copy_p: first move the
+    previous step's P (v220-v227) to v50-v57.  dma: also issue the 9 copies of a
+    later tile (HBM base %[sb], LDS rows from %[m0], lane offsets packed two per
+    register in %[l0..l4]).  prefetch_v: the ring slots the last k-steps free
+    are refilled with the first values fragments (%[v0..v3] + %[bp])."""
+    if prefetch_v:
+        st.add(*[f"v_add_u32 %[v{j}], %[bp], %[v{j}]" for j in range(4)])
     if dma:
-        L += ["s_mov_b32 m0, %[m0]", f"v_and_b32 v{TMP_DMA}, 0xffff, %[l0]"]
+        st.add("s_mov_b32 m0, %[m0]", f"v_and_b32 v{TMP_DMA}, 0xffff, %[l0]")
     for k in range(36):
-        L.append(f"s_waitcnt lgkmcnt({min(15, issued - (k + 1))})")
-        L.append(f"v_mfma_f32_32x32x16_bf16 {s_chain(k)}, {ring4(k)}, {q(k)}, {'0' if k < 2 else s_chain(k)}")
+        st.wait_for(("K", k))
+        st.add(f"v_mfma_f32_32x32x16_bf16 {s_chain(k)}, {ring4(k)}, {q(k)}, {'0' if k < 2 else s_chain(k)}")
         if k == 0 and copy_p:
-            # before chain 1's first MFMA overwrites v216-v223
-            L += [f"v_mov_b32 v{P_BASE + j}, v{TT + j}" for j in range(8)]
+            # before chain 1's first MFMA overwrites the previous P
+            st.add(*[f"v_mov_b32 v{P_BASE + j}, v{TT + j}" for j in range(8)])
         if k + NF < 36:
-            kk = k + NF
-            L.append(f"ds_read_b128 {ring4(k)}, %[k{kk % 4}] offset:{128 * (kk // 4)}")
-            issued += 1
+            k_read(st, k + NF)
+        elif prefetch_v:
+            # slot k mod NF is free now; values fragment f lives in slot f mod NF
+            v_reads(st, k % NF)
         if dma and k % 4 == 1:
-            L.append(f"global_load_lds_dwordx4 v{TMP_DMA}, %[sb] offset:0")
+            st.add(f"global_load_lds_dwordx4 v{TMP_DMA}, %[sb] offset:0")
         if dma and k % 4 == 3 and k // 4 < 8:
             d = k // 4 + 1  # next copy
-            L.append("s_add_u32 m0, m0, 0x400")
+            st.add("s_add_u32 m0, m0, 0x400")
             if d % 2 == 0:
-                L.append(f"v_and_b32 v{TMP_DMA}, 0xffff, %[l{d // 2}]")
+                st.add(f"v_and_b32 v{TMP_DMA}, 0xffff, %[l{d // 2}]")
             else:
-                L.append(f"v_lshrrev_b32 v{TMP_DMA}, 16, %[l{d // 2}]")
-    L += [f"v_sub_u32 %[k{j}], %[k{j}], %[bs]" for j in range(4)]
-    L += ["s_nop 7", "s_nop 7", "s_nop 4"]
-    return L
+                st.add(f"v_lshrrev_b32 v{TMP_DMA}, 16, %[l{d // 2}]")
 
 
-def pv_part(first_pv, vops, p_regs):
-    """O^T += V^T P^T of the previous tile (LDS buffer %[bp]; P in p_regs),
-    with the VALU list vops interleaved between the MFMAs.  first_pv: the
-    accumulators start at zero."""
-    order = [(mt, j) for j in range(2) for mt in range(16)]
-
-    def reads(i):
-        mt, j = order[i]
-        rl = "%[v0]" if mt % 2 == 0 else "%[v1]"
-        rh = "%[v2]" if mt % 2 == 0 else "%[v3]"
-        off = 128 * (mt >> 1) + 1152 * 16 * j
-        return [f"ds_read_b64_tr_b16 {ring2(i, 0)}, {rl} offset:{off}",
-                f"ds_read_b64_tr_b16 {ring2(i, 1)}, {rh} offset:{off}"]
-
-    L = [f"v_add_u32 %[v{j}], %[bp], %[v{j}]" for j in range(4)]
-    issued = 0
-    for i in range(NF):
-        L += reads(i)
-        issued += 2
+def pv_part(st, first_pv, vops, p_regs, prefetched, end_v=False):
+    """O^T += V^T P^T (fragments from %[v0..v3], this lane's read offsets plus
+    the buffer base %[bp]; P in p_regs), with the VALU list vops interleaved
+    between the MFMAs (they read the scores, so they start after 21 wait
+    states).  first_pv: the accumulators start at zero.  prefetched: the first
+    NF fragments are already queued.  end_v: the slots freed by the last MFMAs
+    are refilled with the first fragments of the current tile's own values
+    (%[vn0..vn3] = offsets + %[bs]) for the segment's last values step."""
+    if not prefetched:
+        st.add(*[f"v_add_u32 %[v{j}], %[bp], %[v{j}]" for j in range(4)])
+        for i in range(NF):
+            v_reads(st, i)
     per = (len(vops) + 27) // 28
     vi = 0
     for i in range(32):
-        mt, j = order[i]
-        L.append(f"s_waitcnt lgkmcnt({min(15, issued - 2 * (i + 1))})")
+        mt, j = PV_ORDER[i]
+        st.wait_for(("V", i))
         src_c = "0" if (first_pv and j == 0) else acc(mt)
-        L.append(f"v_mfma_f32_32x32x16_bf16 {acc(mt)}, {ring4(i)}, {p_regs[j]}, {src_c}")
+        st.add(f"v_mfma_f32_32x32x16_bf16 {acc(mt)}, {ring4(i)}, {p_regs[j]}, {src_c}")
         if i + NF < 32:
-            L += reads(i + NF)
-            issued += 2
-        if i >= 2:  # the first MFMAs cover the LDS issue start
-            L += vops[vi:vi + per]
+            v_reads(st, i + NF)
+        if i == 1 and vops:
+            st.add("s_nop 7", "s_nop 7", "s_nop 4")  # score results of the last k-steps
+        if i >= 2:
+            st.add(*vops[vi:vi + per])
             vi += per
-    L += vops[vi:]
-    L += [f"v_sub_u32 %[v{j}], %[v{j}], %[bp]" for j in range(4)]
-    L += ["s_nop 7", "s_nop 7", "s_nop 4"]
-    return L
+        if end_v and i == 32 - NF:
+            st.add(*vops[vi:])
+            vi = len(vops)
+            st.add(*[f"v_add_u32 %[vn{j}], %[bs], %[vo{j}]" for j in range(4)])
+        if end_v and i >= 32 - NF:
+            # slot i mod NF is free now: the segment's last values step's
+            # fragment i mod NF goes there (not waited for in this block)
+            mt2, j2 = PV_ORDER[i % NF]
+            rl = f"%[vn{0 if mt2 % 2 == 0 else 1}]"
+            rh = f"%[vn{2 if mt2 % 2 == 0 else 3}]"
+            off = 128 * (mt2 >> 1) + 1152 * 16 * j2
+            st.lds(f"ds_read_b64_tr_b16 {ring2(i % NF, 0)}, {rl} offset:{off}", ("N", i % NF))
+            st.lds(f"ds_read_b64_tr_b16 {ring2(i % NF, 1)}, {rh} offset:{off}", ("N", i % NF))
+    st.add(*vops[vi:])
+    st.add(*[f"v_sub_u32 %[v{j}], %[v{j}], %[bp]" for j in range(4)])
+
+
+COPY_LOADS = 9  # HBM->LDS copies per wave per tile
+
+
+def tail(st):
+    """Wait for the next tile's copy, pass the workgroup barrier, and read the
+    next tile's first K fragments into the ring (%[k0..k3] = %[ko0..ko3] +
+    %[bn]).  Issued after that tile's copy: (%[tail] = 2) this step's copy,
+    or (%[tail] = 1) nothing; %[tail] = 0: no next tile."""
+    st.add("s_cmp_eq_u32 %[tail], 0", "s_cbranch_scc1 9f",
+           "s_cmp_eq_u32 %[tail], 1", "s_cbranch_scc1 8f",
+           f"s_waitcnt vmcnt({COPY_LOADS})", "s_branch 7f",
+           "8:", "s_waitcnt vmcnt(0)",
+           "7:", "s_barrier")
+    st.add(*[f"v_add_u32 %[k{j}], %[bn], %[ko{j}]" for j in range(4)])
+    for i in range(NF):
+        st.add(f"ds_read_b128 {ring4(i)}, %[k{i % 4}] offset:{128 * (i // 4)}")
+    st.add("9:")
 
 
 P_FIXED = (f"v[{P_BASE}:{P_BASE + 3}]", f"v[{P_BASE + 4}:{P_BASE + 7}]")
 P_NEW = (f"v[{TT}:{TT + 3}]", f"v[{TT + 4}:{TT + 7}]")
+VNEXT = tuple(f"v{TT + 12 + j}" for j in range(4))   # free after the softmax sum
 
 
 def cstr(lines, indent="      "):
     return "\n".join(f'{indent}"{l}\\n"' for l in lines)
 
 
-KOFF = '[k0] "+v"(koff[0]), [k1] "+v"(koff[1]), [k2] "+v"(koff[2]), [k3] "+v"(koff[3])'
+KCUR = '[k0] "+v"(kcur[0]), [k1] "+v"(kcur[1]), [k2] "+v"(kcur[2]), [k3] "+v"(kcur[3])'
+KOFF_IN = '[ko0] "v"(koff[0]), [ko1] "v"(koff[1]), [ko2] "v"(koff[2]), [ko3] "v"(koff[3])'
 VOFF = '[v0] "+v"(voff[0]), [v1] "+v"(voff[1]), [v2] "+v"(voff[2]), [v3] "+v"(voff[3])'
 STATS = '[mref] "+v"(mref), [lsum] "+v"(lsum)'
 FAC = '[fac] "=&v"(fac)'
@@ -227,37 +295,84 @@ def emit():
          f"#define MLA_VCLOBBERS {VCLOB_ALL}",
          f"#define MLA_ACLOBBERS {ACLOB_ALL}",
          ""]
-    # fused step: S(t) [+ copies] then PV(t-1) with softmax(t)
-    for dma in (0, 1):
-        for first_pv in (0, 1):
-            for masked in (0, 1):
-                if dma and masked:
-                    continue
-                args = ["uint32_t (&koff)[4]", "uint32_t (&voff)[4]", "uint32_t bs", "uint32_t bp", "float c",
-                        "float& mref", "float& lsum", "float& fac"]
-                ins = ['[bs] "s"(bs), [bp] "s"(bp), [c] "s"(c)']
-                if masked:
-                    args += ["int lo", "int hi"]
-                    ins.append('[lo] "v"(lo), [hi] "v"(hi)')
-                if dma:
-                    args += ["const char* sb", "uint32_t m0b", "const uint32_t (&lofs)[5]"]
-                    ins.append(DMA_IN)
-                body = s_part(dma, True) + pv_part(first_pv, softmax_ops(False, masked), P_FIXED)
-                o += block(f"tile_step_d{dma}_f{first_pv}_m{masked}", args, body, [STATS, FAC, KOFF, VOFF], ins,
-                           ', "m0"' if dma else "")
-    # first tile of a segment: S(t) and softmax(t) (sets the reference maximum)
-    for masked in (0, 1):
-        args = ["uint32_t (&koff)[4]", "uint32_t bs", "float c", "float& mref", "float& lsum"]
-        ins = ['[bs] "s"(bs), [c] "s"(c)']
-        if masked:
-            args += ["int lo", "int hi"]
-            ins.append('[lo] "v"(lo), [hi] "v"(hi)')
-        body = s_part(0, False) + softmax_ops(True, masked)
-        o += block(f"tile_first_m{masked}", args, body, [STATS, KOFF], ins)
-    # last values step of a segment (P of the last tile still in v216-v223)
+    # Every block below starts with the tile's first NF K fragments already in
+    # the ring (queued).  "end" is what follows the values step: the tail
+    # (barrier, next tile's K fragments) or, when the tile ends its segment,
+    # the reads of the tile's own first values fragments (for tile_last_pv).
+    for kind in ("step", "first"):
+        for end in ("tail", "lastv"):
+            for dma in (0, 1):
+                for first_pv in ((0, 1) if kind == "step" else (0,)):
+                    for masked in (0, 1):
+                        if dma and masked:
+                            continue
+                        args = ["uint32_t (&kcur)[4]", "const uint32_t (&koff)[4]", "uint32_t (&voff)[4]",
+                                "uint32_t bs", "uint32_t bp", "uint32_t bn", "uint32_t tail", "float c",
+                                "float& mref", "float& lsum"]
+                        ins = ['[bs] "s"(bs), [bp] "s"(bp), [bn] "s"(bn), [tail] "s"(tail), [c] "s"(c)',
+                               KOFF_IN]
+                        outs = [STATS, KCUR, VOFF]
+                        if kind == "step":
+                            args.append("float& fac")
+                            outs.append(FAC)
+                        if end == "lastv":
+                            args.append("uint32_t (&vn)[4]")
+                            outs.append('[vn0] "=&v"(vn[0]), [vn1] "=&v"(vn[1]), [vn2] "=&v"(vn[2]), [vn3] "=&v"(vn[3])')
+                            ins.append('[vo0] "v"(vo[0]), [vo1] "v"(vo[1]), [vo2] "v"(vo[2]), [vo3] "v"(vo[3])')
+                            args.append("const uint32_t (&vo)[4]")
+                        if masked:
+                            args += ["int lo", "int hi"]
+                            ins.append('[lo] "v"(lo), [hi] "v"(hi)')
+                        if dma:
+                            args += ["const char* sb", "uint32_t m0b", "const uint32_t (&lofs)[5]"]
+                            ins.append(DMA_IN)
+                        st = Stream()
+                        st.queue = [("K", i) for i in range(NF)]
+                        if kind == "step":
+                            s_part(st, dma, True, True)
+                            pv_part(st, first_pv, softmax_ops(False, masked), P_FIXED, True, end == "lastv")
+                        else:
+                            # a first tile's own values step (one-tile segment) reads from
+                            # the S tail's prefetch: %[bp] is the tile's own buffer then
+                            s_part(st, dma, False, end == "lastv")
+                            st.add("s_nop 7", "s_nop 7", "s_nop 4")  # score results of the last k-steps
+                            st.add(*softmax_ops(True, masked))
+                            if end == "lastv":
+                                st.add(*[f"v_sub_u32 %[v{j}], %[v{j}], %[bp]" for j in range(4)])
+                                st.add(*[f"v_add_u32 %[vn{j}], %[bs], %[vo{j}]" for j in range(4)])
+                        if end == "tail":
+                            tail(st)
+                        name = f"tile_{kind}_{end}_d{dma}" + (f"_f{first_pv}" if kind == "step" else "") + \
+                               f"_m{masked}"
+                        o += block(name, args, st.lines, outs, ins, ', "m0", "scc"' if dma else ', "scc"')
+    # the segment's last values step: O^T += V_T^T P_T^T (fragments queued by
+    # the previous block, P in v220-v227), then the tail
     for first_pv in (0, 1):
-        args = ["uint32_t (&voff)[4]", "uint32_t bp"]
-        o += block(f"tile_pv_f{first_pv}", args, pv_part(first_pv, [], P_NEW), [VOFF], ['[bp] "s"(bp)'])
+        st = Stream()
+        # the fragments in flight, in issue order: each went into the ring slot
+        # that one of the previous block's last MFMAs freed (fragment f lives in
+        # slot f mod NF): after a first tile's block (one-tile segment:
+        # first_pv) the last score k-steps, after a step's block the last
+        # values MFMAs
+        order = [k % NF for k in range(36 - NF, 36)] if first_pv else [i % NF for i in range(32 - NF, 32)]
+        st.queue = [("V", f) for f in order for _ in range(2)]
+        st.add("s_nop 1")  # P was written by VALU at the end of the previous block
+        pv_rest(st, first_pv, P_NEW, ("%[vn0]", "%[vn1]", "%[vn2]", "%[vn3]"))
+        tail(st)
+        o += block(f"tile_last_pv_f{first_pv}",
+                   ["uint32_t (&kcur)[4]", "const uint32_t (&koff)[4]", "const uint32_t (&vn)[4]", "uint32_t bn",
+                    "uint32_t tail"],
+                   st.lines, [KCUR],
+                   ['[bn] "s"(bn), [tail] "s"(tail)', KOFF_IN,
+                    '[vn0] "v"(vn[0]), [vn1] "v"(vn[1]), [vn2] "v"(vn[2]), [vn3] "v"(vn[3])'],
+                   ', "scc"')
+    # the first K fragments of a workgroup's first tile (after its first barrier)
+    st = Stream()
+    st.add(*[f"v_add_u32 %[k{j}], %[bn], %[ko{j}]" for j in range(4)])
+    for i in range(NF):
+        st.add(f"ds_read_b128 {ring4(i)}, %[k{i % 4}] offset:{128 * (i // 4)}")
+    o += block("tile_prefetch_k", ["uint32_t (&kcur)[4]", "const uint32_t (&koff)[4]", "uint32_t bn"],
+               st.lines, [KCUR], ['[bn] "s"(bn)', KOFF_IN])
     # queries: 32 k-steps of q_lat (ql: this lane's row + 8 g) then 4 of q_pe
     L = [f"global_load_dwordx4 {q(k)}, %[ql], off offset:{32 * k}" for k in range(32)]
     L += [f"global_load_dwordx4 {q(32 + k)}, %[qp], off offset:{32 * k}" for k in range(4)]
@@ -266,23 +381,38 @@ def emit():
     o += block("zero_q", [], [f"v_mov_b32 v{Q_BASE + r}, 0" for r in range(144)], [], [])
     # unnormalised O^T of this lane's head: orow[0 .. 511] (orow includes 4 g);
     # lane (n32, g) holds dims 32 mt + 8 (i / 4) + 4 g + i % 4.  Registers go
-    # out through the ring, each group reused six stores later.
-    L = []
+    # out through the score registers (free between segments), each group
+    # reused six stores later; the ring may hold the next tile's K fragments.
+    L = ["s_nop 7", "s_nop 7", "s_nop 4"]  # the last MFMA results must have landed
     n = 0
     for mt in range(16):
         for a4 in range(4):
-            r = RING + 4 * (n % NF)
+            r = SS + 4 * (n % 6)
             L += [f"v_accvgpr_read_b32 v{r + e}, a{16 * mt + 4 * a4 + e}" for e in range(4)]
             L.append(f"global_store_dwordx4 %[orow], v[{r}:{r + 3}], off offset:{4 * (32 * mt + 8 * a4)}")
             n += 1
     o += block("store_acc", ["float* orow"], L, [], ['[orow] "v"(orow)'])
-    # scale this lane's accumulators by fac (rare: after a reference move)
+    # scale this lane's accumulators by fac (rare: after a reference move);
+    # temporaries: score chain 0 (P of the tile is in chain 1, fragments in the ring)
     L = ["s_nop 7", "s_nop 7", "s_nop 4"]  # the last MFMA results must have landed
     for r in range(256):
-        t = RING + (r % 24)
+        t = SS + (r % 16)
         L += [f"v_accvgpr_read_b32 v{t}, a{r}", f"v_mul_f32 v{t}, %[fac], v{t}", f"v_accvgpr_write_b32 a{r}, v{t}"]
     o += block("rescale_acc", ["float fac"], L, [], ['[fac] "v"(fac)'])
     return "\n".join(o)
+
+
+def pv_rest(st, first_pv, p_regs, vregs):
+    """A values step whose first NF fragments (addresses vregs) are already
+    queued; no VALU interleave.  The accumulators read afterwards by the
+    segment's stores get their wait states there."""
+    for i in range(32):
+        mt, j = PV_ORDER[i]
+        st.wait_for(("V", i))
+        src_c = "0" if (first_pv and j == 0) else acc(mt)
+        st.add(f"v_mfma_f32_32x32x16_bf16 {acc(mt)}, {ring4(i)}, {p_regs[j]}, {src_c}")
+        if i + NF < 32:
+            v_reads(st, i + NF, vregs)
 
 
 if __name__ == "__main__":

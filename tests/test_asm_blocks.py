@@ -1,0 +1,37 @@
+"""The generated inline-assembly blocks of the MFMA attention kernel: the
+committed include matches its generator, and a replay of each block finds no
+LDS read consumed before it landed and no ring slot overwritten too early."""
+import importlib.util
+import subprocess
+import sys
+from pathlib import Path
+
+CSRC = Path(__file__).resolve().parents[1] / "paged_mla_latent_write_amd" / "csrc"
+
+
+def _load(name):
+    spec = importlib.util.spec_from_file_location(name, CSRC / f"{name}.py")
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_include_matches_generator():
+    out = subprocess.run([sys.executable, str(CSRC / "gen_attn_mfma_asm.py")], capture_output=True, text=True,
+                         check=True).stdout
+    assert out == (CSRC / "attn_mfma_asm.inc").read_text()
+
+
+def test_blocks_wait_for_their_lds_reads():
+    n, problems = _load("check_attn_mfma_asm").check((CSRC / "attn_mfma_asm.inc").read_text())
+    assert n > 10 and not problems, problems[:5]
+
+
+def test_checker_catches_a_ring_slot_reused_too_early():
+    # plant a mistake: drop every lgkmcnt wait from one block
+    text = (CSRC / "attn_mfma_asm.inc").read_text()
+    start = text.index("void tile_step_tail_d1_f0_m0(")
+    end = text.index("\n}\n", start)
+    planted = text[:start] + text[start:end].replace("s_waitcnt lgkmcnt(", "s_nop 0 // (") + text[end:]
+    n, problems = _load("check_attn_mfma_asm").check(planted)
+    assert problems
