@@ -360,6 +360,26 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
     const int tok_first = ((vlo >> 5) + (seg_begin - item_ts)) * kTile;
 
     for (int tt = seg_begin; tt < seg_end; ++tt, ++tn) {
+      // The common case -- a tile inside the segment (not its first, second
+      // or last), fully visible, whose copy two tiles ahead is contiguous --
+      // runs as a tight loop with a single block variant.
+      if (wave_active && tt - 1 > seg_begin && tt + 1 < seg_end && tn + 2 < ntiles) {
+        while (tt + 1 < seg_end && tn + 2 < ntiles && cursor_contiguous(cur, a)) {
+          const int tok0 = tok_first + (tt - seg_begin) * kTile;
+          if (!(tok0 >= vlo && tok0 + kTile <= vhi)) break;
+          const char* sb = cursor_src(cur, a);
+          const uint32_t lds_copy = __builtin_amdgcn_readfirstlane(lds_wave + ((tn + 2) & 3) * kTileBytes);
+          cursor_advance(cur, a, m);
+          const uint32_t bs = lds_base + (tn & 3) * kTileBytes;
+          const uint32_t bp = lds_base + ((tn - 1) & 3) * kTileBytes;
+          const uint32_t bn = lds_base + ((tn + 1) & 3) * kTileBytes;
+          float fac;
+          tile_step_tail_d1_f0_m0(kcur, koff, voff, bs, bp, bn, 2u, c, m_ref, l_sum, fac, sb, lds_copy, lofs);
+          if (__any(fac != 1.f)) rescale_acc(fac);
+          ++tt;
+          ++tn;
+        }
+      }
       // copies of tile tn + 2: inside the step block when the tile is
       // contiguous, else issued here
       const bool copy = tn + 2 < ntiles;
