@@ -314,7 +314,8 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
   cur.item = first_item;
   cursor_enter_item(cur, a, m);
   cursor_fetch_pages(cur, a);
-  const uint32_t lds_wave = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(bufs[0])) + wave * kLoads * 1024;
+  const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(bufs[0])) + wave * kLoads * 1024);
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     if (p < ntiles) {
@@ -361,21 +362,33 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
 
     for (int tt = seg_begin; tt < seg_end; ++tt, ++tn) {
       // The common case -- a tile inside the segment (not its first, second
-      // or last), fully visible, whose copy two tiles ahead is contiguous --
-      // runs as a tight loop with a single block variant.
-      if (wave_active && tt - 1 > seg_begin && tt + 1 < seg_end && tn + 2 < ntiles) {
-        while (tt + 1 < seg_end && tn + 2 < ntiles && cursor_contiguous(cur, a)) {
-          const int tok0 = tok_first + (tt - seg_begin) * kTile;
-          if (!(tok0 >= vlo && tok0 + kTile <= vhi)) break;
+      // or last) whose copy two tiles ahead lies inside the same item, not at
+      // its edges, and in one page -- runs as a tight loop with a single block
+      // variant.  Those tiles are wholly visible, and so is the next copy's,
+      // whose page id the block itself reads (in bounds: it is a tile of the
+      // same item) and has waited for when it returns, so no wait for it
+      // lands between the blocks.  The cursor's second page id is not kept
+      // up to date here; with pages of at least one tile it is never used.
+      if (wave_active && tt - 1 > seg_begin && a.kv.page_size >= kTile) {
+        const int hot_end = min(min(seg_end - 1, t1 - 2), item_te - 3);
+        const int psh = a.kv.page_shift;
+        // the first page id came from a compiler-issued load: have it waited
+        // for here, not at the head of every iteration
+        if (tt < hot_end) asm volatile("" ::"s"(cur.pg0));
+        while (tt < hot_end) {
           const char* sb = cursor_src(cur, a);
-          const uint32_t lds_copy = __builtin_amdgcn_readfirstlane(lds_wave + ((tn + 2) & 3) * kTileBytes);
-          cursor_advance(cur, a, m);
+          const uint32_t lds_copy = lds_wave + ((tn + 2) & 3) * kTileBytes;
+          ++cur.tile;
+          cur.tok += kTile;
+          const int32_t* pga = (const int32_t*)(cur.bt_row + (cur.tok >> psh));
           const uint32_t bs = lds_base + (tn & 3) * kTileBytes;
           const uint32_t bp = lds_base + ((tn - 1) & 3) * kTileBytes;
           const uint32_t bn = lds_base + ((tn + 1) & 3) * kTileBytes;
           float fac;
-          tile_step_tail_d1_f0_m0(kcur, koff, voff, bs, bp, bn, 2u, c, m_ref, l_sum, fac, sb, lds_copy, lofs);
-          if (__any(fac != 1.f)) rescale_acc(fac);
+          uint64_t moved;
+          tile_step_tail_d1_f0_m0_pg(kcur, koff, voff, bs, bp, bn, 2u, c, m_ref, l_sum, fac, moved, sb, lds_copy,
+                                     lofs, pga, cur.pg0);
+          if (moved) rescale_acc(fac);
           ++tt;
           ++tn;
         }
@@ -421,30 +434,31 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
           tile_last_pv_f1(kcur, koff, vn, bn, tail);
         }
       } else {
-        float fac;  // 2^(old - new) reference when the tile moved it, else 1
+        float fac;       // 2^(old - new) when the tile moved this lane's reference, else 1
+        uint64_t moved;  // lanes whose reference moved
         const bool fpv = tt - 1 == seg_begin;  // first values step of the segment: O starts at 0
         if (!last) {
           if (fpv) {
-            if (masked) tile_step_tail_d0_f1_m1(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, lo, hi);
-            else if (fused_copy) tile_step_tail_d1_f1_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, sb, lds_copy, lofs);
-            else tile_step_tail_d0_f1_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac);
+            if (masked) tile_step_tail_d0_f1_m1(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, moved, lo, hi);
+            else if (fused_copy) tile_step_tail_d1_f1_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, moved, sb, lds_copy, lofs);
+            else tile_step_tail_d0_f1_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, moved);
           } else {
-            if (masked) tile_step_tail_d0_f0_m1(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, lo, hi);
-            else if (fused_copy) tile_step_tail_d1_f0_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, sb, lds_copy, lofs);
-            else tile_step_tail_d0_f0_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac);
+            if (masked) tile_step_tail_d0_f0_m1(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, moved, lo, hi);
+            else if (fused_copy) tile_step_tail_d1_f0_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, moved, sb, lds_copy, lofs);
+            else tile_step_tail_d0_f0_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, moved);
           }
-          if (__any(fac != 1.f)) rescale_acc(fac);  // rare: a score far above the reference
+          if (moved) rescale_acc(fac);  // rare: a score far above the reference
         } else {
           if (fpv) {
-            if (masked) tile_step_lastv_d0_f1_m1(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, vn, voff, lo, hi);
-            else if (fused_copy) tile_step_lastv_d1_f1_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, vn, voff, sb, lds_copy, lofs);
-            else tile_step_lastv_d0_f1_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, vn, voff);
+            if (masked) tile_step_lastv_d0_f1_m1(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, moved, vn, voff, lo, hi);
+            else if (fused_copy) tile_step_lastv_d1_f1_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, moved, vn, voff, sb, lds_copy, lofs);
+            else tile_step_lastv_d0_f1_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, moved, vn, voff);
           } else {
-            if (masked) tile_step_lastv_d0_f0_m1(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, vn, voff, lo, hi);
-            else if (fused_copy) tile_step_lastv_d1_f0_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, vn, voff, sb, lds_copy, lofs);
-            else tile_step_lastv_d0_f0_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, vn, voff);
+            if (masked) tile_step_lastv_d0_f0_m1(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, moved, vn, voff, lo, hi);
+            else if (fused_copy) tile_step_lastv_d1_f0_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, moved, vn, voff, sb, lds_copy, lofs);
+            else tile_step_lastv_d0_f0_m0(kcur, koff, voff, bs, bp, bn, tail, c, m_ref, l_sum, fac, moved, vn, voff);
           }
-          if (__any(fac != 1.f)) rescale_acc(fac);  // before the tile's own values step
+          if (moved) rescale_acc(fac);  // before the tile's own values step
           tile_last_pv_f0(kcur, koff, vn, bn, tail);
         }
       }

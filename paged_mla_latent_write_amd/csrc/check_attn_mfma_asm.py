@@ -6,7 +6,9 @@ For every block it replays the instruction list and checks that
   1. no MFMA reads a ring register whose LDS read has not been waited for
      (lgkmcnt counts reads in issue order; reads complete in order), and
   2. no LDS read overwrites a ring register that still holds data no MFMA has
-     read yet (a ring slot reused too early).
+     read yet (a ring slot reused too early), and
+  3. every scalar load is waited for (lgkmcnt(0)) before the block ends: its
+     result leaves the block in a register the compiler takes as ready.
 Blocks that start a tile step begin with all ring registers holding data read
 by the previous block's tail.
 """
@@ -40,8 +42,13 @@ def check(text):
         starts_with_ring = name.startswith(("tile_step", "tile_first", "tile_last_pv"))
         live = set(range(ring, 256)) if starts_with_ring else set()
         in_flight = []
+        smem_open = None
         for ln in lines:
             op = ln.split(" ")[0]
+            if op.startswith("s_load"):
+                smem_open = ln
+            elif op == "s_waitcnt" and "lgkmcnt(0)" in ln:
+                smem_open = None
             if op.startswith("ds_read"):
                 dst = regs(ln.split(" ")[1].rstrip(","))
                 if dst & live:
@@ -58,6 +65,8 @@ def check(text):
                     if any(r & q for q in in_flight):
                         problems.append(f"{name}: MFMA before its LDS read landed: {ln}")
                     live -= r
+        if smem_open:
+            problems.append(f"{name}: scalar load not waited for before the block ends: {smem_open}")
     return len(blocks), problems
 
 

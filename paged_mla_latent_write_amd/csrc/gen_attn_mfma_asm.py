@@ -102,14 +102,16 @@ def softmax_ops(first, masked):
         # A tile max above reference + slack moves the reference up to it: the
         # row sum is scaled here and fac = 2^(old - new) is returned so that the
         # caller scales the accumulators (after this block's values step, which
-        # still used the old reference).  NaN compares false: nothing moves.
+        # still used the old reference); the lane mask of the move is returned
+        # in an SGPR pair, so the caller's test is one scalar compare.  NaN
+        # compares false: nothing moves.
         ops += [f"v_add_f32 v{T1}, {SLACK}, %[mref]",
-                f"v_cmp_gt_f32 vcc, v{T0}, v{T1}",
+                f"v_cmp_gt_f32 %[mv], v{T0}, v{T1}",
                 f"v_sub_f32 v{T1}, %[mref], v{T0}",
                 f"v_exp_f32 v{T1}, v{T1}",
                 "s_nop 0",
-                f"v_cndmask_b32 %[fac], 1.0, v{T1}, vcc",
-                f"v_cndmask_b32 %[mref], %[mref], v{T0}, vcc",
+                f"v_cndmask_b32 %[fac], 1.0, v{T1}, %[mv]",
+                f"v_cndmask_b32 %[mref], %[mref], v{T0}, %[mv]",
                 "v_mul_f32 %[lsum], %[lsum], %[fac]"]
     ops += [f"v_sub_f32 {s[i]}, {s[i]}, %[mref]" for i in range(16)]
     ops += [f"v_exp_f32 {s[i]}, {s[i]}" for i in range(16)]
@@ -197,20 +199,25 @@ def s_part(st, dma, copy_p, prefetch_v):
                 st.add(f"v_lshrrev_b32 v{TMP_DMA}, 16, %[l{d // 2}]")
 
 
-def pv_part(st, first_pv, vops, p_regs, prefetched, end_v=False):
+def pv_part(st, first_pv, vops, p_regs, prefetched, end_v=False, smem=None):
     """O^T += V^T P^T (fragments from %[v0..v3], this lane's read offsets plus
     the buffer base %[bp]; P in p_regs), with the VALU list vops interleaved
     between the MFMAs (they read the scores, so they start after 21 wait
     states).  first_pv: the accumulators start at zero.  prefetched: the first
     NF fragments are already queued.  end_v: the slots freed by the last MFMAs
     are refilled with the first fragments of the current tile's own values
-    (%[vn0..vn3] = offsets + %[bs]) for the segment's last values step."""
+    (%[vn0..vn3] = offsets + %[bs]) for the segment's last values step.
+    smem: a scalar load issued before the first MFMA; the block's final
+    lgkmcnt(0) covers it (until it returns it only makes the LDS waits
+    stricter: it is one more operation in flight on the same counter)."""
     if not prefetched:
         st.add(*[f"v_add_u32 %[v{j}], %[bp], %[v{j}]" for j in range(4)])
         for i in range(NF):
             v_reads(st, i)
     per = (len(vops) + 27) // 28
     vi = 0
+    if smem:
+        st.add(smem)
     for i in range(32):
         mt, j = PV_ORDER[i]
         st.wait_for(("V", i))
@@ -272,7 +279,7 @@ KCUR = '[k0] "+v"(kcur[0]), [k1] "+v"(kcur[1]), [k2] "+v"(kcur[2]), [k3] "+v"(kc
 KOFF_IN = '[ko0] "v"(koff[0]), [ko1] "v"(koff[1]), [ko2] "v"(koff[2]), [ko3] "v"(koff[3])'
 VOFF = '[v0] "+v"(voff[0]), [v1] "+v"(voff[1]), [v2] "+v"(voff[2]), [v3] "+v"(voff[3])'
 STATS = '[mref] "+v"(mref), [lsum] "+v"(lsum)'
-FAC = '[fac] "=&v"(fac)'
+FAC = '[fac] "=&v"(fac), [mv] "=&s"(moved)'
 DMA_IN = ('[sb] "s"(sb), [m0] "s"(m0b), [l0] "v"(lofs[0]), [l1] "v"(lofs[1]), [l2] "v"(lofs[2]), '
           '[l3] "v"(lofs[3]), [l4] "v"(lofs[4])')
 CLOBBERS = '"vcc", "memory", MLA_VCLOBBERS, MLA_ACLOBBERS'
@@ -313,7 +320,7 @@ def emit():
                                KOFF_IN]
                         outs = [STATS, KCUR, VOFF]
                         if kind == "step":
-                            args.append("float& fac")
+                            args += ["float& fac", "uint64_t& moved"]
                             outs.append(FAC)
                         if end == "lastv":
                             args.append("uint32_t (&vn)[4]")
@@ -331,6 +338,19 @@ def emit():
                         if kind == "step":
                             s_part(st, dma, True, True)
                             pv_part(st, first_pv, softmax_ops(False, masked), P_FIXED, True, end == "lastv")
+                            if end == "tail" and dma and not first_pv and not masked:
+                                # the same step that also reads one block-table entry (the
+                                # page of a later copy): the result is in %[pg] at the end
+                                st2 = Stream()
+                                st2.queue = [("K", i) for i in range(NF)]
+                                s_part(st2, dma, True, True)
+                                pv_part(st2, first_pv, softmax_ops(False, masked), P_FIXED, True, False,
+                                        "s_load_dword %[pg], %[pga], 0x0")
+                                tail(st2)
+                                o += block(f"tile_step_tail_d{dma}_f{first_pv}_m{masked}_pg",
+                                           args + ["const int32_t* pga", "int32_t& pg"], st2.lines,
+                                           outs + ['[pg] "=&s"(pg)'], ins + ['[pga] "s"(pga)'],
+                                           ', "m0", "scc"')
                         else:
                             # a first tile's own values step (one-tile segment) reads from
                             # the S tail's prefetch: %[bp] is the tile's own buffer then

@@ -1,6 +1,7 @@
 """The generated inline-assembly blocks of the MFMA attention kernel: the
 committed include matches its generator, and a replay of each block finds no
-LDS read consumed before it landed and no ring slot overwritten too early."""
+LDS read consumed before it landed, no ring slot overwritten too early and
+no scalar load left unwaited at the end of a block."""
 import importlib.util
 import subprocess
 import sys
@@ -35,3 +36,15 @@ def test_checker_catches_a_ring_slot_reused_too_early():
     planted = text[:start] + text[start:end].replace("s_waitcnt lgkmcnt(", "s_nop 0 // (") + text[end:]
     n, problems = _load("check_attn_mfma_asm").check(planted)
     assert problems
+
+
+def test_checker_catches_an_unwaited_scalar_load():
+    # plant a mistake: drop the waits that follow the block-table read
+    text = (CSRC / "attn_mfma_asm.inc").read_text()
+    start = text.index("void tile_step_tail_d1_f0_m0_pg(")
+    end = text.index("\n}\n", start)
+    body = text[start:end]
+    assert "s_load_dword" in body
+    planted = text[:start] + body.replace("s_waitcnt lgkmcnt(0)", "s_waitcnt lgkmcnt(1)") + text[end:]
+    n, problems = _load("check_attn_mfma_asm").check(planted)
+    assert any("scalar load" in p for p in problems)
