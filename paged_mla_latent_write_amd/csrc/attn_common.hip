@@ -83,27 +83,56 @@ __global__ __launch_bounds__(kPlanThreads) void plan_items_kernel(
   }
   if (tid == 0) tile_start[Nq] = carry;
   __syncthreads();
-  // Each workgroup's first tile and the item that owns it (the last item whose
-  // first tile is <= it, so items with no tiles are skipped).
+  // Workgroup ranges: the tile stream cut into G ranges of equal estimated
+  // cost, a tile costing 1 and each item kSegmentCostTiles more.  On that
+  // virtual axis item i starts at V_i = tile_start[i] + kSegmentCostTiles * i,
+  // its surcharge first, then its tiles; a cut that falls in a surcharge moves
+  // to the item's first tile (a range may then be empty).
   const int64_t W = carry;
+  const int64_t VT = W + static_cast<int64_t>(kSegmentCostTiles) * Nq;
   for (int g = tid; g <= G; g += kPlanThreads) {
-    const int32_t t = static_cast<int32_t>(wg_tile_begin(g, W, G));
-    wg_tile[g] = t;
-    if (g < G) {
-      int lo = 0, hi = Nq;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (tile_start[mid] <= t) lo = mid; else hi = mid;
-      }
-      wg_item[g] = lo;
+    const int64_t vb = static_cast<int64_t>(g) * VT / G;
+    int lo = 0, hi = Nq + 1;  // largest i <= Nq with V_i <= vb
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tile_start[mid] + static_cast<int64_t>(kSegmentCostTiles) * mid <= vb) lo = mid; else hi = mid;
     }
+    const int64_t ts = tile_start[lo];
+    const int64_t n = lo < Nq ? tile_start[lo + 1] - ts : 0;
+    const int64_t into = vb - ts - static_cast<int64_t>(kSegmentCostTiles) * lo - kSegmentCostTiles;
+    wg_tile[g] = static_cast<int32_t>(ts + min(max(into, int64_t{0}), n));
+  }
+  __syncthreads();
+  // Each workgroup's first item: the last item whose first tile is <= the
+  // range's first tile (items with no tiles are skipped).
+  for (int g = tid; g < G; g += kPlanThreads) {
+    const int32_t t = wg_tile[g];
+    int lo = 0, hi = Nq;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (tile_start[mid] <= t) lo = mid; else hi = mid;
+    }
+    wg_item[g] = lo;
   }
   // The first and last workgroup covering each item (equal when one workgroup
-  // holds all of the item's tiles; both -1 for an item with no tiles).
+  // holds all of the item's tiles; both -1 for an item with no tiles): the
+  // workgroup of tile t is the last g < G with wg_tile[g] <= t.
   for (int i = tid; i < Nq; i += kPlanThreads) {
-    const int64_t ts = tile_start[i], te = tile_start[i + 1];
-    item_wg[2 * i] = te > ts ? static_cast<int32_t>(wg_of_tile(ts, W, G)) : -1;
-    item_wg[2 * i + 1] = te > ts ? static_cast<int32_t>(wg_of_tile(te - 1, W, G)) : -1;
+    const int32_t ts = tile_start[i], te = tile_start[i + 1];
+    int32_t wgs[2] = {-1, -1};
+    if (te > ts) {
+      for (int e = 0; e < 2; ++e) {
+        const int32_t t = e == 0 ? ts : te - 1;
+        int lo = 0, hi = G;
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (wg_tile[mid] <= t) lo = mid; else hi = mid;
+        }
+        wgs[e] = lo;
+      }
+    }
+    item_wg[2 * i] = wgs[0];
+    item_wg[2 * i + 1] = wgs[1];
   }
 }
 

@@ -42,8 +42,7 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a, int hpb) 
   float* al_s = l_s + hpb;           // [hpb]
 
   const int64_t g = blockIdx.x;
-  const int64_t W = a.tile_start[a.num_items];
-  const int64_t t0 = wg_tile_begin(g, W, a.G), t1 = wg_tile_begin(g + 1, W, a.G);
+  const int64_t t0 = a.wg_tile[g], t1 = a.wg_tile[g + 1];
   if (t0 >= t1) return;
   // head blocks: one per grid row (the grid may also have fewer rows)
   for (int hb = blockIdx.y; hb * hpb < a.H; hb += gridDim.y) {

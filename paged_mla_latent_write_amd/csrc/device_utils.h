@@ -74,14 +74,4 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Workgroup g of G owns tiles [g*W/G, (g+1)*W/G) of the item tile stream.
-__device__ __forceinline__ int64_t wg_tile_begin(int64_t g, int64_t W, int64_t G) {
-  return g * W / G;
-}
-
-// The workgroup whose (non-empty) tile range contains tile t.
-__device__ __forceinline__ int64_t wg_of_tile(int64_t t, int64_t W, int64_t G) {
-  return ((t + 1) * G - 1) / W;
-}
-
 }  // namespace mla

@@ -11,6 +11,11 @@ namespace mla {
 // visible key range, aligned to absolute token position (tile k covers
 // positions [32k, 32k + 32)).
 constexpr int kTile = 32;
+// Estimated cost of one segment (an item's run of tiles inside one
+// workgroup's range) beyond its tiles, in tile steps: storing the partial
+// result and loading the next queries, and the slower first, second and last
+// steps.  The split plan balances tiles plus this per item across workgroups.
+constexpr int kSegmentCostTiles = 12;
 
 enum PlanMode { kPlanDecode = 0, kPlanPrefill = 1 };
 enum KvDtype { kKvBf16 = 0, kKvFp8 = 1 };
@@ -35,7 +40,7 @@ struct Plan {
   int32_t* item_lo;      // [Nq] first visible key position
   int32_t* item_hi;      // [Nq] one past the last visible key position
   int32_t* tile_start;   // [Nq + 1] exclusive prefix sum of the items' tile counts
-  int32_t* wg_tile;      // [G + 1] first tile of each workgroup's range (wg_tile_begin)
+  int32_t* wg_tile;      // [G + 1] first tile of each workgroup's range (non-decreasing; may be empty)
   int32_t* wg_item;      // [G] item owning each workgroup's first tile
   int32_t* item_wg;      // [2 Nq] first and last workgroup covering each item's tiles
   int32_t G;             // workgroups the tile stream is divided over
