@@ -363,34 +363,30 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
     for (int tt = seg_begin; tt < seg_end; ++tt, ++tn) {
       // The common case -- a tile inside the segment (not its first, second
       // or last) whose copy two tiles ahead lies inside the same item, not at
-      // its edges, and in one page -- runs as a tight loop with a single block
-      // variant.  Those tiles are wholly visible, and so is the next copy's,
-      // whose page id the block itself reads (in bounds: it is a tile of the
-      // same item) and has waited for when it returns, so no wait for it
-      // lands between the blocks.  The cursor's second page id is not kept
-      // up to date here; with pages of at least one tile it is never used.
+      // its edges, and in one page -- runs as one statement that loops over
+      // those tiles (tile_hot_loop).  Those tiles are wholly visible, and so
+      // is each copy; the loop reads the next copy's page id itself (in
+      // bounds: a tile of the same item).  The cursor's second page id is not
+      // kept up to date there; with pages of at least one tile it is never
+      // used.
       if (wave_active && tt - 1 > seg_begin && a.kv.page_size >= kTile) {
         const int hot_end = min(min(seg_end - 1, t1 - 2), item_te - 3);
-        const int psh = a.kv.page_shift;
-        // the first page id came from a compiler-issued load: have it waited
-        // for here, not at the head of every iteration
-        if (tt < hot_end) asm volatile("" ::"s"(cur.pg0));
-        while (tt < hot_end) {
-          const char* sb = cursor_src(cur, a);
-          const uint32_t lds_copy = lds_wave + ((tn + 2) & 3) * kTileBytes;
-          ++cur.tile;
-          cur.tok += kTile;
-          const int32_t* pga = (const int32_t*)(cur.bt_row + (cur.tok >> psh));
-          const uint32_t bs = lds_base + (tn & 3) * kTileBytes;
-          const uint32_t bp = lds_base + ((tn - 1) & 3) * kTileBytes;
-          const uint32_t bn = lds_base + ((tn + 1) & 3) * kTileBytes;
-          float fac;
-          uint64_t moved;
-          tile_step_tail_d1_f0_m0_pg(kcur, koff, voff, bs, bp, bn, 2u, c, m_ref, l_sum, fac, moved, sb, lds_copy,
-                                     lofs, pga, cur.pg0);
-          if (moved) rescale_acc(fac);
-          ++tt;
-          ++tn;
+        if (tt < hot_end) {
+          const int steps = hot_end - tt;
+          uint32_t n = steps;
+          uint32_t xs = lds_base + (tn & 3) * kTileBytes, xp = lds_base + ((tn - 1) & 3) * kTileBytes;
+          uint32_t xn = lds_base + ((tn + 1) & 3) * kTileBytes, xc = lds_base + ((tn + 2) & 3) * kTileBytes;
+          int tok = cur.tok;
+          int32_t pg = cur.pg0;
+          tile_hot_loop(kcur, koff, voff, c, m_ref, l_sum, xs, xp, xn, xc, lds_wave - lds_base, n, tok, pg,
+                        static_cast<const char*>(a.kv.data), (const int32_t*)cur.bt_row,
+                        static_cast<uint32_t>(a.kv.page_shift), static_cast<uint32_t>(a.kv.page_size - 1),
+                        static_cast<uint32_t>(a.kv.num_pages - 1), static_cast<uint32_t>(kRowBytes), lofs);
+          cur.tile += steps;
+          cur.tok = tok;
+          cur.pg0 = pg;
+          tt += steps;
+          tn += steps;
         }
       }
       // copies of tile tn + 2: inside the step block when the tile is

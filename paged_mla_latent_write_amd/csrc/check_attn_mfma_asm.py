@@ -36,10 +36,10 @@ def regs(tok):
 def check(text):
     ring = ring_base()
     problems = []
-    blocks = re.findall(r"void (\w+)\(.*?\) \{\n  asm volatile\(\n(.*?)\n      :", text, re.S)
+    blocks = re.findall(r"void (\w+)\(.*?\) \{\n(?:  [^\n]*;\n)*  asm volatile\(\n(.*?)\n      :", text, re.S)
     for name, body in blocks:
         lines = [ln.strip().strip('"').replace("\\n", "") for ln in body.split("\n")]
-        starts_with_ring = name.startswith(("tile_step", "tile_first", "tile_last_pv"))
+        starts_with_ring = name.startswith(("tile_step", "tile_first", "tile_last_pv", "tile_hot"))
         live = set(range(ring, 256)) if starts_with_ring else set()
         in_flight = []
         smem_open = None

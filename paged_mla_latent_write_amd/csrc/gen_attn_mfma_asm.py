@@ -10,15 +10,15 @@ one block to the next; the blocks below own them:
     a0-a255    O^T accumulators of the wave's 32 heads: 16 tiles of 32 dims
     v50-v57    P of the previous tile (bf16, B operand of O^T += V^T P^T)
     v58-v201   Q^T fragments: 36 k-steps x 4 registers (q_lat then q_pe)
-    v202       copy-offset temporary
-    v204-v219  score chain 0; v220-v235 score chain 1 (after the softmax sum,
-               v220-v227 hold the new P, v228/v229 are temporaries and
-               v232-v235 the addresses of a segment's last values step)
-    v236-v255  ring of five LDS fragments in flight
+    v202-v203  copy-offset temporary (scores phase), softmax temporaries
+    v204-v219  scores (one accumulation chain: a dependent MFMA chain issues
+               at the full rate)
+    v220-v227  P of the current tile (the softmax output)
+    v228-v255  ring of seven LDS fragments in flight
 
 A tile step is one inline-assembly statement of one wave:
 
-  * S^T[32 tok x 32 heads] = K_t Q^T: 36 MFMA k-steps in two chains, K read
+  * S^T[32 tok x 32 heads] = K_t Q^T: 36 MFMA k-steps in one chain, K read
     from LDS by ds_read_b128 through the ring (optionally with the 9 HBM->LDS
     copies of a later tile interleaved between the MFMAs);
   * O^T += V_{t-1}^T P_{t-1}^T: 32 MFMAs, V^T read by ds_read_b64_tr_b16,
@@ -32,15 +32,15 @@ A tile step is one inline-assembly statement of one wave:
 """
 import sys
 
-NF = 5                      # LDS fragments in flight (ring of 4 NF registers)
-RING = 256 - 4 * NF         # v236-v255
-TT = RING - 16              # score chain 1: v220-v235
-SS = TT - 16                # score chain 0: v204-v219
-TMP_DMA = SS - 2            # v202 (v203 unused; tuples start on even registers)
+NF = 7                      # LDS fragments in flight (ring of 4 NF registers)
+RING = 256 - 4 * NF         # v228-v255
+PN = RING - 8               # v220-v227: P of the current tile
+SS = PN - 16                # v204-v219: scores
+TMP_DMA = SS - 2            # v202: copy offsets (scores phase only)
+T0, T1 = SS - 2, SS - 1     # v202, v203: softmax temporaries (values phase)
 Q_BASE = TMP_DMA - 144      # v58-v201
 P_BASE = Q_BASE - 8         # v50-v57
 NC = P_BASE                 # v0..v49 for the compiler
-T0, T1 = TT + 8, TT + 9     # softmax temporaries (free after the sum)
 NEG_INF = "0xff800000"
 SLACK = "0x41800000"        # 16.0f: slack of the reference maximum (log2 units)
 
@@ -68,16 +68,16 @@ def ring2(i, half):
 
 
 def s_chain(k):
-    return f"v[{SS}:{SS + 15}]" if k % 2 == 0 else f"v[{TT}:{TT + 15}]"
+    return f"v[{SS}:{SS + 15}]"
 
 
 def softmax_ops(first, masked):
-    """The softmax of one tile (scores in both chains) as VALU instructions;
-    leaves P (bf16 pairs) in v220-v227."""
+    """The softmax of one tile (scores in v204-v219) as VALU instructions;
+    leaves P (bf16 pairs) in v220-v227.  The scale %[c] (log2 units) is
+    positive, so the tile maximum is taken on the raw scores and scaled once;
+    each exponent is then one fused multiply-add, s c - m."""
     s = [f"v{SS + i}" for i in range(16)]
-    t = [f"v{TT + i}" for i in range(16)]
-    ops = [f"v_add_f32 {s[i]}, {s[i]}, {t[i]}" for i in range(16)]
-    ops += [f"v_mul_f32 {s[i]}, %[c], {s[i]}" for i in range(16)]
+    ops = []
     if masked:
         # element i of this lane is token tok0 + 8 (i / 4) + 4 g + i % 4; with
         # lo / hi = vlo - tok0 - 4 g, vhi - tok0 - 4 g it is visible iff
@@ -95,7 +95,7 @@ def softmax_ops(first, masked):
     ops.append(f"v_max_f32 v{T0}, v{T0}, {s[15]}")
     # the other wave half holds the same heads (other tokens)
     ops += [f"v_mov_b32 v{T1}, v{T0}", "s_nop 1", f"v_permlane32_swap_b32 v{T1}, v{T1}", "s_nop 1",
-            f"v_max_f32 v{T0}, v{T0}, v{T1}"]
+            f"v_max_f32 v{T0}, v{T0}, v{T1}", f"v_mul_f32 v{T0}, %[c], v{T0}"]
     if first:
         ops.append(f"v_mov_b32 %[mref], v{T0}")
     else:
@@ -113,13 +113,13 @@ def softmax_ops(first, masked):
                 f"v_cndmask_b32 %[fac], 1.0, v{T1}, %[mv]",
                 f"v_cndmask_b32 %[mref], %[mref], v{T0}, %[mv]",
                 "v_mul_f32 %[lsum], %[lsum], %[fac]"]
-    ops += [f"v_sub_f32 {s[i]}, {s[i]}, %[mref]" for i in range(16)]
+    ops += [f"v_fma_f32 {s[i]}, {s[i]}, %[c], -%[mref]" for i in range(16)]
     ops += [f"v_exp_f32 {s[i]}, {s[i]}" for i in range(16)]
     ops.append("s_nop 0")
     ops.append(f"v_add_f32 v{T1}, {s[0]}, {s[1]}")
     ops += [f"v_add_f32 v{T1}, v{T1}, {s[i]}" for i in range(2, 16)]
     ops.append(f"v_add_f32 %[lsum], %[lsum], v{T1}")
-    ops += [f"v_cvt_pk_bf16_f32 v{TT + j}, {s[2 * j]}, {s[2 * j + 1]}" for j in range(8)]
+    ops += [f"v_cvt_pk_bf16_f32 v{PN + j}, {s[2 * j]}, {s[2 * j + 1]}" for j in range(8)]
     return ops
 
 
@@ -179,10 +179,10 @@ def s_part(st, dma, copy_p, prefetch_v):
         st.add("s_mov_b32 m0, %[m0]", f"v_and_b32 v{TMP_DMA}, 0xffff, %[l0]")
     for k in range(36):
         st.wait_for(("K", k))
-        st.add(f"v_mfma_f32_32x32x16_bf16 {s_chain(k)}, {ring4(k)}, {q(k)}, {'0' if k < 2 else s_chain(k)}")
+        st.add(f"v_mfma_f32_32x32x16_bf16 {s_chain(k)}, {ring4(k)}, {q(k)}, {'0' if k == 0 else s_chain(k)}")
         if k == 0 and copy_p:
-            # before chain 1's first MFMA overwrites the previous P
-            st.add(*[f"v_mov_b32 v{P_BASE + j}, v{TT + j}" for j in range(8)])
+            # the previous P leaves the softmax output registers
+            st.add(*[f"v_mov_b32 v{P_BASE + j}, v{PN + j}" for j in range(8)])
         if k + NF < 36:
             k_read(st, k + NF)
         elif prefetch_v:
@@ -250,6 +250,100 @@ def pv_part(st, first_pv, vops, p_regs, prefetched, end_v=False, smem=None):
 COPY_LOADS = 9  # HBM->LDS copies per wave per tile
 
 
+def s_part_hot(st):
+    """The scores step of the hot loop: like s_part with a copy, but the copy's
+    HBM address is formed here, per lane, as a 64-bit VGPR pair (v202:v203 =
+    v220:v221 + offset; v220:v221 = %[data] + row * row bytes, the row being
+    the page of %[pg] (clamped to the cache) times the page size plus the
+    in-page position of %[tok]), so that no 64-bit scalar arithmetic is
+    needed; it then advances %[tok] by one tile and forms the block-table
+    offset %[pgo] of the next copy's page.  The copy lands at %[bc] +
+    %[woff] (M0).  v220:v221 are free once the previous P has moved out."""
+    st.add(*[f"v_add_u32 %[v{j}], %[bp], %[v{j}]" for j in range(4)])
+    st.add("s_add_u32 m0, %[bc], %[woff]")
+    extract = lambda d: (f"v_and_b32 v{TMP_DMA}, 0xffff, %[l{d // 2}]" if d % 2 == 0
+                         else f"v_lshrrev_b32 v{TMP_DMA}, 16, %[l{d // 2}]")
+    add64 = [f"v_add_co_u32 v{TMP_DMA}, vcc, v{PN}, v{TMP_DMA}",
+             f"v_addc_co_u32 v{TMP_DMA + 1}, vcc, v{PN + 1}, 0, vcc"]
+    for k in range(36):
+        st.wait_for(("K", k))
+        st.add(f"v_mfma_f32_32x32x16_bf16 {s_chain(k)}, {ring4(k)}, {q(k)}, {'0' if k == 0 else s_chain(k)}")
+        if k == 0:
+            st.add(*[f"v_mov_b32 v{P_BASE + j}, v{PN + j}" for j in range(8)])
+        if k + NF < 36:
+            k_read(st, k + NF)
+        else:
+            v_reads(st, k % NF)
+        if k == 1:
+            st.add("s_min_u32 %[t0], %[pg], %[np1]", "s_lshl_b32 %[t0], %[t0], %[psh]",
+                   "s_and_b32 %[t1], %[tok], %[pmask]", "s_add_u32 %[t0], %[t0], %[t1]",
+                   f"v_mov_b32 v{TMP_DMA}, %[t0]",
+                   f"v_mad_u64_u32 v[{PN}:{PN + 1}], vcc, v{TMP_DMA}, %[rowb], %[data]",
+                   extract(0), *add64)
+        if k == 3:
+            st.add("s_add_u32 %[tok], %[tok], 32", "s_lshr_b32 %[pgo], %[tok], %[psh]",
+                   "s_lshl_b32 %[pgo], %[pgo], 2")
+        # copy d is issued after MFMA 2 + 4 d; its address is formed one MFMA earlier
+        if k % 4 == 2:
+            st.add(f"global_load_lds_dwordx4 v[{TMP_DMA}:{TMP_DMA + 1}], off")
+        if k % 4 == 1 and 1 <= k // 4 <= 8:
+            st.add("s_add_u32 m0, m0, 0x400", extract(k // 4), *add64)
+
+
+def hot_loop():
+    """The common tile step, repeated %[n] times in one statement: scores of
+    tile t with the copy of tile t + 2 (contiguous, inside one page), values of
+    tile t - 1 with the softmax of tile t, the block-table read of the next
+    copy's page, the wait for tile t + 1 and the barrier, the next tile's
+    first K fragments; then the rare accumulator rescale (out of line), the
+    rotation of the four LDS buffer bases and the loop test."""
+    st = Stream()
+    st.queue = [("K", i) for i in range(NF)]
+    st.add("1:")
+    s_part_hot(st)
+    pv_part(st, False, softmax_ops(False, False), P_FIXED, True, False,
+            "s_load_dword %[pg], %[bt], %[pgo]")
+    st.add(f"s_waitcnt vmcnt({COPY_LOADS})", "s_barrier")
+    st.add(*[f"v_add_u32 %[k{j}], %[bn], %[ko{j}]" for j in range(4)])
+    for i in range(NF):
+        st.add(f"ds_read_b128 {ring4(i)}, %[k{i % 4}] offset:{128 * (i // 4)}")
+    st.add("s_cmp_lg_u64 %[mv], 0", "s_cbranch_scc1 3f",
+           "2:",
+           "s_mov_b32 %[t0], %[bp]", "s_mov_b32 %[bp], %[bs]", "s_mov_b32 %[bs], %[bn]",
+           "s_mov_b32 %[bn], %[bc]", "s_mov_b32 %[bc], %[t0]",
+           "s_sub_u32 %[n], %[n], 1", "s_cmp_lg_u32 %[n], 0", "s_cbranch_scc1 1b",
+           "s_branch 4f",
+           "3:")
+    st.add(*rescale_lines())
+    st.add("s_branch 2b", "4:")
+    args = ["uint32_t (&kcur)[4]", "const uint32_t (&koff)[4]", "uint32_t (&voff)[4]", "float c",
+            "float& mref", "float& lsum", "uint32_t& bs", "uint32_t& bp", "uint32_t& bn", "uint32_t& bc",
+            "uint32_t woff", "uint32_t& n", "int& tok", "int32_t& pg", "const char* data", "const int32_t* bt",
+            "uint32_t psh", "uint32_t pmask", "uint32_t np1", "uint32_t rowb", "const uint32_t (&lofs)[5]"]
+    outs = [STATS, KCUR, VOFF, FAC,
+            '[bs] "+s"(bs), [bp] "+s"(bp), [bn] "+s"(bn), [bc] "+s"(bc), [n] "+s"(n), [tok] "+s"(tok), '
+            '[pg] "+s"(pg)',
+            '[t0] "=&s"(t0), [t1] "=&s"(t1), [pgo] "=&s"(pgo)']
+    ins = ['[c] "s"(c), [woff] "s"(woff), [data] "s"(data), [bt] "s"(bt), [psh] "s"(psh), '
+           '[pmask] "s"(pmask), [np1] "s"(np1), [rowb] "v"(rowb)',
+           KOFF_IN,
+           '[l0] "v"(lofs[0]), [l1] "v"(lofs[1]), [l2] "v"(lofs[2]), [l3] "v"(lofs[3]), [l4] "v"(lofs[4])']
+    o = block("tile_hot_loop", args, st.lines, outs, ins, ', "m0", "scc"',
+              locals_="  float fac;\n  uint64_t moved;\n  uint32_t t0, t1, pgo;\n")
+    return o
+
+
+def rescale_lines():
+    """Scale this lane's accumulators by %[fac] (rare: after a reference move);
+    temporaries: the score registers (P of the tile is in v220-v227, the next
+    K fragments in the ring)."""
+    L = ["s_nop 7", "s_nop 7", "s_nop 4"]  # the last MFMA results must have landed
+    for r in range(256):
+        t = SS + (r % 16)
+        L += [f"v_accvgpr_read_b32 v{t}, a{r}", f"v_mul_f32 v{t}, %[fac], v{t}", f"v_accvgpr_write_b32 a{r}, v{t}"]
+    return L
+
+
 def tail(st):
     """Wait for the next tile's copy, pass the workgroup barrier, and read the
     next tile's first K fragments into the ring (%[k0..k3] = %[ko0..ko3] +
@@ -267,8 +361,7 @@ def tail(st):
 
 
 P_FIXED = (f"v[{P_BASE}:{P_BASE + 3}]", f"v[{P_BASE + 4}:{P_BASE + 7}]")
-P_NEW = (f"v[{TT}:{TT + 3}]", f"v[{TT + 4}:{TT + 7}]")
-VNEXT = tuple(f"v{TT + 12 + j}" for j in range(4))   # free after the softmax sum
+P_NEW = (f"v[{PN}:{PN + 3}]", f"v[{PN + 4}:{PN + 7}]")
 
 
 def cstr(lines, indent="      "):
@@ -285,8 +378,11 @@ DMA_IN = ('[sb] "s"(sb), [m0] "s"(m0b), [l0] "v"(lofs[0]), [l1] "v"(lofs[1]), [l
 CLOBBERS = '"vcc", "memory", MLA_VCLOBBERS, MLA_ACLOBBERS'
 
 
-def block(name, args, body, outs, ins, extra_clob=""):
-    o = [f"__device__ __forceinline__ void {name}({', '.join(args)}) {{", "  asm volatile("]
+def block(name, args, body, outs, ins, extra_clob="", locals_=""):
+    o = [f"__device__ __forceinline__ void {name}({', '.join(args)}) {{"]
+    if locals_:
+        o.append(locals_.rstrip("\n"))
+    o.append("  asm volatile(")
     o.append(cstr(body))
     o.append("      : " + ",\n        ".join(outs))
     o.append("      : " + ",\n        ".join(ins))
@@ -338,19 +434,6 @@ def emit():
                         if kind == "step":
                             s_part(st, dma, True, True)
                             pv_part(st, first_pv, softmax_ops(False, masked), P_FIXED, True, end == "lastv")
-                            if end == "tail" and dma and not first_pv and not masked:
-                                # the same step that also reads one block-table entry (the
-                                # page of a later copy): the result is in %[pg] at the end
-                                st2 = Stream()
-                                st2.queue = [("K", i) for i in range(NF)]
-                                s_part(st2, dma, True, True)
-                                pv_part(st2, first_pv, softmax_ops(False, masked), P_FIXED, True, False,
-                                        "s_load_dword %[pg], %[pga], 0x0")
-                                tail(st2)
-                                o += block(f"tile_step_tail_d{dma}_f{first_pv}_m{masked}_pg",
-                                           args + ["const int32_t* pga", "int32_t& pg"], st2.lines,
-                                           outs + ['[pg] "=&s"(pg)'], ins + ['[pga] "s"(pga)'],
-                                           ', "m0", "scc"')
                         else:
                             # a first tile's own values step (one-tile segment) reads from
                             # the S tail's prefetch: %[bp] is the tile's own buffer then
@@ -412,13 +495,8 @@ def emit():
             L.append(f"global_store_dwordx4 %[orow], v[{r}:{r + 3}], off offset:{4 * (32 * mt + 8 * a4)}")
             n += 1
     o += block("store_acc", ["float* orow"], L, [], ['[orow] "v"(orow)'])
-    # scale this lane's accumulators by fac (rare: after a reference move);
-    # temporaries: score chain 0 (P of the tile is in chain 1, fragments in the ring)
-    L = ["s_nop 7", "s_nop 7", "s_nop 4"]  # the last MFMA results must have landed
-    for r in range(256):
-        t = SS + (r % 16)
-        L += [f"v_accvgpr_read_b32 v{t}, a{r}", f"v_mul_f32 v{t}, %[fac], v{t}", f"v_accvgpr_write_b32 a{r}, v{t}"]
-    o += block("rescale_acc", ["float fac"], L, [], ['[fac] "v"(fac)'])
+    o += block("rescale_acc", ["float fac"], rescale_lines(), [], ['[fac] "v"(fac)'])
+    o += hot_loop()
     return "\n".join(o)
 
 

@@ -226,7 +226,8 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
   a.part_lse = at<float>(workspace, L.part_lse);
   a.part_scale = at<float>(workspace, L.part_scale);
 
-  const bool use_mfma = !generic && mla::mfma_attn_supported(kv, H) &&
+  // (the MFMA kernel takes the tile maximum on unscaled scores: scale > 0)
+  const bool use_mfma = !generic && mla::mfma_attn_supported(kv, H) && attn->scale > 0.f &&
                         (ql_st % 8 == 0) && (ql_sh % 8 == 0) && (qp_st % 8 == 0) &&
                         (qp_sh % 8 == 0) && aligned16(q_lat) && aligned16(q_pe);
   if (attn->kernel_events[0] &&

@@ -41,7 +41,7 @@ def test_checker_catches_a_ring_slot_reused_too_early():
 def test_checker_catches_an_unwaited_scalar_load():
     # plant a mistake: drop the waits that follow the block-table read
     text = (CSRC / "attn_mfma_asm.inc").read_text()
-    start = text.index("void tile_step_tail_d1_f0_m0_pg(")
+    start = text.index("void tile_hot_loop(")
     end = text.index("\n}\n", start)
     body = text[start:end]
     assert "s_load_dword" in body
