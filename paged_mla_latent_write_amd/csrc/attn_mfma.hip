@@ -381,7 +381,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
           tile_hot_loop(kcur, koff, voff, c, m_ref, l_sum, xs, xp, xn, xc, lds_wave - lds_base, n, tok, pg,
                         static_cast<const char*>(a.kv.data), (const int32_t*)cur.bt_row,
                         static_cast<uint32_t>(a.kv.page_shift), static_cast<uint32_t>(a.kv.page_size - 1),
-                        static_cast<uint32_t>(a.kv.num_pages - 1), static_cast<uint32_t>(kRowBytes), lofs);
+                        static_cast<uint32_t>(a.kv.num_pages - 1), lofs);
           cur.tile += steps;
           cur.tok = tok;
           cur.pg0 = pg;

@@ -131,6 +131,7 @@ class Stream:
     def __init__(self):
         self.lines = []
         self.queue = []          # tags of the LDS reads in flight, oldest first
+        self.done = set()        # tags known to have completed
 
     def add(self, *lines):
         self.lines += list(lines)
@@ -141,11 +142,28 @@ class Stream:
 
     def wait_for(self, tag):
         if tag not in self.queue:
+            if tag not in self.done:
+                raise ValueError(f"wait for an LDS read never issued: {tag}")
             return  # already known to have completed (an older wait covered it)
         last = max(i for i, t in enumerate(self.queue) if t == tag)
         after = len(self.queue) - last - 1
         self.lines.append(f"s_waitcnt lgkmcnt({min(15, after)})")
+        self.done.update(self.queue[:last + 1])
         self.queue = self.queue[last + 1:]
+
+    def wait_pair(self, kind, i, n):
+        """Before MFMA i of n: at even i wait for fragments i and i + 1 together
+        (one lgkmcnt per two MFMAs; fragment i + 1 was issued a few MFMAs
+        earlier, so the extra wait is short); at odd i that wait covered it.
+        Of the two, the one issued later is waited for (the values fragments
+        prefetched during the scores are issued out of index order)."""
+        if i % 2 == 1 or i + 1 >= n:
+            self.wait_for((kind, i))
+            return
+        pair = [(kind, i), (kind, i + 1)]
+        pos = [max((j for j, t in enumerate(self.queue) if t == tag), default=-1) for tag in pair]
+        self.wait_for(pair[0] if pos[0] > pos[1] else pair[1])
+        self.wait_for(pair[0])
 
 
 PV_ORDER = [(mt, j) for j in range(2) for mt in range(16)]
@@ -178,7 +196,7 @@ def s_part(st, dma, copy_p, prefetch_v):
     if dma:
         st.add("s_mov_b32 m0, %[m0]", f"v_and_b32 v{TMP_DMA}, 0xffff, %[l0]")
     for k in range(36):
-        st.wait_for(("K", k))
+        st.wait_pair("K", k, 36)
         st.add(f"v_mfma_f32_32x32x16_bf16 {s_chain(k)}, {ring4(k)}, {q(k)}, {'0' if k == 0 else s_chain(k)}")
         if k == 0 and copy_p:
             # the previous P leaves the softmax output registers
@@ -220,7 +238,7 @@ def pv_part(st, first_pv, vops, p_regs, prefetched, end_v=False, smem=None):
         st.add(smem)
     for i in range(32):
         mt, j = PV_ORDER[i]
-        st.wait_for(("V", i))
+        st.wait_pair("V", i, 32)
         src_c = "0" if (first_pv and j == 0) else acc(mt)
         st.add(f"v_mfma_f32_32x32x16_bf16 {acc(mt)}, {ring4(i)}, {p_regs[j]}, {src_c}")
         if i + NF < 32:
@@ -248,25 +266,23 @@ def pv_part(st, first_pv, vops, p_regs, prefetched, end_v=False, smem=None):
 
 
 COPY_LOADS = 9  # HBM->LDS copies per wave per tile
+ROW_BYTES = 1152  # one cached token: 512 latent + 64 rope bf16 values
 
 
 def s_part_hot(st):
     """The scores step of the hot loop: like s_part with a copy, but the copy's
-    HBM address is formed here, per lane, as a 64-bit VGPR pair (v202:v203 =
-    v220:v221 + offset; v220:v221 = %[data] + row * row bytes, the row being
-    the page of %[pg] (clamped to the cache) times the page size plus the
-    in-page position of %[tok]), so that no 64-bit scalar arithmetic is
-    needed; it then advances %[tok] by one tile and forms the block-table
-    offset %[pgo] of the next copy's page.  The copy lands at %[bc] +
-    %[woff] (M0).  v220:v221 are free once the previous P has moved out."""
+    HBM base is formed here: s[96:97] = %[data] (kept in s[98:99]) + row *
+    row bytes, the row being the page of %[pg] (clamped to the cache) times
+    the page size plus the in-page position of %[tok] (fixed registers, as
+    the 64-bit add needs its halves); it then advances %[tok] by one tile
+    and forms the block-table offset %[pgo] of the next copy's page.  The
+    copy lands at %[bc] + %[woff] (M0)."""
     st.add(*[f"v_add_u32 %[v{j}], %[bp], %[v{j}]" for j in range(4)])
     st.add("s_add_u32 m0, %[bc], %[woff]")
     extract = lambda d: (f"v_and_b32 v{TMP_DMA}, 0xffff, %[l{d // 2}]" if d % 2 == 0
                          else f"v_lshrrev_b32 v{TMP_DMA}, 16, %[l{d // 2}]")
-    add64 = [f"v_add_co_u32 v{TMP_DMA}, vcc, v{PN}, v{TMP_DMA}",
-             f"v_addc_co_u32 v{TMP_DMA + 1}, vcc, v{PN + 1}, 0, vcc"]
     for k in range(36):
-        st.wait_for(("K", k))
+        st.wait_pair("K", k, 36)
         st.add(f"v_mfma_f32_32x32x16_bf16 {s_chain(k)}, {ring4(k)}, {q(k)}, {'0' if k == 0 else s_chain(k)}")
         if k == 0:
             st.add(*[f"v_mov_b32 v{P_BASE + j}, v{PN + j}" for j in range(8)])
@@ -277,17 +293,16 @@ def s_part_hot(st):
         if k == 1:
             st.add("s_min_u32 %[t0], %[pg], %[np1]", "s_lshl_b32 %[t0], %[t0], %[psh]",
                    "s_and_b32 %[t1], %[tok], %[pmask]", "s_add_u32 %[t0], %[t0], %[t1]",
-                   f"v_mov_b32 v{TMP_DMA}, %[t0]",
-                   f"v_mad_u64_u32 v[{PN}:{PN + 1}], vcc, v{TMP_DMA}, %[rowb], %[data]",
-                   extract(0), *add64)
+                   f"s_mul_i32 s96, %[t0], {ROW_BYTES}", f"s_mul_hi_u32 s97, %[t0], {ROW_BYTES}",
+                   "s_add_u32 s96, s96, s98", "s_addc_u32 s97, s97, s99", extract(0))
         if k == 3:
             st.add("s_add_u32 %[tok], %[tok], 32", "s_lshr_b32 %[pgo], %[tok], %[psh]",
                    "s_lshl_b32 %[pgo], %[pgo], 2")
-        # copy d is issued after MFMA 2 + 4 d; its address is formed one MFMA earlier
+        # copy d is issued after MFMA 2 + 4 d; its lane offset is unpacked one MFMA earlier
         if k % 4 == 2:
-            st.add(f"global_load_lds_dwordx4 v[{TMP_DMA}:{TMP_DMA + 1}], off")
+            st.add(f"global_load_lds_dwordx4 v{TMP_DMA}, s[96:97] offset:0")
         if k % 4 == 1 and 1 <= k // 4 <= 8:
-            st.add("s_add_u32 m0, m0, 0x400", extract(k // 4), *add64)
+            st.add("s_add_u32 m0, m0, 0x400", extract(k // 4))
 
 
 def hot_loop():
@@ -299,7 +314,7 @@ def hot_loop():
     rotation of the four LDS buffer bases and the loop test."""
     st = Stream()
     st.queue = [("K", i) for i in range(NF)]
-    st.add("1:")
+    st.add("s_mov_b64 s[98:99], %[data]", "1:")
     s_part_hot(st)
     pv_part(st, False, softmax_ops(False, False), P_FIXED, True, False,
             "s_load_dword %[pg], %[bt], %[pgo]")
@@ -319,16 +334,16 @@ def hot_loop():
     args = ["uint32_t (&kcur)[4]", "const uint32_t (&koff)[4]", "uint32_t (&voff)[4]", "float c",
             "float& mref", "float& lsum", "uint32_t& bs", "uint32_t& bp", "uint32_t& bn", "uint32_t& bc",
             "uint32_t woff", "uint32_t& n", "int& tok", "int32_t& pg", "const char* data", "const int32_t* bt",
-            "uint32_t psh", "uint32_t pmask", "uint32_t np1", "uint32_t rowb", "const uint32_t (&lofs)[5]"]
+            "uint32_t psh", "uint32_t pmask", "uint32_t np1", "const uint32_t (&lofs)[5]"]
     outs = [STATS, KCUR, VOFF, FAC,
             '[bs] "+s"(bs), [bp] "+s"(bp), [bn] "+s"(bn), [bc] "+s"(bc), [n] "+s"(n), [tok] "+s"(tok), '
             '[pg] "+s"(pg)',
             '[t0] "=&s"(t0), [t1] "=&s"(t1), [pgo] "=&s"(pgo)']
     ins = ['[c] "s"(c), [woff] "s"(woff), [data] "s"(data), [bt] "s"(bt), [psh] "s"(psh), '
-           '[pmask] "s"(pmask), [np1] "s"(np1), [rowb] "v"(rowb)',
+           '[pmask] "s"(pmask), [np1] "s"(np1)',
            KOFF_IN,
            '[l0] "v"(lofs[0]), [l1] "v"(lofs[1]), [l2] "v"(lofs[2]), [l3] "v"(lofs[3]), [l4] "v"(lofs[4])']
-    o = block("tile_hot_loop", args, st.lines, outs, ins, ', "m0", "scc"',
+    o = block("tile_hot_loop", args, st.lines, outs, ins, ', "m0", "scc", "s96", "s97", "s98", "s99"',
               locals_="  float fac;\n  uint64_t moved;\n  uint32_t t0, t1, pgo;\n")
     return o
 
@@ -506,7 +521,7 @@ def pv_rest(st, first_pv, p_regs, vregs):
     segment's stores get their wait states there."""
     for i in range(32):
         mt, j = PV_ORDER[i]
-        st.wait_for(("V", i))
+        st.wait_pair("V", i, 32)
         src_c = "0" if (first_pv and j == 0) else acc(mt)
         st.add(f"v_mfma_f32_32x32x16_bf16 {acc(mt)}, {ring4(i)}, {p_regs[j]}, {src_c}")
         if i + NF < 32:
