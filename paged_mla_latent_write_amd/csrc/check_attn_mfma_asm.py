@@ -10,7 +10,9 @@ For every block it replays the instruction list and checks that
   3. every scalar load is waited for (lgkmcnt(0)) before the block ends: its
      result leaves the block in a register the compiler takes as ready.
 Blocks that start a tile step begin with all ring registers holding data read
-by the previous block's tail.
+by the previous block's tail.  A block that loops (label 1 and a branch back
+to it) is replayed twice, so reads issued at the end of one pass are checked
+against the waits of the next.
 """
 import re
 import sys
@@ -33,6 +35,36 @@ def regs(tok):
     return {int(m.group(1))} if m else set()
 
 
+def replay(name, lines, ring, live, in_flight, problems):
+    """Replays lines from the given state; returns the state at the end."""
+    smem_open = None
+    for ln in lines:
+        op = ln.split(" ")[0]
+        if op.startswith("s_load"):
+            smem_open = ln
+        elif op == "s_waitcnt" and "lgkmcnt(0)" in ln:
+            smem_open = None
+        if op.startswith("ds_read"):
+            dst = regs(ln.split(" ")[1].rstrip(","))
+            if dst & live:
+                problems.append(f"{name}: LDS read overwrites unread data: {ln}")
+            in_flight.append(dst)
+            live |= dst
+        elif op == "s_waitcnt" and "lgkmcnt" in ln:
+            n = int(re.search(r"lgkmcnt\((\d+)\)", ln).group(1))
+            while len(in_flight) > n:
+                in_flight.pop(0)
+        elif op.startswith("v_mfma"):
+            for tok in (t.rstrip(",") for t in ln.split(" ")[2:4]):
+                r = regs(tok)
+                if any(r & q for q in in_flight):
+                    problems.append(f"{name}: MFMA before its LDS read landed: {ln}")
+                live -= r
+    if smem_open:
+        problems.append(f"{name}: scalar load not waited for before the block ends: {smem_open}")
+    return live, in_flight
+
+
 def check(text):
     ring = ring_base()
     problems = []
@@ -41,33 +73,17 @@ def check(text):
         lines = [ln.strip().strip('"').replace("\\n", "") for ln in body.split("\n")]
         starts_with_ring = name.startswith(("tile_step", "tile_first", "tile_last_pv", "tile_hot"))
         live = set(range(ring, 256)) if starts_with_ring else set()
-        in_flight = []
-        smem_open = None
-        for ln in lines:
-            op = ln.split(" ")[0]
-            if op.startswith("s_load"):
-                smem_open = ln
-            elif op == "s_waitcnt" and "lgkmcnt(0)" in ln:
-                smem_open = None
-            if op.startswith("ds_read"):
-                dst = regs(ln.split(" ")[1].rstrip(","))
-                if dst & live:
-                    problems.append(f"{name}: LDS read overwrites unread data: {ln}")
-                in_flight.append(dst)
-                live |= dst
-            elif op == "s_waitcnt" and "lgkmcnt" in ln:
-                n = int(re.search(r"lgkmcnt\((\d+)\)", ln).group(1))
-                while len(in_flight) > n:
-                    in_flight.pop(0)
-            elif op.startswith("v_mfma"):
-                for tok in (t.rstrip(",") for t in ln.split(" ")[2:4]):
-                    r = regs(tok)
-                    if any(r & q for q in in_flight):
-                        problems.append(f"{name}: MFMA before its LDS read landed: {ln}")
-                    live -= r
-        if smem_open:
-            problems.append(f"{name}: scalar load not waited for before the block ends: {smem_open}")
-    return len(blocks), problems
+        if "1:" in lines and "s_cbranch_scc1 1b" in lines:
+            # a loop: its reads still in flight at the back edge carry into
+            # the next pass, so the body is replayed twice from the entry state
+            a, b = lines.index("1:"), lines.index("s_cbranch_scc1 1b")
+            live, in_flight = replay(name, lines[:a], ring, live, [], problems)
+            for _ in range(2):
+                live, in_flight = replay(name, lines[a:b], ring, live, in_flight, problems)
+            replay(name, lines[b:], ring, live, in_flight, problems)
+        else:
+            replay(name, lines, ring, live, [], problems)
+    return len(blocks), sorted(set(problems))
 
 
 if __name__ == "__main__":

@@ -67,6 +67,20 @@ def ring2(i, half):
     return f"v[{b}:{b + 1}]"
 
 
+# Values fragment f lives in ring slot (f + VSLOT) mod NF: the scores step
+# frees slots in the order 36 - NF .. 35 (mod NF), so with this offset the
+# values fragments prefetched there are issued in index order.
+VSLOT = (36 - NF) % NF
+
+
+def vring4(i):
+    return ring4(i + VSLOT)
+
+
+def vring2(i, half):
+    return ring2(i + VSLOT, half)
+
+
 def s_chain(k):
     return f"v[{SS}:{SS + 15}]"
 
@@ -151,6 +165,11 @@ class Stream:
         self.done.update(self.queue[:last + 1])
         self.queue = self.queue[last + 1:]
 
+    def wait_all(self):
+        self.lines.append("s_waitcnt lgkmcnt(0)")
+        self.done.update(self.queue)
+        self.queue = []
+
     def wait_pair(self, kind, i, n):
         """Before MFMA i of n: at even i wait for fragments i and i + 1 together
         (one lgkmcnt per two MFMAs; fragment i + 1 was issued a few MFMAs
@@ -175,8 +194,8 @@ def v_reads(st, i, regs=("%[v0]", "%[v1]", "%[v2]", "%[v3]")):
     rl = regs[0] if mt % 2 == 0 else regs[1]
     rh = regs[2] if mt % 2 == 0 else regs[3]
     off = 128 * (mt >> 1) + 1152 * 16 * j
-    st.lds(f"ds_read_b64_tr_b16 {ring2(i, 0)}, {rl} offset:{off}", ("V", i))
-    st.lds(f"ds_read_b64_tr_b16 {ring2(i, 1)}, {rh} offset:{off}", ("V", i))
+    st.lds(f"ds_read_b64_tr_b16 {vring2(i, 0)}, {rl} offset:{off}", ("V", i))
+    st.lds(f"ds_read_b64_tr_b16 {vring2(i, 1)}, {rh} offset:{off}", ("V", i))
 
 
 def k_read(st, k):
@@ -204,8 +223,8 @@ def s_part(st, dma, copy_p, prefetch_v):
         if k + NF < 36:
             k_read(st, k + NF)
         elif prefetch_v:
-            # slot k mod NF is free now; values fragment f lives in slot f mod NF
-            v_reads(st, k % NF)
+            # slot k mod NF is free now; values fragment f lives in slot (f + VSLOT) mod NF
+            v_reads(st, (k - VSLOT) % NF)
         if dma and k % 4 == 1:
             st.add(f"global_load_lds_dwordx4 v{TMP_DMA}, %[sb] offset:0")
         if dma and k % 4 == 3 and k // 4 < 8:
@@ -217,7 +236,7 @@ def s_part(st, dma, copy_p, prefetch_v):
                 st.add(f"v_lshrrev_b32 v{TMP_DMA}, 16, %[l{d // 2}]")
 
 
-def pv_part(st, first_pv, vops, p_regs, prefetched, end_v=False, smem=None):
+def pv_part(st, first_pv, vops, p_regs, prefetched, end_v=False, smem=None, early_tail=None):
     """O^T += V^T P^T (fragments from %[v0..v3], this lane's read offsets plus
     the buffer base %[bp]; P in p_regs), with the VALU list vops interleaved
     between the MFMAs (they read the scores, so they start after 21 wait
@@ -225,24 +244,29 @@ def pv_part(st, first_pv, vops, p_regs, prefetched, end_v=False, smem=None):
     NF fragments are already queued.  end_v: the slots freed by the last MFMAs
     are refilled with the first fragments of the current tile's own values
     (%[vn0..vn3] = offsets + %[bs]) for the segment's last values step.
-    smem: a scalar load issued before the first MFMA; the block's final
+    smem: a scalar load issued after the third MFMA; the block's final
     lgkmcnt(0) covers it (until it returns it only makes the LDS waits
-    stricter: it is one more operation in flight on the same counter)."""
+    stricter: it is one more operation in flight on the same counter).
+    early_tail: after MFMA early_tail (all values fragments read by then),
+    wait for the next tile's copy, pass the barrier and read the next tile's
+    first K fragments into the ring slots freed so far and then after each
+    remaining MFMA, so the next scores step starts on landed fragments
+    (order: EARLY_TAIL_ORDER)."""
     if not prefetched:
         st.add(*[f"v_add_u32 %[v{j}], %[bp], %[v{j}]" for j in range(4)])
         for i in range(NF):
             v_reads(st, i)
     per = (len(vops) + 27) // 28
     vi = 0
-    if smem:
-        st.add(smem)
     for i in range(32):
         mt, j = PV_ORDER[i]
         st.wait_pair("V", i, 32)
         src_c = "0" if (first_pv and j == 0) else acc(mt)
-        st.add(f"v_mfma_f32_32x32x16_bf16 {acc(mt)}, {ring4(i)}, {p_regs[j]}, {src_c}")
+        st.add(f"v_mfma_f32_32x32x16_bf16 {acc(mt)}, {vring4(i)}, {p_regs[j]}, {src_c}")
         if i + NF < 32:
             v_reads(st, i + NF)
+        if i == 2 and smem:
+            st.add(smem)
         if i == 1 and vops:
             st.add("s_nop 7", "s_nop 7", "s_nop 4")  # score results of the last k-steps
         if i >= 2:
@@ -252,6 +276,17 @@ def pv_part(st, first_pv, vops, p_regs, prefetched, end_v=False, smem=None):
             st.add(*vops[vi:])
             vi = len(vops)
             st.add(*[f"v_add_u32 %[vn{j}], %[bs], %[vo{j}]" for j in range(4)])
+        if early_tail is not None and i == early_tail:
+            assert early_tail >= 32 - NF
+            st.wait_all()
+            st.add(f"s_waitcnt vmcnt({COPY_LOADS})", "s_barrier")
+            st.add(*[f"v_add_u32 %[k{j}], %[bn], %[ko{j}]" for j in range(4)])
+        if early_tail is not None and i >= early_tail:
+            # the slots freed by MFMAs 32 - NF .. i get no more values
+            # fragments: the slot of MFMA x takes the K fragment of that slot
+            for x in (range(32 - NF, i + 1) if i == early_tail else [i]):
+                k = (x + VSLOT) % NF
+                st.add(f"ds_read_b128 {ring4(k)}, %[k{k % 4}] offset:{128 * (k // 4)}")
         if end_v and i >= 32 - NF:
             # slot i mod NF is free now: the segment's last values step's
             # fragment i mod NF goes there (not waited for in this block)
@@ -259,13 +294,16 @@ def pv_part(st, first_pv, vops, p_regs, prefetched, end_v=False, smem=None):
             rl = f"%[vn{0 if mt2 % 2 == 0 else 1}]"
             rh = f"%[vn{2 if mt2 % 2 == 0 else 3}]"
             off = 128 * (mt2 >> 1) + 1152 * 16 * j2
-            st.lds(f"ds_read_b64_tr_b16 {ring2(i % NF, 0)}, {rl} offset:{off}", ("N", i % NF))
-            st.lds(f"ds_read_b64_tr_b16 {ring2(i % NF, 1)}, {rh} offset:{off}", ("N", i % NF))
+            st.lds(f"ds_read_b64_tr_b16 {vring2(i % NF, 0)}, {rl} offset:{off}", ("N", i % NF))
+            st.lds(f"ds_read_b64_tr_b16 {vring2(i % NF, 1)}, {rh} offset:{off}", ("N", i % NF))
     st.add(*vops[vi:])
     st.add(*[f"v_sub_u32 %[v{j}], %[v{j}], %[bp]" for j in range(4)])
 
 
 COPY_LOADS = 9  # HBM->LDS copies per wave per tile
+EARLY_TAIL = 27  # hot loop: the tail follows values MFMA 27
+# issue order of the next tile's first K fragments after an early tail
+EARLY_TAIL_ORDER = [(x + VSLOT) % NF for x in range(32 - NF, 32)]
 ROW_BYTES = 1152  # one cached token: 512 latent + 64 rope bf16 values
 
 
@@ -289,7 +327,7 @@ def s_part_hot(st):
         if k + NF < 36:
             k_read(st, k + NF)
         else:
-            v_reads(st, k % NF)
+            v_reads(st, (k - VSLOT) % NF)
         if k == 1:
             st.add("s_min_u32 %[t0], %[pg], %[np1]", "s_lshl_b32 %[t0], %[t0], %[psh]",
                    "s_and_b32 %[t1], %[tok], %[pmask]", "s_add_u32 %[t0], %[t0], %[t1]",
@@ -309,19 +347,18 @@ def hot_loop():
     """The common tile step, repeated %[n] times in one statement: scores of
     tile t with the copy of tile t + 2 (contiguous, inside one page), values of
     tile t - 1 with the softmax of tile t, the block-table read of the next
-    copy's page, the wait for tile t + 1 and the barrier, the next tile's
-    first K fragments; then the rare accumulator rescale (out of line), the
-    rotation of the four LDS buffer bases and the loop test."""
+    copy's page, and -- before the last four values MFMAs, once every values
+    fragment has landed -- the wait for tile t + 1, the barrier and the next
+    tile's first K fragments; then the rare accumulator rescale (out of
+    line), the rotation of the four LDS buffer bases and the loop test."""
     st = Stream()
-    st.queue = [("K", i) for i in range(NF)]
-    st.add("s_mov_b64 s[98:99], %[data]", "1:")
+    # (entered with every LDS read landed, so the first iteration may assume
+    # the loop's own order of the first K fragments)
+    st.queue = [("K", k) for k in EARLY_TAIL_ORDER]
+    st.add("s_mov_b64 s[98:99], %[data]", "s_waitcnt lgkmcnt(0)", "1:")
     s_part_hot(st)
     pv_part(st, False, softmax_ops(False, False), P_FIXED, True, False,
-            "s_load_dword %[pg], %[bt], %[pgo]")
-    st.add(f"s_waitcnt vmcnt({COPY_LOADS})", "s_barrier")
-    st.add(*[f"v_add_u32 %[k{j}], %[bn], %[ko{j}]" for j in range(4)])
-    for i in range(NF):
-        st.add(f"ds_read_b128 {ring4(i)}, %[k{i % 4}] offset:{128 * (i // 4)}")
+            "s_load_dword %[pg], %[bt], %[pgo]", early_tail=EARLY_TAIL)
     st.add("s_cmp_lg_u64 %[mv], 0", "s_cbranch_scc1 3f",
            "2:",
            "s_mov_b32 %[t0], %[bp]", "s_mov_b32 %[bp], %[bs]", "s_mov_b32 %[bs], %[bn]",
@@ -330,7 +367,9 @@ def hot_loop():
            "s_branch 4f",
            "3:")
     st.add(*rescale_lines())
-    st.add("s_branch 2b", "4:")
+    # the K fragments in flight leave in the loop's order; the blocks after it
+    # assume index order, so they are waited for here
+    st.add("s_branch 2b", "4:", "s_waitcnt lgkmcnt(0)")
     args = ["uint32_t (&kcur)[4]", "const uint32_t (&koff)[4]", "uint32_t (&voff)[4]", "float c",
             "float& mref", "float& lsum", "uint32_t& bs", "uint32_t& bp", "uint32_t& bn", "uint32_t& bc",
             "uint32_t woff", "uint32_t& n", "int& tok", "int32_t& pg", "const char* data", "const int32_t* bt",
@@ -469,10 +508,10 @@ def emit():
         st = Stream()
         # the fragments in flight, in issue order: each went into the ring slot
         # that one of the previous block's last MFMAs freed (fragment f lives in
-        # slot f mod NF): after a first tile's block (one-tile segment:
+        # slot (f + VSLOT) mod NF): after a first tile's block (one-tile segment:
         # first_pv) the last score k-steps, after a step's block the last
         # values MFMAs
-        order = [k % NF for k in range(36 - NF, 36)] if first_pv else [i % NF for i in range(32 - NF, 32)]
+        order = [(k - VSLOT) % NF for k in range(36 - NF, 36)] if first_pv else [i % NF for i in range(32 - NF, 32)]
         st.queue = [("V", f) for f in order for _ in range(2)]
         st.add("s_nop 1")  # P was written by VALU at the end of the previous block
         pv_rest(st, first_pv, P_NEW, ("%[vn0]", "%[vn1]", "%[vn2]", "%[vn3]"))
@@ -523,7 +562,7 @@ def pv_rest(st, first_pv, p_regs, vregs):
         mt, j = PV_ORDER[i]
         st.wait_pair("V", i, 32)
         src_c = "0" if (first_pv and j == 0) else acc(mt)
-        st.add(f"v_mfma_f32_32x32x16_bf16 {acc(mt)}, {ring4(i)}, {p_regs[j]}, {src_c}")
+        st.add(f"v_mfma_f32_32x32x16_bf16 {acc(mt)}, {vring4(i)}, {p_regs[j]}, {src_c}")
         if i + NF < 32:
             v_reads(st, i + NF, vregs)
 

@@ -48,3 +48,17 @@ def test_checker_catches_an_unwaited_scalar_load():
     planted = text[:start] + body.replace("s_waitcnt lgkmcnt(0)", "s_waitcnt lgkmcnt(1)") + text[end:]
     n, problems = _load("check_attn_mfma_asm").check(planted)
     assert any("scalar load" in p for p in problems)
+
+
+def test_checker_follows_reads_across_the_loop_back_edge():
+    # plant a mistake: the hot loop's first wait no longer covers the K
+    # fragments its previous pass read (only a two-pass replay sees them)
+    text = (CSRC / "attn_mfma_asm.inc").read_text()
+    start = text.index("void tile_hot_loop(")
+    end = text.index("\n}\n", start)
+    body = text[start:end]
+    top = body.index('"1:\\n"')
+    w = body.index("s_waitcnt lgkmcnt(", top)
+    planted = text[:start] + body[:w] + "s_waitcnt lgkmcnt(9)" + body[body.index(")", w) + 1:] + text[end:]
+    n, problems = _load("check_attn_mfma_asm").check(planted)
+    assert any("tile_hot_loop: MFMA before its LDS read landed" in p for p in problems)
