@@ -16,6 +16,8 @@
 //    from global memory.  o_lat is fp32; each A fragment is split into a bf16
 //    high part and a bf16 remainder and both are multiplied (two MFMAs), which
 //    keeps the product accurate to about 2^-16 relative.
+#include <math.h>
+
 #include "device_utils.h"
 #include "mla_internal.h"
 
@@ -23,6 +25,7 @@ namespace mla {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -187,6 +190,153 @@ __global__ __launch_bounds__(256) void up_project_mfma_kernel(const float* __res
   }
 }
 
+// Combine + up-projection in one pass, for the split-KV decode/prefill path:
+// a workgroup owns one head and 32 items.  Phase 1 merges each item's row of
+// o_lat from the partial results of the workgroups its tiles were cut across
+// (the same log-sum-exp merge as combine_segments, slots 2g+1 for the first
+// workgroup and 2g after it) or takes the attention kernel's own row for an
+// uncut item, normalises it and stages it in LDS as a bf16 high part and a
+// bf16 remainder; phase 2 is the up-projection of up_project_mfma_kernel<1>
+// with A fragments from LDS.  o_lat itself is never written.
+constexpr int kCupMaxR = 512;
+constexpr int kCupPitch = kCupMaxR + 8;  // bf16 per staged row (16 B pad: bank spread)
+
+__global__ __launch_bounds__(256) void combine_up_project_kernel(AttnArgs a, const uint16_t* __restrict__ w_uv,
+                                                                 int32_t Dv, uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) __bf16 o_hi[32 * kCupPitch];
+  __shared__ __attribute__((aligned(16))) __bf16 o_lo[32 * kCupPitch];
+  const int h = blockIdx.y;
+  const int m0 = blockIdx.x * 32;
+  const int H = a.H, R = a.kv.R, Nq = a.num_items;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int g = lane >> 5, n32 = lane & 31;
+  const int v = 32 * wave + n32;
+  const bool v_ok = 32 * wave < Dv;
+
+  // W_UV[h][v] B fragments of every k-step, loaded first: their latency
+  // overlaps the merge below
+  i16x8 b[kCupMaxR / 16];
+  {
+    const uint16_t* wrow = w_uv + (static_cast<int64_t>(h) * Dv + (v_ok ? v : 0)) * R;
+#pragma unroll
+    for (int u = 0; u < kCupMaxR / 16; ++u)
+      if (16 * u < R) b[u] = *reinterpret_cast<const i16x8*>(wrow + 16 * u + 8 * g);
+  }
+
+  // ---- phase 1: thread (il, j) merges columns 32 e + 4 j .. + 3 (e < R / 32) of
+  // item m0 + il: the item's eight threads read 128 contiguous bytes per load
+  {
+    const int il = t >> 3, j = t & 7;
+    const int item = m0 + il;
+    const int nv = R / 32;                // float4 per thread (<= 16)
+    const int c0 = 4 * j;
+    float acc[kCupMaxR / 8];
+#pragma unroll
+    for (int e = 0; e < kCupMaxR / 8; ++e) acc[e] = 0.f;
+    float m = -INFINITY, tot = 0.f;
+    if (item < Nq) {
+      const int64_t row = static_cast<int64_t>(item) * H + h;
+      const int g0 = a.item_wg[2 * item], g1 = a.item_wg[2 * item + 1];
+      if (g0 >= 0 && g0 == g1) {
+        // uncut: the attention kernel wrote the unnormalised row and 1 / l
+        const float sc = a.o_scale[row];
+        const float4* src = reinterpret_cast<const float4*>(a.o_lat + row * R + c0);
+#pragma unroll
+        for (int e = 0; e < kCupMaxR / 32; ++e) {
+          if (e < nv) {
+            const float4 x = src[8 * e];
+            acc[4 * e] = x.x * sc;
+            acc[4 * e + 1] = x.y * sc;
+            acc[4 * e + 2] = x.z * sc;
+            acc[4 * e + 3] = x.w * sc;
+          }
+        }
+        m = 0.f;
+        tot = 1.f;
+      } else if (g0 >= 0) {
+        // segments two at a time: both loads issued, then merged against the
+        // running maximum
+        for (int gb = g0; gb <= g1; gb += 2) {
+          float l[2], sc[2];
+          float4 x[2][kCupMaxR / 32];
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const int gg = gb + p;
+            const bool live = gg <= g1 && a.wg_tile[gg] != a.wg_tile[gg + 1];  // (no tiles: no slot)
+            const int64_t slot = (gg == g0) ? 2 * gg + 1 : 2 * gg;
+            l[p] = live ? a.part_lse[slot * H + h] : -INFINITY;
+            sc[p] = live ? a.part_scale[slot * H + h] : 0.f;
+            const float4* src = reinterpret_cast<const float4*>(a.part_o + (slot * H + h) * R + c0);
+#pragma unroll
+            for (int e = 0; e < kCupMaxR / 32; ++e)
+              x[p][e] = (live && e < nv) ? src[8 * e] : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+          const float mb = fmaxf(m, fmaxf(l[0], l[1]));
+          if (mb > m) {  // uniform within the item's eight threads
+            const float f = expf(m - mb);
+            tot *= f;
+#pragma unroll
+            for (int e = 0; e < kCupMaxR / 8; ++e) acc[e] *= f;
+            m = mb;
+          }
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            if (l[p] == -INFINITY) continue;
+            const float e_l = expf(l[p] - m);
+            tot += e_l;
+            const float w = e_l * sc[p];
+#pragma unroll
+            for (int e = 0; e < kCupMaxR / 32; ++e) {
+              acc[4 * e] = fmaf(w, x[p][e].x, acc[4 * e]);
+              acc[4 * e + 1] = fmaf(w, x[p][e].y, acc[4 * e + 1]);
+              acc[4 * e + 2] = fmaf(w, x[p][e].z, acc[4 * e + 2]);
+              acc[4 * e + 3] = fmaf(w, x[p][e].w, acc[4 * e + 3]);
+            }
+          }
+        }
+        if (j == 0) a.lse[row] = tot > 0.f ? m + logf(tot) : -INFINITY;
+      } else if (j == 0) {
+        a.lse[row] = -INFINITY;  // no visible keys: out 0, lse -inf
+      }
+    }
+    const float inv = tot > 0.f ? 1.f / tot : 0.f;
+#pragma unroll
+    for (int e = 0; e < kCupMaxR / 32; ++e) {
+      if (e < nv) {
+        bf16x4 hi, lo;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float x = acc[4 * e + q] * inv;
+          hi[q] = static_cast<__bf16>(x);
+          lo[q] = static_cast<__bf16>(x - static_cast<float>(hi[q]));
+        }
+        *reinterpret_cast<bf16x4*>(o_hi + il * kCupPitch + 32 * e + c0) = hi;
+        *reinterpret_cast<bf16x4*>(o_lo + il * kCupPitch + 32 * e + c0) = lo;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- phase 2: out[item, h, v] = W_UV[h][v] . o[item], wave w: v in [32 w, 32 w + 32)
+  if (!v_ok) return;
+  f32x16 acc = f32x16{};
+#pragma unroll
+  for (int u = 0; u < kCupMaxR / 16; ++u) {
+    const int k = 16 * u;
+    if (k >= R) break;
+    const bf16x8 hi = *reinterpret_cast<const bf16x8*>(o_hi + n32 * kCupPitch + k + 8 * g);
+    const bf16x8 lo = *reinterpret_cast<const bf16x8*>(o_lo + n32 * kCupPitch + k + 8 * g);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, __builtin_bit_cast(bf16x8, b[u]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, __builtin_bit_cast(bf16x8, b[u]), acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int item = m0 + 8 * (i >> 2) + 4 * g + (i & 3);
+    if (item < Nq) out[(static_cast<int64_t>(item) * H + h) * Dv + v] = f32_to_bf16(acc[i]);
+  }
+}
+
 int pick_mt(int Nq) { return Nq <= 32 ? 1 : (Nq <= 64 ? 2 : 4); }
 
 // The up-projection streams W_UV once per 32 * MT items; small batches take
@@ -201,6 +351,17 @@ bool absorb_mfma_supported(int32_t Dn, int32_t R) {
 
 bool up_project_mfma_supported(int32_t R, int32_t Dv) {
   return R % 16 == 0 && Dv % 32 == 0 && Dv <= 128;
+}
+
+bool combine_up_project_supported(int32_t R, int32_t Dv) {
+  return up_project_mfma_supported(R, Dv) && R % 32 == 0 && R <= kCupMaxR;
+}
+
+hipError_t launch_combine_up_project(const AttnArgs& a, const uint16_t* w_uv, int32_t Dv, uint16_t* out,
+                                     hipStream_t s) {
+  const dim3 grid((a.num_items + 31) / 32, a.H);
+  hipLaunchKernelGGL(combine_up_project_kernel, grid, dim3(256), 0, s, a, w_uv, Dv, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_absorb_mfma(const uint16_t* q_nope, int64_t st, int64_t sh, const uint16_t* w_uk,

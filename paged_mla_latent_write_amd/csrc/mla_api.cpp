@@ -238,6 +238,10 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
   if (attn->kernel_events[1] &&
       hipEventRecord(static_cast<hipEvent_t>(attn->kernel_events[1]), s) != hipSuccess)
     return MLA_ERR_HIP;
+  if (attn->w_uv && !generic && mla::combine_up_project_supported(R, attn->v_head_dim) &&
+      aligned16(attn->w_uv))
+    return to_status(mla::launch_combine_up_project(a, static_cast<const uint16_t*>(attn->w_uv),
+                                                    attn->v_head_dim, static_cast<uint16_t*>(out), s));
   e = mla::launch_combine_segments(a, s);
   if (e != hipSuccess) return MLA_ERR_HIP;
 

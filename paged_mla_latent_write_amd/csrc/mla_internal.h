@@ -114,6 +114,13 @@ hipError_t launch_up_project_mfma(const float* o_lat, const float* o_scale, cons
                                   int32_t num_items, int32_t H, int32_t R, int32_t Dv, uint16_t* out,
                                   hipStream_t s);
 
+// Combine of cut items fused with the up-projection (head_gemm.hip): reads
+// the partial slots (or an uncut item's o_lat row) and writes out and the lse
+// of cut and empty items; o_lat is not written.
+bool combine_up_project_supported(int32_t R, int32_t Dv);
+hipError_t launch_combine_up_project(const AttnArgs& a, const uint16_t* w_uv, int32_t Dv, uint16_t* out,
+                                     hipStream_t s);
+
 hipError_t launch_dense_combine(const float* o_part, const float* lse_part, int32_t num_splits,
                                 int32_t rows, int32_t dim, float* o, float* lse, hipStream_t s);
 
