@@ -73,6 +73,11 @@ struct AttnArgs {
   float* part_o;          // [2G][H][R] fp32 partials (cut items)
   float* part_lse;        // [2G][H]
   float* part_scale;      // [2G][H]
+  // fp8 MFMA kernel: per workgroup, 1 when a score passed its segment's
+  // reference maximum by more than 2^64 (the generic kernel then recomputes
+  // that workgroup's range exactly), else 0
+  int32_t* redo;          // [G]
+  const int32_t* redo_only;  // generic kernel: non-null = only workgroups with redo_only[g] != 0
 };
 
 // ---- launchers (each returns the launch's hipGetLastError) ----
@@ -90,6 +95,11 @@ hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t s);
 // True when the MFMA split-KV kernel handles this shape (R 512, Dr 64, H <= 128).
 bool mfma_attn_supported(const CacheView& kv, int32_t H);
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
+
+// True when the fp8 MFMA split-KV kernel handles this shape (E4M3 cache,
+// R 512, Dr 64, H <= 128).
+bool mfma_fp8_attn_supported(const CacheView& kv, int32_t H);
+hipError_t launch_attn_mfma_fp8(const AttnArgs& a, hipStream_t s);
 
 hipError_t launch_combine_segments(const AttnArgs& a, hipStream_t s);
 

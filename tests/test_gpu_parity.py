@@ -248,6 +248,52 @@ def test_decode_latent_io_and_needle(mla):
     assert np.max(np.abs(bf16_host_f64(out)[0] - c_j[None, :])) < 2e-2
 
 
+@pytest.mark.parametrize("ps", [16, 32, 64, 128])
+def test_decode_fp8_mfma_page_sizes(mla, ps):
+    """fp8 cache on the matrix-core path: ragged contexts (tile edges, one-token
+    and multi-page requests) over every supported page size, sharp queries."""
+    say(f"decode fp8 mfma ps={ps}")
+    d = W.Dims(H=128, R=512, Dr=64, Dn=128, Dv=128, page_size=ps)
+    case = W.custom(d, [1, 31, 32, 33, 64, 65, 700, 2049], seed=710 + ps, kv_dtype=O.KV_FP8, sharp=True)
+    check_decode(mla, case, label=f" ps={ps}")
+    check_decode(mla, case, num_workgroups=7, label=f" ps={ps} G=7")
+
+
+@pytest.mark.parametrize("window", [1, 33, 500])
+def test_decode_fp8_mfma_window(mla, window):
+    say(f"decode fp8 mfma window={window}")
+    d = W.Dims(H=64, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
+    case = W.custom(d, [40, 700, 2049], seed=730 + window, kv_dtype=O.KV_FP8, window=window, sharp=True)
+    check_decode(mla, case, label=f" w={window}")
+
+
+@pytest.mark.parametrize("G", [1, 2])
+def test_decode_fp8_score_jump_is_recomputed(mla, G):
+    """fp8 cache: a key whose score passes its segment's first-tile maximum by
+    about 2^97 (log2 units) makes the matrix-core kernel hand the workgroup's
+    range to the exact recompute; the output is still the oracle's (the
+    needle's latent)."""
+    say(f"decode fp8 score jump G={G}")
+    d = W.Dims(H=32, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
+    case = W.custom(d, [300, 41], seed=740, kv_dtype=O.KV_FP8)
+    cache = populate_device(mla, case)
+    hc, hs = host_cache(case)
+    X = O.gather_latent(hc, hs, case.kv_dtype, 0, case.block_tables[0], int(case.context_lens[0]))
+    j = 260  # tile 8 of request 0: not the first tile of its segment with one or two workgroups
+    c_j = X[j, :d.R]
+    q_lat = np.zeros((2, d.H, d.R))
+    q_lat[0] = 70.0 / (case.scale * (c_j @ c_j)) * c_j
+    q_bits = W.f32_to_bf16_bits(q_lat.astype(np.float32))
+    out, lse = mla.decode(cache, 0, dev_bf16(q_bits), dev_bf16(case.q_pe), dev(case.block_tables),
+                          dev(case.context_lens), scale=case.scale, num_workgroups=G)
+    torch.cuda.synchronize()
+    ref, ref_lse = O.decode(hc, hs, case.kv_dtype, 0, q_bits, case.q_pe, case.block_tables,
+                            case.context_lens, None, None, case.scale, 0)
+    assert_close(bf16_host_f64(out), ref, FP8_TOL, f"fp8 jump G={G}")
+    assert_lse_close(lse.cpu().numpy(), ref_lse, LSE_ATOL[case.kv_dtype], f"fp8 jump G={G} lse")
+    assert np.max(np.abs(bf16_host_f64(out)[0] - c_j[None, :])) < 2e-2
+
+
 # ---------------------------------------------------------------------------
 # Combine
 # ---------------------------------------------------------------------------
