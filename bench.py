@@ -50,7 +50,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=100)
-    p.add_argument("--workload", default="v3", choices=["v3", "v3fp8", "v2lite"])
+    p.add_argument("--workload", default="v3", choices=["v3", "v3fp8", "v2lite", "mixed"])
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="CPU time budget for the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -133,12 +133,127 @@ def cpu_baseline(case, budget_s, gpu_out_f64):
                       f"{write_s:.1f} s untimed"}, err
 
 
+MIXED_METRIC = "mixed MLA layer step (write + chunked prefill + decode, sliding-window layers) attended-KV-pairs/s"
+
+
+def mixed_pairs(ml):
+    """(prefill, decode) attended (query row, key) pairs of one mixed layer."""
+    P, w = ml.n_prefill, ml.window
+    pre = 0
+    for b in range(P):
+        n = int(ml.context_lens[b])
+        m = int(ml.query_start_loc[b + 1] - ml.query_start_loc[b])
+        p = np.arange(n - m, n, dtype=np.int64)
+        pre += int(np.sum(p + 1 if w <= 0 else np.minimum(w, p + 1)))
+    n = ml.context_lens[P:].astype(np.int64)
+    dec = int(np.sum(n if w <= 0 else np.minimum(w, n)))
+    return pre, dec
+
+
+def main_mixed(args):
+    """The mixed step at full size: per layer, write the step's new tokens
+    (8 chunks of 512 + 120 decode tokens), prefill the chunks, decode the 120
+    requests; layers 0 and 2 use a 128-token window."""
+    import torch
+
+    from paged_mla_latent_write_amd import mla
+    from paged_mla_latent_write_amd import workloads as W
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def bf16(u16):
+        return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def i(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    layers = []
+    cache = None
+    for l in range(len(W.MIXED_WINDOWS)):
+        ml = W.mixed(l)
+        if cache is None:
+            cache = mla.KVCache.empty(ml.num_layers, ml.num_pages, ml.dims.page_size, ml.dims.R, ml.dims.Dr)
+            cache.data.view(torch.int16).fill_(0x7FC0)
+        mla.write_kv(cache, l, bf16(ml.pre_c_kv), bf16(ml.pre_k_pe), i(ml.pre_slots))
+        P = ml.n_prefill
+        layers.append(dict(
+            ml=ml, new=(bf16(ml.new_c_kv), bf16(ml.new_k_pe), i(ml.new_slots)),
+            qp=(bf16(ml.q_nope_p), bf16(ml.q_pe_p)), qd=(bf16(ml.q_nope_d), bf16(ml.q_pe_d)),
+            w=(bf16(ml.w_uk), bf16(ml.w_uv)), qsl=i(ml.query_start_loc),
+            bt_p=i(ml.block_tables[:P]), ctx_p=i(ml.context_lens[:P]),
+            bt_d=i(ml.block_tables[P:]), ctx_d=i(ml.context_lens[P:]),
+            pairs=mixed_pairs(ml)))
+        print(f"[bench] mixed: layer {l} built", file=sys.stderr, flush=True)
+    d = layers[0]["ml"].dims
+    chunk = int(np.max(np.diff(layers[0]["ml"].query_start_loc)))
+    K = args.steps
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in layers] for _ in range(K)]
+
+    def step(k=None):
+        for li, L in enumerate(layers):
+            ml = L["ml"]
+            e = ev[k][li] if k is not None else None
+            if e: e[0].record()
+            mla.write_kv(cache, ml.layer, *L["new"])
+            if e: e[1].record()
+            mla.prefill_chunk(cache, ml.layer, *L["qp"], L["qsl"], chunk, L["bt_p"], L["ctx_p"],
+                              scale=ml.scale, w_uk=L["w"][0], w_uv=L["w"][1], window=ml.window)
+            if e: e[2].record()
+            mla.decode(cache, ml.layer, *L["qd"], L["bt_d"], L["ctx_d"], scale=ml.scale,
+                       w_uk=L["w"][0], w_uv=L["w"][1], window=ml.window)
+            if e: e[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] mixed: warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(k)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_layer = {}
+    for li, L in enumerate(layers):
+        ts = np.array([[ev[k][li][c].elapsed_time(ev[k][li][c + 1]) for c in range(3)] for k in range(K)])
+        med = np.median(ts, axis=0)
+        pre, dec = L["pairs"]
+        per_layer[f"L{li}"] = {"window": L["ml"].window, "write_ms": float(med[0]),
+                               "prefill_ms": float(med[1]), "decode_ms": float(med[2]),
+                               "prefill_pairs": pre, "decode_tokens": dec,
+                               "prefill_tflops": pre * 2 * d.H * (2 * d.R + d.Dr) / (med[1] * 1e-3) / 1e12,
+                               "decode_gbs": dec * d.D * 2 / (med[2] * 1e-3) / 1e9}
+        print(f"[bench] mixed L{li}: {per_layer[f'L{li}']}", file=sys.stderr, flush=True)
+    pairs = sum(sum(L["pairs"]) for L in layers)
+    flops = pairs * 2 * d.H * (2 * d.R + d.Dr)
+    step_s = wall / K
+    tflops = flops / step_s / 1e12
+    line = {
+        "metric": MIXED_METRIC, "value": pairs * K / wall, "unit": "pairs/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": step_s * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; N(0,1)/sqrt(dim) latents and queries, random-init W_UK/W_UV)",
+        "config": {"workload": "mixed step: 8 x 512-token chunks + 120 decode requests per layer, "
+                               "4 layers, windows (128, 0, 128, 0)",
+                   "heads": d.H, "kv_lora_rank": d.R, "qk_rope": d.Dr, "page_size": d.page_size,
+                   "attended_pairs": pairs},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "whole step (prefill dominates the flops)"},
+        "per_layer": per_layer,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(multi-GPU sharding is described, not built)"}))
         sys.exit(2)
+    if args.workload == "mixed":
+        return main_mixed(args)
     import torch
 
     from paged_mla_latent_write_amd import mla
@@ -218,7 +333,7 @@ def main():
     traffic_bytes = None if (args.generic or fp8) else measured_traffic(args.workload)
     traffic = None if traffic_bytes is None else traffic_bytes / (kern_ms * 1e-3) / 1e9
     tflops = flops / (kern_ms * 1e-3) / 1e12
-    if flops / kv_bytes * 1e3 > BF16_MFMA_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBS:
+    if flops / kv_bytes > BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
         # past the bf16 ridge (the fp8 cache: 580 B per token for the same
         # bf16-MFMA flops): the matrix cores bind
         roofline = {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",

@@ -18,6 +18,8 @@
 //    keeps the product accurate to about 2^-16 relative.
 #include <math.h>
 
+#include <algorithm>
+
 #include "device_utils.h"
 #include "mla_internal.h"
 
@@ -46,24 +48,9 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* __rest
   __shared__ __attribute__((aligned(16))) char wt[kAbsMaxDn * kAbsPitch];
   const int c0 = blockIdx.x * kAbsCols;  // this workgroup's 128 output columns
   const int h = blockIdx.y;
-  const int m0 = blockIdx.z * 32 * MT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, n32 = lane & 31;
   const int ksteps = Dn / 16;
-
-  // A fragments: q_nope rows of this wave's M tiles (all waves hold the same)
-  i16x8 af[MT][kAbsMaxDn / 16];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int item = m0 + 32 * mt + n32;
-#pragma unroll
-    for (int k = 0; k < kAbsMaxDn / 16; ++k) {
-      i16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (k < ksteps && item < Nq)
-        v = *reinterpret_cast<const i16x8*>(q_nope + item * st + h * sh + 16 * k + 8 * g);
-      af[mt][k] = v;
-    }
-  }
 
   // transposed-read lane offsets (see the attention kernel for the layout)
   const int q = lane >> 4, jj = lane & 15, rr = jj >> 2, c4 = jj & 3;
@@ -88,6 +75,23 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* __rest
       if (d < Dn) *reinterpret_cast<i16x8*>(wt + d * kAbsPitch + c * 16) = wv[j];
     }
     __syncthreads();
+  }
+  // item blocks of 32 MT: one per workgroup for decode-sized batches, several
+  // for prefill-sized ones (the staged W_UK block is reused)
+  for (int m0 = blockIdx.z * 32 * MT; m0 < Nq; m0 += gridDim.z * 32 * MT) {
+    // A fragments: q_nope rows of this wave's M tiles (all waves hold the same)
+    i16x8 af[MT][kAbsMaxDn / 16];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int item = m0 + 32 * mt + n32;
+#pragma unroll
+      for (int k = 0; k < kAbsMaxDn / 16; ++k) {
+        i16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (k < ksteps && item < Nq)
+          v = *reinterpret_cast<const i16x8*>(q_nope + item * st + h * sh + 16 * k + 8 * g);
+        af[mt][k] = v;
+      }
+    }
     f32x16 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
@@ -368,7 +372,11 @@ hipError_t launch_absorb_mfma(const uint16_t* q_nope, int64_t st, int64_t sh, co
                               int32_t num_items, int32_t H, int32_t Dn, int32_t R, uint16_t* q_lat,
                               hipStream_t s) {
   const int mt = pick_mt(num_items);
-  const dim3 grid(R / kAbsCols, H, (num_items + 32 * mt - 1) / (32 * mt));
+  // the W_UK block (Dn x 128 columns) is staged once per workgroup: at most
+  // ~2048 workgroups in all, so large item counts loop over several blocks
+  const int nblk = (num_items + 32 * mt - 1) / (32 * mt);
+  const int gz = std::min(nblk, std::max(1, 2048 / std::max(1, (R / kAbsCols) * H)));
+  const dim3 grid(R / kAbsCols, H, gz);
   switch (mt) {
     case 1: hipLaunchKernelGGL(absorb_mfma_kernel<1>, grid, dim3(256), 0, s, q_nope, st, sh, w_uk, num_items, H, Dn, R, q_lat); break;
     case 2: hipLaunchKernelGGL(absorb_mfma_kernel<2>, grid, dim3(256), 0, s, q_nope, st, sh, w_uk, num_items, H, Dn, R, q_lat); break;
