@@ -20,12 +20,12 @@
 
 #include "device_utils.h"
 #include "mla_internal.h"
+#include "plan_device.h"
 
 namespace mla {
 namespace {
 
 constexpr int kPlanThreads = 1024;
-constexpr int kPlanLds = 4096;  // tile_start / wg_tile entries mirrored in LDS
 
 __global__ __launch_bounds__(kPlanThreads) void plan_items_kernel(
     int mode, int32_t B, int32_t Nq, const int32_t* __restrict__ ctx,
@@ -35,130 +35,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_items_kernel(
     int32_t* __restrict__ wg_item, int32_t* __restrict__ item_wg) {
   __shared__ int32_t buf[kPlanThreads];
   __shared__ int32_t carry;
-  // The binary searches below read tile_start and wg_tile from LDS copies
-  // when they fit (each probe of a global copy written by this kernel is a
-  // full memory round trip).
   __shared__ int32_t ts_lds[kPlanLds];
   __shared__ int32_t wt_lds[kPlanLds];
-  const bool ts_fits = Nq + 1 <= kPlanLds, wt_fits = G + 1 <= kPlanLds;
-  const int tid = threadIdx.x;
-  if (tid == 0) carry = 0;
-  // (prefill) query_start_loc for the per-row request search, in the space
-  // wg_tile takes later
-  const bool qsl_fits = mode != kPlanDecode && B + 1 <= kPlanLds;
-  if (qsl_fits)
-    for (int b = tid; b <= B; b += kPlanThreads) wt_lds[b] = qsl[b];
-  __syncthreads();
-  const int32_t* qsl_tab = qsl_fits ? wt_lds : qsl;
-  for (int base = 0; base < Nq; base += kPlanThreads) {
-    const int i = base + tid;
-    int32_t nt = 0;
-    if (i < Nq) {
-      int b, p;
-      if (mode == kPlanDecode) {
-        b = i;
-        const int n = min(max(ctx[b], 0), max_ctx);
-        p = n - 1;
-      } else {
-        int lo = 0, hi = B;  // largest b < B with qsl[b] <= i
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (qsl_tab[mid] <= i) lo = mid; else hi = mid;
-        }
-        b = lo;
-        const int n = min(max(ctx[b], 0), max_ctx);
-        const int m = qsl_tab[b + 1] - qsl_tab[b];
-        p = min(n - m + (i - qsl_tab[b]), n - 1);
-      }
-      int lo_t = 0, hi_t = 0;
-      if (p >= 0) {
-        hi_t = p + 1;
-        lo_t = window > 0 ? max(0, p - window + 1) : 0;
-      }
-      item_b[i] = b;
-      item_lo[i] = lo_t;
-      item_hi[i] = hi_t;
-      nt = hi_t > lo_t ? (hi_t + kTile - 1) / kTile - lo_t / kTile : 0;
-    }
-    // inclusive scan over the block (Hillis-Steele)
-    buf[tid] = nt;
-    __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-      const int32_t add = tid >= off ? buf[tid - off] : 0;
-      __syncthreads();
-      buf[tid] += add;
-      __syncthreads();
-    }
-    if (i < Nq) {
-      tile_start[i] = carry + buf[tid] - nt;
-      if (ts_fits) ts_lds[i] = carry + buf[tid] - nt;
-    }
-    __syncthreads();
-    if (tid == kPlanThreads - 1) carry += buf[tid];
-    __syncthreads();
-  }
-  if (tid == 0) {
-    tile_start[Nq] = carry;
-    if (ts_fits) ts_lds[Nq] = carry;
-  }
-  __syncthreads();
-  const int32_t* ts_tab = ts_fits ? ts_lds : tile_start;
-  // Workgroup ranges: the tile stream cut into G ranges of equal estimated
-  // cost, a tile costing 1 and each item kSegmentCostTiles more.  On that
-  // virtual axis item i starts at V_i = tile_start[i] + kSegmentCostTiles * i,
-  // its surcharge first, then its tiles; a cut that falls in a surcharge moves
-  // to the item's first tile (a range may then be empty).
-  const int64_t W = carry;
-  const int64_t VT = W + static_cast<int64_t>(kSegmentCostTiles) * Nq;
-  for (int g = tid; g <= G; g += kPlanThreads) {
-    const int64_t vb = static_cast<int64_t>(g) * VT / G;
-    int lo = 0, hi = Nq + 1;  // largest i <= Nq with V_i <= vb
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (ts_tab[mid] + static_cast<int64_t>(kSegmentCostTiles) * mid <= vb) lo = mid; else hi = mid;
-    }
-    const int64_t ts = ts_tab[lo];
-    const int64_t n = lo < Nq ? ts_tab[lo + 1] - ts : 0;
-    const int64_t into = vb - ts - static_cast<int64_t>(kSegmentCostTiles) * lo - kSegmentCostTiles;
-    const int32_t t = static_cast<int32_t>(ts + min(max(into, int64_t{0}), n));
-    wg_tile[g] = t;
-    if (wt_fits) wt_lds[g] = t;
-  }
-  __syncthreads();
-  const int32_t* wt_tab = wt_fits ? wt_lds : wg_tile;
-  // Each workgroup's first item: the last item whose first tile is <= the
-  // range's first tile (items with no tiles are skipped).
-  for (int g = tid; g < G; g += kPlanThreads) {
-    const int32_t t = wt_tab[g];
-    int lo = 0, hi = Nq;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (ts_tab[mid] <= t) lo = mid; else hi = mid;
-    }
-    wg_item[g] = lo;
-  }
-  // The first and last workgroup covering each item (equal when one workgroup
-  // holds all of the item's tiles; both -1 for an item with no tiles): the
-  // workgroup of tile t is the last g < G with wg_tile[g] <= t.
-  for (int i = tid; i < Nq; i += kPlanThreads) {
-    const int32_t ts = ts_tab[i], te = ts_tab[i + 1];
-    int32_t wgs[2] = {-1, -1};
-    if (te > ts) {
-      for (int e = 0; e < 2; ++e) {
-        const int32_t t = e == 0 ? ts : te - 1;
-        int lo = 0, hi = G;
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (wt_tab[mid] <= t) lo = mid; else hi = mid;
-        }
-        wgs[e] = lo;
-      }
-    }
-    item_wg[2 * i] = wgs[0];
-    item_wg[2 * i + 1] = wgs[1];
-  }
+  plan_items_body<kPlanThreads>(buf, &carry, ts_lds, wt_lds, mode, B, Nq, ctx, qsl, window, max_ctx,
+                                item_b, item_lo, item_hi, tile_start, G, wg_tile, wg_item, item_wg);
 }
-
 // One wave per (item, head).  Items whose tiles all fell to one workgroup were
 // finished by the attention kernel; empty items get o = 0, lse = -inf; cut
 // items are merged from the partial slots of the workgroups that cover them

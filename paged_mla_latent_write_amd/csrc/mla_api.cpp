@@ -170,22 +170,6 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
   int64_t ql_st = qn_st, ql_sh = qn_sh;
   const bool generic = (attn->flags & MLA_FLAG_GENERIC_KERNELS) != 0;
   const auto aligned16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
-  if (attn->w_uk) {
-    uint16_t* ql = at<uint16_t>(workspace, L.q_lat);
-    const bool mfma = !generic && mla::absorb_mfma_supported(attn->qk_nope_dim, R) &&
-                      aligned16(q_nope) && aligned16(attn->w_uk) && qn_st % 8 == 0 && qn_sh % 8 == 0;
-    e = mfma ? mla::launch_absorb_mfma(static_cast<const uint16_t*>(q_nope), qn_st, qn_sh,
-                                       static_cast<const uint16_t*>(attn->w_uk), num_items, H,
-                                       attn->qk_nope_dim, R, ql, s)
-             : mla::launch_absorb(static_cast<const uint16_t*>(q_nope), qn_st, qn_sh,
-                                  static_cast<const uint16_t*>(attn->w_uk), num_items, H,
-                                  attn->qk_nope_dim, R, ql, s);
-    if (e != hipSuccess) return MLA_ERR_HIP;
-    q_lat = ql;
-    ql_st = static_cast<int64_t>(H) * R;
-    ql_sh = R;
-  }
-
   mla::Plan plan;
   plan.item_b = at<int32_t>(workspace, L.item_b);
   plan.item_lo = at<int32_t>(workspace, L.item_lo);
@@ -195,9 +179,31 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
   plan.wg_item = at<int32_t>(workspace, L.wg_item);
   plan.item_wg = at<int32_t>(workspace, L.item_wg);
   plan.G = L.G;
-  e = mla::launch_plan(mode, batch, num_items, context_lens, qsl, attn->window,
-                       static_cast<int32_t>(max_ctx64), plan, s);
-  if (e != hipSuccess) return MLA_ERR_HIP;
+  const mla::PlanArgs pa{mode, batch, num_items, context_lens, qsl, attn->window,
+                         static_cast<int32_t>(max_ctx64), plan};
+  bool planned = false;  // the MFMA absorb launch computes the plan too
+
+  if (attn->w_uk) {
+    uint16_t* ql = at<uint16_t>(workspace, L.q_lat);
+    const bool mfma = !generic && mla::absorb_mfma_supported(attn->qk_nope_dim, R) &&
+                      aligned16(q_nope) && aligned16(attn->w_uk) && qn_st % 8 == 0 && qn_sh % 8 == 0;
+    e = mfma ? mla::launch_absorb_mfma(static_cast<const uint16_t*>(q_nope), qn_st, qn_sh,
+                                       static_cast<const uint16_t*>(attn->w_uk), num_items, H,
+                                       attn->qk_nope_dim, R, ql, &pa, s)
+             : mla::launch_absorb(static_cast<const uint16_t*>(q_nope), qn_st, qn_sh,
+                                  static_cast<const uint16_t*>(attn->w_uk), num_items, H,
+                                  attn->qk_nope_dim, R, ql, s);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+    planned = mfma;
+    q_lat = ql;
+    ql_st = static_cast<int64_t>(H) * R;
+    ql_sh = R;
+  }
+  if (!planned) {
+    e = mla::launch_plan(mode, batch, num_items, context_lens, qsl, attn->window,
+                         static_cast<int32_t>(max_ctx64), plan, s);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+  }
 
   AttnArgs a;
   memset(&a, 0, sizeof(a));

@@ -90,6 +90,17 @@ hipError_t launch_plan(int mode, int32_t batch, int32_t num_items, const int32_t
                        const int32_t* query_start_loc, int32_t window, int32_t max_ctx,
                        const Plan& plan, hipStream_t s);
 
+// The split plan's inputs and outputs, for a launch that runs it beside other
+// work (launch_absorb_mfma).
+struct PlanArgs {
+  int mode;
+  int32_t batch, num_items;
+  const int32_t* context_lens;
+  const int32_t* query_start_loc;
+  int32_t window, max_ctx;
+  Plan plan;
+};
+
 hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t s);
 
 // True when the MFMA split-KV kernel handles this shape (R 512, Dr 64, H <= 128).
@@ -117,9 +128,11 @@ hipError_t launch_latent_out(const float* o_lat, const float* o_scale, int32_t n
 // Matrix-core versions of the two per-head projections (head_gemm.hip).
 bool absorb_mfma_supported(int32_t Dn, int32_t R);
 bool up_project_mfma_supported(int32_t R, int32_t Dv);
+// With `plan` non-null the same launch also computes the split plan, in one
+// extra workgroup.
 hipError_t launch_absorb_mfma(const uint16_t* q_nope, int64_t st, int64_t sh, const uint16_t* w_uk,
                               int32_t num_items, int32_t H, int32_t Dn, int32_t R, uint16_t* q_lat,
-                              hipStream_t s);
+                              const PlanArgs* plan, hipStream_t s);
 hipError_t launch_up_project_mfma(const float* o_lat, const float* o_scale, const uint16_t* w_uv,
                                   int32_t num_items, int32_t H, int32_t R, int32_t Dv, uint16_t* out,
                                   hipStream_t s);
