@@ -478,12 +478,28 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
       lse_dst = a.part_lse + slot * a.H;
       scl_dst = a.part_scale + slot * a.H;
     }
-    if (wave_active && head_ok) {
+    // A wave whose 32 heads all exist stores through LDS (coalesced rows),
+    // using its own 9 KB copy region of the buffers of the segment's last two
+    // tiles: every wave has finished with those once it passed the last
+    // tile's barrier, and the WG's last segment (no such barrier) gets one
+    // here.  Its next copy into either region is issued by this wave itself,
+    // after these reads.
+    const bool lds_store = (wave + 1) * 32 <= a.H;
+    if (ctile >= t1) __syncthreads();
+    if (wave_active && lds_store) {
+      const uint32_t reg_a = lds_base + ((tn - 2) & 3) * kTileBytes + wave * kLoads * 1024;
+      const uint32_t reg_b = lds_base + ((tn - 1) & 3) * kTileBytes + wave * kLoads * 1024;
+      const uint32_t w_off = n32 * 272 + 16 * g;
+      const uint32_t r_off = (lane >> 4) * 272 + (lane & 15) * 16;
+      store_acc_lds(reinterpret_cast<char*>(o_dst + static_cast<int64_t>(wave * 32) * kR),
+                    (lane >> 4) * 2048 + (lane & 15) * 16, reg_a + w_off, reg_b + w_off, reg_a + r_off,
+                    reg_b + r_off);
+    } else if (wave_active && head_ok) {
       store_acc(o_dst + static_cast<int64_t>(head) * kR + 4 * g);
-      if (g == 0) {
-        lse_dst[head] = (m_ref + log2f(l_tot)) * kLn2;
-        scl_dst[head] = 1.0f / l_tot;
-      }
+    }
+    if (wave_active && head_ok && g == 0) {
+      lse_dst[head] = (m_ref + log2f(l_tot)) * kLn2;
+      scl_dst[head] = 1.0f / l_tot;
     }
     // the next segment's queries (its first K fragments are already read)
     if (ctile < t1 && wave_active && head_ok) {

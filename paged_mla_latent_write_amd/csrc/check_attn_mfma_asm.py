@@ -3,8 +3,9 @@
     python check_attn_mfma_asm.py        # exit status 1 on a problem
 
 For every block it replays the instruction list and checks that
-  1. no MFMA reads a ring register whose LDS read has not been waited for
-     (lgkmcnt counts reads in issue order; reads complete in order), and
+  1. no MFMA reads a ring register, and no global store stores a register,
+     whose LDS read has not been waited for (lgkmcnt counts LDS operations in
+     issue order; they complete in order), and
   2. no LDS read overwrites a ring register that still holds data no MFMA has
      read yet (a ring slot reused too early), and
   3. every scalar load is waited for (lgkmcnt(0)) before the block ends: its
@@ -49,7 +50,9 @@ def replay(name, lines, ring, live, in_flight, problems):
             if dst & live:
                 problems.append(f"{name}: LDS read overwrites unread data: {ln}")
             in_flight.append(dst)
-            live |= dst
+            live |= {r for r in dst if r >= ring}  # (only ring slots have MFMA consumers)
+        elif op.startswith("ds_write"):
+            in_flight.append(set())  # counts on lgkmcnt like a read
         elif op == "s_waitcnt" and "lgkmcnt" in ln:
             n = int(re.search(r"lgkmcnt\((\d+)\)", ln).group(1))
             while len(in_flight) > n:
@@ -60,6 +63,11 @@ def replay(name, lines, ring, live, in_flight, problems):
                 if any(r & q for q in in_flight):
                     problems.append(f"{name}: MFMA before its LDS read landed: {ln}")
                 live -= r
+        elif op.startswith(("global_store", "buffer_store")):
+            # store data read from registers an LDS read has not filled yet
+            data = regs(ln.split(" ")[2].rstrip(","))
+            if any(data & q for q in in_flight):
+                problems.append(f"{name}: store before its LDS read landed: {ln}")
     if smem_open:
         problems.append(f"{name}: scalar load not waited for before the block ends: {smem_open}")
     return live, in_flight

@@ -387,6 +387,42 @@ def hot_loop():
     return o
 
 
+def store_acc_lds():
+    """The wave's unnormalised O^T (32 heads x 512 dims, a0-a255) to its 64 KB
+    of rows [head][512] at %[base], through LDS so that every global store
+    writes four 256-byte row pieces (a direct store of the MFMA layout writes
+    32 pieces of 32 bytes per instruction).  Eight rounds of 64 dims: the
+    accumulators of two m-tiles go to a padded row-major LDS block (32 rows of
+    272 bytes, at %[wa] / %[wb] = block + 272 head + 16 g, alternating between
+    two 9 KB blocks), are read back four rows per instruction (%[ra] / %[rb] =
+    block + 272 (lane / 16) + 16 (lane % 16)) and stored (%[soff] = 2048 (lane /
+    16) + 16 (lane % 16)).  Temporaries: the query registers (free between
+    segments: the next segment's queries are loaded after this)."""
+    L = ["s_nop 7", "s_nop 7", "s_nop 4"]  # the last MFMA results must have landed
+    OFF = Q_BASE  # v58-v65: store offsets of the eight row groups
+    L += [f"v_add_u32 v{OFF + i}, {8192 * i}, %[soff]" for i in range(8)]
+    for r in range(8):
+        wa, ra = ("%[wa]", "%[ra]") if r % 2 == 0 else ("%[wb]", "%[rb]")
+        T = Q_BASE + 8 + 64 * (r % 2)  # 32 accumulator values, then 32 read back
+        for m in range(2):
+            mt = 2 * r + m
+            for a4 in range(4):
+                t = T + 16 * m + 4 * a4
+                L += [f"v_accvgpr_read_b32 v{t + e}, a{16 * mt + 4 * a4 + e}" for e in range(4)]
+                L.append(f"ds_write_b128 {wa}, v[{t}:{t + 3}] offset:{128 * m + 32 * a4}")
+        rd = T + 32
+        for i in range(8):
+            L.append(f"ds_read_b128 v[{rd + 4 * i}:{rd + 4 * i + 3}], {ra} offset:{1088 * i}")
+        for i in range(8):
+            # LDS operations of one wave complete in order: read i has landed
+            # once at most the 7 - i later ones are outstanding
+            L.append(f"s_waitcnt lgkmcnt({7 - i})")
+            L.append(f"global_store_dwordx4 v{OFF + i}, v[{rd + 4 * i}:{rd + 4 * i + 3}], %[base] offset:{256 * r}")
+    return block("store_acc_lds", ["char* base", "uint32_t soff", "uint32_t wa", "uint32_t wb", "uint32_t ra",
+                                   "uint32_t rb"], L, [],
+                 ['[base] "s"(base), [soff] "v"(soff), [wa] "v"(wa), [wb] "v"(wb), [ra] "v"(ra), [rb] "v"(rb)'])
+
+
 def rescale_lines():
     """Scale this lane's accumulators by %[fac] (rare: after a reference move);
     temporaries: the score registers (P of the tile is in v220-v227, the next
@@ -550,6 +586,7 @@ def emit():
             n += 1
     o += block("store_acc", ["float* orow"], L, [], ['[orow] "v"(orow)'])
     o += block("rescale_acc", ["float fac"], rescale_lines(), [], ['[fac] "v"(fac)'])
+    o += store_acc_lds()
     o += hot_loop()
     return "\n".join(o)
 
