@@ -260,7 +260,11 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
   // every tile (so the copy rate does not drop) but skip the arithmetic.
   const bool wave_active = wave * 32 < a.H;
 
-  const int64_t wg = blockIdx.x;
+  // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+  // L2); ranges are numbered so that consecutive ranges -- which mostly share
+  // an item, and so its queries -- run on the same XCD.
+  const int64_t wg = (gridDim.x & 7) == 0 ? (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3)
+                                          : blockIdx.x;
   const int t0 = m.wg_tile[wg], t1 = m.wg_tile[wg + 1];
   if (t0 >= t1) return;
   const int ntiles = t1 - t0;

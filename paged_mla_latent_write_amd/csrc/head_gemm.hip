@@ -220,39 +220,30 @@ __global__ __launch_bounds__(256) void up_project_mfma_kernel(const float* __res
 constexpr int kCupMaxR = 512;
 constexpr int kCupPitch = kCupMaxR + 8;  // bf16 per staged row (16 B pad: bank spread)
 
-__global__ __launch_bounds__(256) void combine_up_project_kernel(AttnArgs a, const uint16_t* __restrict__ w_uv,
-                                                                 int32_t Dv, uint16_t* __restrict__ out) {
+constexpr int kCupThreads = 512;
+constexpr int kCupSegBatch = 4;  // partial rows of one item loaded together
+
+__global__ __launch_bounds__(kCupThreads) void combine_up_project_kernel(AttnArgs a,
+                                                                         const uint16_t* __restrict__ w_uv,
+                                                                         int32_t Dv, uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) __bf16 o_hi[32 * kCupPitch];
   __shared__ __attribute__((aligned(16))) __bf16 o_lo[32 * kCupPitch];
   const int h = blockIdx.y;
   const int m0 = blockIdx.x * 32;
   const int H = a.H, R = a.kv.R, Nq = a.num_items;
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-  const int g = lane >> 5, n32 = lane & 31;
-  const int v = 32 * wave + n32;
-  const bool v_ok = 32 * wave < Dv;
 
-  // W_UV[h][v] B fragments of every k-step, loaded first: their latency
-  // overlaps the merge below
-  i16x8 b[kCupMaxR / 16];
+  // ---- phase 1: the 16 threads (il, j) of item m0 + il merge its columns
+  // 4 j + 64 e .. + 3: each load of the item's threads reads 256 contiguous
+  // bytes.  The rows of up to four segments are requested at once, as soon as
+  // the item's workgroup range is known, so most items take one round trip.
   {
-    const uint16_t* wrow = w_uv + (static_cast<int64_t>(h) * Dv + (v_ok ? v : 0)) * R;
-#pragma unroll
-    for (int u = 0; u < kCupMaxR / 16; ++u)
-      if (16 * u < R) b[u] = *reinterpret_cast<const i16x8*>(wrow + 16 * u + 8 * g);
-  }
-
-  // ---- phase 1: thread (il, j) merges columns 32 e + 4 j .. + 3 (e < R / 32) of
-  // item m0 + il: the item's eight threads read 128 contiguous bytes per load
-  {
-    const int il = t >> 3, j = t & 7;
+    constexpr int kE = kCupMaxR / 64;
+    const int il = t >> 4, j = t & 15;
     const int item = m0 + il;
-    const int nv = R / 32;                // float4 per thread (<= 16)
-    const int c0 = 4 * j;
-    float acc[kCupMaxR / 8];
+    float4 acc[kE];
 #pragma unroll
-    for (int e = 0; e < kCupMaxR / 8; ++e) acc[e] = 0.f;
+    for (int e = 0; e < kE; ++e) acc[e] = make_float4(0.f, 0.f, 0.f, 0.f);
     float m = -INFINITY, tot = 0.f;
     if (item < Nq) {
       const int64_t row = static_cast<int64_t>(item) * H + h;
@@ -260,57 +251,61 @@ __global__ __launch_bounds__(256) void combine_up_project_kernel(AttnArgs a, con
       if (g0 >= 0 && g0 == g1) {
         // uncut: the attention kernel wrote the unnormalised row and 1 / l
         const float sc = a.o_scale[row];
-        const float4* src = reinterpret_cast<const float4*>(a.o_lat + row * R + c0);
+        const float4* src = reinterpret_cast<const float4*>(a.o_lat + row * R);
 #pragma unroll
-        for (int e = 0; e < kCupMaxR / 32; ++e) {
-          if (e < nv) {
-            const float4 x = src[8 * e];
-            acc[4 * e] = x.x * sc;
-            acc[4 * e + 1] = x.y * sc;
-            acc[4 * e + 2] = x.z * sc;
-            acc[4 * e + 3] = x.w * sc;
+        for (int e = 0; e < kE; ++e) {
+          const int c = 4 * j + 64 * e;
+          if (c < R) {
+            const float4 x = src[c >> 2];
+            acc[e] = make_float4(x.x * sc, x.y * sc, x.z * sc, x.w * sc);
           }
         }
         m = 0.f;
         tot = 1.f;
       } else if (g0 >= 0) {
-        // segments two at a time: both loads issued, then merged against the
-        // running maximum
-        for (int gb = g0; gb <= g1; gb += 2) {
-          float l[2], sc[2];
-          float4 x[2][kCupMaxR / 32];
+        for (int gb = g0; gb <= g1; gb += kCupSegBatch) {
+          float l[kCupSegBatch], sc[kCupSegBatch];
+          float4 x[kCupSegBatch][kE];
 #pragma unroll
-          for (int p = 0; p < 2; ++p) {
+          for (int p = 0; p < kCupSegBatch; ++p) {
             const int gg = gb + p;
-            const bool live = gg <= g1 && a.wg_tile[gg] != a.wg_tile[gg + 1];  // (no tiles: no slot)
+            const bool in = gg <= g1;
+            // A workgroup range of the item with no tiles wrote no slot: its
+            // (stale) row is loaded with the others but gets no weight.
+            const bool live = in && a.wg_tile[gg] != a.wg_tile[gg + 1];
             const int64_t slot = (gg == g0) ? 2 * gg + 1 : 2 * gg;
-            l[p] = live ? a.part_lse[slot * H + h] : -INFINITY;
-            sc[p] = live ? a.part_scale[slot * H + h] : 0.f;
-            const float4* src = reinterpret_cast<const float4*>(a.part_o + (slot * H + h) * R + c0);
+            const float lp = in ? a.part_lse[slot * H + h] : -INFINITY;
+            sc[p] = in ? a.part_scale[slot * H + h] : 0.f;
+            const float4* src = reinterpret_cast<const float4*>(a.part_o + (slot * H + h) * R);
 #pragma unroll
-            for (int e = 0; e < kCupMaxR / 32; ++e)
-              x[p][e] = (live && e < nv) ? src[8 * e] : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int e = 0; e < kE; ++e) {
+              const int c = 4 * j + 64 * e;
+              x[p][e] = (in && c < R) ? src[c >> 2] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+            l[p] = live ? lp : -INFINITY;
           }
-          const float mb = fmaxf(m, fmaxf(l[0], l[1]));
-          if (mb > m) {  // uniform within the item's eight threads
+          float mb = m;
+#pragma unroll
+          for (int p = 0; p < kCupSegBatch; ++p) mb = fmaxf(mb, l[p]);
+          if (mb > m) {  // uniform within the item's threads
             const float f = expf(m - mb);
             tot *= f;
 #pragma unroll
-            for (int e = 0; e < kCupMaxR / 8; ++e) acc[e] *= f;
+            for (int e = 0; e < kE; ++e) acc[e] = make_float4(acc[e].x * f, acc[e].y * f, acc[e].z * f, acc[e].w * f);
             m = mb;
           }
 #pragma unroll
-          for (int p = 0; p < 2; ++p) {
+          for (int p = 0; p < kCupSegBatch; ++p) {
             if (l[p] == -INFINITY) continue;
             const float e_l = expf(l[p] - m);
             tot += e_l;
             const float w = e_l * sc[p];
 #pragma unroll
-            for (int e = 0; e < kCupMaxR / 32; ++e) {
-              acc[4 * e] = fmaf(w, x[p][e].x, acc[4 * e]);
-              acc[4 * e + 1] = fmaf(w, x[p][e].y, acc[4 * e + 1]);
-              acc[4 * e + 2] = fmaf(w, x[p][e].z, acc[4 * e + 2]);
-              acc[4 * e + 3] = fmaf(w, x[p][e].w, acc[4 * e + 3]);
+            for (int e = 0; e < kE; ++e) {
+              acc[e].x = fmaf(w, x[p][e].x, acc[e].x);
+              acc[e].y = fmaf(w, x[p][e].y, acc[e].y);
+              acc[e].z = fmaf(w, x[p][e].z, acc[e].z);
+              acc[e].w = fmaf(w, x[p][e].w, acc[e].w);
             }
           }
         }
@@ -321,24 +316,35 @@ __global__ __launch_bounds__(256) void combine_up_project_kernel(AttnArgs a, con
     }
     const float inv = tot > 0.f ? 1.f / tot : 0.f;
 #pragma unroll
-    for (int e = 0; e < kCupMaxR / 32; ++e) {
-      if (e < nv) {
+    for (int e = 0; e < kE; ++e) {
+      const int c = 4 * j + 64 * e;
+      if (c < R) {
+        const float xs[4] = {acc[e].x * inv, acc[e].y * inv, acc[e].z * inv, acc[e].w * inv};
         bf16x4 hi, lo;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float x = acc[4 * e + q] * inv;
-          hi[q] = static_cast<__bf16>(x);
-          lo[q] = static_cast<__bf16>(x - static_cast<float>(hi[q]));
+          hi[q] = static_cast<__bf16>(xs[q]);
+          lo[q] = static_cast<__bf16>(xs[q] - static_cast<float>(hi[q]));
         }
-        *reinterpret_cast<bf16x4*>(o_hi + il * kCupPitch + 32 * e + c0) = hi;
-        *reinterpret_cast<bf16x4*>(o_lo + il * kCupPitch + 32 * e + c0) = lo;
+        *reinterpret_cast<bf16x4*>(o_hi + il * kCupPitch + c) = hi;
+        *reinterpret_cast<bf16x4*>(o_lo + il * kCupPitch + c) = lo;
       }
     }
   }
   __syncthreads();
 
-  // ---- phase 2: out[item, h, v] = W_UV[h][v] . o[item], wave w: v in [32 w, 32 w + 32)
-  if (!v_ok) return;
+  // ---- phase 2: out[item, h, v] = W_UV[h][v] . o[item], wave w < 4: v in [32 w, 32 w + 32)
+  const int lane = t & 63, wave = t >> 6;
+  const int g = lane >> 5, n32 = lane & 31;
+  const int v = 32 * wave + n32;
+  if (32 * wave >= Dv) return;
+  i16x8 b[kCupMaxR / 16];
+  {
+    const uint16_t* wrow = w_uv + (static_cast<int64_t>(h) * Dv + v) * R;
+#pragma unroll
+    for (int u = 0; u < kCupMaxR / 16; ++u)
+      if (16 * u < R) b[u] = *reinterpret_cast<const i16x8*>(wrow + 16 * u + 8 * g);
+  }
   f32x16 acc = f32x16{};
 #pragma unroll
   for (int u = 0; u < kCupMaxR / 16; ++u) {
@@ -379,7 +385,7 @@ bool combine_up_project_supported(int32_t R, int32_t Dv) {
 hipError_t launch_combine_up_project(const AttnArgs& a, const uint16_t* w_uv, int32_t Dv, uint16_t* out,
                                      hipStream_t s) {
   const dim3 grid((a.num_items + 31) / 32, a.H);
-  hipLaunchKernelGGL(combine_up_project_kernel, grid, dim3(256), 0, s, a, w_uv, Dv, out);
+  hipLaunchKernelGGL(combine_up_project_kernel, grid, dim3(kCupThreads), 0, s, a, w_uv, Dv, out);
   return hipGetLastError();
 }
 
