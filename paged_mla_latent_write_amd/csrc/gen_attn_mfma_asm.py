@@ -32,7 +32,7 @@ A tile step is one inline-assembly statement of one wave:
 """
 import sys
 
-NF = 7                      # LDS fragments in flight (ring of 4 NF registers)
+NF = 6                      # LDS fragments in flight (ring of 4 NF registers)
 RING = 256 - 4 * NF         # v228-v255
 PN = RING - 8               # v220-v227: P of the current tile
 SS = PN - 16                # v204-v219: scores
