@@ -320,13 +320,10 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
   cursor_fetch_pages(cur, a);
   const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>(bufs[0])) + wave * kLoads * 1024);
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    if (p < ntiles) {
-      cursor_copy<NW>(cur, a, lds_wave + p * kTileBytes, lofs);
-      cursor_advance(cur, a, m);
-    }
-  }
+  // tile 0, then the first item's queries, then tile 1: the first step needs
+  // only the first two (the wait below leaves tile 1's copies in flight)
+  cursor_copy<NW>(cur, a, lds_wave, lofs);
+  cursor_advance(cur, a, m);
 
   uint32_t koff[4], kcur[4], voff[4];
 #pragma unroll
@@ -342,13 +339,17 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
   // compiler does not allocate; only the blocks of attn_mfma_asm.inc touch them.
   zero_q();
   int c_item = advance_item(m, a.num_items, first_item, t0);
-  // the first item's queries (lanes of heads >= H keep zeros); the load
-  // block waits for them, which also covers the first copies
+  // the first item's queries (lanes of heads >= H keep zeros)
   if (wave_active && head_ok)
-    load_q(a.q_lat + c_item * a.q_lat_st + head * a.q_lat_sh + 8 * g,
-           a.q_pe + c_item * a.q_pe_st + head * a.q_pe_sh + 8 * g);
-  if (ntiles > 1) wait_vmcnt<kLoads>();
-  else wait_vmcnt<0>();
+    load_q_nowait(a.q_lat + c_item * a.q_lat_st + head * a.q_lat_sh + 8 * g,
+                  a.q_pe + c_item * a.q_pe_st + head * a.q_pe_sh + 8 * g);
+  if (ntiles > 1) {
+    cursor_copy<NW>(cur, a, lds_wave + kTileBytes, lofs);
+    cursor_advance(cur, a, m);
+    wait_vmcnt<kLoads>();  // tile 0 and the queries have landed
+  } else {
+    wait_vmcnt<0>();
+  }
   __syncthreads();  // barrier 0: tile 0 is in LDS
   if (wave_active) tile_prefetch_k(kcur, koff, lds_base);
 

@@ -569,6 +569,9 @@ def emit():
     # queries: 32 k-steps of q_lat (ql: this lane's row + 8 g) then 4 of q_pe
     L = [f"global_load_dwordx4 {q(k)}, %[ql], off offset:{32 * k}" for k in range(32)]
     L += [f"global_load_dwordx4 {q(32 + k)}, %[qp], off offset:{32 * k}" for k in range(4)]
+    # (without the wait: the kernel's first queries, waited for by the caller)
+    o += block("load_q_nowait", ["const uint16_t* ql", "const uint16_t* qp"], L, [],
+               ['[ql] "v"(ql), [qp] "v"(qp)'])
     L.append("s_waitcnt vmcnt(0)")
     o += block("load_q", ["const uint16_t* ql", "const uint16_t* qp"], L, [], ['[ql] "v"(ql), [qp] "v"(qp)'])
     o += block("zero_q", [], [f"v_mov_b32 v{Q_BASE + r}, 0" for r in range(144)], [], [])
