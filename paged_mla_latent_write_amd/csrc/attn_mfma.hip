@@ -335,7 +335,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
   const uint32_t lds_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(bufs[0]));
   const float c = a.scale_log2;
 
-  // Q (v58-v201) and the O^T accumulators (a0-a255) live in registers the
+  // Q (v62-v205) and the O^T accumulators (a0-a255) live in registers the
   // compiler does not allocate; only the blocks of attn_mfma_asm.inc touch them.
   zero_q();
   int c_item = advance_item(m, a.num_items, first_item, t0);

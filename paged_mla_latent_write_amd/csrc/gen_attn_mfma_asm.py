@@ -8,13 +8,13 @@ amdgpu_num_vgpr), so every register above is reserved and keeps its value from
 one block to the next; the blocks below own them:
 
     a0-a255    O^T accumulators of the wave's 32 heads: 16 tiles of 32 dims
-    v50-v57    P of the previous tile (bf16, B operand of O^T += V^T P^T)
-    v58-v201   Q^T fragments: 36 k-steps x 4 registers (q_lat then q_pe)
-    v202-v203  copy-offset temporary (scores phase), softmax temporaries
-    v204-v219  scores (one accumulation chain: a dependent MFMA chain issues
+    v54-v61    P of the previous tile (bf16, B operand of O^T += V^T P^T)
+    v62-v205   Q^T fragments: 36 k-steps x 4 registers (q_lat then q_pe)
+    v206-v207  copy-offset temporary (scores phase), softmax temporaries
+    v208-v223  scores (one accumulation chain: a dependent MFMA chain issues
                at the full rate)
-    v220-v227  P of the current tile (the softmax output)
-    v228-v255  ring of seven LDS fragments in flight
+    v224-v231  P of the current tile (the softmax output)
+    v232-v255  ring of six LDS fragments in flight
 
 A tile step is one inline-assembly statement of one wave:
 
@@ -33,14 +33,14 @@ A tile step is one inline-assembly statement of one wave:
 import sys
 
 NF = 6                      # LDS fragments in flight (ring of 4 NF registers)
-RING = 256 - 4 * NF         # v228-v255
-PN = RING - 8               # v220-v227: P of the current tile
-SS = PN - 16                # v204-v219: scores
-TMP_DMA = SS - 2            # v202: copy offsets (scores phase only)
-T0, T1 = SS - 2, SS - 1     # v202, v203: softmax temporaries (values phase)
-Q_BASE = TMP_DMA - 144      # v58-v201
-P_BASE = Q_BASE - 8         # v50-v57
-NC = P_BASE                 # v0..v49 for the compiler
+RING = 256 - 4 * NF         # v232-v255
+PN = RING - 8               # v224-v231: P of the current tile
+SS = PN - 16                # v208-v223: scores
+TMP_DMA = SS - 2            # v206: copy offsets (scores phase only)
+T0, T1 = SS - 2, SS - 1     # v206, v207: softmax temporaries (values phase)
+Q_BASE = TMP_DMA - 144      # v62-v205
+P_BASE = Q_BASE - 8         # v54-v61
+NC = P_BASE                 # v0..v53 for the compiler
 NEG_INF = "0xff800000"
 SLACK = "0x41800000"        # 16.0f: slack of the reference maximum (log2 units)
 
@@ -86,8 +86,8 @@ def s_chain(k):
 
 
 def softmax_ops(first, masked):
-    """The softmax of one tile (scores in v204-v219) as VALU instructions;
-    leaves P (bf16 pairs) in v220-v227.  The scale %[c] (log2 units) is
+    """The softmax of one tile (scores in v208-v223) as VALU instructions;
+    leaves P (bf16 pairs) in v224-v231.  The scale %[c] (log2 units) is
     positive, so the tile maximum is taken on the raw scores and scaled once;
     each exponent is then one fused multiply-add, s c - m."""
     s = [f"v{SS + i}" for i in range(16)]
@@ -206,7 +206,7 @@ def s_part(st, dma, copy_p, prefetch_v):
     """Scores of the current tile.  Its first NF K fragments are already in the
     ring (read by the previous block's tail, addresses %[k0..k3] = this lane's
     K row offsets within the tile's LDS buffer).  copy_p: first move the
-    previous step's P (v220-v227) to v50-v57.  dma: also issue the 9 copies of a
+    previous step's P (v224-v231) to v54-v61.  dma: also issue the 9 copies of a
     later tile (HBM base %[sb], LDS rows from %[m0], lane offsets packed two per
     register in %[l0..l4]).  prefetch_v: the ring slots the last k-steps free
     are refilled with the first values fragments (%[v0..v3] + %[bp])."""
@@ -399,7 +399,7 @@ def store_acc_lds():
     16) + 16 (lane % 16)).  Temporaries: the query registers (free between
     segments: the next segment's queries are loaded after this)."""
     L = ["s_nop 7", "s_nop 7", "s_nop 4"]  # the last MFMA results must have landed
-    OFF = Q_BASE  # v58-v65: store offsets of the eight row groups
+    OFF = Q_BASE  # v62-v69: store offsets of the eight row groups
     L += [f"v_add_u32 v{OFF + i}, {8192 * i}, %[soff]" for i in range(8)]
     for r in range(8):
         wa, ra = ("%[wa]", "%[ra]") if r % 2 == 0 else ("%[wb]", "%[rb]")
@@ -425,7 +425,7 @@ def store_acc_lds():
 
 def rescale_lines():
     """Scale this lane's accumulators by %[fac] (rare: after a reference move);
-    temporaries: the score registers (P of the tile is in v220-v227, the next
+    temporaries: the score registers (P of the tile is in v224-v231, the next
     K fragments in the ring)."""
     L = ["s_nop 7", "s_nop 7", "s_nop 4"]  # the last MFMA results must have landed
     for r in range(256):
@@ -539,7 +539,7 @@ def emit():
                                f"_m{masked}"
                         o += block(name, args, st.lines, outs, ins, ', "m0", "scc"' if dma else ', "scc"')
     # the segment's last values step: O^T += V_T^T P_T^T (fragments queued by
-    # the previous block, P in v220-v227), then the tail
+    # the previous block, P in v224-v231), then the tail
     for first_pv in (0, 1):
         st = Stream()
         # the fragments in flight, in issue order: each went into the ring slot
