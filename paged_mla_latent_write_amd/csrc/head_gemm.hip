@@ -10,8 +10,10 @@
 // columns); each wave computes 32 output columns with v_mfma_f32_32x32x16_bf16.
 //  * absorb: the W_UK[h] column block is staged in LDS (rows padded to 288 B)
 //    and read as the B operand with ds_read_b64_tr_b16 (W_UK rows run along
-//    the output dimension, the MFMA wants runs along K).  bf16 in, fp32
-//    accumulate, bf16 out.
+//    the output dimension, the MFMA wants runs along K).  The block's query
+//    rows and its output tile pass through LDS as well, so global memory sees
+//    whole 256-byte rows (a lane's own fragment would take one cache line per
+//    lane and instruction).  bf16 in, fp32 accumulate, bf16 out.
 //  * up-project: W_UV rows already run along K, so B fragments come straight
 //    from global memory.  o_lat is fp32; each A fragment is split into a bf16
 //    high part and a bf16 remainder and both are multiplied (two MFMAs), which
@@ -39,6 +41,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kAbsCols = 128;              // W_UK columns staged per chunk
 constexpr int kAbsPitch = kAbsCols * 2 + 32;  // bytes per staged row (padded)
 constexpr int kAbsMaxDn = 128;
+constexpr int kAbsQPitch = kAbsMaxDn * 2 + 16;  // bytes per staged query / output row (padded)
+static_assert(kAbsCols * 2 <= kAbsMaxDn * 2, "the output tile fits the query rows");
 
 template <int MT>
 __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* __restrict__ q_nope,
@@ -48,6 +52,7 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* __rest
                                                           int32_t R, uint16_t* __restrict__ q_lat,
                                                           PlanArgs pa) {
   __shared__ __attribute__((aligned(16))) char wt[kAbsMaxDn * kAbsPitch];
+  __shared__ __attribute__((aligned(16))) char qs[32 * MT * kAbsQPitch];
   static_assert((256 + 1 + 2 * kPlanLds) * 4 <= kAbsMaxDn * kAbsPitch, "plan LDS fits the staging buffer");
   if (blockIdx.x * kAbsCols >= R) {
     // the extra column of workgroups: one computes the split plan, in the
@@ -63,7 +68,8 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* __rest
   }
   const int c0 = blockIdx.x * kAbsCols;  // this workgroup's 128 output columns
   const int h = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
   const int g = lane >> 5, n32 = lane & 31;
   const int ksteps = Dn / 16;
 
@@ -72,6 +78,32 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* __rest
   const int tr_off = (8 * g + rr) * kAbsPitch + (32 * wave + 16 * (q & 1) + 4 * c4) * 2;
   const uint16_t* wh = w_uk + static_cast<int64_t>(h) * Dn * R;
 
+  // The block's query rows are staged in LDS (sixteen threads read one 256-byte
+  // row), and so is its output tile (written back as 256-byte rows): a lane's
+  // own MFMA fragments would touch one cache line per lane and instruction.
+  constexpr int kQPer = 32 * MT * (kAbsMaxDn / 8) / 256;  // 16-byte chunks per thread
+  i16x8 qv[kQPer];
+  auto load_q = [&](int m0) {
+#pragma unroll
+    for (int j = 0; j < kQPer; ++j) {
+      const int idx = t + 256 * j;
+      const int r = idx / (kAbsMaxDn / 8), c = idx % (kAbsMaxDn / 8);
+      const int item = m0 + r;
+      i16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (item < Nq && c < Dn / 8) v = *reinterpret_cast<const i16x8*>(q_nope + item * st + h * sh + 8 * c);
+      qv[j] = v;
+    }
+  };
+  auto store_q = [&]() {
+#pragma unroll
+    for (int j = 0; j < kQPer; ++j) {
+      const int idx = t + 256 * j;
+      const int r = idx / (kAbsMaxDn / 8), c = idx % (kAbsMaxDn / 8);
+      *reinterpret_cast<i16x8*>(qs + r * kAbsQPitch + c * 16) = qv[j];
+    }
+  };
+  const int m_first = blockIdx.z * 32 * MT, m_stride = gridDim.z * 32 * MT;
+  if (m_first < Nq) load_q(m_first);
   {
     // stage W_UK[h][0:Dn][c0 : c0 + 128]: all loads first (16 B per thread
     // per step), then the LDS stores
@@ -79,34 +111,22 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* __rest
     i16x8 wv[kStage];
 #pragma unroll
     for (int j = 0; j < kStage; ++j) {
-      const int idx = threadIdx.x + 256 * j;
+      const int idx = t + 256 * j;
       const int d = idx / (kAbsCols / 8), c = idx % (kAbsCols / 8);
       if (d < Dn) wv[j] = *reinterpret_cast<const i16x8*>(wh + static_cast<int64_t>(d) * R + c0 + 8 * c);
     }
 #pragma unroll
     for (int j = 0; j < kStage; ++j) {
-      const int idx = threadIdx.x + 256 * j;
+      const int idx = t + 256 * j;
       const int d = idx / (kAbsCols / 8), c = idx % (kAbsCols / 8);
       if (d < Dn) *reinterpret_cast<i16x8*>(wt + d * kAbsPitch + c * 16) = wv[j];
     }
-    __syncthreads();
   }
+  store_q();
+  __syncthreads();
   // item blocks of 32 MT: one per workgroup for decode-sized batches, several
   // for prefill-sized ones (the staged W_UK block is reused)
-  for (int m0 = blockIdx.z * 32 * MT; m0 < Nq; m0 += gridDim.z * 32 * MT) {
-    // A fragments: q_nope rows of this wave's M tiles (all waves hold the same)
-    i16x8 af[MT][kAbsMaxDn / 16];
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int item = m0 + 32 * mt + n32;
-#pragma unroll
-      for (int k = 0; k < kAbsMaxDn / 16; ++k) {
-        i16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (k < ksteps && item < Nq)
-          v = *reinterpret_cast<const i16x8*>(q_nope + item * st + h * sh + 16 * k + 8 * g);
-        af[mt][k] = v;
-      }
-    }
+  for (int m0 = m_first; m0 < Nq; m0 += m_stride) {
     f32x16 acc[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x16{};
@@ -118,20 +138,41 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* __rest
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(i16x4))(base + 4 * kAbsPitch));
         const i16x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af[mt][k]),
+        for (int mt = 0; mt < MT; ++mt) {
+          const i16x8 af = *reinterpret_cast<const i16x8*>(qs + (32 * mt + n32) * kAbsQPitch + (16 * k + 8 * g) * 2);
+          acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, af),
                                                             __builtin_bit_cast(bf16x8, b), acc[mt],
                                                             0, 0, 0);
+        }
       }
     }
-    const int col = c0 + 32 * wave + n32;
+    const int m1 = m0 + m_stride;
+    if (m1 < Nq) load_q(m1);  // the next block's queries: in flight during the stores
+    __syncthreads();          // every wave has read its query fragments
+    // the output tile [32 MT items][128 columns] as bf16 rows in the query buffer
+    const int col = 32 * wave + n32;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int item = m0 + 32 * mt + 8 * (i >> 2) + 4 * g + (i & 3);
-        if (item < Nq) q_lat[(static_cast<int64_t>(item) * H + h) * R + col] = f32_to_bf16(acc[mt][i]);
+        const int r = 32 * mt + 8 * (i >> 2) + 4 * g + (i & 3);
+        *reinterpret_cast<uint16_t*>(qs + r * kAbsQPitch + col * 2) = f32_to_bf16(acc[mt][i]);
       }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 32 * MT * (kAbsCols / 8) / 256; ++j) {
+      const int idx = t + 256 * j;
+      const int r = idx / (kAbsCols / 8), c = idx % (kAbsCols / 8);
+      const int item = m0 + r;
+      if (item < Nq)
+        *reinterpret_cast<i16x8*>(q_lat + (static_cast<int64_t>(item) * H + h) * R + c0 + 8 * c) =
+            *reinterpret_cast<const i16x8*>(qs + r * kAbsQPitch + c * 16);
+    }
+    if (m1 < Nq) {
+      __syncthreads();  // the output tile has been read
+      store_q();
+      __syncthreads();
     }
   }
 }
