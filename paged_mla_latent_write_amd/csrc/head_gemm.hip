@@ -372,20 +372,22 @@ __global__ __launch_bounds__(kCupThreads) void combine_up_project_kernel(AttnArg
       }
     }
   }
-  __syncthreads();
-
-  // ---- phase 2: out[item, h, v] = W_UV[h][v] . o[item], wave w < 4: v in [32 w, 32 w + 32)
+  // ---- phase 2: out[item, h, v] = W_UV[h][v] . o[item], wave w < 4: v in [32 w, 32 w + 32).
+  // Its W_UV fragments are requested before the barrier, so their latency
+  // overlaps the other waves' merging.
   const int lane = t & 63, wave = t >> 6;
   const int g = lane >> 5, n32 = lane & 31;
   const int v = 32 * wave + n32;
-  if (32 * wave >= Dv) return;
+  const bool up_wave = 32 * wave < Dv;
   i16x8 b[kCupMaxR / 16];
-  {
+  if (up_wave) {
     const uint16_t* wrow = w_uv + (static_cast<int64_t>(h) * Dv + v) * R;
 #pragma unroll
     for (int u = 0; u < kCupMaxR / 16; ++u)
       if (16 * u < R) b[u] = *reinterpret_cast<const i16x8*>(wrow + 16 * u + 8 * g);
   }
+  __syncthreads();
+  if (!up_wave) return;
   f32x16 acc = f32x16{};
 #pragma unroll
   for (int u = 0; u < kCupMaxR / 16; ++u) {
