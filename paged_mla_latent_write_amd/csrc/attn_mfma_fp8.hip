@@ -20,9 +20,12 @@
 //  * one step later the whole workgroup converts the staged codes once into a
 //    bf16 tile (the layout and swizzle of the bf16 kernel's tiles), so the
 //    four waves do not each convert the keys they all read.
-//  * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16 exactly as
-//    in the bf16 kernel's first form (compiler-scheduled): Q in VGPRs, the
-//    512 x 32 accumulator in AGPRs, V^T read with ds_read_b64_tr_b16.
+//  * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16 as two
+//    hand-scheduled blocks per tile (attn_mfma_fp8_asm.inc, generated): K and
+//    V^T fragments (ds_read_b128, ds_read_b64_tr_b16) stream through a ring of
+//    registers a few MFMAs ahead, Q and the 512 x 32 accumulator sit in the
+//    registers the bf16 kernel reserves for them (the compiler is limited to
+//    the rest); the scales and the softmax run in C++ between the blocks.
 //  * online softmax in base 2 against a reference maximum fixed by each
 //    segment's first tile, so the accumulators are never rescaled (a rescale
 //    of the compiler-held accumulators does not fit the register file beside
@@ -36,6 +39,12 @@
 
 namespace mla {
 namespace {
+
+// Q (v62-v205), the accumulators (a0-a255) and the register ring: load_q,
+// zero_q and store_acc from the bf16 kernel's blocks, and the fp8 kernel's own
+// scores and values blocks
+#include "attn_mfma_asm.inc"
+#include "attn_mfma_fp8_asm.inc"
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -101,7 +110,12 @@ __device__ __forceinline__ int advance_item(const Meta& m, int num_items, int it
 // Tokens outside the visible range load a clamped (valid) token's codes; their
 // scores are masked and their scales zeroed before use.
 __device__ __forceinline__ void copy_tile(const AttnArgs& a, const Meta& m, int item, int64_t tile,
-                                          uint32_t stage, int wave, int lane) {
+                                          uint32_t stage, int wave, int lane_in) {
+  // (an opaque copy of the lane index: the per-lane address arithmetic below is
+  // then recomputed per tile rather than hoisted out of the tile loop, where it
+  // would hold ~15 registers)
+  int lane = lane_in;
+  asm volatile("" : "+v"(lane));
   const int b = m.item_b[item];
   const int vlo = m.item_lo[item], vhi = m.item_hi[item];
   const int tok0 = ((vlo >> 5) + static_cast<int>(tile - m.tile_start[item])) * kTile;
@@ -154,7 +168,9 @@ __device__ __forceinline__ void copy_tile(const AttnArgs& a, const Meta& m, int 
 // values, chunk j at slot (j & ~7) | ((j & 7) ^ swz(t))).  Thread i handles
 // 16-code chunks i, i + 256, ...
 __device__ __forceinline__ void convert_tile(LDS_PTR(const char) stage, LDS_PTR(char) tile) {
-  for (int c = threadIdx.x; c < kCodeChunks; c += 256) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));  // (not hoisted out of the tile loop, as in copy_tile)
+  for (int c = tid; c < kCodeChunks; c += 256) {
     const int t = c / 36, m2 = c - 36 * (c / 36);
     const i32x4 v = *reinterpret_cast<LDS_PTR(const i32x4)>(stage + 16 * c);
     bf16x8 lo, hi;
@@ -174,7 +190,7 @@ __device__ __forceinline__ void convert_tile(LDS_PTR(const char) stage, LDS_PTR(
   }
 }
 
-__global__ __launch_bounds__(256, 1) void attn_mfma_fp8_kernel(
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(kCompilerVgprs))) void attn_mfma_fp8_kernel(
     AttnArgs a, const int32_t* __restrict__ item_b, const int32_t* __restrict__ item_lo,
     const int32_t* __restrict__ item_hi, const int32_t* __restrict__ tile_start,
     const int32_t* __restrict__ block_tables) {
@@ -241,8 +257,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_fp8_kernel(
   __syncthreads();
   convert_tile(stages[0], tiles[0]);
 
-  bf16x8 qf[kKSteps];
-  f32x16 acc[kMTiles];
+  zero_q();  // lanes of heads >= H keep zero queries
 
   int tn = 0;
   int c_item = first_item;
@@ -252,23 +267,10 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_fp8_kernel(
     const int64_t item_ts = m.tile_start[c_item], item_te = m.tile_start[c_item + 1];
     const int64_t seg_begin = ctile;
     const int64_t seg_end = item_te < t1 ? item_te : t1;
-    if (wave_active) {
-      const uint16_t* ql = a.q_lat + c_item * a.q_lat_st + head * a.q_lat_sh;
-      const uint16_t* qp = a.q_pe + c_item * a.q_pe_st + head * a.q_pe_sh;
-#pragma unroll
-      for (int k = 0; k < kKSteps; ++k) {
-        i16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (head_ok) {
-          const uint16_t* src = k < kR / 16 ? ql + 16 * k + 8 * g : qp + 16 * (k - kR / 16) + 8 * g;
-          v = *reinterpret_cast<const i16x8*>(src);
-        }
-        qf[k] = __builtin_bit_cast(bf16x8, v);
-      }
-#pragma unroll
-      for (int mt = 0; mt < kMTiles; ++mt) acc[mt] = f32x16{};
-#pragma unroll
-      for (int k = 0; k < kKSteps; ++k) asm volatile("" : "+v"(qf[k]));
-    }
+    // the item's queries (waits for every copy in flight too)
+    if (wave_active && head_ok)
+      load_q(a.q_lat + c_item * a.q_lat_st + head * a.q_lat_sh + 8 * g,
+             a.q_pe + c_item * a.q_pe_st + head * a.q_pe_sh + 8 * g);
     float m_ref = 0.f, l_sum = 0.f;
     const int vlo = m.item_lo[c_item], vhi = m.item_hi[c_item];
     const int tok_first = ((vlo >> 5) + static_cast<int>(seg_begin - item_ts)) * kTile;
@@ -285,16 +287,13 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_fp8_kernel(
       const int tok0 = tok_first + static_cast<int>(tt - seg_begin) * kTile;
 
       if (wave_active) {
-        f32x16 s = {};
-#pragma unroll
-        for (int k = 0; k < kKSteps; ++k) {
-          const int off = koff[k & 3] + ((2 * k) & ~7) * 16;
-          const i16x8 kv = *reinterpret_cast<LDS_PTR(const i16x8)>(buf + off);
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), qf[k], s, 0, 0, 0);
-        }
+        const uint32_t bbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(buf));
+        const uint32_t kcur[4] = {bbase + static_cast<uint32_t>(koff[0]), bbase + static_cast<uint32_t>(koff[1]),
+                                  bbase + static_cast<uint32_t>(koff[2]), bbase + static_cast<uint32_t>(koff[3])};
+        float s[16];
+        fp8_scores(kcur, s);
         // per-token scale (zero for tokens outside the visible range, whose
         // staged scale may be anything), mask, scale to log2 units
-        float st[16];
         float tmax = -INFINITY;
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
@@ -304,8 +303,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_fp8_kernel(
             const int i = 4 * i4 + e;
             const int tok = tok0 + 8 * i4 + 4 * g + e;
             const bool vis = tok >= vlo && tok < vhi;
-            st[i] = vis ? sv[e] : 0.f;
-            const float v = vis ? s[i] * st[i] * a.scale_log2 : -INFINITY;
+            const float v = vis ? s[i] * sv[e] * a.scale_log2 : -INFINITY;
             s[i] = v;
             tmax = fmaxf(tmax, v);
           }
@@ -313,28 +311,33 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_fp8_kernel(
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
         if (tt == seg_begin) m_ref = tmax;
         else if (tmax > m_ref + kSlack) overflow = true;
-        bf16x8 pb[2];
+        // P * s_t as bf16 pairs (element i of the lane's 16 is the low half
+        // of pair i / 2 when i is even), the B operand of the values MFMAs;
+        // the scales are read again rather than held across the exponentials
+        uint32_t pb[8];
         float psum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = __builtin_amdgcn_exp2f(s[i] - m_ref);
-          psum += p;
-          pb[i >> 3][i & 7] = static_cast<__bf16>(p * st[i]);
-        }
-        l_sum += psum;
-
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 sv = *reinterpret_cast<LDS_PTR(const f32x4)>(scl + 8 * i4 + 4 * g);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-#pragma unroll
-          for (int mt = 0; mt < kMTiles; ++mt) {
-            const int lo_off = ((mt & 1) ? voff_odd : voff_even) + 128 * (mt >> 1) + kRowBytes * 16 * j;
-            const int hi_off = ((mt & 1) ? voff_odd_h : voff_even_h) + 128 * (mt >> 1) + kRowBytes * 16 * j;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<LDS_PTR(i16x4)>(buf + lo_off));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<LDS_PTR(i16x4)>(buf + hi_off));
-            const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            acc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), pb[j], acc[mt], 0, 0, 0);
+          for (int e = 0; e < 4; e += 2) {
+            const int i = 4 * i4 + e;
+            const int tok = tok0 + 8 * i4 + 4 * g + e;
+            const float s0 = (tok >= vlo && tok < vhi) ? sv[e] : 0.f;
+            const float s1 = (tok + 1 >= vlo && tok + 1 < vhi) ? sv[e + 1] : 0.f;
+            const float p0 = __builtin_amdgcn_exp2f(s[i] - m_ref);
+            const float p1 = __builtin_amdgcn_exp2f(s[i + 1] - m_ref);
+            psum += p0 + p1;
+            pb[i >> 1] = static_cast<uint32_t>(f32_to_bf16(p0 * s0)) |
+                         (static_cast<uint32_t>(f32_to_bf16(p1 * s1)) << 16);
           }
         }
+        l_sum += psum;
+        const uint32_t vcur[4] = {bbase + static_cast<uint32_t>(voff_even), bbase + static_cast<uint32_t>(voff_odd),
+                                  bbase + static_cast<uint32_t>(voff_even_h),
+                                  bbase + static_cast<uint32_t>(voff_odd_h)};
+        if (tt == seg_begin) fp8_values_f1(vcur, pb);
+        else fp8_values_f0(vcur, pb);
       }
     }
     ctile = seg_end;
@@ -356,15 +359,7 @@ __global__ __launch_bounds__(256, 1) void attn_mfma_fp8_kernel(
       scl_dst = a.part_scale + slot * a.H;
     }
     if (wave_active && head_ok) {
-      float* orow = o_dst + static_cast<int64_t>(head) * kR;
-#pragma unroll
-      for (int mt = 0; mt < kMTiles; ++mt) {
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          const f32x4 v = {acc[mt][4 * a4 + 0], acc[mt][4 * a4 + 1], acc[mt][4 * a4 + 2], acc[mt][4 * a4 + 3]};
-          *reinterpret_cast<f32x4*>(orow + 32 * mt + 8 * a4 + 4 * g) = v;
-        }
-      }
+      store_acc(o_dst + static_cast<int64_t>(head) * kR + 4 * g);
       if (g == 0) {
         lse_dst[head] = (m_ref + log2f(l_tot)) * kLn2;
         scl_dst[head] = 1.0f / l_tot;

@@ -2,6 +2,7 @@
 attention kernel (attn_mfma.hip).
 
     python gen_attn_mfma_asm.py > attn_mfma_asm.inc
+    python gen_attn_mfma_asm.py --fp8 > attn_mfma_fp8_asm.inc
 
 Register plan.  The kernel limits the compiler to v0..v{NC-1} (attribute
 amdgpu_num_vgpr), so every register above is reserved and keeps its value from
@@ -607,5 +608,52 @@ def pv_rest(st, first_pv, p_regs, vregs):
             v_reads(st, i + NF, vregs)
 
 
+def emit_fp8():
+    """The matrix-core steps of the fp8-cache kernel (attn_mfma_fp8.hip), which
+    converts each tile to bf16 in LDS first (the bf16 kernel's layout): the
+    scores and the values of one tile as two blocks, each with its LDS
+    fragments pipelined through the ring as in the blocks above; the per-token
+    scales and the softmax stay in the kernel's C++ between them.  Q and the
+    accumulators use the registers of the blocks above (load_q, zero_q and
+    store_acc come from attn_mfma_asm.inc)."""
+    o = ["// Generated by gen_attn_mfma_asm.py --fp8; do not edit by hand.", ""]
+    # scores S^T = K Q^T of the tile whose bf16 rows are at %[k0..k3] (this
+    # lane's K row offsets plus the buffer base); the 16 results leave in s[]
+    st = Stream()
+    for i in range(NF):
+        k_read(st, i)
+    for k in range(36):
+        st.wait_pair("K", k, 36)
+        st.add(f"v_mfma_f32_32x32x16_bf16 {s_chain(k)}, {ring4(k)}, {q(k)}, {'0' if k == 0 else s_chain(k)}")
+        if k + NF < 36:
+            k_read(st, k + NF)
+    st.add("s_nop 7", "s_nop 7", "s_nop 4")  # the last MFMA's results must have landed
+    st.add(*[f"v_mov_b32 %[s{i}], v{SS + i}" for i in range(16)])
+    outs = [", ".join(f'[s{i}] "=v"(s[{i}])' for i in range(16))]
+    o += block("fp8_scores", ["const uint32_t (&kcur)[4]", "float (&s)[16]"], st.lines, outs,
+               ['[k0] "v"(kcur[0]), [k1] "v"(kcur[1]), [k2] "v"(kcur[2]), [k3] "v"(kcur[3])'])
+    # values O^T += V^T P^T of the same tile (%[v0..v3]: this lane's transposed
+    # read offsets plus the buffer base; P as eight registers of bf16 pairs);
+    # f1: the segment's first tile, whose MFMAs start the accumulators at zero
+    for first in (0, 1):
+        st = Stream()
+        st.add(*[f"v_mov_b32 v{P_BASE + j}, %[p{j}]" for j in range(8)])
+        st.add("s_nop 1")  # P written by VALU just before the MFMAs read it
+        for i in range(NF):
+            v_reads(st, i)
+        for i in range(32):
+            mt, j = PV_ORDER[i]
+            st.wait_pair("V", i, 32)
+            src_c = "0" if (first and j == 0) else acc(mt)
+            st.add(f"v_mfma_f32_32x32x16_bf16 {acc(mt)}, {vring4(i)}, {P_FIXED[j]}, {src_c}")
+            if i + NF < 32:
+                v_reads(st, i + NF)
+        ins = ['[v0] "v"(vcur[0]), [v1] "v"(vcur[1]), [v2] "v"(vcur[2]), [v3] "v"(vcur[3])',
+               ", ".join(f'[p{j}] "v"(p[{j}])' for j in range(8))]
+        o += block(f"fp8_values_f{first}", ["const uint32_t (&vcur)[4]", "const uint32_t (&p)[8]"], st.lines,
+                   [], ins)
+    return "\n".join(o)
+
+
 if __name__ == "__main__":
-    sys.stdout.write(emit() + "\n")
+    sys.stdout.write((emit_fp8() if "--fp8" in sys.argv[1:] else emit()) + "\n")

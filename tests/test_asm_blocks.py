@@ -23,6 +23,17 @@ def test_include_matches_generator():
     assert out == (CSRC / "attn_mfma_asm.inc").read_text()
 
 
+def test_fp8_include_matches_generator():
+    out = subprocess.run([sys.executable, str(CSRC / "gen_attn_mfma_asm.py"), "--fp8"], capture_output=True,
+                         text=True, check=True).stdout
+    assert out == (CSRC / "attn_mfma_fp8_asm.inc").read_text()
+
+
+def test_fp8_blocks_wait_for_their_lds_reads():
+    n, problems = _load("check_attn_mfma_asm").check((CSRC / "attn_mfma_fp8_asm.inc").read_text())
+    assert n == 3 and not problems, problems[:5]
+
+
 def test_blocks_wait_for_their_lds_reads():
     n, problems = _load("check_attn_mfma_asm").check((CSRC / "attn_mfma_asm.inc").read_text())
     assert n > 10 and not problems, problems[:5]
