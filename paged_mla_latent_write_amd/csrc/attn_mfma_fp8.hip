@@ -292,44 +292,52 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(kCompilerVgp
                                   bbase + static_cast<uint32_t>(koff[2]), bbase + static_cast<uint32_t>(koff[3])};
         float s[16];
         fp8_scores(kcur, s);
-        // per-token scale (zero for tokens outside the visible range, whose
-        // staged scale may be anything), mask, scale to log2 units
+        // per-token scale, mask, scale to log2 units; P * s_t as bf16 pairs
+        // (element i of the lane's 16 is the low half of pair i / 2 when i is
+        // even), the B operand of the values MFMAs.  The scales are read again
+        // rather than held across the exponentials.  Tokens outside the
+        // visible range (only in a tile that is not wholly inside it) get a
+        // score of -inf and a scale of zero: their staged scale may be anything.
+        const bool partial = !(tok0 >= vlo && tok0 + kTile <= vhi);  // uniform
         float tmax = -INFINITY;
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const f32x4 sv = *reinterpret_cast<LDS_PTR(const f32x4)>(scl + 8 * i4 + 4 * g);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * i4 + e;
-            const int tok = tok0 + 8 * i4 + 4 * g + e;
-            const bool vis = tok >= vlo && tok < vhi;
-            const float v = vis ? s[i] * sv[e] * a.scale_log2 : -INFINITY;
-            s[i] = v;
-            tmax = fmaxf(tmax, v);
+          for (int e = 0; e < 4; ++e) s[4 * i4 + e] *= sv[e] * a.scale_log2;
+        }
+        if (partial) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int tok = tok0 + 8 * (i >> 2) + 4 * g + (i & 3);
+            if (tok < vlo || tok >= vhi) s[i] = -INFINITY;
           }
         }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[i]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
         if (tt == seg_begin) m_ref = tmax;
         else if (tmax > m_ref + kSlack) overflow = true;
-        // P * s_t as bf16 pairs (element i of the lane's 16 is the low half
-        // of pair i / 2 when i is even), the B operand of the values MFMAs;
-        // the scales are read again rather than held across the exponentials
         uint32_t pb[8];
         float psum = 0.f;
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-          const f32x4 sv = *reinterpret_cast<LDS_PTR(const f32x4)>(scl + 8 * i4 + 4 * g);
+          f32x4 sv = *reinterpret_cast<LDS_PTR(const f32x4)>(scl + 8 * i4 + 4 * g);
+          if (partial) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int tok = tok0 + 8 * i4 + 4 * g + e;
+              if (tok < vlo || tok >= vhi) sv[e] = 0.f;
+            }
+          }
 #pragma unroll
           for (int e = 0; e < 4; e += 2) {
             const int i = 4 * i4 + e;
-            const int tok = tok0 + 8 * i4 + 4 * g + e;
-            const float s0 = (tok >= vlo && tok < vhi) ? sv[e] : 0.f;
-            const float s1 = (tok + 1 >= vlo && tok + 1 < vhi) ? sv[e + 1] : 0.f;
             const float p0 = __builtin_amdgcn_exp2f(s[i] - m_ref);
             const float p1 = __builtin_amdgcn_exp2f(s[i + 1] - m_ref);
             psum += p0 + p1;
-            pb[i >> 1] = static_cast<uint32_t>(f32_to_bf16(p0 * s0)) |
-                         (static_cast<uint32_t>(f32_to_bf16(p1 * s1)) << 16);
+            const bf16x2 pk = {static_cast<__bf16>(p0 * sv[e]), static_cast<__bf16>(p1 * sv[e + 1])};  // RNE
+            pb[i >> 1] = __builtin_bit_cast(uint32_t, pk);
           }
         }
         l_sum += psum;

@@ -4,6 +4,8 @@ LDS read consumed before it landed, no ring slot overwritten too early and
 no scalar load left unwaited at the end of a block."""
 import importlib.util
 import subprocess
+
+import pytest
 import sys
 from pathlib import Path
 
@@ -73,3 +75,48 @@ def test_checker_follows_reads_across_the_loop_back_edge():
     planted = text[:start] + body[:w] + "s_waitcnt lgkmcnt(9)" + body[body.index(")", w) + 1:] + text[end:]
     n, problems = _load("check_attn_mfma_asm").check(planted)
     assert any("tile_hot_loop: MFMA before its LDS read landed" in p for p in problems)
+
+
+def _compiler_registers(src):
+    """Highest VGPR index and number of AGPR references in the compiler's own
+    code (outside the inline-assembly blocks) of one kernel source."""
+    import re
+    import shutil
+    import tempfile
+
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    with tempfile.TemporaryDirectory() as d:
+        out = Path(d) / "k.s"
+        subprocess.run([hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
+                        "-Xclang", "-packed-fp32-ops", "-I", str(CSRC), "-I", str(CSRC.parents[1] / "include"),
+                        "-x", "hip", "--cuda-device-only", "-S", str(CSRC / src), "-o", str(out)],
+                       check=True, capture_output=True)
+        text = out.read_text()
+    top, agprs, in_asm = -1, 0, False
+    for ln in text.splitlines():
+        if ";;#ASMSTART" in ln:
+            in_asm = True
+        elif ";;#ASMEND" in ln:
+            in_asm = False
+        elif not in_asm and ln.startswith("\t") and not ln.startswith("\t."):
+            for m in re.finditer(r"\bv(\d+)\b|v\[(\d+):(\d+)\]", ln):
+                top = max(top, int(m.group(1) or m.group(3)))
+            agprs += len(re.findall(r"\ba(\d+)\b|a\[\d+:\d+\]", ln))
+    return top, agprs
+
+
+@pytest.mark.parametrize("src", ["attn_mfma.hip", "attn_mfma_fp8.hip"])
+def test_compiler_code_leaves_reserved_registers_alone(src):
+    """The queries, scores, ring and accumulators live in registers the blocks
+    own from one block to the next.  amdgpu_num_vgpr only steers the compiler
+    (under pressure it goes past it), so the compiled kernel is checked: its
+    own code may use the registers of the previous tile's P (each block that
+    reads them writes them first) but nothing from the queries up."""
+    import shutil
+
+    if not (shutil.which("hipcc") or Path("/opt/rocm/bin/hipcc").exists()):
+        pytest.skip("hipcc not available")
+    gen = _load("gen_attn_mfma_asm")
+    top, agprs = _compiler_registers(src)
+    assert top < gen.Q_BASE, f"{src}: compiler code uses v{top} (queries start at v{gen.Q_BASE})"
+    assert agprs == 0, f"{src}: compiler code references accumulator registers"
