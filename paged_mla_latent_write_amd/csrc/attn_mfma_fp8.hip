@@ -198,6 +198,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(kCompilerVgp
                (CONST_PTR(int32_t))tile_start, (CONST_PTR(int32_t))block_tables};
   __shared__ __attribute__((aligned(1024))) char lds_tile[2][kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_stage[4][kStageBytes];
+  // this thread's five conversion chunks (see convert_tile): entry j holds the
+  // two 16-byte destinations of chunk tid + 256 j in a bf16 tile (low and high
+  // 16 bits); a thread with no fifth chunk repeats its fourth
+  __shared__ __attribute__((aligned(16))) uint32_t conv_tab[256][8];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -256,6 +260,19 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(kCompilerVgp
   else wait_vmcnt<0>();
   __syncthreads();
   convert_tile(stages[0], tiles[0]);
+  {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      int c = tid + 256 * j;
+      if (c >= kCodeChunks) c -= 256;
+      const int t = c / 36, m2 = c - 36 * (c / 36);
+      const int j0 = 2 * m2, j1 = 2 * m2 + 1;
+      const int p0 = (j0 & ~7) | ((j0 & 7) ^ swz(t)), p1 = (j1 & ~7) | ((j1 & 7) ^ swz(t));
+      conv_tab[tid][j] = static_cast<uint32_t>(t * kRowBytes + 16 * p0) |
+                         (static_cast<uint32_t>(t * kRowBytes + 16 * p1) << 16);
+    }
+  }
 
   zero_q();  // lanes of heads >= H keep zero queries
 
@@ -281,7 +298,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(kCompilerVgp
       else wait_vmcnt<0>();
       __syncthreads();  // tile tn + 1 staged; tile tn converted; buffers of tn - 1 free
       if (tn + 3 < ntiles) copy_next(tn + 3);
-      if (tn + 1 < ntiles) convert_tile(stages[(tn + 1) & 3], tiles[(tn + 1) & 1]);
+      // the next tile's conversion: inside this tile's values step (below)
+      // in the waves that compute, here in the others
+      const bool conv_next = tn + 1 < ntiles;
+      if (conv_next && !wave_active) convert_tile(stages[(tn + 1) & 3], tiles[(tn + 1) & 1]);
       LDS_PTR(char) buf = tiles[tn & 1];
       LDS_PTR(const float) scl = (LDS_PTR(const float))(stages[tn & 3] + kCodeBytes);
       const int tok0 = tok_first + static_cast<int>(tt - seg_begin) * kTile;
@@ -344,8 +364,19 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(kCompilerVgp
         const uint32_t vcur[4] = {bbase + static_cast<uint32_t>(voff_even), bbase + static_cast<uint32_t>(voff_odd),
                                   bbase + static_cast<uint32_t>(voff_even_h),
                                   bbase + static_cast<uint32_t>(voff_odd_h)};
-        if (tt == seg_begin) fp8_values_f1(vcur, pb);
-        else fp8_values_f0(vcur, pb);
+        if (conv_next) {
+          const uint32_t tid = threadIdx.x;
+          const uint32_t cs = stage_addr(tn + 1) + 16 * tid;
+          const uint32_t cs4 = cs + (tid < kCodeChunks - 1024 ? 16384u : 12288u);
+          const uint32_t ct = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&conv_tab[0][0])) + 32 * tid;
+          const uint32_t tb = __builtin_amdgcn_readfirstlane(
+              static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tiles[(tn + 1) & 1])));
+          if (tt == seg_begin) fp8_values_conv_f1(vcur, pb, cs, cs4, ct, tb);
+          else fp8_values_conv_f0(vcur, pb, cs, cs4, ct, tb);
+        } else {
+          if (tt == seg_begin) fp8_values_f1(vcur, pb);
+          else fp8_values_f0(vcur, pb);
+        }
       }
     }
     ctile = seg_end;

@@ -652,6 +652,61 @@ def emit_fp8():
                ", ".join(f'[p{j}] "v"(p[{j}])' for j in range(8))]
         o += block(f"fp8_values_f{first}", ["const uint32_t (&vcur)[4]", "const uint32_t (&p)[8]"], st.lines,
                    [], ins)
+    # the same values step with the next tile's conversion interleaved: this
+    # lane's five 16-code chunks of the staged tile (%[cs] + 4096 j, the fifth
+    # at %[cs4]) become bf16 rows of the next tile buffer (%[tb] plus the two
+    # 16-bit offsets of the lane's entry j in the table at %[ct]).  The score
+    # and P registers are free during the values step and hold the table
+    # entries (v208-v215), two code buffers (v216-v223) and the converted
+    # values (v224-v231); the block waits for its LDS writes before it ends,
+    # since the caller's barrier publishes the converted tile.
+    D, C, OUT = SS, SS + 8, PN
+    CONV_AT = [3, 9, 15, 21, 26]  # the MFMA after which chunk j is converted
+    for first in (0, 1):
+        st = Stream()
+        st.add(*[f"v_mov_b32 v{P_BASE + j}, %[p{j}]" for j in range(8)])
+        st.lds(f"ds_read_b128 v[{D}:{D + 3}], %[ct] offset:0", ("D", 0))
+        st.lds(f"ds_read_b128 v[{D + 4}:{D + 7}], %[ct] offset:16", ("D", 1))
+
+        def code_read(j):
+            b = C + 4 * (j % 2)
+            src = "%[cs4] offset:0" if j == 4 else f"%[cs] offset:{4096 * j}"
+            st.lds(f"ds_read_b128 v[{b}:{b + 3}], {src}", ("C", j))
+
+        code_read(0)
+        code_read(1)
+        for i in range(NF):
+            v_reads(st, i)
+        for i in range(32):
+            mt, j = PV_ORDER[i]
+            st.wait_pair("V", i, 32)
+            src_c = "0" if (first and j == 0) else acc(mt)
+            st.add(f"v_mfma_f32_32x32x16_bf16 {acc(mt)}, {vring4(i)}, {P_FIXED[j]}, {src_c}")
+            if i + NF < 32:
+                v_reads(st, i + NF)
+            if i in CONV_AT:
+                c = CONV_AT.index(i)
+                b = C + 4 * (c % 2)
+                st.wait_for(("C", c))
+                st.wait_for(("D", 1 if c >= 4 else 0))
+                if c > 0:
+                    st.wait_for(("W", c - 1))  # its writes have read OUT, T0 and T1
+                for k in range(4):
+                    st.add(f"v_cvt_scalef32_pk_bf16_fp8 v{OUT + 2 * k}, v{b + k}, 1.0",
+                           f"v_cvt_scalef32_pk_bf16_fp8 v{OUT + 2 * k + 1}, v{b + k}, 1.0 op_sel:[1,0,0]")
+                if c + 2 <= 4:
+                    code_read(c + 2)  # into the buffer the conversions just read
+                st.add(f"v_and_b32 v{T0}, 0xffff, v{D + c}", f"v_add_u32 v{T0}, %[tb], v{T0}",
+                       f"v_lshrrev_b32 v{T1}, 16, v{D + c}", f"v_add_u32 v{T1}, %[tb], v{T1}")
+                st.lds(f"ds_write_b128 v{T0}, v[{OUT}:{OUT + 3}]", ("W", c))
+                st.lds(f"ds_write_b128 v{T1}, v[{OUT + 4}:{OUT + 7}]", ("W", c))
+        st.wait_all()
+        ins = ['[v0] "v"(vcur[0]), [v1] "v"(vcur[1]), [v2] "v"(vcur[2]), [v3] "v"(vcur[3])',
+               ", ".join(f'[p{j}] "v"(p[{j}])' for j in range(8)),
+               '[cs] "v"(cs), [cs4] "v"(cs4), [ct] "v"(ct), [tb] "s"(tb)']
+        o += block(f"fp8_values_conv_f{first}",
+                   ["const uint32_t (&vcur)[4]", "const uint32_t (&p)[8]", "uint32_t cs", "uint32_t cs4",
+                    "uint32_t ct", "uint32_t tb"], st.lines, [], ins)
     return "\n".join(o)
 
 
