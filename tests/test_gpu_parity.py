@@ -267,6 +267,20 @@ def test_decode_fp8_mfma_window(mla, window):
     check_decode(mla, case, label=f" w={window}")
 
 
+@pytest.mark.parametrize("kv", [O.KV_BF16, O.KV_FP8])
+@pytest.mark.parametrize("H", [40, 100])
+def test_decode_mfma_partly_filled_waves(mla, kv, H):
+    """Head counts that leave a wave partly filled (its lanes past H hold zero
+    queries and store nothing) and, for 40 heads, whole waves without heads,
+    which still copy -- and on the fp8 path convert -- their share of every
+    tile; ragged contexts, sharp queries, one and several workgroups."""
+    say(f"decode mfma H={H} {kv}")
+    d = W.Dims(H=H, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
+    case = W.custom(d, [1, 33, 700, 2049], seed=750 + H, kv_dtype=kv, sharp=True)
+    check_decode(mla, case, label=f" H={H}")
+    check_decode(mla, case, num_workgroups=5, label=f" H={H} G=5")
+
+
 @pytest.mark.parametrize("G", [1, 2])
 def test_decode_fp8_score_jump_is_recomputed(mla, G):
     """fp8 cache: a key whose score passes its segment's first-tile maximum by
