@@ -19,7 +19,10 @@
 //    (18 of codes, one of scales that waves 2 and 3 both issue).
 //  * one step later the whole workgroup converts the staged codes once into a
 //    bf16 tile (the layout and swizzle of the bf16 kernel's tiles), so the
-//    four waves do not each convert the keys they all read.
+//    four waves do not each convert the keys they all read.  Two bf16 tiles
+//    alternate: tile t + 1 is converted during tile t's values step, between
+//    its MFMAs (each lane its five 16-code chunks, destinations from a table
+//    in LDS), and published by the barrier that starts step t + 1.
 //  * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16 as two
 //    hand-scheduled blocks per tile (attn_mfma_fp8_asm.inc, generated): K and
 //    V^T fragments (ds_read_b128, ds_read_b64_tr_b16) stream through a ring of
@@ -27,11 +30,10 @@
 //    registers the bf16 kernel reserves for them (the compiler is limited to
 //    the rest); the scales and the softmax run in C++ between the blocks.
 //  * online softmax in base 2 against a reference maximum fixed by each
-//    segment's first tile, so the accumulators are never rescaled (a rescale
-//    of the compiler-held accumulators does not fit the register file beside
-//    Q).  Probabilities up to 2^64 stay far inside fp32; a score beyond that
-//    flags the workgroup, whose range the generic kernel then recomputes
-//    exactly (redo).
+//    segment's first tile, so the accumulators are never rescaled (the blocks
+//    hold no rescale step).  Probabilities up to 2^64 stay far inside fp32; a
+//    score beyond that flags the workgroup, whose range the generic kernel
+//    then recomputes exactly (redo).
 #include <math.h>
 
 #include "device_utils.h"
@@ -62,8 +64,6 @@ constexpr int kCodeRow = kD;                   // 576: one fp8 row
 constexpr int kCodeBytes = kTile * kCodeRow;   // 18432
 constexpr int kStageBytes = kCodeBytes + 4 * kTile;  // codes + 32 fp32 scales
 constexpr int kCodeChunks = kCodeBytes / 16;   // 1152 16-byte chunks
-constexpr int kKSteps = kD / 16;               // 36
-constexpr int kMTiles = kR / 32;               // 16
 constexpr int kCopies = 5;                     // copy instructions per wave per tile
 constexpr float kSlack = 64.0f;                // reference slack (log2 units)
 
