@@ -262,8 +262,12 @@ constexpr int kCupMaxR = 512;
 constexpr int kCupPitch = kCupMaxR + 8;  // bf16 per staged row (16 B pad: bank spread)
 
 constexpr int kCupThreads = 512;
-constexpr int kCupSegBatch = 4;  // partial rows of one item loaded together
 
+// SB: partial rows of one item loaded together.  SB = 1 is the low-register
+// form for large item counts (prefill): phase 2 then loads its W_UV fragments
+// eight k-steps at a time instead of all before the barrier, so that two
+// workgroups fit on a compute unit.
+template <int SB>
 __global__ __launch_bounds__(kCupThreads) void combine_up_project_kernel(AttnArgs a,
                                                                          const uint16_t* __restrict__ w_uv,
                                                                          int32_t Dv, uint16_t* __restrict__ out) {
@@ -304,11 +308,11 @@ __global__ __launch_bounds__(kCupThreads) void combine_up_project_kernel(AttnArg
         m = 0.f;
         tot = 1.f;
       } else if (g0 >= 0) {
-        for (int gb = g0; gb <= g1; gb += kCupSegBatch) {
-          float l[kCupSegBatch], sc[kCupSegBatch];
-          float4 x[kCupSegBatch][kE];
+        for (int gb = g0; gb <= g1; gb += SB) {
+          float l[SB], sc[SB];
+          float4 x[SB][kE];
 #pragma unroll
-          for (int p = 0; p < kCupSegBatch; ++p) {
+          for (int p = 0; p < SB; ++p) {
             const int gg = gb + p;
             const bool in = gg <= g1;
             // A workgroup range of the item with no tiles wrote no slot: its
@@ -327,7 +331,7 @@ __global__ __launch_bounds__(kCupThreads) void combine_up_project_kernel(AttnArg
           }
           float mb = m;
 #pragma unroll
-          for (int p = 0; p < kCupSegBatch; ++p) mb = fmaxf(mb, l[p]);
+          for (int p = 0; p < SB; ++p) mb = fmaxf(mb, l[p]);
           if (mb > m) {  // uniform within the item's threads
             const float f = expf(m - mb);
             tot *= f;
@@ -336,7 +340,7 @@ __global__ __launch_bounds__(kCupThreads) void combine_up_project_kernel(AttnArg
             m = mb;
           }
 #pragma unroll
-          for (int p = 0; p < kCupSegBatch; ++p) {
+          for (int p = 0; p < SB; ++p) {
             if (l[p] == -INFINITY) continue;
             const float e_l = expf(l[p] - m);
             tot += e_l;
@@ -379,24 +383,34 @@ __global__ __launch_bounds__(kCupThreads) void combine_up_project_kernel(AttnArg
   const int g = lane >> 5, n32 = lane & 31;
   const int v = 32 * wave + n32;
   const bool up_wave = 32 * wave < Dv;
-  i16x8 b[kCupMaxR / 16];
-  if (up_wave) {
-    const uint16_t* wrow = w_uv + (static_cast<int64_t>(h) * Dv + v) * R;
+  const uint16_t* wrow = w_uv + (static_cast<int64_t>(h) * Dv + (up_wave ? v : 0)) * R;
+  constexpr int kPre = SB > 1 ? kCupMaxR / 16 : 8;  // fragments held at once
+  i16x8 b[kPre];
+  if (SB > 1 && up_wave) {
 #pragma unroll
-    for (int u = 0; u < kCupMaxR / 16; ++u)
+    for (int u = 0; u < kPre; ++u)
       if (16 * u < R) b[u] = *reinterpret_cast<const i16x8*>(wrow + 16 * u + 8 * g);
   }
   __syncthreads();
   if (!up_wave) return;
   f32x16 acc = f32x16{};
 #pragma unroll
-  for (int u = 0; u < kCupMaxR / 16; ++u) {
-    const int k = 16 * u;
-    if (k >= R) break;
-    const bf16x8 hi = *reinterpret_cast<const bf16x8*>(o_hi + n32 * kCupPitch + k + 8 * g);
-    const bf16x8 lo = *reinterpret_cast<const bf16x8*>(o_lo + n32 * kCupPitch + k + 8 * g);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, __builtin_bit_cast(bf16x8, b[u]), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, __builtin_bit_cast(bf16x8, b[u]), acc, 0, 0, 0);
+  for (int u0 = 0; u0 < kCupMaxR / 16; u0 += kPre) {
+    if (16 * u0 >= R) break;
+    if (SB == 1) {
+#pragma unroll
+      for (int u = 0; u < kPre; ++u)
+        if (16 * (u0 + u) < R) b[u] = *reinterpret_cast<const i16x8*>(wrow + 16 * (u0 + u) + 8 * g);
+    }
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int k = 16 * (u0 + u);
+      if (k >= R) break;
+      const bf16x8 hi = *reinterpret_cast<const bf16x8*>(o_hi + n32 * kCupPitch + k + 8 * g);
+      const bf16x8 lo = *reinterpret_cast<const bf16x8*>(o_lo + n32 * kCupPitch + k + 8 * g);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, __builtin_bit_cast(bf16x8, b[u]), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, __builtin_bit_cast(bf16x8, b[u]), acc, 0, 0, 0);
+    }
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -428,7 +442,10 @@ bool combine_up_project_supported(int32_t R, int32_t Dv) {
 hipError_t launch_combine_up_project(const AttnArgs& a, const uint16_t* w_uv, int32_t Dv, uint16_t* out,
                                      hipStream_t s) {
   const dim3 grid((a.num_items + 31) / 32, a.H);
-  hipLaunchKernelGGL(combine_up_project_kernel, grid, dim3(kCupThreads), 0, s, a, w_uv, Dv, out);
+  if (a.num_items > 256)  // prefill-sized: many workgroups, most items uncut
+    hipLaunchKernelGGL(combine_up_project_kernel<1>, grid, dim3(kCupThreads), 0, s, a, w_uv, Dv, out);
+  else
+    hipLaunchKernelGGL(combine_up_project_kernel<4>, grid, dim3(kCupThreads), 0, s, a, w_uv, Dv, out);
   return hipGetLastError();
 }
 
