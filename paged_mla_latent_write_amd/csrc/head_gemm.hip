@@ -384,32 +384,45 @@ __global__ __launch_bounds__(kCupThreads) void combine_up_project_kernel(AttnArg
   const int v = 32 * wave + n32;
   const bool up_wave = 32 * wave < Dv;
   const uint16_t* wrow = w_uv + (static_cast<int64_t>(h) * Dv + (up_wave ? v : 0)) * R;
-  constexpr int kPre = SB > 1 ? kCupMaxR / 16 : 8;  // fragments held at once
-  i16x8 b[kPre];
-  if (SB > 1 && up_wave) {
+  i16x8 b[SB > 1 ? kCupMaxR / 16 : 1];
+  if constexpr (SB > 1) {
+    if (up_wave) {
 #pragma unroll
-    for (int u = 0; u < kPre; ++u)
-      if (16 * u < R) b[u] = *reinterpret_cast<const i16x8*>(wrow + 16 * u + 8 * g);
+      for (int u = 0; u < kCupMaxR / 16; ++u)
+        if (16 * u < R) b[u] = *reinterpret_cast<const i16x8*>(wrow + 16 * u + 8 * g);
+    }
   }
   __syncthreads();
   if (!up_wave) return;
   f32x16 acc = f32x16{};
+  if constexpr (SB > 1) {
 #pragma unroll
-  for (int u0 = 0; u0 < kCupMaxR / 16; u0 += kPre) {
-    if (16 * u0 >= R) break;
-    if (SB == 1) {
-#pragma unroll
-      for (int u = 0; u < kPre; ++u)
-        if (16 * (u0 + u) < R) b[u] = *reinterpret_cast<const i16x8*>(wrow + 16 * (u0 + u) + 8 * g);
-    }
-#pragma unroll
-    for (int u = 0; u < kPre; ++u) {
-      const int k = 16 * (u0 + u);
+    for (int u = 0; u < kCupMaxR / 16; ++u) {
+      const int k = 16 * u;
       if (k >= R) break;
       const bf16x8 hi = *reinterpret_cast<const bf16x8*>(o_hi + n32 * kCupPitch + k + 8 * g);
       const bf16x8 lo = *reinterpret_cast<const bf16x8*>(o_lo + n32 * kCupPitch + k + 8 * g);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, __builtin_bit_cast(bf16x8, b[u]), acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, __builtin_bit_cast(bf16x8, b[u]), acc, 0, 0, 0);
+    }
+  } else {
+    // eight k-steps' fragments at a time
+#pragma unroll
+    for (int u0 = 0; u0 < kCupMaxR / 16; u0 += 8) {
+      if (16 * u0 >= R) break;
+      i16x8 bw[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (16 * (u0 + u) < R) bw[u] = *reinterpret_cast<const i16x8*>(wrow + 16 * (u0 + u) + 8 * g);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int k = 16 * (u0 + u);
+        if (k >= R) break;
+        const bf16x8 hi = *reinterpret_cast<const bf16x8*>(o_hi + n32 * kCupPitch + k + 8 * g);
+        const bf16x8 lo = *reinterpret_cast<const bf16x8*>(o_lo + n32 * kCupPitch + k + 8 * g);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, __builtin_bit_cast(bf16x8, bw[u]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, __builtin_bit_cast(bf16x8, bw[u]), acc, 0, 0, 0);
+      }
     }
   }
 #pragma unroll
