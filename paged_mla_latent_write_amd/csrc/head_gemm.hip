@@ -432,7 +432,7 @@ __global__ __launch_bounds__(kCupThreads) void combine_up_project_kernel(AttnArg
   }
 }
 
-int pick_mt(int Nq) { return Nq <= 32 ? 1 : (Nq <= 64 ? 2 : 4); }
+int pick_mt(int Nq) { return Nq <= 64 ? 1 : 4; }
 
 // The up-projection streams W_UV once per 32 * MT items; small batches take
 // one 32-item tile per workgroup so that the grid still covers the chip.
