@@ -124,3 +124,18 @@ def test_argument_validation_without_device():
     assert mla._combine(P(1), P(1), 2, 0, 4, 8, P(1), P(1), None) == mla.MLA_OK
     assert mla._combine(None, P(1), 2, 1, 4, 8, P(1), P(1), None) == mla.MLA_ERR_INVALID_ARGUMENT
     assert mla._combine(P(1), P(1), -1, 1, 4, 8, P(1), P(1), None) == mla.MLA_ERR_INVALID_ARGUMENT
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py runs on one GPU only; asking for more exits with a message
+    (before anything touches a GPU)."""
+    import json
+    import subprocess
+    import sys
+    from pathlib import Path
+
+    bench = Path(__file__).resolve().parents[1] / "bench.py"
+    r = subprocess.run([sys.executable, str(bench), "--gpus", "2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
