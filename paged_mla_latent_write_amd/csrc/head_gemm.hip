@@ -266,25 +266,30 @@ constexpr int kCupThreads = 512;
 // SB: partial rows of one item loaded together.  SB = 1 is the low-register
 // form for large item counts (prefill): phase 2 then loads its W_UV fragments
 // eight k-steps at a time instead of all before the barrier, so that two
-// workgroups fit on a compute unit.
-template <int SB>
+// workgroups fit on a compute unit.  IPW: items per workgroup, 32 or (grids
+// smaller than the chip: few heads and requests) 4, merged by 128 threads each
+// with up to SB = 16 segments per round trip; the up-projection's MFMA rows
+// past those items are computed and discarded.
+template <int SB, int IPW>
 __global__ __launch_bounds__(kCupThreads) void combine_up_project_kernel(AttnArgs a,
                                                                          const uint16_t* __restrict__ w_uv,
                                                                          int32_t Dv, uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) __bf16 o_hi[32 * kCupPitch];
   __shared__ __attribute__((aligned(16))) __bf16 o_lo[32 * kCupPitch];
   const int h = blockIdx.y;
-  const int m0 = blockIdx.x * 32;
+  const int m0 = blockIdx.x * IPW;
   const int H = a.H, R = a.kv.R, Nq = a.num_items;
+  constexpr int kTpi = kCupThreads / IPW;  // threads per item
   const int t = threadIdx.x;
 
-  // ---- phase 1: the 16 threads (il, j) of item m0 + il merge its columns
-  // 4 j + 64 e .. + 3: each load of the item's threads reads 256 contiguous
-  // bytes.  The rows of up to four segments are requested at once, as soon as
-  // the item's workgroup range is known, so most items take one round trip.
+  // ---- phase 1: the kTpi threads (il, j) of item m0 + il merge its columns
+  // 4 j + 4 kTpi e .. + 3: each load of the item's threads reads 16 kTpi
+  // contiguous bytes.  The rows of up to SB segments are requested at once, as
+  // soon as the item's workgroup range is known, so most items take one round
+  // trip.
   {
-    constexpr int kE = kCupMaxR / 64;
-    const int il = t >> 4, j = t & 15;
+    constexpr int kE = kCupMaxR / (4 * kTpi);  // float4 per thread per row
+    const int il = t / kTpi, j = t % kTpi;
     const int item = m0 + il;
     float4 acc[kE];
 #pragma unroll
@@ -299,7 +304,7 @@ __global__ __launch_bounds__(kCupThreads) void combine_up_project_kernel(AttnArg
         const float4* src = reinterpret_cast<const float4*>(a.o_lat + row * R);
 #pragma unroll
         for (int e = 0; e < kE; ++e) {
-          const int c = 4 * j + 64 * e;
+          const int c = 4 * j + 4 * kTpi * e;
           if (c < R) {
             const float4 x = src[c >> 2];
             acc[e] = make_float4(x.x * sc, x.y * sc, x.z * sc, x.w * sc);
@@ -324,7 +329,7 @@ __global__ __launch_bounds__(kCupThreads) void combine_up_project_kernel(AttnArg
             const float4* src = reinterpret_cast<const float4*>(a.part_o + (slot * H + h) * R);
 #pragma unroll
             for (int e = 0; e < kE; ++e) {
-              const int c = 4 * j + 64 * e;
+              const int c = 4 * j + 4 * kTpi * e;
               x[p][e] = (in && c < R) ? src[c >> 2] : make_float4(0.f, 0.f, 0.f, 0.f);
             }
             l[p] = live ? lp : -INFINITY;
@@ -362,7 +367,7 @@ __global__ __launch_bounds__(kCupThreads) void combine_up_project_kernel(AttnArg
     const float inv = tot > 0.f ? 1.f / tot : 0.f;
 #pragma unroll
     for (int e = 0; e < kE; ++e) {
-      const int c = 4 * j + 64 * e;
+      const int c = 4 * j + 4 * kTpi * e;
       if (c < R) {
         const float xs[4] = {acc[e].x * inv, acc[e].y * inv, acc[e].z * inv, acc[e].w * inv};
         bf16x4 hi, lo;
@@ -427,8 +432,9 @@ __global__ __launch_bounds__(kCupThreads) void combine_up_project_kernel(AttnArg
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int item = m0 + 8 * (i >> 2) + 4 * g + (i & 3);
-    if (item < Nq) out[(static_cast<int64_t>(item) * H + h) * Dv + v] = f32_to_bf16(acc[i]);
+    const int row = 8 * (i >> 2) + 4 * g + (i & 3);
+    const int item = m0 + row;
+    if (row < IPW && item < Nq) out[(static_cast<int64_t>(item) * H + h) * Dv + v] = f32_to_bf16(acc[i]);
   }
 }
 
@@ -454,11 +460,17 @@ bool combine_up_project_supported(int32_t R, int32_t Dv) {
 
 hipError_t launch_combine_up_project(const AttnArgs& a, const uint16_t* w_uv, int32_t Dv, uint16_t* out,
                                      hipStream_t s) {
-  const dim3 grid((a.num_items + 31) / 32, a.H);
-  if (a.num_items > 256)  // prefill-sized: many workgroups, most items uncut
-    hipLaunchKernelGGL(combine_up_project_kernel<1>, grid, dim3(kCupThreads), 0, s, a, w_uv, Dv, out);
-  else
-    hipLaunchKernelGGL(combine_up_project_kernel<4>, grid, dim3(kCupThreads), 0, s, a, w_uv, Dv, out);
+  const int blocks32 = (a.num_items + 31) / 32;
+  if (a.num_items > 256) {  // prefill-sized: many workgroups, most items uncut
+    hipLaunchKernelGGL((combine_up_project_kernel<1, 32>), dim3(blocks32, a.H), dim3(kCupThreads), 0, s, a, w_uv,
+                       Dv, out);
+  } else if (blocks32 * a.H < 256) {  // fewer workgroups than compute units
+    hipLaunchKernelGGL((combine_up_project_kernel<16, 4>), dim3((a.num_items + 3) / 4, a.H), dim3(kCupThreads), 0,
+                       s, a, w_uv, Dv, out);
+  } else {
+    hipLaunchKernelGGL((combine_up_project_kernel<4, 32>), dim3(blocks32, a.H), dim3(kCupThreads), 0, s, a, w_uv,
+                       Dv, out);
+  }
   return hipGetLastError();
 }
 
