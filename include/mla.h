@@ -26,6 +26,22 @@
  *     the kernels so that they never read or write outside the buffers, and
  *     the results for the affected rows are then unspecified.  A failed
  *     kernel launch returns MLA_ERR_HIP.  The library never aborts.
+ *   - Debug check: with the environment variable MLA_DEBUG_CHECK set (to
+ *     anything but "" or "0"), every call first copies its index arrays to
+ *     the host, waits for the stream, and verifies the caller contract:
+ *     0 <= context_lens[b] <= max_blocks_per_seq * page_size; the first
+ *     ceil(context_lens[b] / page_size) block-table entries name pages of the
+ *     cache; query_start_loc starts at 0, never decreases, ends at
+ *     total_q_tokens ("[unified-memory] ...", Two pre-existing issues, item 1:
+ *     a query count disagreeing with the last query_start_loc entry crashed
+ *     the kernel there) and each chunk fits its context and max_q_len; write
+ *     slots are negative or name distinct slots of the cache.  A violation
+ *     returns MLA_ERR_INVALID_ARGUMENT with nothing enqueued.  The check
+ *     synchronises, so under stream capture it returns MLA_ERR_UNSUPPORTED.
+ *   - Thread safety: the library keeps no per-call state between calls; its
+ *     only process-wide state (a per-device compute-unit count and a kernel
+ *     attribute flag) is held in atomics.  Calls that share a workspace or
+ *     write the same outputs must not overlap.
  *   - bf16 values are IEEE binary32 truncated to the top 16 bits (bfloat16).
  */
 #ifndef MLA_H_

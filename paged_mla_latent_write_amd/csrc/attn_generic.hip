@@ -12,6 +12,8 @@
 // Grid: (G workgroups of the tile stream) x (head blocks of hpb heads).
 #include <math.h>
 
+#include <atomic>
+
 #include "device_utils.h"
 #include "mla_internal.h"
 
@@ -20,6 +22,7 @@ namespace {
 
 constexpr int kSub = 16;      // tokens per LDS sub-tile
 constexpr int kMaxAcc = 16;   // accumulators per thread
+constexpr int kMaxAttrDevices = 64;
 
 __device__ __forceinline__ float load_latent(const CacheView& kv, int64_t row, int d) {
   if (kv.dtype == kKvBf16) {
@@ -188,11 +191,16 @@ hipError_t launch_attn_generic(const AttnArgs& a, hipStream_t s) {
   const int nhb = (a.H + hpb - 1) / hpb;
   const size_t smem =
       sizeof(float) * (static_cast<size_t>(hpb) * a.kv.D + kSub * (a.kv.D + 1) + hpb * kSub + 3 * hpb);
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(attn_generic_kernel),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr_set = true;
+  // The dynamic-LDS limit is raised once per device.  The flags are atomics:
+  // threads that race on a first launch each set the same attribute.
+  static std::atomic<bool> attr_set[kMaxAttrDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  if (dev < 0 || dev >= kMaxAttrDevices || !attr_set[dev].load(std::memory_order_acquire)) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_generic_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxAttrDevices) attr_set[dev].store(true, std::memory_order_release);
   }
   hipLaunchKernelGGL(attn_generic_kernel, dim3(a.G, nhb), dim3(256), smem, s, a, hpb);
   return hipGetLastError();

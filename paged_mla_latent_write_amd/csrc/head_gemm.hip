@@ -461,10 +461,11 @@ bool combine_up_project_supported(int32_t R, int32_t Dv) {
 hipError_t launch_combine_up_project(const AttnArgs& a, const uint16_t* w_uv, int32_t Dv, uint16_t* out,
                                      hipStream_t s) {
   const int blocks32 = (a.num_items + 31) / 32;
-  if (a.num_items > 256) {  // prefill-sized: many workgroups, most items uncut
+  const int cus = std::max(1, current_cu_count());
+  if (a.num_items > cus) {  // prefill-sized: many workgroups, most items uncut
     hipLaunchKernelGGL((combine_up_project_kernel<1, 32>), dim3(blocks32, a.H), dim3(kCupThreads), 0, s, a, w_uv,
                        Dv, out);
-  } else if (blocks32 * a.H < 256) {  // fewer workgroups than compute units
+  } else if (blocks32 * a.H < cus) {  // fewer workgroups than compute units
     hipLaunchKernelGGL((combine_up_project_kernel<16, 4>), dim3((a.num_items + 3) / 4, a.H), dim3(kCupThreads), 0,
                        s, a, w_uv, Dv, out);
   } else {

@@ -4,7 +4,11 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
+
+#include <atomic>
+#include <vector>
 
 #include "../../include/mla.h"
 #include "mla_internal.h"
@@ -19,18 +23,28 @@ constexpr int kMaxDevices = 64;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-// Compute units of the current device (cached per device id).
-int current_cu_count() {
-  static int cached[kMaxDevices] = {0};
+// Compute units of the current device, cached per device id.  The cache is
+// an array of atomics: concurrent first calls from several threads each
+// query the device and store the same value.
+std::atomic<int> g_cu_count[kMaxDevices];
+
+}  // namespace
+
+int mla::current_cu_count() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
-  if (dev < kMaxDevices && cached[dev] > 0) return cached[dev];
+  if (dev < kMaxDevices) {
+    const int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   int n = 0;
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
     return -1;
-  if (dev < kMaxDevices) cached[dev] = n;
+  if (dev < kMaxDevices) g_cu_count[dev].store(n, std::memory_order_relaxed);
   return n;
 }
+
+namespace {
 
 bool page_size_ok(int ps) { return ps == 16 || ps == 32 || ps == 64 || ps == 128; }
 
@@ -73,7 +87,7 @@ struct Layout {
 bool make_layout(const mla_cache* c, const mla_attn* a, int64_t num_items, Layout* L) {
   int G = a->num_workgroups;
   if (G <= 0) {
-    G = current_cu_count();
+    G = mla::current_cu_count();
     if (G <= 0) return false;
   }
   const int64_t H = a->num_heads, R = c->kv_lora_rank;
@@ -120,13 +134,101 @@ T* at(void* base, size_t off) {
 
 mla_status to_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
+// ---- MLA_DEBUG_CHECK: host-side validation of device-array contents ----
+//
+// With the environment variable MLA_DEBUG_CHECK set to anything but "" or
+// "0", each call first copies its index arrays (context lengths, the used
+// prefix of the block tables, query_start_loc, slot mappings) to the host,
+// waits for them, and checks the caller contract the kernels otherwise only
+// clamp against.  A violation returns MLA_ERR_INVALID_ARGUMENT and enqueues
+// nothing.  The check synchronises the stream, so it is refused
+// (MLA_ERR_UNSUPPORTED) while the stream is being captured into a graph.
+// The contract is the one whose violation the pages report as a crash
+// ("[unified-memory] Let Kimi-Linear use the paged MLA attention backends",
+// Two pre-existing issues, item 1: a query count that disagrees with the
+// last query_start_loc entry).
+
+bool debug_check_enabled() {
+  const char* v = getenv("MLA_DEBUG_CHECK");
+  return v != nullptr && v[0] != 0 && !(v[0] == '0' && v[1] == 0);
+}
+
+mla_status debug_prepare(hipStream_t s) {
+  if (s == nullptr) return MLA_OK;  // the null stream cannot be captured
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) return MLA_ERR_HIP;
+  return cs == hipStreamCaptureStatusNone ? MLA_OK : MLA_ERR_UNSUPPORTED;
+}
+
+template <typename T>
+mla_status fetch(std::vector<T>* dst, const T* src, size_t n, hipStream_t s) {
+  dst->assign(n, T{});
+  if (n == 0) return MLA_OK;
+  if (hipMemcpyAsync(dst->data(), src, n * sizeof(T), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return MLA_ERR_HIP;
+  return hipStreamSynchronize(s) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+// Attention calls: 0 <= n_b <= max_blocks * page_size; the first
+// ceil(n_b / page_size) block-table entries of each request name a page of
+// the cache; for prefill, query_start_loc starts at 0, does not decrease,
+// ends at total_q_tokens, and each request's chunk fits its context and
+// max_q_len.
+mla_status debug_check_attention(int mode, const mla_cache* c, const int32_t* block_tables,
+                                 int32_t max_blocks, const int32_t* context_lens, int32_t batch,
+                                 const int32_t* qsl, int32_t total_q, int32_t max_q_len,
+                                 hipStream_t s) {
+  mla_status st = debug_prepare(s);
+  if (st != MLA_OK) return st;
+  std::vector<int32_t> ctx, bt, q;
+  if ((st = fetch(&ctx, context_lens, batch, s)) != MLA_OK) return st;
+  if ((st = fetch(&bt, block_tables, static_cast<size_t>(batch) * max_blocks, s)) != MLA_OK)
+    return st;
+  const int64_t ps = c->page_size;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = ctx[b];
+    if (n < 0 || n > static_cast<int64_t>(max_blocks) * ps) return MLA_ERR_INVALID_ARGUMENT;
+    for (int64_t j = 0; j < (n + ps - 1) / ps; ++j) {
+      const int32_t pg = bt[static_cast<size_t>(b) * max_blocks + j];
+      if (pg < 0 || pg >= c->num_pages) return MLA_ERR_INVALID_ARGUMENT;
+    }
+  }
+  if (mode == mla::kPlanPrefill) {
+    if ((st = fetch(&q, qsl, static_cast<size_t>(batch) + 1, s)) != MLA_OK) return st;
+    if (q[0] != 0 || q[batch] != total_q) return MLA_ERR_INVALID_ARGUMENT;
+    for (int32_t b = 0; b < batch; ++b) {
+      const int64_t m = static_cast<int64_t>(q[b + 1]) - q[b];
+      if (m < 0 || m > ctx[b] || m > max_q_len) return MLA_ERR_INVALID_ARGUMENT;
+    }
+  }
+  return MLA_OK;
+}
+
+// Cache writes: every slot is negative (a pad row) or names a slot of the
+// cache, and the non-negative slots of one call are distinct.
+mla_status debug_check_slots(const mla_cache* c, const int64_t* slot_mapping, int32_t num_tokens,
+                             hipStream_t s) {
+  mla_status st = debug_prepare(s);
+  if (st != MLA_OK) return st;
+  std::vector<int64_t> sl;
+  if ((st = fetch(&sl, slot_mapping, num_tokens, s)) != MLA_OK) return st;
+  const int64_t slots = static_cast<int64_t>(c->num_pages) * c->page_size;
+  std::vector<uint8_t> seen(static_cast<size_t>(slots), 0);
+  for (const int64_t v : sl) {
+    if (v < 0) continue;
+    if (v >= slots || seen[static_cast<size_t>(v)]) return MLA_ERR_INVALID_ARGUMENT;
+    seen[static_cast<size_t>(v)] = 1;
+  }
+  return MLA_OK;
+}
+
 // Shared by decode (one item per request) and prefill (one item per query row).
 mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, const mla_attn* attn,
                          const void* q_nope, int64_t qn_st, int64_t qn_sh, const void* q_pe,
                          int64_t qp_st, int64_t qp_sh, const int32_t* qsl, int32_t num_items,
                          const int32_t* block_tables, int32_t max_blocks,
-                         const int32_t* context_lens, int32_t batch, void* out,
-                         float* lse_or_null, void* workspace, size_t workspace_bytes,
+                         const int32_t* context_lens, int32_t batch, int32_t max_q_len,
+                         void* out, float* lse_or_null, void* workspace, size_t workspace_bytes,
                          void* stream) {
   mla_status st = check_cache(cache);
   if (st != MLA_OK) return st;
@@ -148,6 +250,11 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MLA_ERR_WORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_check_enabled()) {
+    st = debug_check_attention(mode, cache, block_tables, max_blocks, context_lens, batch, qsl,
+                               num_items, max_q_len, s);
+    if (st != MLA_OK) return st;
+  }
   const int H = attn->num_heads, R = cache->kv_lora_rank;
 
   const int64_t layer_elems =
@@ -315,6 +422,10 @@ mla_status mla_write_kv(const mla_cache* cache, int32_t layer_idx, const void* c
   if (!c_kv || !slot_mapping || (cache->qk_rope_dim > 0 && !k_pe)) return MLA_ERR_INVALID_ARGUMENT;
   if (c_kv_row_stride < cache->kv_lora_rank || k_pe_row_stride < cache->qk_rope_dim)
     return MLA_ERR_INVALID_ARGUMENT;
+  if (debug_check_enabled()) {
+    st = debug_check_slots(cache, slot_mapping, num_tokens, static_cast<hipStream_t>(stream));
+    if (st != MLA_OK) return st;
+  }
   const int64_t slots = static_cast<int64_t>(cache->num_pages) * cache->page_size;
   const int64_t D = cache->kv_lora_rank + cache->qk_rope_dim;
   void* layer = static_cast<char*>(cache->data) + layer_idx * slots * D * elem_bytes(cache->dtype);
@@ -355,7 +466,7 @@ mla_status mla_decode(const mla_cache* cache, int32_t layer_idx, const mla_attn*
                       void* workspace, size_t workspace_bytes, void* stream) {
   return run_attention(mla::kPlanDecode, cache, layer_idx, attn, q_nope, q_nope_stride_b,
                        q_nope_stride_h, q_pe, q_pe_stride_b, q_pe_stride_h, nullptr, batch,
-                       block_tables, max_blocks_per_seq, context_lens, batch, out, lse_or_null,
+                       block_tables, max_blocks_per_seq, context_lens, batch, 1, out, lse_or_null,
                        workspace, workspace_bytes, stream);
 }
 
@@ -370,8 +481,8 @@ mla_status mla_prefill_chunk(const mla_cache* cache, int32_t layer_idx, const ml
   if (total_q_tokens < 0 || max_q_len < 0) return MLA_ERR_INVALID_ARGUMENT;
   return run_attention(mla::kPlanPrefill, cache, layer_idx, attn, q_nope, q_nope_stride_t,
                        q_nope_stride_h, q_pe, q_pe_stride_t, q_pe_stride_h, query_start_loc,
-                       total_q_tokens, block_tables, max_blocks_per_seq, context_lens, batch, out,
-                       lse_or_null, workspace, workspace_bytes, stream);
+                       total_q_tokens, block_tables, max_blocks_per_seq, context_lens, batch,
+                       max_q_len, out, lse_or_null, workspace, workspace_bytes, stream);
 }
 
 mla_status mla_decode_combine(const float* o_part, const float* lse_part, int32_t num_splits,

@@ -80,6 +80,9 @@ struct AttnArgs {
   const int32_t* redo_only;  // generic kernel: non-null = only workgroups with redo_only[g] != 0
 };
 
+// Compute units of the current device (cached per device; -1 on error).
+int current_cu_count();
+
 // ---- launchers (each returns the launch's hipGetLastError) ----
 hipError_t launch_write_kv(void* cache_layer, float* scale_layer, int32_t dtype, int64_t num_slots,
                            int32_t R, int32_t Dr, const uint16_t* c_kv, int64_t c_stride,

@@ -45,9 +45,10 @@ __global__ __launch_bounds__(256) void write_kv_bf16_kernel(
 }
 
 // Per-token fp8 quantisation: amax over the token's R + Dr values, scale =
-// amax / 448 rounded once to fp32 (the division is done in double and
-// rounded to float, which equals the correctly rounded fp32 quotient), code =
-// E4M3 round-to-nearest-even of x / scale (same division rule), saturating.
+// amax / 448 as a correctly rounded fp32 quotient, code = E4M3
+// round-to-nearest-even of x / scale (also a correctly rounded fp32
+// quotient), saturating.  hipcc's fp32 division is IEEE correctly rounded
+// unless fast-math options are given, and the build gives none.
 __global__ __launch_bounds__(256) void write_kv_fp8_kernel(
     uint8_t* __restrict__ cache, float* __restrict__ scale_out, int64_t num_slots, int32_t R,
     int32_t Dr, const uint16_t* __restrict__ c_kv, int64_t c_stride,
@@ -74,17 +75,12 @@ __global__ __launch_bounds__(256) void write_kv_fp8_kernel(
     amax = fmaxf(amax, fabsf(x));
   }
   amax = wave_max(amax);
-  const float scale =
-      amax == 0.f ? 1.0f : static_cast<float>(static_cast<double>(amax) / 448.0);
-  const double dscale = static_cast<double>(scale);
+  const float scale = amax == 0.f ? 1.0f : amax / 448.0f;
   uint8_t* dst = cache + s * D;
 #pragma unroll
   for (int k = 0; k < kMaxPerLane; ++k) {
     const int j = lane + 64 * k;
-    if (j < D) {
-      const float q = static_cast<float>(static_cast<double>(v[k]) / dscale);
-      dst[j] = static_cast<uint8_t>(f32_to_e4m3_satfinite(q));
-    }
+    if (j < D) dst[j] = static_cast<uint8_t>(f32_to_e4m3_satfinite(v[k] / scale));
   }
   if (lane == 0) scale_out[s] = scale;
 }

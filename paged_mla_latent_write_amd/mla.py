@@ -110,6 +110,35 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _keep_alive_on(stream, *tensors):
+    """Tensors this module allocated are used by kernels queued on `stream`.
+    When that is not the current stream, tell torch's caching allocator, so
+    their memory is not handed to other work before those kernels finish.  A
+    raw stream handle cannot be recorded: then every buffer must come from the
+    caller."""
+    if stream is None:
+        return
+    if not isinstance(stream, torch.cuda.Stream):
+        if tensors:
+            raise ValueError("with a raw stream handle, pass out, lse and workspace explicitly")
+        return
+    if stream == torch.cuda.current_stream(stream.device):
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _same_device(*tensors):
+    devs = {t.device for t in tensors if t is not None}
+    _need(len(devs) <= 1, f"tensors on different devices: {sorted(str(d) for d in devs)}")
+
+
 @dataclass
 class KVCache:
     """Caller-owned latent cache: data [L, P, ps, R + Dr] (bfloat16, or uint8
@@ -162,18 +191,70 @@ def _attn_struct(num_heads, qk_nope_dim, v_head_dim, w_uk, w_uv, scale, window, 
 
 
 def _row_strides(q):
-    assert q.dim() == 3 and q.stride(2) == 1 and q.dtype == torch.bfloat16
+    _need(q.dim() == 3 and q.stride(2) == 1 and q.dtype == torch.bfloat16,
+          "queries must be bf16 [rows, H, D] with unit inner stride")
     return q.stride(0), q.stride(1)
+
+
+def _check_heads(cache, q_nope, q_pe, w_uk, w_uv):
+    """Host-known shapes of the queries and the per-head weights; returns
+    (qk_nope_dim or 0, output width)."""
+    R, Dr = cache.kv_lora_rank, cache.qk_rope_dim
+    _need(q_nope.dim() == 3 and q_pe.dim() == 3, "q_nope and q_pe must be [rows, H, D]")
+    rows, H = int(q_nope.shape[0]), int(q_nope.shape[1])
+    _need(tuple(q_pe.shape) == (rows, H, Dr), f"q_pe must be [{rows}, {H}, {Dr}], got {tuple(q_pe.shape)}")
+    if w_uk is None:
+        dn = 0
+        _need(q_nope.shape[2] == R, f"without w_uk, q_nope must be latent: [{rows}, {H}, {R}]")
+    else:
+        dn = int(w_uk.shape[1])
+        _need(w_uk.dim() == 3 and tuple(w_uk.shape) == (H, dn, R),
+              f"w_uk must be [{H}, qk_nope_dim, {R}], got {tuple(w_uk.shape)}")
+        _need(q_nope.shape[2] == dn, f"q_nope's last dim {q_nope.shape[2]} != w_uk's {dn}")
+    if w_uv is None:
+        dv = R
+    else:
+        dv = int(w_uv.shape[1])
+        _need(w_uv.dim() == 3 and w_uv.shape[0] == H and w_uv.shape[2] == R,
+              f"w_uv must be [{H}, v_head_dim, {R}], got {tuple(w_uv.shape)}")
+    return dn, dv
+
+
+def _check_tables(block_tables, context_lens, B):
+    _need(block_tables.dtype == torch.int32 and block_tables.dim() == 2 and
+          block_tables.is_contiguous(), "block_tables: contiguous int32 [B, max_blocks]")
+    _need(context_lens.dtype == torch.int32 and context_lens.dim() == 1 and
+          context_lens.is_contiguous(), "context_lens: contiguous int32 [B]")
+    _need(block_tables.shape[0] == B and context_lens.numel() == B,
+          f"block_tables has {block_tables.shape[0]} rows and context_lens {context_lens.numel()} "
+          f"entries; the batch has {B}")
+    _need(block_tables.shape[1] > 0, "block_tables needs at least one column")
+
+
+def _check_outputs(out, lse, shape):
+    if out is not None:
+        _need(tuple(out.shape) == shape and out.dtype == torch.bfloat16 and out.is_contiguous(),
+              f"out must be contiguous bf16 {shape}")
+    if lse is not None:
+        _need(tuple(lse.shape) == shape[:2] and lse.dtype == torch.float32 and lse.is_contiguous(),
+              f"lse must be contiguous fp32 {shape[:2]}")
 
 
 def write_kv(cache: KVCache, layer_idx: int, c_kv: torch.Tensor, k_pe: torch.Tensor,
              slot_mapping: torch.Tensor, stream=None):
     """Scatter rows [c_kv | k_pe] (bf16 [T, R], [T, Dr], unit inner stride)
     into layer `layer_idx` at slot_mapping (int64 [T]; negative = pad row)."""
-    assert c_kv.dtype == torch.bfloat16 and k_pe.dtype == torch.bfloat16
-    assert c_kv.stride(-1) == 1 and k_pe.stride(-1) == 1 and slot_mapping.dtype == torch.int64
-    st = cache.struct()
+    _need(c_kv.dtype == torch.bfloat16 and k_pe.dtype == torch.bfloat16, "c_kv and k_pe must be bf16")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.dim() == 1, "slot_mapping: int64 [T]")
+    _need(c_kv.dim() == 2 and c_kv.shape[1] == cache.kv_lora_rank and c_kv.stride(-1) == 1,
+          f"c_kv must be [T, {cache.kv_lora_rank}] with unit inner stride")
+    _need(k_pe.dim() == 2 and k_pe.shape[1] == cache.qk_rope_dim and k_pe.stride(-1) == 1,
+          f"k_pe must be [T, {cache.qk_rope_dim}] with unit inner stride")
     T = int(c_kv.shape[0])
+    _need(k_pe.shape[0] == T and slot_mapping.numel() == T and slot_mapping.is_contiguous(),
+          "c_kv, k_pe and slot_mapping must have the same number of tokens")
+    _same_device(cache.data, c_kv, k_pe, slot_mapping)
+    st = cache.struct()
     _check(_write_kv(ctypes.byref(st), layer_idx, _ptr(c_kv), c_kv.stride(0), _ptr(k_pe),
                      k_pe.stride(0), _ptr(slot_mapping), T, _stream(stream)), "mla_write_kv")
 
@@ -189,7 +270,9 @@ def prefill_workspace_size(cache: KVCache, attn: MlaAttnStruct, batch: int, tota
 
 
 class Workspace:
-    """A reusable device workspace that grows on demand (torch-allocated)."""
+    """A reusable device workspace that grows on demand (torch-allocated).
+    When it is used on a stream other than the current one, pass that stream
+    as a torch.cuda.Stream so the binding can record it on the buffer."""
 
     def __init__(self):
         self.buf = None
@@ -207,22 +290,30 @@ def decode(cache: KVCache, layer_idx: int, q_nope, q_pe, block_tables, context_l
     w_uk is None), q_pe bf16 [B, H, Dr]; block_tables int32 [B, max_blocks];
     context_lens int32 [B].  Returns (out bf16 [B, H, Dv or R], lse fp32 [B, H])."""
     B, H = int(q_nope.shape[0]), int(q_nope.shape[1])
-    dn = int(w_uk.shape[1]) if w_uk is not None else 0
-    dv = int(w_uv.shape[1]) if w_uv is not None else cache.kv_lora_rank
+    dn, dv = _check_heads(cache, q_nope, q_pe, w_uk, w_uv)
+    _check_tables(block_tables, context_lens, B)
+    _check_outputs(out, lse, (B, H, dv))
+    _same_device(cache.data, q_nope, q_pe, w_uk, w_uv, block_tables, context_lens, out, lse)
     attn = _attn_struct(H, dn, dv, w_uk, w_uv, scale, window, num_workgroups, flags, kernel_events)
     st = cache.struct()
-    assert block_tables.dtype == torch.int32 and block_tables.is_contiguous()
-    assert context_lens.dtype == torch.int32 and context_lens.is_contiguous()
     max_blocks = int(block_tables.shape[1])
     dev = q_nope.device
+    fresh = []
     if out is None:
         out = torch.empty((B, H, dv), dtype=torch.bfloat16, device=dev)
+        fresh.append(out)
     if lse is None and want_lse:
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+        fresh.append(lse)
     nbytes = int(_decode_ws(ctypes.byref(st), ctypes.byref(attn), B, max_blocks))
     if nbytes == 0 and B > 0:
         raise MlaError(MLA_ERR_INVALID_ARGUMENT, "mla_decode_workspace_size")
     ws = (workspace or Workspace()).get(nbytes, dev)
+    if workspace is None:
+        fresh.append(ws)
+    elif isinstance(stream, torch.cuda.Stream):
+        ws.record_stream(stream)
+    _keep_alive_on(stream, *fresh)
     qs_b, qs_h = _row_strides(q_nope)
     ps_b, ps_h = _row_strides(q_pe)
     _check(_decode(ctypes.byref(st), layer_idx, ctypes.byref(attn), _ptr(q_nope), qs_b, qs_h,
@@ -238,22 +329,36 @@ def prefill_chunk(cache: KVCache, layer_idx: int, q_nope, q_pe, query_start_loc,
     """Causal chunked prefill.  q_nope bf16 [Tq, H, Dn], q_pe bf16 [Tq, H, Dr];
     query_start_loc int32 [B + 1]; context_lens int32 [B] (chunk included)."""
     Tq, H = int(q_nope.shape[0]), int(q_nope.shape[1])
+    _need(context_lens.dim() == 1, "context_lens: int32 [B]")
     B = int(context_lens.shape[0])
-    dn = int(w_uk.shape[1]) if w_uk is not None else 0
-    dv = int(w_uv.shape[1]) if w_uv is not None else cache.kv_lora_rank
+    dn, dv = _check_heads(cache, q_nope, q_pe, w_uk, w_uv)
+    _check_tables(block_tables, context_lens, B)
+    _need(query_start_loc.dtype == torch.int32 and query_start_loc.dim() == 1 and
+          query_start_loc.numel() == B + 1 and query_start_loc.is_contiguous(),
+          "query_start_loc: contiguous int32 [B + 1]")
+    _check_outputs(out, lse, (Tq, H, dv))
+    _same_device(cache.data, q_nope, q_pe, w_uk, w_uv, block_tables, context_lens, query_start_loc,
+                 out, lse)
     attn = _attn_struct(H, dn, dv, w_uk, w_uv, scale, window, num_workgroups, flags, kernel_events)
     st = cache.struct()
-    assert query_start_loc.dtype == torch.int32 and query_start_loc.numel() == B + 1
     max_blocks = int(block_tables.shape[1])
     dev = q_nope.device
+    fresh = []
     if out is None:
         out = torch.empty((Tq, H, dv), dtype=torch.bfloat16, device=dev)
+        fresh.append(out)
     if lse is None and want_lse:
         lse = torch.empty((Tq, H), dtype=torch.float32, device=dev)
+        fresh.append(lse)
     nbytes = int(_prefill_ws(ctypes.byref(st), ctypes.byref(attn), B, Tq, max_blocks))
     if nbytes == 0 and Tq > 0:
         raise MlaError(MLA_ERR_INVALID_ARGUMENT, "mla_prefill_workspace_size")
     ws = (workspace or Workspace()).get(nbytes, dev)
+    if workspace is None:
+        fresh.append(ws)
+    elif isinstance(stream, torch.cuda.Stream):
+        ws.record_stream(stream)
+    _keep_alive_on(stream, *fresh)
     qs_t, qs_h = _row_strides(q_nope)
     ps_t, ps_h = _row_strides(q_pe)
     _check(_prefill(ctypes.byref(st), layer_idx, ctypes.byref(attn), _ptr(q_nope), qs_t, qs_h,

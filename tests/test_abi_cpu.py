@@ -139,3 +139,66 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode != 0
     msg = json.loads(r.stdout.strip().splitlines()[-1])
     assert "one GPU" in msg["error"]
+
+
+def test_binding_rejects_mismatched_shapes():
+    """The binding checks every host-known shape before it calls the ABI: a
+    short block table or context_lens, queries whose head count or width
+    disagrees with the weights or the cache, and wrong output buffers raise
+    ValueError (CPU tensors: nothing reaches a device)."""
+    import torch
+
+    from paged_mla_latent_write_amd import mla
+
+    B, H, R, Dr, Dn, Dv = 4, 8, 64, 16, 32, 32
+    cache = mla.KVCache.empty(1, 16, 16, R, Dr, device="cpu")
+    bf = dict(dtype=torch.bfloat16)
+    q_nope, q_pe = torch.zeros(B, H, Dn, **bf), torch.zeros(B, H, Dr, **bf)
+    w_uk, w_uv = torch.zeros(H, Dn, R, **bf), torch.zeros(H, Dv, R, **bf)
+    bt = torch.zeros(B, 4, dtype=torch.int32)
+    ctx = torch.ones(B, dtype=torch.int32)
+
+    def dec(**kw):
+        args = dict(q_nope=q_nope, q_pe=q_pe, block_tables=bt, context_lens=ctx, w_uk=w_uk, w_uv=w_uv)
+        args.update(kw)
+        return mla.decode(cache, 0, args.pop("q_nope"), args.pop("q_pe"), args.pop("block_tables"),
+                          args.pop("context_lens"), scale=0.1, **args)
+
+    bad = [
+        dict(block_tables=bt[:3]),                                   # short block table
+        dict(context_lens=ctx[:3]),                                  # short context_lens
+        dict(block_tables=bt.to(torch.int64)),                       # wrong index type
+        dict(q_pe=torch.zeros(B, H - 1, Dr, **bf)),                  # head count mismatch
+        dict(q_pe=torch.zeros(B, H, Dr + 8, **bf)),                  # rope width != cache
+        dict(w_uk=torch.zeros(H, Dn, R + 8, **bf)),                  # W_UK rank != cache
+        dict(w_uk=torch.zeros(H - 2, Dn, R, **bf)),                  # W_UK heads != queries
+        dict(q_nope=torch.zeros(B, H, Dn + 16, **bf)),               # q_nope width != W_UK
+        dict(w_uv=torch.zeros(H, Dv, R - 8, **bf)),                  # W_UV rank != cache
+        dict(w_uk=None),                                             # latent q must be [.., R]
+        dict(out=torch.zeros(B, H, Dv + 1, **bf)),                   # wrong output shape
+        dict(lse=torch.zeros(B, H, dtype=torch.float64)),            # wrong lse dtype
+    ]
+    for kw in bad:
+        with pytest.raises(ValueError):
+            dec(**kw)
+
+    qsl = torch.tensor([0, 1, 2, 3, 4], dtype=torch.int32)
+
+    def pre(**kw):
+        args = dict(q_nope=q_nope, q_pe=q_pe, qsl=qsl, block_tables=bt, context_lens=ctx)
+        args.update(kw)
+        return mla.prefill_chunk(cache, 0, args.pop("q_nope"), args.pop("q_pe"), args.pop("qsl"), 1,
+                                 args.pop("block_tables"), args.pop("context_lens"), scale=0.1,
+                                 w_uk=w_uk, w_uv=w_uv, **args)
+
+    for kw in (dict(qsl=qsl[:4]), dict(block_tables=bt[:2]), dict(qsl=qsl.to(torch.int64))):
+        with pytest.raises(ValueError):
+            pre(**kw)
+
+    slots = torch.zeros(3, dtype=torch.int64)
+    for c, r, s in ((torch.zeros(3, R + 1, **bf), torch.zeros(3, Dr, **bf), slots),
+                    (torch.zeros(3, R, **bf), torch.zeros(2, Dr, **bf), slots),
+                    (torch.zeros(3, R, **bf), torch.zeros(3, Dr, **bf), slots[:2]),
+                    (torch.zeros(3, R, **bf), torch.zeros(3, Dr, **bf), slots.to(torch.int32))):
+        with pytest.raises(ValueError):
+            mla.write_kv(cache, 0, c, r, s)

@@ -1,7 +1,8 @@
 """GPU parity: the HIP path through the C ABI against the fp64 oracle on the
 same seeded inputs.  Writes are compared bit for bit; attention outputs within
 max-abs 2e-2 / rel-L2 5e-3 (bf16 cache) or 0.1 / 3e-2 (fp8 cache), over the
-call's output tensor (or, at full sizes, over sampled requests and rows)."""
+call's output tensor.  At full sizes every request is compared; the mixed
+step's prefill compares every 8th row of each chunk plus its last row."""
 import math
 
 import numpy as np
@@ -74,21 +75,32 @@ def test_write_kv_bit_exact_with_pads_layers_and_overwrite(mla, kv_dtype):
     assert T > 0
 
 
-def test_write_fp8_full_size_sampled_rows(mla):
-    """fp8 quantisation at the V3 fp8 workload's size: every token written, a
-    sample of 1/16 of them compared byte for byte (codes and scales)."""
-    say("write_kv fp8 v3fp8 population")
+@pytest.fixture(scope="module")
+def v3fp8_population(mla):
+    """The V3 fp8 workload's cache, written once: on the device by
+    mla_write_kv, on the host by the oracle's write.  Plain and sharp variants
+    share it (their queries differ, their population does not)."""
     case = W.v3fp8()
+    say("v3fp8 population: device write + oracle write")
     cache = populate_device(mla, case)
-    idx = np.arange(0, case.ctx_slots.size, 16)
-    codes, scl = O.fp8_quantize_tokens(np.concatenate([case.ctx_c_kv[idx], case.ctx_k_pe[idx]], axis=1))
-    s = torch.from_numpy(case.ctx_slots[idx]).cuda()
-    ps = case.dims.page_size
-    got = cache.data[0].view(-1, case.dims.D)[s].cpu().numpy()
-    gs = cache.scale[0].reshape(-1)[s].cpu().numpy()
-    assert np.array_equal(got, codes)
-    assert np.array_equal(gs.view(np.uint32), scl.view(np.uint32))
-    assert ps == 64
+    hc = host_cache(case)
+    yield case, cache, hc
+    del cache
+    torch.cuda.empty_cache()
+
+
+def test_write_fp8_full_size_every_token(mla, v3fp8_population):
+    """fp8 quantisation at the V3 fp8 workload's size (128 requests x 8192
+    tokens): the whole device cache, codes and scales, equals the oracle's
+    byte for byte, unused rows included."""
+    say("write_kv fp8 v3fp8 population, every byte")
+    case, cache, (hc, hs) = v3fp8_population
+    got = cache.data.cpu().numpy()
+    assert got.shape == hc.shape
+    diff = int(np.count_nonzero(got != hc))
+    assert diff == 0, f"{diff} code bytes differ"
+    gs = cache.scale.cpu().numpy()
+    assert np.array_equal(gs.view(np.uint32), hs.view(np.uint32)), "fp8 scales differ"
 
 
 def test_write_fp8_codec_edges(mla):
@@ -154,22 +166,25 @@ def test_decode_v2lite(mla, sharp, flags):
     check_decode(mla, W.v2lite(sharp=sharp), flags=flags)
 
 
-def v3_sample(case):
-    ctx = case.context_lens
-    return sorted({0, int(np.argmax(ctx)), int(np.argmin(ctx)), 17, 33, case.batch - 1})
+@pytest.mark.parametrize("sharp", [False, True])
+def test_decode_v3_full_size(mla, sharp):
+    """DeepSeek-V3 shape, every one of the 64 requests compared."""
+    say(f"decode v3 sharp={sharp}")
+    check_decode(mla, W.v3(sharp=sharp))
 
 
 @pytest.mark.parametrize("sharp", [False, True])
-def test_decode_v3_full_size(mla, sharp):
-    say(f"decode v3 sharp={sharp}")
-    case = W.v3(sharp=sharp)
-    check_decode(mla, case, requests=v3_sample(case))
-
-
-def test_decode_v3fp8_full_size(mla):
-    say("decode v3fp8 sharp")
-    case = W.v3fp8(sharp=True)
-    check_decode(mla, case, requests=[0, 5, 64, 127])
+def test_decode_v3fp8_full_size(mla, v3fp8_population, sharp):
+    """V3 shape over the fp8 cache, every one of the 128 requests compared."""
+    say(f"decode v3fp8 sharp={sharp}")
+    base, cache, hcache = v3fp8_population
+    case = W.v3fp8(sharp=sharp)
+    assert np.array_equal(case.ctx_slots, base.ctx_slots)
+    assert np.array_equal(case.ctx_c_kv[::4096], base.ctx_c_kv[::4096])
+    out, lse = gpu_decode(mla, case, cache)
+    ref, ref_lse = oracle_decode(case, hcache)
+    assert_close(bf16_host_f64(out), ref, FP8_TOL, f"v3fp8 sharp={sharp} out")
+    assert_lse_close(lse.cpu().numpy(), ref_lse, LSE_ATOL[O.KV_FP8], f"v3fp8 sharp={sharp} lse")
 
 
 @pytest.mark.parametrize("G", [1, 3, 7, 1000])
@@ -179,6 +194,29 @@ def test_decode_forced_partitions(mla, G):
     d = W.Dims(H=16, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
     case = W.custom(d, [1, 31, 32, 33, 64, 65, 700, 2049], seed=201, sharp=True)
     check_decode(mla, case, num_workgroups=G, label=f" G={G}")
+
+
+@pytest.mark.parametrize("G", [1, 3, 7, 1000])
+def test_decode_forced_partitions_wide_batch(mla, G):
+    """128 heads and 40 requests: enough 32-item blocks x heads to fill the
+    chip, so the combine runs its 32-items-per-workgroup form, whose merge of
+    cut items (several rounds of segments, empty ranges, both partial slots of
+    a workgroup) is then checked in full."""
+    say(f"decode forced G={G}, 128 heads x 40 requests")
+    d = W.Dims(H=128, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
+    ctx = [1, 31, 32, 33, 64, 65, 700, 2049] * 5
+    case = W.custom(d, ctx, seed=210 + G, sharp=True)
+    check_decode(mla, case, num_workgroups=G, label=f" G={G} B=40")
+
+
+@pytest.mark.parametrize("G", [1, 7, 1000])
+def test_prefill_forced_partitions_many_rows(mla, G):
+    """More query rows than compute units: the prefill-sized combine form,
+    with rows cut across workgroups under every forced partition."""
+    say(f"prefill forced G={G}, 300 rows")
+    d = W.Dims(H=16, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
+    case = W.prefill_case(d, [0, 37, 900], [100, 120, 80], seed=230 + G, sharp=True)
+    check_prefill(mla, case, num_workgroups=G, label=f" G={G} rows=300")
 
 
 @pytest.mark.parametrize("window", [1, 2, 31, 32, 33, 128, 5000])
@@ -393,39 +431,75 @@ def test_prefill_rows_match_decode_on_gpu(mla):
 # Mixed batch with sliding window (4-layer cache)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("layer", [0, 1])
-def test_mixed_step_full_size(mla, layer):
-    """Per layer: write the step's 4216 new tokens, prefill the 8 chunks, decode
-    the 120 single-token requests.  Sampled rows against the oracle."""
-    say(f"mixed step layer {layer}")
-    ml = W.mixed(layer, sharp=True)
-    d = ml.dims
-    cache = new_device_cache(mla, ml.num_layers, ml.num_pages, d, O.KV_BF16)
-    mla.write_kv(cache, layer, dev_bf16(ml.pre_c_kv), dev_bf16(ml.pre_k_pe), dev(ml.pre_slots))
-    mla.write_kv(cache, layer, dev_bf16(ml.new_c_kv), dev_bf16(ml.new_k_pe), dev(ml.new_slots))
-    w_uk, w_uv = dev_bf16(ml.w_uk), dev_bf16(ml.w_uv)
-    P = ml.n_prefill
-    bt = dev(ml.block_tables)
-    ctx = dev(ml.context_lens)
-    pout, plse = mla.prefill_chunk(cache, layer, dev_bf16(ml.q_nope_p), dev_bf16(ml.q_pe_p),
-                                   dev(ml.query_start_loc), 512, bt[:P], ctx[:P], scale=ml.scale,
-                                   w_uk=w_uk, w_uv=w_uv, window=ml.window)
-    dout, dlse = mla.decode(cache, layer, dev_bf16(ml.q_nope_d), dev_bf16(ml.q_pe_d), bt[P:], ctx[P:],
-                            scale=ml.scale, w_uk=w_uk, w_uv=w_uv, window=ml.window)
+def mixed_rows(ml):
+    """Prefill rows compared: every 8th row of each chunk plus its last row."""
+    rows = []
+    for b in range(ml.n_prefill):
+        s0, s1 = int(ml.query_start_loc[b]), int(ml.query_start_loc[b + 1])
+        rows += list(range(s0, s1, 8)) + [s1 - 1]
+    return sorted(set(rows))
+
+
+@pytest.fixture(scope="module")
+def mixed_step(mla):
+    """The whole mixed step at full size, as the serving step runs it: one
+    4-layer cache holding every layer's population, then per layer the write
+    of the step's 4216 new tokens, the prefill of the 8 chunks and the decode
+    of the 120 single-token requests.  Returns the layers and their outputs
+    (host copies)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    say("mixed step: generating 4 layers")
+    with ThreadPoolExecutor(4) as ex:
+        layers = list(ex.map(lambda l: W.mixed(l, sharp=True), range(len(W.MIXED_WINDOWS))))
+    d = layers[0].dims
+    cache = new_device_cache(mla, layers[0].num_layers, layers[0].num_pages, d, O.KV_BF16)
+    for ml in layers:
+        mla.write_kv(cache, ml.layer, dev_bf16(ml.pre_c_kv), dev_bf16(ml.pre_k_pe), dev(ml.pre_slots))
     torch.cuda.synchronize()
+    results = []
+    for ml in layers:
+        say(f"mixed step: layer {ml.layer} (window {ml.window})")
+        P = ml.n_prefill
+        bt, ctx = dev(ml.block_tables), dev(ml.context_lens)
+        w_uk, w_uv = dev_bf16(ml.w_uk), dev_bf16(ml.w_uv)
+        mla.write_kv(cache, ml.layer, dev_bf16(ml.new_c_kv), dev_bf16(ml.new_k_pe), dev(ml.new_slots))
+        pout, plse = mla.prefill_chunk(cache, ml.layer, dev_bf16(ml.q_nope_p), dev_bf16(ml.q_pe_p),
+                                       dev(ml.query_start_loc), 512, bt[:P].contiguous(),
+                                       ctx[:P].contiguous(), scale=ml.scale, w_uk=w_uk, w_uv=w_uv,
+                                       window=ml.window)
+        dout, dlse = mla.decode(cache, ml.layer, dev_bf16(ml.q_nope_d), dev_bf16(ml.q_pe_d),
+                                bt[P:].contiguous(), ctx[P:].contiguous(), scale=ml.scale,
+                                w_uk=w_uk, w_uv=w_uv, window=ml.window)
+        torch.cuda.synchronize()
+        results.append((bf16_host_f64(pout), plse.cpu().numpy(), bf16_host_f64(dout),
+                        dlse.cpu().numpy()))
+    del cache
+    torch.cuda.empty_cache()
+    return layers, results
+
+
+@pytest.mark.parametrize("layer", [0, 1, 2, 3])
+def test_mixed_step_full_size(mla, mixed_step, layer):
+    """One layer of the mixed step against the oracle: all 120 decodes, and
+    every 8th prefill row of each chunk plus its last row (520 of 4096)."""
+    layers, results = mixed_step
+    ml = layers[layer]
+    pout, plse, dout, dlse = results[layer]
+    say(f"mixed step layer {layer}: oracle")
+    d = ml.dims
+    P = ml.n_prefill
     hc = np.full((1, ml.num_pages, 64, d.D), W.BF16_NAN, dtype=np.uint16)
     hs = np.full((1, ml.num_pages, 64), np.nan, dtype=np.float32)
     O.write_kv(hc, hs, 0, ml.pre_c_kv, ml.pre_k_pe, ml.pre_slots)
     O.write_kv(hc, hs, 0, ml.new_c_kv, ml.new_k_pe, ml.new_slots)
-    rows = sorted({0, 1, 255, 511, 512, 1500, 2047, 3000, 4095})
+    rows = mixed_rows(ml)
     ref, ref_lse = O.prefill_chunk(hc, hs, O.KV_BF16, 0, ml.q_nope_p, ml.q_pe_p, ml.query_start_loc,
                                    ml.block_tables[:P], ml.context_lens[:P], ml.w_uk, ml.w_uv,
                                    ml.scale, ml.window, rows=rows)
-    assert_close(bf16_host_f64(pout)[rows], ref[rows], BF16_TOL, f"mixed L{layer} prefill")
-    assert_lse_close(plse.cpu().numpy()[rows], ref_lse[rows], LSE_ATOL[O.KV_BF16])
-    reqs = [0, 7, 50, 119]
+    assert_close(pout[rows], ref[rows], BF16_TOL, f"mixed L{layer} prefill ({len(rows)} rows)")
+    assert_lse_close(plse[rows], ref_lse[rows], LSE_ATOL[O.KV_BF16], f"mixed L{layer} prefill lse")
     dref, dref_lse = O.decode(hc, hs, O.KV_BF16, 0, ml.q_nope_d, ml.q_pe_d, ml.block_tables[P:],
-                              ml.context_lens[P:], ml.w_uk, ml.w_uv, ml.scale, ml.window,
-                              requests=reqs)
-    assert_close(bf16_host_f64(dout)[reqs], dref[reqs], BF16_TOL, f"mixed L{layer} decode")
-    assert_lse_close(dlse.cpu().numpy()[reqs], dref_lse[reqs], LSE_ATOL[O.KV_BF16])
+                              ml.context_lens[P:], ml.w_uk, ml.w_uv, ml.scale, ml.window)
+    assert_close(dout, dref, BF16_TOL, f"mixed L{layer} decode (all 120)")
+    assert_lse_close(dlse, dref_lse, LSE_ATOL[O.KV_BF16], f"mixed L{layer} decode lse")
