@@ -189,6 +189,30 @@ mla_status mla_decode(const mla_cache* cache, int32_t layer_idx, const mla_attn*
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_decode_noalloc - mla_decode without a caller workspace, for callers that
+ * cannot allocate device memory (code under graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, results and
+ * errors as mla_decode, minus workspace / workspace_bytes.
+ *
+ * The workspace is a device array inside the library, MLA_NOALLOC_SCRATCH_BYTES
+ * bytes on every GPU the library runs on, held until the process ends.  Its
+ * device address is looked up on the first call made with a device current.
+ * A call whose mla_decode_workspace_size exceeds MLA_NOALLOC_SCRATCH_BYTES
+ * returns MLA_ERR_WORKSPACE and enqueues nothing (192 MiB covers one GPU's
+ * full 128-head set at 128 requests with one workgroup per compute unit).
+ * The call allocates nothing.  All calls on one GPU share the array: calls
+ * that overlap in time on one GPU (two streams, two threads) race and must
+ * not be issued.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)192 << 20)
+mla_status mla_decode_noalloc(const mla_cache* cache, int32_t layer_idx, const mla_attn* attn,
+                              const void* q_nope, int64_t q_nope_stride_b, int64_t q_nope_stride_h,
+                              const void* q_pe, int64_t q_pe_stride_b, int64_t q_pe_stride_h,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens, int32_t batch,
+                              void* out, float* lse_or_null, void* stream);
+
+/*
  * mla_decode_combine - log-sum-exp merge of split-KV partial results
  * (the identity lse = log sum_s exp(lse_s), o = sum_s exp(lse_s - lse) o_s;
  * the pages do not state it).

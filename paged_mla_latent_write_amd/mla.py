@@ -35,8 +35,10 @@ MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3 = 1
 MLA_FLAG_GENERIC_KERNELS = 1
 
-EXPORTED = ("mla_write_kv", "mla_decode_workspace_size", "mla_decode", "mla_decode_combine",
-            "mla_prefill_workspace_size", "mla_prefill_chunk", "mla_status_string", "mla_version")
+EXPORTED = ("mla_write_kv", "mla_decode_workspace_size", "mla_decode", "mla_decode_noalloc",
+            "mla_decode_combine", "mla_prefill_workspace_size", "mla_prefill_chunk",
+            "mla_status_string", "mla_version")
+NOALLOC_SCRATCH_BYTES = 192 << 20  # MLA_NOALLOC_SCRATCH_BYTES in include/mla.h
 
 
 class MlaCacheStruct(ctypes.Structure):
@@ -73,6 +75,8 @@ _write_kv = _sig("mla_write_kv", _I32, _CP, _I32, _P, _I64, _P, _I64, _P, _I32, 
 _decode_ws = _sig("mla_decode_workspace_size", _SZ, _CP, _AP, _I32, _I32)
 _decode = _sig("mla_decode", _I32, _CP, _I32, _AP, _P, _I64, _I64, _P, _I64, _I64, _P, _I32, _P,
                _I32, _P, _P, _P, _SZ, _P)
+_decode_noalloc = _sig("mla_decode_noalloc", _I32, _CP, _I32, _AP, _P, _I64, _I64, _P, _I64, _I64, _P,
+                      _I32, _P, _I32, _P, _P, _P)
 _combine = _sig("mla_decode_combine", _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P)
 _prefill_ws = _sig("mla_prefill_workspace_size", _SZ, _CP, _AP, _I32, _I32, _I32)
 _prefill = _sig("mla_prefill_chunk", _I32, _CP, _I32, _AP, _P, _I64, _I64, _P, _I64, _I64, _P, _I32,
@@ -319,6 +323,30 @@ def decode(cache: KVCache, layer_idx: int, q_nope, q_pe, block_tables, context_l
     _check(_decode(ctypes.byref(st), layer_idx, ctypes.byref(attn), _ptr(q_nope), qs_b, qs_h,
                    _ptr(q_pe), ps_b, ps_h, _ptr(block_tables), max_blocks, _ptr(context_lens), B,
                    _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)), "mla_decode")
+    return out, lse
+
+
+def decode_noalloc(cache: KVCache, layer_idx: int, q_nope, q_pe, block_tables, context_lens, *,
+                   scale, out, lse=None, w_uk=None, w_uv=None, window=0, num_workgroups=0, flags=0,
+                   stream=None):
+    """mla_decode with the library's own device scratch array as workspace:
+    no allocation anywhere, so `out` (and `lse`, if wanted) must be given.
+    Calls that overlap on one GPU share the scratch array and must not be
+    issued."""
+    B, H = int(q_nope.shape[0]), int(q_nope.shape[1])
+    dn, dv = _check_heads(cache, q_nope, q_pe, w_uk, w_uv)
+    _check_tables(block_tables, context_lens, B)
+    _need(out is not None, "decode_noalloc allocates nothing: pass out")
+    _check_outputs(out, lse, (B, H, dv))
+    _same_device(cache.data, q_nope, q_pe, w_uk, w_uv, block_tables, context_lens, out, lse)
+    attn = _attn_struct(H, dn, dv, w_uk, w_uv, scale, window, num_workgroups, flags)
+    st = cache.struct()
+    qs_b, qs_h = _row_strides(q_nope)
+    ps_b, ps_h = _row_strides(q_pe)
+    _check(_decode_noalloc(ctypes.byref(st), layer_idx, ctypes.byref(attn), _ptr(q_nope), qs_b, qs_h,
+                           _ptr(q_pe), ps_b, ps_h, _ptr(block_tables), int(block_tables.shape[1]),
+                           _ptr(context_lens), B, _ptr(out), _ptr(lse), _stream(stream)),
+           "mla_decode_noalloc")
     return out, lse
 
 
