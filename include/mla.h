@@ -153,6 +153,45 @@ mla_status mla_write_kv(const mla_cache* cache, int32_t layer_idx,
                         const int64_t* slot_mapping, int32_t num_tokens, void* stream);
 
 /*
+ * Normalisation and rotation folded into the cache write ("Support dsv4
+ * model", Model Architecture and Inference: fused normalization/RoPE and
+ * packed KV writers; [CHUNK] "Future work": the cache holds kv_c_normed, the
+ * latent after its RMSNorm).  Read by host pointer during the call.
+ *   norm_weight : bf16 [kv_lora_rank]; NULL writes the latent as given
+ *   norm_eps    : RMSNorm epsilon, finite and >= 0
+ *   cos_sin     : fp32 [max_position][qk_rope_dim], the caller's RoPE table:
+ *                 for position p the cosines of its qk_rope_dim/2 angles, then
+ *                 their sines; NULL writes k_pe as given
+ *   positions   : int64 [num_tokens] (device), each token's position; needed
+ *                 with cos_sin.  Positions outside [0, max_position) are a
+ *                 caller error (clamped on the device)
+ *   rope_interleaved : 1 rotates pairs (2i, 2i+1), 0 pairs (i, i + Dr/2)
+ */
+typedef struct {
+  const void* norm_weight;
+  float norm_eps;
+  const float* cos_sin;
+  const int64_t* positions;
+  int32_t max_position;
+  int32_t rope_interleaved;
+} mla_kv_transform;
+
+/*
+ * mla_write_kv_fused - mla_write_kv of the transformed rows: for each token,
+ *   latent  c' = bf16( c / sqrt(mean(c^2) + eps) * norm_weight )   (RMSNorm)
+ *   rope    r' = bf16( (a cos - b sin, b cos + a sin) on each pair (a, b) )
+ * (arithmetic in fp32 on the device, each value rounded to bf16 to nearest
+ * even), then written exactly as mla_write_kv writes [c' | r'] (bit copy, or
+ * the fp8 quantisation).  Arguments and errors as mla_write_kv; c_kv and k_pe
+ * are the un-normalised latent and the un-rotated rope part.
+ */
+mla_status mla_write_kv_fused(const mla_cache* cache, int32_t layer_idx,
+                              const void* c_kv, int64_t c_kv_row_stride,
+                              const void* k_pe, int64_t k_pe_row_stride,
+                              const mla_kv_transform* transform,
+                              const int64_t* slot_mapping, int32_t num_tokens, void* stream);
+
+/*
  * Workspace bytes mla_decode needs for these arguments (0 if the arguments
  * are invalid).  Depends on batch, heads, dims, w_uk/w_uv presence and the
  * number of workgroups (the device's compute-unit count unless forced).

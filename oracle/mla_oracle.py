@@ -50,6 +50,11 @@ What is computed (all in float64 unless stated):
   stale pad-row locations scatter garbage into live pages).
 * Split-KV combine: the log-sum-exp merge of partial results over disjoint
   key subsets (the pages are silent; this is the textbook identity).
+* Fused write ("Support dsv4 model", Model Architecture and Inference: fused
+  normalization/RoPE and packed KV writers; [CHUNK] "Future work": the cache
+  holds kv_c_normed): RMSNorm of the latent and RoPE of the rope part, each
+  rounded to bf16, then the ordinary write.  The readings are stated at
+  write_kv_fused.
 """
 from __future__ import annotations
 
@@ -160,6 +165,90 @@ def write_kv(cache, cache_scale, layer, c_kv_bits, k_pe_bits, slot_mapping, kv_d
         codes, sc = fp8_quantize_tokens(rows)
         cache[layer, pages, offs, :] = codes
         cache_scale[layer, pages, offs] = sc
+
+
+# --------------------------------------------------------------------------
+# Fused normalisation and RoPE before the cache write ("Support dsv4 model",
+# Model Architecture and Inference: fused normalization/RoPE and packed KV
+# writers; "[Attention] MLA with chunked prefill", Future work: the cache holds
+# kv_c_normed, the latent after its RMSNorm; "feat(serving): DeepSeek-V2/V3
+# paged-attention shim (MLA)", Changes: the HF MLA projection + RoPE are
+# reproduced before the cache).  Readings, since the pages give no formulas:
+#   * RMSNorm over the R latent values: y = x / sqrt(mean(x^2) + eps) * w, with
+#     a bf16 weight w [R] and the caller's eps;
+#   * RoPE on the Dr rope values with a caller-supplied table cos_sin
+#     [max_pos, Dr] (cos of the Dr/2 angles of a position, then their sines),
+#     on pairs (2i, 2i+1) ("interleaved") or (i, i + Dr/2) ("half split"):
+#     (a, b) -> (a cos - b sin, b cos + a sin), angle i of the position;
+#   * both results are rounded to bf16 (nearest even) before the write, as the
+#     unfused producer would hand bf16 rows to the write; the write itself is
+#     write_kv's (bit copy, or the fp8 quantisation).
+# --------------------------------------------------------------------------
+
+
+def f64_to_bf16_bits(x) -> np.ndarray:
+    """Round float64 values to bfloat16 (nearest, ties to even) in one step
+    (no intermediate float32 rounding).  Finite inputs below 2^128."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros(x.shape, dtype=np.float64)
+    nz = x != 0
+    _, e = np.frexp(np.abs(x[nz]))              # |x| = f * 2^e, f in [0.5, 1)
+    # bf16 keeps 8 significant bits for normal values (exponent >= -126) and
+    # a fixed quantum of 2^-133 below that
+    quantum = np.ldexp(1.0, np.maximum(e - 8, -133))
+    out[nz] = np.rint(x[nz] / quantum) * quantum  # exact scaling; rint ties to even
+    assert np.all(np.abs(out) < 2.0 ** 128), "bf16 overflow"
+    bits = (out.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    # keep the sign of values that round to zero
+    bits |= np.where(np.signbit(x), np.uint16(0x8000), np.uint16(0))
+    return bits
+
+
+def rms_norm(x_bits, weight_bits, eps):
+    """y = x / sqrt(mean(x^2) + eps) * w over the last axis, in float64."""
+    x = bf16_bits_to_f64(x_bits)
+    w = bf16_bits_to_f64(weight_bits)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + float(eps)) * w
+
+
+def rope_pairs(dr, interleaved):
+    """Index pairs (first, second) the rotation acts on, one per angle."""
+    h = dr // 2
+    i = np.arange(h)
+    return (2 * i, 2 * i + 1) if interleaved else (i, i + h)
+
+
+def rope_rotate(x_bits, positions, cos_sin, interleaved):
+    """Rotate each pair (a, b) of x [T, Dr] by angle i of its token's position:
+    (a cos - b sin, b cos + a sin), cos / sin read from the fp32 table
+    cos_sin[position] (first half cosines, second half sines).  float64."""
+    x = bf16_bits_to_f64(x_bits)
+    pos = np.asarray(positions, dtype=np.int64)
+    tab = np.asarray(cos_sin, dtype=np.float32).astype(np.float64)
+    dr = x.shape[-1]
+    h = dr // 2
+    cos, sin = tab[pos, :h], tab[pos, h:]
+    first, second = rope_pairs(dr, interleaved)
+    a, b = x[:, first], x[:, second]
+    y = np.empty_like(x)
+    y[:, first] = a * cos - b * sin
+    y[:, second] = b * cos + a * sin
+    return y
+
+
+def write_kv_fused(cache, cache_scale, layer, c_kv_bits, k_pe_bits, slot_mapping, positions,
+                   norm_weight_bits, eps, cos_sin, interleaved, kv_dtype=KV_BF16):
+    """The cache write with the latent's RMSNorm and the rope part's rotation
+    folded in: write_kv of bf16(rms_norm(c_kv)) and bf16(rope(k_pe)).  A None
+    weight skips the norm, a None table the rotation (the row is then copied
+    as given).  Pad rows (slot < 0) are skipped like write_kv's."""
+    c = (c_kv_bits if norm_weight_bits is None
+         else f64_to_bf16_bits(rms_norm(c_kv_bits, norm_weight_bits, eps)))
+    r = (k_pe_bits if cos_sin is None
+         else f64_to_bf16_bits(rope_rotate(k_pe_bits, positions, cos_sin, interleaved)))
+    write_kv(cache, cache_scale, layer, c, r, slot_mapping, kv_dtype)
+    return c, r
 
 
 # --------------------------------------------------------------------------

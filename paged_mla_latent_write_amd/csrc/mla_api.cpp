@@ -438,6 +438,48 @@ mla_status mla_write_kv(const mla_cache* cache, int32_t layer_idx, const void* c
   return to_status(e);
 }
 
+mla_status mla_write_kv_fused(const mla_cache* cache, int32_t layer_idx, const void* c_kv,
+                              int64_t c_kv_row_stride, const void* k_pe, int64_t k_pe_row_stride,
+                              const mla_kv_transform* tf, const int64_t* slot_mapping,
+                              int32_t num_tokens, void* stream) {
+  mla_status st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if (layer_idx < 0 || layer_idx >= cache->num_layers || num_tokens < 0 || !tf)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (!isfinite(tf->norm_eps) || tf->norm_eps < 0.f) return MLA_ERR_INVALID_ARGUMENT;
+  if (tf->cos_sin && (!tf->positions || tf->max_position <= 0 || cache->qk_rope_dim % 2 != 0))
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (num_tokens == 0) return MLA_OK;
+  if (!c_kv || !slot_mapping || (cache->qk_rope_dim > 0 && !k_pe)) return MLA_ERR_INVALID_ARGUMENT;
+  if (c_kv_row_stride < cache->kv_lora_rank || k_pe_row_stride < cache->qk_rope_dim)
+    return MLA_ERR_INVALID_ARGUMENT;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_check_enabled()) {
+    if ((st = debug_check_slots(cache, slot_mapping, num_tokens, s)) != MLA_OK) return st;
+    if (tf->cos_sin) {
+      std::vector<int64_t> pos;
+      if ((st = fetch(&pos, tf->positions, num_tokens, s)) != MLA_OK) return st;
+      for (const int64_t p : pos)
+        if (p < 0 || p >= tf->max_position) return MLA_ERR_INVALID_ARGUMENT;
+    }
+  }
+  const int64_t slots = static_cast<int64_t>(cache->num_pages) * cache->page_size;
+  const int64_t D = cache->kv_lora_rank + cache->qk_rope_dim;
+  void* layer = static_cast<char*>(cache->data) + layer_idx * slots * D * elem_bytes(cache->dtype);
+  float* scale = cache->dtype == MLA_KV_FP8_E4M3 ? cache->scale + layer_idx * slots : nullptr;
+  mla::KvTransform k;
+  k.norm_weight = static_cast<const uint16_t*>(tf->norm_weight);
+  k.eps = tf->norm_eps;
+  k.cos_sin = tf->cos_sin;
+  k.positions = tf->positions;
+  k.max_position = tf->max_position;
+  k.interleaved = tf->rope_interleaved != 0;
+  return to_status(mla::launch_write_kv_fused(
+      layer, scale, cache->dtype == MLA_KV_BF16 ? mla::kKvBf16 : mla::kKvFp8, slots,
+      cache->kv_lora_rank, cache->qk_rope_dim, static_cast<const uint16_t*>(c_kv), c_kv_row_stride,
+      static_cast<const uint16_t*>(k_pe), k_pe_row_stride, slot_mapping, num_tokens, k, s));
+}
+
 size_t mla_decode_workspace_size(const mla_cache* cache, const mla_attn* attn, int32_t batch,
                                  int32_t max_blocks_per_seq) {
   if (check_cache(cache) != MLA_OK || check_attn(attn) != MLA_OK || batch < 0 ||

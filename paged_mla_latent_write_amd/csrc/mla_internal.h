@@ -83,11 +83,27 @@ struct AttnArgs {
 // Compute units of the current device (cached per device; -1 on error).
 int current_cu_count();
 
+// Device-side view of mla_kv_transform (the fused write's norm and rotation).
+struct KvTransform {
+  const uint16_t* norm_weight;  // bf16 [R], or null: no RMSNorm
+  float eps;
+  const float* cos_sin;         // fp32 [max_position][Dr], or null: no rotation
+  const int64_t* positions;     // [T]
+  int32_t max_position;
+  int32_t interleaved;          // 1: pairs (2i, 2i+1); 0: pairs (i, i + Dr/2)
+};
+
 // ---- launchers (each returns the launch's hipGetLastError) ----
 hipError_t launch_write_kv(void* cache_layer, float* scale_layer, int32_t dtype, int64_t num_slots,
                            int32_t R, int32_t Dr, const uint16_t* c_kv, int64_t c_stride,
                            const uint16_t* k_pe, int64_t k_stride, const int64_t* slots,
                            int32_t num_tokens, hipStream_t s);
+
+hipError_t launch_write_kv_fused(void* cache_layer, float* scale_layer, int32_t dtype,
+                                 int64_t num_slots, int32_t R, int32_t Dr, const uint16_t* c_kv,
+                                 int64_t c_stride, const uint16_t* k_pe, int64_t k_stride,
+                                 const int64_t* slots, int32_t num_tokens, const KvTransform& tf,
+                                 hipStream_t s);
 
 hipError_t launch_plan(int mode, int32_t batch, int32_t num_items, const int32_t* context_lens,
                        const int32_t* query_start_loc, int32_t window, int32_t max_ctx,

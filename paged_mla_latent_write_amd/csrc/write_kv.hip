@@ -85,7 +85,122 @@ __global__ __launch_bounds__(256) void write_kv_fp8_kernel(
   if (lane == 0) scale_out[s] = scale;
 }
 
+// The write with the latent's RMSNorm and the rope part's rotation folded in
+// ("Support dsv4 model", Model Architecture and Inference: fused
+// normalization/RoPE and packed KV writers; "[Attention] MLA with chunked
+// prefill", Future work: the cache holds kv_c_normed).  One wavefront per
+// token, element j of the row in lane j % 64, slot j / 64 of the lane's
+// registers:
+//   latent  y = x * (1 / sqrt(sum(x^2) / R + eps)) * w    (fp32, wave-wide sum)
+//   rope    (a, b) -> (a cos - b sin, b cos + a sin), the pair's partner read
+//           from the input row, angle i of the token's position in the table
+// Each result is rounded to bf16 (nearest even), then written exactly as
+// write_kv writes a bf16 row: a bit copy, or the per-token E4M3 quantisation.
+template <bool kFp8>
+__global__ __launch_bounds__(256) void write_kv_fused_kernel(
+    void* __restrict__ cache, float* __restrict__ scale_out, int64_t num_slots, int32_t R,
+    int32_t Dr, const uint16_t* __restrict__ c_kv, int64_t c_stride,
+    const uint16_t* __restrict__ k_pe, int64_t k_stride, const int64_t* __restrict__ slots,
+    int32_t T, KvTransform tf) {
+  const int lane = threadIdx.x & 63;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
+  if (i >= T) return;
+  const int64_t s = slots[i];
+  if (s < 0 || s >= num_slots) return;
+  const int D = R + Dr;
+  const uint16_t* src_c = c_kv + i * c_stride;
+  const uint16_t* src_r = k_pe + i * k_stride;
+  constexpr int kMaxPerLane = 16;  // D <= 1024
+  float v[kMaxPerLane];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxPerLane; ++k) {
+    const int j = lane + 64 * k;
+    float x = 0.f;
+    if (j < R) {
+      x = bf16_to_f32(src_c[j]);
+      ss = fmaf(x, x, ss);
+    } else if (j < D) {
+      x = bf16_to_f32(src_r[j - R]);
+    }
+    v[k] = x;
+  }
+  if (tf.norm_weight != nullptr) {
+    const float r = 1.0f / sqrtf(wave_sum(ss) / static_cast<float>(R) + tf.eps);
+#pragma unroll
+    for (int k = 0; k < kMaxPerLane; ++k) {
+      const int j = lane + 64 * k;
+      if (j < R) v[k] = bf16_to_f32(f32_to_bf16(v[k] * r * bf16_to_f32(tf.norm_weight[j])));
+    }
+  }
+  if (tf.cos_sin != nullptr) {
+    const int64_t pos = min(max(tf.positions[i], int64_t{0}), static_cast<int64_t>(tf.max_position - 1));
+    const float* cs = tf.cos_sin + pos * Dr;
+    const int h = Dr >> 1;
+#pragma unroll
+    for (int k = 0; k < kMaxPerLane; ++k) {
+      const int j = lane + 64 * k;
+      if (j >= R && j < D) {
+        const int jr = j - R;
+        int fi, partner;
+        bool first;
+        if (tf.interleaved) {
+          fi = jr >> 1;
+          partner = jr ^ 1;
+          first = (jr & 1) == 0;
+        } else {
+          first = jr < h;
+          fi = first ? jr : jr - h;
+          partner = first ? jr + h : jr - h;
+        }
+        const float c = cs[fi], sn = cs[h + fi];
+        const float xp = bf16_to_f32(src_r[partner]);
+        const float y = first ? v[k] * c - xp * sn : v[k] * c + xp * sn;
+        v[k] = bf16_to_f32(f32_to_bf16(y));
+      }
+    }
+  }
+  if (!kFp8) {
+    uint16_t* dst = static_cast<uint16_t*>(cache) + s * D;
+#pragma unroll
+    for (int k = 0; k < kMaxPerLane; ++k) {
+      const int j = lane + 64 * k;
+      if (j < D) dst[j] = static_cast<uint16_t>(__float_as_uint(v[k]) >> 16);
+    }
+    return;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxPerLane; ++k) amax = fmaxf(amax, fabsf(v[k]));
+  amax = wave_max(amax);
+  const float scale = amax == 0.f ? 1.0f : amax / 448.0f;
+  uint8_t* dst = static_cast<uint8_t*>(cache) + s * D;
+#pragma unroll
+  for (int k = 0; k < kMaxPerLane; ++k) {
+    const int j = lane + 64 * k;
+    if (j < D) dst[j] = static_cast<uint8_t>(f32_to_e4m3_satfinite(v[k] / scale));
+  }
+  if (lane == 0) scale_out[s] = scale;
+}
+
 }  // namespace
+
+hipError_t launch_write_kv_fused(void* cache_layer, float* scale_layer, int32_t dtype,
+                                 int64_t num_slots, int32_t R, int32_t Dr, const uint16_t* c_kv,
+                                 int64_t c_stride, const uint16_t* k_pe, int64_t k_stride,
+                                 const int64_t* slots, int32_t num_tokens, const KvTransform& tf,
+                                 hipStream_t s) {
+  const dim3 grid((num_tokens + kWavesPerBlock - 1) / kWavesPerBlock);
+  const dim3 block(64 * kWavesPerBlock);
+  if (dtype == kKvBf16) {
+    hipLaunchKernelGGL(write_kv_fused_kernel<false>, grid, block, 0, s, cache_layer, nullptr,
+                       num_slots, R, Dr, c_kv, c_stride, k_pe, k_stride, slots, num_tokens, tf);
+  } else {
+    hipLaunchKernelGGL(write_kv_fused_kernel<true>, grid, block, 0, s, cache_layer, scale_layer,
+                       num_slots, R, Dr, c_kv, c_stride, k_pe, k_stride, slots, num_tokens, tf);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_write_kv(void* cache_layer, float* scale_layer, int32_t dtype, int64_t num_slots,
                            int32_t R, int32_t Dr, const uint16_t* c_kv, int64_t c_stride,

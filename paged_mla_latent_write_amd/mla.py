@@ -35,7 +35,7 @@ MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3 = 1
 MLA_FLAG_GENERIC_KERNELS = 1
 
-EXPORTED = ("mla_write_kv", "mla_decode_workspace_size", "mla_decode", "mla_decode_noalloc",
+EXPORTED = ("mla_write_kv", "mla_write_kv_fused", "mla_decode_workspace_size", "mla_decode", "mla_decode_noalloc",
             "mla_decode_combine", "mla_prefill_workspace_size", "mla_prefill_chunk",
             "mla_status_string", "mla_version")
 NOALLOC_SCRATCH_BYTES = 192 << 20  # MLA_NOALLOC_SCRATCH_BYTES in include/mla.h
@@ -56,6 +56,12 @@ class MlaAttnStruct(ctypes.Structure):
                 ("kernel_events", ctypes.c_void_p * 2)]
 
 
+class MlaKvTransformStruct(ctypes.Structure):
+    _fields_ = [("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float),
+                ("cos_sin", ctypes.c_void_p), ("positions", ctypes.c_void_p),
+                ("max_position", ctypes.c_int32), ("rope_interleaved", ctypes.c_int32)]
+
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
@@ -72,6 +78,8 @@ def _sig(name, res, *args):
 
 
 _write_kv = _sig("mla_write_kv", _I32, _CP, _I32, _P, _I64, _P, _I64, _P, _I32, _P)
+_write_kv_fused = _sig("mla_write_kv_fused", _I32, _CP, _I32, _P, _I64, _P, _I64,
+                       ctypes.POINTER(MlaKvTransformStruct), _P, _I32, _P)
 _decode_ws = _sig("mla_decode_workspace_size", _SZ, _CP, _AP, _I32, _I32)
 _decode = _sig("mla_decode", _I32, _CP, _I32, _AP, _P, _I64, _I64, _P, _I64, _I64, _P, _I32, _P,
                _I32, _P, _P, _P, _SZ, _P)
@@ -261,6 +269,40 @@ def write_kv(cache: KVCache, layer_idx: int, c_kv: torch.Tensor, k_pe: torch.Ten
     st = cache.struct()
     _check(_write_kv(ctypes.byref(st), layer_idx, _ptr(c_kv), c_kv.stride(0), _ptr(k_pe),
                      k_pe.stride(0), _ptr(slot_mapping), T, _stream(stream)), "mla_write_kv")
+
+
+def write_kv_fused(cache: KVCache, layer_idx: int, c_kv: torch.Tensor, k_pe: torch.Tensor,
+                   slot_mapping: torch.Tensor, *, positions=None, norm_weight=None, eps=1e-6,
+                   cos_sin=None, interleaved=True, stream=None):
+    """mla_write_kv of bf16(RMSNorm(c_kv) * norm_weight) and bf16(RoPE(k_pe)):
+    c_kv the un-normalised latent bf16 [T, R], k_pe the un-rotated rope part
+    bf16 [T, Dr], positions int64 [T], norm_weight bf16 [R] (None: no norm),
+    cos_sin fp32 [max_position, Dr] (None: no rotation)."""
+    _need(c_kv.dtype == torch.bfloat16 and k_pe.dtype == torch.bfloat16, "c_kv and k_pe must be bf16")
+    _need(c_kv.dim() == 2 and c_kv.shape[1] == cache.kv_lora_rank and c_kv.stride(-1) == 1,
+          f"c_kv must be [T, {cache.kv_lora_rank}] with unit inner stride")
+    _need(k_pe.dim() == 2 and k_pe.shape[1] == cache.qk_rope_dim and k_pe.stride(-1) == 1,
+          f"k_pe must be [T, {cache.qk_rope_dim}] with unit inner stride")
+    T = int(c_kv.shape[0])
+    _need(k_pe.shape[0] == T and slot_mapping.dtype == torch.int64 and slot_mapping.numel() == T
+          and slot_mapping.is_contiguous(), "c_kv, k_pe and slot_mapping (int64) must have T tokens")
+    if norm_weight is not None:
+        _need(norm_weight.dtype == torch.bfloat16 and norm_weight.is_contiguous() and
+              norm_weight.numel() == cache.kv_lora_rank, "norm_weight: contiguous bf16 [R]")
+    max_pos = 0
+    if cos_sin is not None:
+        _need(cos_sin.dtype == torch.float32 and cos_sin.dim() == 2 and cos_sin.is_contiguous() and
+              cos_sin.shape[1] == cache.qk_rope_dim, "cos_sin: contiguous fp32 [max_position, Dr]")
+        _need(positions is not None and positions.dtype == torch.int64 and positions.numel() == T and
+              positions.is_contiguous(), "positions: contiguous int64 [T]")
+        max_pos = int(cos_sin.shape[0])
+    _same_device(cache.data, c_kv, k_pe, slot_mapping, positions, norm_weight, cos_sin)
+    tf = MlaKvTransformStruct(_ptr(norm_weight), float(eps), _ptr(cos_sin), _ptr(positions), max_pos,
+                              1 if interleaved else 0)
+    st = cache.struct()
+    _check(_write_kv_fused(ctypes.byref(st), layer_idx, _ptr(c_kv), c_kv.stride(0), _ptr(k_pe),
+                           k_pe.stride(0), ctypes.byref(tf), _ptr(slot_mapping), T, _stream(stream)),
+           "mla_write_kv_fused")
 
 
 def decode_workspace_size(cache: KVCache, attn: MlaAttnStruct, batch: int, max_blocks: int) -> int:

@@ -363,3 +363,50 @@ def prefill_case(dims: Dims, prefix_lens, chunk_lens, *, seed=0, window=0, sharp
                 ctx_slots=slots_for(bt, ctx, dims.page_size), block_tables=bt, context_lens=ctx,
                 q_nope=q_nope, q_pe=q_pe, w_uk=w_uk, w_uv=w_uv, query_start_loc=qsl,
                 poison_page=poison, meta=dict(seed=seed, sharp=sharp))
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the cache write with the latent's RMSNorm and the rope rotation
+# folded in
+# ---------------------------------------------------------------------------
+
+def rope_table(max_pos, dr, theta=10000.0):
+    """A caller's RoPE table, fp32 [max_pos, dr]: for position p the cosines
+    of p * theta^(-2i/dr), i < dr/2, then their sines (angles in float64,
+    rounded once to float32).  An input of the write, like its rows."""
+    inv = theta ** (-np.arange(0, dr, 2, dtype=np.float64) / dr)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+
+
+@dataclass
+class FusedWriteCase:
+    """Pre-norm latents c_kv [T, R] and un-rotated k_pe [T, Dr] (bf16 bits),
+    their positions [T] int64, slots [T] int64 (some -1 pad rows), a bf16 norm
+    weight [R], eps, and a rope table [max_pos, Dr] fp32."""
+    dims: Dims
+    num_pages: int
+    c_kv: np.ndarray
+    k_pe: np.ndarray
+    positions: np.ndarray
+    slots: np.ndarray
+    norm_weight: np.ndarray
+    eps: float
+    cos_sin: np.ndarray
+
+
+def fused_write_case(dims: Dims, T, *, seed=0, num_pages=None, max_pos=40000, pad_every=0,
+                     c_std=1.0, k_std=1.0):
+    rng = _rng(seed)
+    ps = dims.page_size
+    num_pages = num_pages or (T + ps - 1) // ps + 1
+    slots = rng.permutation(num_pages * ps)[:T].astype(np.int64)
+    if pad_every:
+        slots[::pad_every] = -1
+    c_kv = bf16_normal(rng, (T, dims.R), c_std)
+    k_pe = bf16_normal(rng, (T, dims.Dr), k_std)
+    positions = rng.integers(0, max_pos, size=T).astype(np.int64)
+    w = f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(dims.R)).astype(np.float32))
+    return FusedWriteCase(dims=dims, num_pages=num_pages, c_kv=c_kv, k_pe=k_pe, positions=positions,
+                          slots=slots, norm_weight=w, eps=1e-6, cos_sin=rope_table(max_pos, dims.Dr))
+

@@ -499,6 +499,134 @@ def test_fp8_decode_uses_dequantised_values():
 
 
 # ---------------------------------------------------------------------------
+# Fused RMSNorm + RoPE write
+# ---------------------------------------------------------------------------
+
+def test_f64_to_bf16_matches_torch_on_float32_and_ties_to_even():
+    rng = np.random.default_rng(7)
+    x32 = np.concatenate([rng.standard_normal(50000).astype(np.float32) * 10.0 ** rng.integers(-30, 30, 50000),
+                          np.array([0.0, -0.0, 1e-40, -1e-40, 3e38], np.float32)]).astype(np.float32)
+    want = torch.from_numpy(x32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.f64_to_bf16_bits(x32.astype(np.float64)), want)
+    # exact midpoints between neighbouring bf16 values go to the even one,
+    # and the smallest step past a midpoint goes away from it
+    grid = O.bf16_bits_to_f64(np.arange(0x3F80, 0x3F90, dtype=np.uint16))  # 1.0 .. 1.1171875
+    mids = (grid[:-1] + grid[1:]) / 2
+    got = O.f64_to_bf16_bits(mids)
+    lo_bits = np.arange(0x3F80, 0x3F8F, dtype=np.uint16)
+    assert np.array_equal(got, np.where(lo_bits % 2 == 0, lo_bits, lo_bits + 1))
+    assert np.array_equal(O.f64_to_bf16_bits(np.nextafter(mids, np.inf)), lo_bits + 1)
+    assert np.array_equal(O.f64_to_bf16_bits(np.nextafter(mids, -np.inf)), lo_bits)
+    # a float64 just past a midpoint that float32 would round onto the midpoint
+    # (double rounding) still goes up
+    tricky = grid[0] + 2.0 ** -8 + 2.0 ** -40
+    assert O.f64_to_bf16_bits(np.array([tricky]))[0] == 0x3F81
+
+
+def test_rms_norm_closed_forms_and_torch():
+    rng = np.random.default_rng(8)
+    R = 512
+    c = W.f32_to_bf16_bits(np.full((1, R), 0.75, np.float32))
+    w = W.f32_to_bf16_bits(np.full(R, 1.5, np.float32))
+    y = O.rms_norm(c, w, 0.0)
+    assert np.allclose(y, 1.5, rtol=0, atol=1e-15)          # constant row -> weight
+    y = O.rms_norm(c, w, 1.0)
+    assert np.allclose(y, 0.75 / math.sqrt(0.5625 + 1.0) * 1.5, rtol=1e-15)
+    x = W.bf16_normal(rng, (16, R), 2.0)
+    wr = W.f32_to_bf16_bits((1 + 0.1 * rng.standard_normal(R)).astype(np.float32))
+    want = torch.nn.functional.rms_norm(torch.from_numpy(O.bf16_bits_to_f64(x)), (R,),
+                                        torch.from_numpy(O.bf16_bits_to_f64(wr)), eps=1e-6).numpy()
+    assert np.max(np.abs(O.rms_norm(x, wr, 1e-6) - want)) < 1e-13
+    # scale invariance with eps = 0
+    x2 = W.f32_to_bf16_bits(O.bf16_bits_to_f32(x) * np.float32(4.0))
+    assert np.max(np.abs(O.rms_norm(x2, wr, 0.0) - O.rms_norm(x, wr, 0.0))) < 1e-13
+
+
+@pytest.mark.parametrize("interleaved", [True, False])
+def test_rope_relative_position_property(interleaved):
+    """RoPE's defining property: <rope(q, p), rope(k, p')> depends on p - p'
+    only; and position 0 is the identity, pair norms are kept."""
+    rng = np.random.default_rng(9)
+    Dr = 64
+    tab = W.rope_table(4096, Dr)
+    q = W.bf16_normal(rng, (1, Dr), 1.0)
+    k = W.bf16_normal(rng, (1, Dr), 1.0)
+    dots = []
+    for base in (0, 77, 1000, 3000):
+        qa = O.rope_rotate(q, [base + 19], tab, interleaved)
+        kb = O.rope_rotate(k, [base], tab, interleaved)
+        dots.append(float((qa @ kb.T)[0, 0]))
+    assert max(dots) - min(dots) < 2e-5 * max(abs(d) for d in dots)
+    assert np.array_equal(O.rope_rotate(q, [0], tab, interleaved), O.bf16_bits_to_f64(q))
+    y = O.rope_rotate(q, [1234], tab, interleaved)
+    a, b = O.rope_pairs(Dr, interleaved)
+    x = O.bf16_bits_to_f64(q)
+    n_in = x[:, a] ** 2 + x[:, b] ** 2
+    n_out = y[:, a] ** 2 + y[:, b] ** 2
+    assert np.allclose(n_in, n_out, rtol=2e-7)
+
+
+def test_rope_layouts_agree_through_the_pair_permutation():
+    rng = np.random.default_rng(10)
+    Dr = 64
+    tab = W.rope_table(100, Dr)
+    x = W.bf16_normal(rng, (5, Dr), 1.0)
+    pos = rng.integers(0, 100, 5)
+    ia, ib = O.rope_pairs(Dr, True)
+    ha, hb = O.rope_pairs(Dr, False)
+    perm = np.empty(Dr, dtype=np.int64)
+    perm[ha], perm[hb] = ia, ib          # half-split slot j holds interleaved element perm[j]
+    y_int = O.rope_rotate(x, pos, tab, True)
+    y_half = O.rope_rotate(x[:, perm], pos, tab, False)
+    assert np.array_equal(y_half, y_int[:, perm])
+
+
+def test_fused_write_without_norm_or_rope_is_write_kv():
+    d = W.Dims(H=1, R=64, Dr=16, Dn=8, Dv=8, page_size=16)
+    fc = W.fused_write_case(d, 40, seed=11, pad_every=5)
+    for kv in (O.KV_BF16, O.KV_FP8):
+        dt = np.uint16 if kv == O.KV_BF16 else np.uint8
+        a = np.zeros((1, fc.num_pages, 16, d.D), dt)
+        b = np.zeros_like(a)
+        sa = np.zeros((1, fc.num_pages, 16), np.float32)
+        sb = np.zeros_like(sa)
+        O.write_kv(a, sa, 0, fc.c_kv, fc.k_pe, fc.slots, kv)
+        O.write_kv_fused(b, sb, 0, fc.c_kv, fc.k_pe, fc.slots, fc.positions, None, 0.0, None, True, kv)
+        assert np.array_equal(a, b) and np.array_equal(sa, sb)
+
+
+def test_fused_write_rows_are_normed_and_rotated():
+    """Read back through the cache: the latent part has unit RMS up to the
+    weight and bf16 rounding, and the rope part keeps each pair's norm."""
+    d = W.Dims(H=1, R=512, Dr=64, Dn=8, Dv=8, page_size=64)
+    fc = W.fused_write_case(d, 30, seed=12, c_std=3.0)
+    cache = np.zeros((1, fc.num_pages, 64, d.D), np.uint16)
+    O.write_kv_fused(cache, None, 0, fc.c_kv, fc.k_pe, fc.slots, fc.positions, fc.norm_weight,
+                     fc.eps, fc.cos_sin, True)
+    rows = O.bf16_bits_to_f64(cache[0].reshape(-1, d.D)[fc.slots])
+    w = O.bf16_bits_to_f64(fc.norm_weight)
+    rms = np.sqrt(np.mean((rows[:, :512] / w) ** 2, axis=1))
+    assert np.allclose(rms, 1.0, atol=5e-3)
+    x = O.bf16_bits_to_f64(fc.k_pe)
+    a, b = O.rope_pairs(64, True)
+    assert np.allclose(rows[:, 512:][:, a] ** 2 + rows[:, 512:][:, b] ** 2, x[:, a] ** 2 + x[:, b] ** 2,
+                       rtol=2e-2, atol=1e-6)
+
+
+def test_planted_rope_sign_is_caught(monkeypatch):
+    real = O.rope_rotate
+
+    def bad(x_bits, positions, cos_sin, interleaved):
+        tab = np.asarray(cos_sin, np.float32).copy()
+        tab[:, tab.shape[1] // 2:] *= -1  # rotate the wrong way for one operand only
+        return real(x_bits, positions, tab if np.asarray(positions).ravel()[0] % 2 else cos_sin,
+                    interleaved)
+    monkeypatch.setattr(O, "rope_rotate", bad)
+    with pytest.raises(AssertionError):
+        test_rope_relative_position_property(True)
+
+
+# ---------------------------------------------------------------------------
 # Planted mistakes: the pins above must catch them
 # ---------------------------------------------------------------------------
 
