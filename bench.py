@@ -68,7 +68,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=100)
-    p.add_argument("--workload", default="v3", choices=["v3", "v3fp8", "v2lite", "mixed"])
+    p.add_argument("--workload", default="v3", choices=["v3", "v3fp8", "v2lite", "mixed", "v3sparse"])
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="CPU time budget for the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -223,7 +223,10 @@ def clock_medians(clocks):
     return res
 
 
-def cpu_baseline(case, budget_s, gpu_out_f64):
+SPARSE_TOPK = 2048
+
+
+def cpu_baseline(case, budget_s, gpu_out_f64, lists=None):
     """Time the oracle on requests taken in order until the budget is spent."""
     from oracle import mla_oracle as O
 
@@ -238,13 +241,19 @@ def cpu_baseline(case, budget_s, gpu_out_f64):
     while len(done) < case.batch and (elapsed < budget_s or len(done) < 1):
         b = len(done)
         t0 = time.perf_counter()
-        out, _ = O.decode(hc, hs, case.kv_dtype, 0, case.q_nope, case.q_pe, case.block_tables,
-                          case.context_lens, case.w_uk, case.w_uv, case.scale, case.window,
-                          requests=[b])
+        if lists is None:
+            out, _ = O.decode(hc, hs, case.kv_dtype, 0, case.q_nope, case.q_pe, case.block_tables,
+                              case.context_lens, case.w_uk, case.w_uv, case.scale, case.window,
+                              requests=[b])
+            tokens += int(case.context_lens[b])
+        else:
+            out, _ = O.sparse_attention(hc, hs, case.kv_dtype, 0, case.q_nope, case.q_pe, lists,
+                                        case.block_tables, case.context_lens, case.w_uk, case.w_uv,
+                                        case.scale, case.window, rows=[b])
+            tokens += int(np.sum((lists[b] >= 0) & (lists[b] < case.context_lens[b])))
         elapsed += time.perf_counter() - t0
         outs.append(out[b])
         done.append(b)
-        tokens += int(case.context_lens[b])
     threads = blas_threads()
     model, affinity = host_info()
     ref = np.stack(outs)
@@ -253,7 +262,8 @@ def cpu_baseline(case, budget_s, gpu_out_f64):
            "rel_l2": float(np.linalg.norm(got - ref) / np.linalg.norm(ref))}
     return {"value": tokens / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "cpu_model": model, "cores_available": affinity,
-            "sample": f"fp64 numpy oracle (absorbed form) on the first {len(done)} of {case.batch} "
+            "sample": f"fp64 numpy oracle (absorbed form{'' if lists is None else ', key lists'}) on "
+                      f"the first {len(done)} of {case.batch} "
                       f"requests ({tokens} attended tokens, {elapsed:.1f} s); cache write "
                       f"{write_s:.1f} s untimed"}, err
 
@@ -464,9 +474,16 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    case = {"v3": W.v3, "v3fp8": W.v3fp8, "v2lite": W.v2lite}[args.workload]()
+    case = {"v3": W.v3, "v3fp8": W.v3fp8, "v2lite": W.v2lite, "v3sparse": W.v3}[args.workload]()
     d = case.dims
     B = case.batch
+    sparse = args.workload == "v3sparse"
+    lists_np = lists = None
+    if sparse:
+        # one 2048-entry key list per request: distinct positions of its context
+        lists_np = W.key_lists(1400, case.context_lens - 1, case.context_lens, SPARSE_TOPK,
+                               pad_frac=0.0, invalid_frac=0.0)
+        lists = torch.from_numpy(lists_np).to(dev)
 
     def bf16(u16):
         return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -505,13 +522,20 @@ def main():
 
     def step(ev=None):
         mla.write_kv(cache, case.layer, new_c, new_r, new_slots)
-        mla.decode(cache, case.layer, q_nope, q_pe, bt, ctx, scale=case.scale, w_uk=w_uk, w_uv=w_uv,
-                   window=case.window, out=out, lse=lse, workspace=ws, flags=flags,
-                   kernel_events=ev)
+        if sparse:
+            mla.sparse_attention(cache, case.layer, q_nope, q_pe, lists, bt, ctx, scale=case.scale,
+                                 w_uk=w_uk, w_uv=w_uv, window=case.window, out=out, lse=lse,
+                                 workspace=ws, flags=flags, kernel_events=ev)
+        else:
+            mla.decode(cache, case.layer, q_nope, q_pe, bt, ctx, scale=case.scale, w_uk=w_uk,
+                       w_uv=w_uv, window=case.window, out=out, lse=lse, workspace=ws, flags=flags,
+                       kernel_events=ev)
 
     protocol = None
     if args.protocol_steps > 0:
-        kv_set = int(case.context_lens.astype(np.int64).sum()) * (d.D * (1 if fp8 else 2) + (4 if fp8 else 0))
+        kept = (int(np.sum((lists_np >= 0) & (lists_np < case.context_lens[:, None]))) if sparse
+                else int(case.context_lens.astype(np.int64).sum()))
+        kv_set = kept * (d.D * (1 if fp8 else 2) + (4 if fp8 else 0))
         protocol = protocol_phase(torch, step, args.protocol_steps, dev, kv_set < FLUSH_BELOW_BYTES)
         print(f"[bench] protocol: {protocol}", file=sys.stderr, flush=True)
 
@@ -538,7 +562,10 @@ def main():
     print(f"[bench] timed {K} steps: {wall * 1e3 / K:.3f} ms/step, attention kernel {kern_ms:.3f} ms",
           file=sys.stderr, flush=True)
 
-    tokens = int(case.context_lens.astype(np.int64).sum())
+    if sparse:
+        tokens = int(np.sum((lists_np >= 0) & (lists_np < case.context_lens[:, None])))
+    else:
+        tokens = int(case.context_lens.astype(np.int64).sum())
     per_tok_bytes = d.D * (1 if fp8 else 2) + (4 if fp8 else 0)
     kv_bytes = tokens * per_tok_bytes
     flops = tokens * 2 * d.H * (2 * d.R + d.Dr)
@@ -578,12 +605,15 @@ def main():
         "config": {
             "workload": {"v3": "DeepSeek-V3-shape MLA decode, one GPU's full head set",
                          "v3fp8": "V3-shape MLA decode with fp8 e4m3 latent cache",
-                         "v2lite": "DeepSeek-V2-Lite-shape MLA decode"}[args.workload],
+                         "v2lite": "DeepSeek-V2-Lite-shape MLA decode",
+                         "v3sparse": f"V3-shape MLA decode over {SPARSE_TOPK}-entry key lists "
+                                     f"(index-list attention)"}[args.workload],
             "batch": B, "heads": d.H, "kv_lora_rank": d.R, "qk_rope": d.Dr, "qk_nope": d.Dn,
             "v_head": d.Dv, "page_size": d.page_size,
             "context_lens": f"{int(case.context_lens.min())}..{int(case.context_lens.max())}",
             "attended_tokens": tokens, "kv_cache": case.kv_dtype,
-            "step": "mla_write_kv(batch newest tokens) + mla_decode",
+            "step": "mla_write_kv(batch newest tokens) + "
+                    + ("mla_sparse_attention" if sparse else "mla_decode"),
             "kernels": "generic" if args.generic else "default",
         },
         "step_hbm_gbs": (kv_bytes + fixed_bytes) / step_s / 1e9,
@@ -597,7 +627,7 @@ def main():
     if not args.no_cpu_baseline:
         bits = out.view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32) << 16
         gpu_out = bits.view(np.float32).astype(np.float64)
-        base, err = cpu_baseline(case, args.cpu_seconds, gpu_out)
+        base, err = cpu_baseline(case, args.cpu_seconds, gpu_out, lists_np)
         line["cpu_baseline"] = base
         line["parity_sample"] = err
     print(json.dumps(line), flush=True)

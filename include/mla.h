@@ -296,6 +296,41 @@ mla_status mla_prefill_chunk(const mla_cache* cache, int32_t layer_idx, const ml
                              void* out, float* lse_or_null,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Index-list (top-k / sparse) attention ("[Models] Support MLA_SWA
+ * functionality", Modifications: a top-k indexer builds each query's key
+ * list, the sliding window is expressed as such a list; "Support dsv4 model",
+ * Model Architecture and Inference: sparse index construction).
+ *
+ * Query row r attends to the positions key_indices[r][0 .. topk-1] of its
+ * request's sequence that its ordinary visible range holds: t <= p, and
+ * p - w < t with a window w > 0 (attn->window), where p is the row's position
+ * (decode: n_b - 1; prefill: n_b - m_b + i as in mla_prefill_chunk).
+ * Negative entries are unused slots; entries outside the range are ignored;
+ * a position listed twice in one row is a caller error.  A row with no kept
+ * key gets out 0 and lse -inf.  The softmax does not depend on list order.
+ *   key_indices     : int32 [num_q][topk] (device), row r's list
+ *   query_start_loc : int32 [batch + 1] (device) for prefill rows, or NULL
+ *                     for decode (then num_q == batch, row b = request b)
+ *   max_q_len       : host; the longest chunk (prefill), ignored for decode
+ *   other arguments : as mla_decode / mla_prefill_chunk (q rows [num_q][H][..],
+ *                     out [num_q][H][Dv or R], lse [num_q][H] or NULL)
+ * The kept rows of each query are first gathered, in list order, into pages
+ * of the workspace; the rows are then attended by the decode kernels.  Query
+ * rows are processed in chunks that bound that gather to 512 MiB.
+ */
+size_t mla_sparse_workspace_size(const mla_cache* cache, const mla_attn* attn, int32_t batch,
+                                 int32_t num_q, int32_t topk, int32_t max_blocks_per_seq);
+mla_status mla_sparse_attention(const mla_cache* cache, int32_t layer_idx, const mla_attn* attn,
+                                const void* q_nope, int64_t q_nope_stride_t,
+                                int64_t q_nope_stride_h, const void* q_pe, int64_t q_pe_stride_t,
+                                int64_t q_pe_stride_h, const int32_t* key_indices, int32_t topk,
+                                const int32_t* query_start_loc, int32_t num_q, int32_t max_q_len,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t batch,
+                                void* out, float* lse_or_null,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* mla_status_string(mla_status status);
 

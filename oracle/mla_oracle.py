@@ -404,6 +404,59 @@ def prefill_chunk(cache, cache_scale, kv_dtype, layer, q_nope_bits, q_pe_bits, q
     return out, lse
 
 
+def sparse_visible(key_list, p, window):
+    """Index-list attention ("[Models] Support MLA_SWA functionality",
+    Modifications: a top-k indexer builds each query's key list, and the
+    sliding window is expressed as such a list; "Support dsv4 model", Model
+    Architecture and Inference: sparse index construction).  Reading: a query
+    at position p attends to the listed positions that its ordinary visible
+    range holds (causal, and the window when w > 0); negative entries are
+    unused slots and other entries are ignored.  Listed positions must be
+    distinct.  Returns the kept positions in list order."""
+    lst = np.asarray(key_list, dtype=np.int64)
+    lo, hi = visible_range(p, window)
+    keep = lst[(lst >= lo) & (lst < hi)]
+    assert np.unique(keep).size == keep.size, "a position listed twice"
+    return keep
+
+
+def sparse_attention(cache, cache_scale, kv_dtype, layer, q_nope_bits, q_pe_bits, key_indices,
+                     block_tables, context_lens, w_uk_bits, w_uv_bits, scale, window=0,
+                     query_start_loc=None, form="absorbed", rows=None):
+    """Attention of each query row over its key list (see sparse_visible).
+    Decode (query_start_loc None): row b is request b's query at n_b - 1.
+    Prefill: rows query_start_loc[b] .. query_start_loc[b+1]-1 are request b's
+    chunk at positions n_b - m_b + i.  key_indices [rows, K] int.  Returns
+    (out [rows, H, Dv or R], lse [rows, H]); rows not in `rows` stay NaN."""
+    R = cache.shape[3] - np.asarray(q_pe_bits).shape[-1]
+    qn = bf16_bits_to_f64(q_nope_bits)
+    qp = bf16_bits_to_f64(q_pe_bits)
+    w_uk, w_uv = _weights(w_uk_bits), _weights(w_uv_bits)
+    Tq, H = qn.shape[0], qn.shape[1]
+    dv = R if w_uv is None else w_uv.shape[1]
+    out = np.full((Tq, H, dv), np.nan)
+    lse = np.full((Tq, H), np.nan)
+    attend = _attend(form)
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    if query_start_loc is None:
+        qsl = np.arange(len(ctx) + 1, dtype=np.int64)
+    else:
+        qsl = np.asarray(query_start_loc, dtype=np.int64)
+    wanted = None if rows is None else set(int(r) for r in rows)
+    for b in range(len(qsl) - 1):
+        s0, s1 = int(qsl[b]), int(qsl[b + 1])
+        m, n = s1 - s0, int(ctx[b])
+        mine = [r for r in range(s0, s1) if wanted is None or r in wanted]
+        if not mine:
+            continue
+        X = gather_latent(cache, cache_scale, kv_dtype, layer, block_tables[b], n)
+        for r in mine:
+            p = n - m + (r - s0)
+            keep = sparse_visible(key_indices[r], p, window)
+            out[r], lse[r] = attend(qn[r], qp[r], X[keep], w_uk, w_uv, scale, R)
+    return out, lse
+
+
 def combine(o_parts, lse_parts):
     """Log-sum-exp merge of partials over disjoint key subsets:
     lse = log sum_s exp(lse_s); o = sum_s exp(lse_s - lse) o_s.  A partial with

@@ -7,6 +7,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <atomic>
 #include <vector>
 
@@ -124,6 +125,57 @@ bool make_layout(const mla_cache* c, const mla_attn* a, int64_t num_items, Layou
   L->redo = off;
   off = align_up(off + sizeof(int32_t) * G);
   L->total = off;
+  return true;
+}
+
+// Index-list attention workspace: per chunk of query rows, the compacted
+// rows (and fp8 scales), kept counts and identity block tables, then the
+// dense decode workspace for one chunk.
+constexpr size_t kSparseCompactBudget = size_t{512} << 20;
+
+struct SparseLayout {
+  int64_t chunk = 0;
+  int32_t rows_per_item = 0, nblk = 0;
+  size_t data = 0, scale = 0, ctx = 0, bt = 0, dense = 0, total = 0;
+  Layout dense_layout;
+};
+
+mla_cache compact_cache_desc(const mla_cache* c, void* data, float* scale, int64_t items, int32_t nblk) {
+  mla_cache cc = *c;
+  cc.data = data;
+  cc.scale = scale;
+  cc.num_layers = 1;
+  cc.num_pages = static_cast<int32_t>(items * nblk);
+  cc.page_size = mla::kCompactPage;
+  return cc;
+}
+
+bool make_sparse_layout(const mla_cache* c, const mla_attn* a, int64_t num_q, int32_t topk,
+                        SparseLayout* S) {
+  const int64_t rows = std::max<int64_t>(mla::kCompactPage,
+                                         (static_cast<int64_t>(topk) + mla::kCompactPage - 1) /
+                                             mla::kCompactPage * mla::kCompactPage);
+  if (rows > (1 << 24)) return false;
+  S->rows_per_item = static_cast<int32_t>(rows);
+  S->nblk = static_cast<int32_t>(rows / mla::kCompactPage);
+  const bool fp8 = c->dtype == MLA_KV_FP8_E4M3;
+  const size_t row_bytes = static_cast<size_t>(c->kv_lora_rank + c->qk_rope_dim) * elem_bytes(c->dtype);
+  const size_t per_item = rows * row_bytes + (fp8 ? rows * 4 : 0);
+  S->chunk = std::max<int64_t>(1, std::min<int64_t>(num_q, kSparseCompactBudget / per_item));
+  if (S->chunk * S->nblk >= (1ll << 31)) return false;
+  size_t off = 0;
+  S->data = off;
+  off = align_up(off + S->chunk * rows * row_bytes);
+  S->scale = off;
+  if (fp8) off = align_up(off + S->chunk * rows * sizeof(float));
+  S->ctx = off;
+  off = align_up(off + S->chunk * sizeof(int32_t));
+  S->bt = off;
+  off = align_up(off + S->chunk * S->nblk * sizeof(int32_t));
+  S->dense = off;
+  const mla_cache cc = compact_cache_desc(c, nullptr, nullptr, S->chunk, S->nblk);
+  if (!make_layout(&cc, a, S->chunk, &S->dense_layout)) return false;
+  S->total = off + S->dense_layout.total;
   return true;
 }
 
@@ -478,6 +530,96 @@ mla_status mla_write_kv_fused(const mla_cache* cache, int32_t layer_idx, const v
       layer, scale, cache->dtype == MLA_KV_BF16 ? mla::kKvBf16 : mla::kKvFp8, slots,
       cache->kv_lora_rank, cache->qk_rope_dim, static_cast<const uint16_t*>(c_kv), c_kv_row_stride,
       static_cast<const uint16_t*>(k_pe), k_pe_row_stride, slot_mapping, num_tokens, k, s));
+}
+
+size_t mla_sparse_workspace_size(const mla_cache* cache, const mla_attn* attn, int32_t batch,
+                                 int32_t num_q, int32_t topk, int32_t max_blocks_per_seq) {
+  if (check_cache(cache) != MLA_OK || check_attn(attn) != MLA_OK || batch < 0 || num_q < 0 ||
+      topk <= 0 || max_blocks_per_seq <= 0)
+    return 0;
+  SparseLayout S;
+  if (!make_sparse_layout(cache, attn, std::max<int64_t>(num_q, 1), topk, &S)) return 0;
+  return S.total;
+}
+
+mla_status mla_sparse_attention(const mla_cache* cache, int32_t layer_idx, const mla_attn* attn,
+                                const void* q_nope, int64_t q_nope_stride_t,
+                                int64_t q_nope_stride_h, const void* q_pe, int64_t q_pe_stride_t,
+                                int64_t q_pe_stride_h, const int32_t* key_indices, int32_t topk,
+                                const int32_t* query_start_loc, int32_t num_q, int32_t max_q_len,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, int32_t batch, void* out,
+                                float* lse_or_null, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  mla_status st = check_cache(cache);
+  if (st != MLA_OK) return st;
+  if ((st = check_attn(attn)) != MLA_OK) return st;
+  if (layer_idx < 0 || layer_idx >= cache->num_layers) return MLA_ERR_INVALID_ARGUMENT;
+  if (batch < 0 || num_q < 0 || topk <= 0 || max_blocks_per_seq <= 0 || max_q_len < 0)
+    return MLA_ERR_INVALID_ARGUMENT;
+  if (!query_start_loc && num_q != batch) return MLA_ERR_INVALID_ARGUMENT;
+  if (batch == 0 || num_q == 0) return MLA_OK;
+  if (!q_nope || !q_pe || !key_indices || !block_tables || !context_lens || !out)
+    return MLA_ERR_INVALID_ARGUMENT;
+  const int64_t max_ctx64 = static_cast<int64_t>(max_blocks_per_seq) * cache->page_size;
+  if (max_ctx64 > (1ll << 30)) return MLA_ERR_UNSUPPORTED;
+  SparseLayout S;
+  if (!make_sparse_layout(cache, attn, num_q, topk, &S)) return MLA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < S.total) return MLA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MLA_ERR_WORKSPACE;
+  const int64_t slots = static_cast<int64_t>(cache->num_pages) * cache->page_size;
+  const int64_t D = cache->kv_lora_rank + cache->qk_rope_dim;
+  const char* layer = static_cast<const char*>(cache->data) + layer_idx * slots * D * elem_bytes(cache->dtype);
+  const uintptr_t need_align = cache->dtype == MLA_KV_BF16 ? 16 : 8;
+  if ((reinterpret_cast<uintptr_t>(layer) & (need_align - 1)) != 0) return MLA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_check_enabled()) {
+    st = debug_check_attention(query_start_loc ? mla::kPlanPrefill : mla::kPlanDecode, cache,
+                               block_tables, max_blocks_per_seq, context_lens, batch,
+                               query_start_loc, num_q, query_start_loc ? max_q_len : 1, s);
+    if (st != MLA_OK) return st;
+  }
+  const int H = attn->num_heads;
+  const int dv = attn->w_uv ? attn->v_head_dim : cache->kv_lora_rank;
+  mla_attn dense = *attn;
+  dense.window = 0;  // applied by the compaction
+  for (int64_t r0 = 0; r0 < num_q; r0 += S.chunk) {
+    const int32_t n = static_cast<int32_t>(std::min<int64_t>(S.chunk, num_q - r0));
+    mla::CompactArgs ca;
+    ca.cache = layer;
+    ca.scale = cache->dtype == MLA_KV_FP8_E4M3 ? cache->scale + layer_idx * slots : nullptr;
+    ca.num_pages = cache->num_pages;
+    ca.page_size = cache->page_size;
+    ca.page_shift = __builtin_ctz(static_cast<unsigned>(cache->page_size));
+    ca.D = static_cast<int32_t>(D);
+    ca.elem_bytes = static_cast<int32_t>(elem_bytes(cache->dtype));
+    ca.key_indices = key_indices;
+    ca.topk = topk;
+    ca.query_start_loc = query_start_loc;
+    ca.batch = batch;
+    ca.context_lens = context_lens;
+    ca.block_tables = block_tables;
+    ca.max_blocks = max_blocks_per_seq;
+    ca.max_ctx = max_ctx64;
+    ca.window = attn->window;
+    ca.row0 = r0;
+    ca.rows_per_item = S.rows_per_item;
+    ca.out_data = at<char>(workspace, S.data);
+    ca.out_scale = cache->dtype == MLA_KV_FP8_E4M3 ? at<float>(workspace, S.scale) : nullptr;
+    ca.out_ctx = at<int32_t>(workspace, S.ctx);
+    ca.out_bt = at<int32_t>(workspace, S.bt);
+    if (mla::launch_compact_keys(ca, n, s) != hipSuccess) return MLA_ERR_HIP;
+    const mla_cache cc = compact_cache_desc(cache, ca.out_data, ca.out_scale, n, S.nblk);
+    st = run_attention(mla::kPlanDecode, &cc, 0, &dense,
+                       static_cast<const uint16_t*>(q_nope) + r0 * q_nope_stride_t, q_nope_stride_t,
+                       q_nope_stride_h, static_cast<const uint16_t*>(q_pe) + r0 * q_pe_stride_t,
+                       q_pe_stride_t, q_pe_stride_h, nullptr, n, ca.out_bt, S.nblk, ca.out_ctx, n, 1,
+                       static_cast<uint16_t*>(out) + r0 * H * dv,
+                       lse_or_null ? lse_or_null + r0 * H : nullptr, at<char>(workspace, S.dense),
+                       S.dense_layout.total, stream);
+    if (st != MLA_OK) return st;
+  }
+  return MLA_OK;
 }
 
 size_t mla_decode_workspace_size(const mla_cache* cache, const mla_attn* attn, int32_t batch,

@@ -93,6 +93,30 @@ struct KvTransform {
   int32_t interleaved;          // 1: pairs (2i, 2i+1); 0: pairs (i, i + Dr/2)
 };
 
+// Index-list attention: the compaction of each query item's kept keys into
+// its own run of kCompactPage-token pages (sparse.hip).
+constexpr int kCompactPage = 64;
+struct CompactArgs {
+  const void* cache;             // layer base, [num_pages][page_size][D]
+  const float* scale;            // layer base [num_pages][page_size] (fp8), else null
+  int32_t num_pages, page_size, page_shift, D, elem_bytes;
+  const int32_t* key_indices;    // [rows][topk]
+  int32_t topk;
+  const int32_t* query_start_loc;  // [batch + 1] (prefill) or null (decode)
+  int32_t batch;
+  const int32_t* context_lens;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  int64_t max_ctx;               // max_blocks * page_size
+  int32_t window;
+  int64_t row0;                  // first query row of this launch
+  int32_t rows_per_item;         // pages per item * kCompactPage
+  void* out_data;                // [items][rows_per_item][D]
+  float* out_scale;              // [items][rows_per_item] (fp8), else null
+  int32_t* out_ctx;              // [items] kept keys
+  int32_t* out_bt;               // [items][rows_per_item / kCompactPage] identity block table
+};
+
 // ---- launchers (each returns the launch's hipGetLastError) ----
 hipError_t launch_write_kv(void* cache_layer, float* scale_layer, int32_t dtype, int64_t num_slots,
                            int32_t R, int32_t Dr, const uint16_t* c_kv, int64_t c_stride,
@@ -104,6 +128,8 @@ hipError_t launch_write_kv_fused(void* cache_layer, float* scale_layer, int32_t 
                                  int64_t c_stride, const uint16_t* k_pe, int64_t k_stride,
                                  const int64_t* slots, int32_t num_tokens, const KvTransform& tf,
                                  hipStream_t s);
+
+hipError_t launch_compact_keys(const CompactArgs& a, int32_t items, hipStream_t s);
 
 hipError_t launch_plan(int mode, int32_t batch, int32_t num_items, const int32_t* context_lens,
                        const int32_t* query_start_loc, int32_t window, int32_t max_ctx,

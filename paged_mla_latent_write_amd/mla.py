@@ -37,6 +37,7 @@ MLA_FLAG_GENERIC_KERNELS = 1
 
 EXPORTED = ("mla_write_kv", "mla_write_kv_fused", "mla_decode_workspace_size", "mla_decode", "mla_decode_noalloc",
             "mla_decode_combine", "mla_prefill_workspace_size", "mla_prefill_chunk",
+            "mla_sparse_workspace_size", "mla_sparse_attention",
             "mla_status_string", "mla_version")
 NOALLOC_SCRATCH_BYTES = 192 << 20  # MLA_NOALLOC_SCRATCH_BYTES in include/mla.h
 
@@ -89,6 +90,9 @@ _combine = _sig("mla_decode_combine", _I32, _P, _P, _I32, _I32, _I32, _I32, _P, 
 _prefill_ws = _sig("mla_prefill_workspace_size", _SZ, _CP, _AP, _I32, _I32, _I32)
 _prefill = _sig("mla_prefill_chunk", _I32, _CP, _I32, _AP, _P, _I64, _I64, _P, _I64, _I64, _P, _I32,
                 _I32, _P, _I32, _P, _I32, _P, _P, _P, _SZ, _P)
+_sparse_ws = _sig("mla_sparse_workspace_size", _SZ, _CP, _AP, _I32, _I32, _I32, _I32)
+_sparse = _sig("mla_sparse_attention", _I32, _CP, _I32, _AP, _P, _I64, _I64, _P, _I64, _I64, _P, _I32,
+               _P, _I32, _I32, _P, _I32, _P, _I32, _P, _P, _P, _SZ, _P)
 _status_string = _sig("mla_status_string", ctypes.c_char_p, _I32)
 _version = _sig("mla_version", ctypes.c_char_p)
 
@@ -435,6 +439,60 @@ def prefill_chunk(cache: KVCache, layer_idx: int, q_nope, q_pe, query_start_loc,
                     _ptr(q_pe), ps_t, ps_h, _ptr(query_start_loc), Tq, int(max_q_len),
                     _ptr(block_tables), max_blocks, _ptr(context_lens), B, _ptr(out), _ptr(lse),
                     _ptr(ws), ws.numel(), _stream(stream)), "mla_prefill_chunk")
+    return out, lse
+
+
+def sparse_attention(cache: KVCache, layer_idx: int, q_nope, q_pe, key_indices, block_tables,
+                     context_lens, *, scale, query_start_loc=None, max_q_len=0, w_uk=None,
+                     w_uv=None, window=0, out=None, lse=None, want_lse=True, workspace=None,
+                     num_workgroups=0, flags=0, kernel_events=None, stream=None):
+    """Index-list attention: query row r attends to the listed positions
+    key_indices[r] (int32 [rows, topk]; -1 unused) inside its causal / window
+    range.  Decode when query_start_loc is None (one row per request), else
+    prefill rows as in prefill_chunk.  Returns (out, lse)."""
+    rows, H = int(q_nope.shape[0]), int(q_nope.shape[1])
+    _need(context_lens.dim() == 1, "context_lens: int32 [B]")
+    B = int(context_lens.shape[0])
+    dn, dv = _check_heads(cache, q_nope, q_pe, w_uk, w_uv)
+    _check_tables(block_tables, context_lens, B)
+    _need(key_indices.dtype == torch.int32 and key_indices.dim() == 2 and key_indices.is_contiguous()
+          and key_indices.shape[0] == rows and key_indices.shape[1] > 0,
+          f"key_indices: contiguous int32 [{rows}, topk]")
+    if query_start_loc is None:
+        _need(rows == B, "decode: one query row per request")
+    else:
+        _need(query_start_loc.dtype == torch.int32 and query_start_loc.numel() == B + 1 and
+              query_start_loc.is_contiguous(), "query_start_loc: contiguous int32 [B + 1]")
+    _check_outputs(out, lse, (rows, H, dv))
+    _same_device(cache.data, q_nope, q_pe, w_uk, w_uv, key_indices, block_tables, context_lens,
+                 query_start_loc, out, lse)
+    attn = _attn_struct(H, dn, dv, w_uk, w_uv, scale, window, num_workgroups, flags, kernel_events)
+    st = cache.struct()
+    topk = int(key_indices.shape[1])
+    max_blocks = int(block_tables.shape[1])
+    dev = q_nope.device
+    fresh = []
+    if out is None:
+        out = torch.empty((rows, H, dv), dtype=torch.bfloat16, device=dev)
+        fresh.append(out)
+    if lse is None and want_lse:
+        lse = torch.empty((rows, H), dtype=torch.float32, device=dev)
+        fresh.append(lse)
+    nbytes = int(_sparse_ws(ctypes.byref(st), ctypes.byref(attn), B, rows, topk, max_blocks))
+    if nbytes == 0 and rows > 0:
+        raise MlaError(MLA_ERR_INVALID_ARGUMENT, "mla_sparse_workspace_size")
+    ws = (workspace or Workspace()).get(nbytes, dev)
+    if workspace is None:
+        fresh.append(ws)
+    elif isinstance(stream, torch.cuda.Stream):
+        ws.record_stream(stream)
+    _keep_alive_on(stream, *fresh)
+    qs_t, qs_h = _row_strides(q_nope)
+    ps_t, ps_h = _row_strides(q_pe)
+    _check(_sparse(ctypes.byref(st), layer_idx, ctypes.byref(attn), _ptr(q_nope), qs_t, qs_h,
+                   _ptr(q_pe), ps_t, ps_h, _ptr(key_indices), topk, _ptr(query_start_loc), rows,
+                   int(max_q_len), _ptr(block_tables), max_blocks, _ptr(context_lens), B, _ptr(out),
+                   _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)), "mla_sparse_attention")
     return out, lse
 
 

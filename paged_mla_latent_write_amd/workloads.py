@@ -410,3 +410,30 @@ def fused_write_case(dims: Dims, T, *, seed=0, num_pages=None, max_pos=40000, pa
     return FusedWriteCase(dims=dims, num_pages=num_pages, c_kv=c_kv, k_pe=k_pe, positions=positions,
                           slots=slots, norm_weight=w, eps=1e-6, cos_sin=rope_table(max_pos, dims.Dr))
 
+
+# ---------------------------------------------------------------------------
+# Key lists for index-list (top-k) attention
+# ---------------------------------------------------------------------------
+
+def key_lists(seed, query_pos, context_lens_per_row, topk, *, pad_frac=0.1, invalid_frac=0.05):
+    """One key list of `topk` int32 entries per query row: distinct positions
+    drawn from [0, p] (p the row's query position), in random order; about
+    pad_frac of the slots are -1 (unused) and invalid_frac hold positions the
+    row must ignore (future positions p < t < n, or t >= n)."""
+    rng = _rng(seed)
+    rows = len(query_pos)
+    out = np.full((rows, topk), -1, dtype=np.int32)
+    for r in range(rows):
+        p, n = int(query_pos[r]), int(context_lens_per_row[r])
+        n_pad = int(round(pad_frac * topk))
+        n_bad = int(round(invalid_frac * topk))
+        n_ok = min(topk - n_pad - n_bad, p + 1)
+        ok = rng.choice(p + 1, size=n_ok, replace=False) if n_ok > 0 else np.zeros(0, np.int64)
+        bad = rng.integers(p + 1, n + 1000, size=n_bad)
+        bad = np.setdiff1d(bad, ok)  # never a duplicate of a kept key
+        vals = np.concatenate([ok, bad])
+        rng.shuffle(vals)
+        slots = rng.permutation(topk)[:len(vals)]
+        out[r, slots] = vals
+    return out
+

@@ -627,6 +627,125 @@ def test_planted_rope_sign_is_caught(monkeypatch):
 
 
 # ---------------------------------------------------------------------------
+# Index-list (top-k) attention
+# ---------------------------------------------------------------------------
+
+def _sparse_case(window=0, sharp=True, ctx=(40, 77, 5)):
+    case = W.custom(small_dims(H=3, R=16, Dr=8, Dn=8, Dv=8, ps=8), list(ctx), seed=61, sharp=True,
+                    window=window)
+    return case
+
+
+def test_sparse_list_covering_the_range_equals_dense():
+    """A list holding every visible position (shuffled, with pads, future and
+    out-of-range positions) gives the dense result."""
+    for window in (0, 6):
+        case = _sparse_case(window)
+        cache, sc = build_cache(case)
+        rng = np.random.default_rng(5)
+        K = 100
+        lists = np.full((case.batch, K), -1, np.int32)
+        for b, n in enumerate(case.context_lens):
+            vals = np.concatenate([rng.permutation(int(n)), [int(n) + 3, int(n) + 50]])
+            lists[b, rng.permutation(K)[:len(vals)]] = vals
+        got, glse = O.sparse_attention(cache, sc, case.kv_dtype, 0, case.q_nope, case.q_pe, lists,
+                                       case.block_tables, case.context_lens, case.w_uk, case.w_uv,
+                                       case.scale, window)
+        ref, rlse = run_decode(case, cache, sc, window=window)
+        assert rel(got, ref) < 1e-12 and np.max(np.abs(glse - rlse)) < 1e-12
+
+
+def test_sparse_list_brute_force_and_window_as_list():
+    """Scalar brute force over the listed keys (contiguous rows, math.fsum),
+    and the window expressed as a key list equals the windowed decode."""
+    case = _sparse_case()
+    cache, sc = build_cache(case)
+    d = case.dims
+    qpos = case.context_lens - 1
+    lists = W.key_lists(62, qpos, case.context_lens, 24)
+    got, _ = O.sparse_attention(cache, sc, case.kv_dtype, 0, case.q_nope, case.q_pe, lists,
+                                case.block_tables, case.context_lens, case.w_uk, case.w_uv, case.scale)
+    wuk = O.bf16_bits_to_f64(case.w_uk)
+    wuv = O.bf16_bits_to_f64(case.w_uv)
+    for b in range(case.batch):
+        rows = request_rows(case, b)
+        c = O.bf16_bits_to_f64(case.ctx_c_kv[rows])
+        r = O.bf16_bits_to_f64(case.ctx_k_pe[rows])
+        keys = [int(t) for t in lists[b] if 0 <= t <= qpos[b]]
+        qn = O.bf16_bits_to_f64(case.q_nope[b])
+        qp = O.bf16_bits_to_f64(case.q_pe[b])
+        for h in range(d.H):
+            sc_ = [case.scale * math.fsum([math.fsum(qn[h][i] * wuk[h][i][j] * c[t][j]
+                                                     for i in range(d.Dn) for j in range(d.R)),
+                                           math.fsum(qp[h][i] * r[t][i] for i in range(d.Dr))])
+                   for t in keys]
+            m = max(sc_)
+            e = [math.exp(x - m) for x in sc_]
+            tot = math.fsum(e)
+            want = [math.fsum(e[k] * math.fsum(wuv[h][v][j] * c[keys[k]][j] for j in range(d.R))
+                              for k in range(len(keys))) / tot for v in range(d.Dv)]
+            assert rel(got[b, h], np.array(want)) < 1e-11
+    # window 6 as a key list
+    w = 6
+    wl = np.full((case.batch, 10), -1, np.int32)
+    for b, n in enumerate(case.context_lens):
+        pos = np.arange(max(0, int(n) - w), int(n))
+        wl[b, :len(pos)] = pos[::-1]
+    got, _ = O.sparse_attention(cache, sc, case.kv_dtype, 0, case.q_nope, case.q_pe, wl,
+                                case.block_tables, case.context_lens, case.w_uk, case.w_uv, case.scale)
+    ref, _ = run_decode(case, cache, sc, window=w)
+    assert rel(got, ref) < 1e-12
+
+
+def test_sparse_prefill_rows_and_edge_lists():
+    """Prefill rows see only listed keys up to their own position; a
+    one-entry list returns that token's value; an empty list gives 0, -inf;
+    a repeated position is refused."""
+    d = small_dims(H=2, R=16, Dr=8, Dn=8, Dv=8, ps=8)
+    case = W.prefill_case(d, [20, 3], [6, 4], seed=63, sharp=True)
+    cache, sc = build_cache(case)
+    Tq = case.q_nope.shape[0]
+    lists = np.full((Tq, 30), -1, np.int32)
+    for b in range(2):
+        s0, s1 = int(case.query_start_loc[b]), int(case.query_start_loc[b + 1])
+        n = int(case.context_lens[b])
+        for r in range(s0, s1):
+            lists[r, :n] = np.random.default_rng(r).permutation(n)  # includes future keys
+    got, _ = O.sparse_attention(cache, sc, case.kv_dtype, 0, case.q_nope, case.q_pe, lists,
+                                case.block_tables, case.context_lens, case.w_uk, case.w_uv,
+                                case.scale, query_start_loc=case.query_start_loc)
+    ref, _ = O.prefill_chunk(cache, sc, case.kv_dtype, 0, case.q_nope, case.q_pe, case.query_start_loc,
+                             case.block_tables, case.context_lens, case.w_uk, case.w_uv, case.scale)
+    assert rel(got, ref) < 1e-12
+    one = np.full((Tq, 4), -1, np.int32)
+    one[:, 1] = 2
+    got, lse = O.sparse_attention(cache, sc, case.kv_dtype, 0, case.q_nope, case.q_pe, one,
+                                  case.block_tables, case.context_lens, case.w_uk, case.w_uv,
+                                  case.scale, query_start_loc=case.query_start_loc)
+    X0 = O.gather_latent(cache, sc, case.kv_dtype, 0, case.block_tables[0], 26)
+    want = np.einsum("hvr,r->hv", O.bf16_bits_to_f64(case.w_uv), X0[2, :16])
+    assert np.max(np.abs(got[0] - want)) < 1e-13
+    none = np.full((Tq, 4), -1, np.int32)
+    got, lse = O.sparse_attention(cache, sc, case.kv_dtype, 0, case.q_nope, case.q_pe, none,
+                                  case.block_tables, case.context_lens, case.w_uk, case.w_uv,
+                                  case.scale, query_start_loc=case.query_start_loc)
+    assert (got == 0).all() and np.isneginf(lse).all()
+    with pytest.raises(AssertionError):
+        O.sparse_visible([3, 5, 3], 10, 0)
+
+
+def test_planted_sparse_future_key_is_caught(monkeypatch):
+    """A key list filter that forgets the causal bound lets prefill rows see
+    listed future tokens; the prefill pin catches it."""
+    def no_causal_bound(key_list, p, window):
+        lst = np.asarray(key_list, dtype=np.int64)
+        return lst[lst >= O.visible_range(p, window)[0]]
+    monkeypatch.setattr(O, "sparse_visible", no_causal_bound)
+    with pytest.raises(AssertionError):
+        test_sparse_prefill_rows_and_edge_lists()
+
+
+# ---------------------------------------------------------------------------
 # Planted mistakes: the pins above must catch them
 # ---------------------------------------------------------------------------
 
