@@ -78,6 +78,8 @@ def parse():
     p.add_argument("--protocol-steps", type=int, default=300,
                    help="steps of the per-step protocol (512 MB cache-evicting write between steps, "
                         "median/min from HIP events), run before the timed loop; 0 skips it")
+    p.add_argument("--prefill-form", default="auto", choices=["auto", "absorbed", "expanded"],
+                   help="mixed workload: the prefill form (auto lets the library choose)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="first run a 1 GiB device copy 3 times (the known-size kernel that "
                         "scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings)")
@@ -325,6 +327,8 @@ def main_mixed(args):
     K = args.steps
     ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in layers] for _ in range(K)]
 
+    pflags = {"auto": 0, "absorbed": mla.MLA_FLAG_PREFILL_ABSORBED,
+              "expanded": mla.MLA_FLAG_PREFILL_EXPANDED}[args.prefill_form]
     for L in layers:
         ml = L["ml"]
         L["pout"] = torch.empty((ml.q_nope_p.shape[0], d.H, d.Dv), dtype=torch.bfloat16, device=dev)
@@ -340,7 +344,7 @@ def main_mixed(args):
             if e: e[1].record()
             mla.prefill_chunk(cache, ml.layer, *L["qp"], L["qsl"], chunk, L["bt_p"], L["ctx_p"],
                               scale=ml.scale, w_uk=L["w"][0], w_uv=L["w"][1], window=ml.window,
-                              out=L["pout"], want_lse=False, workspace=L["ws"][0])
+                              out=L["pout"], want_lse=False, workspace=L["ws"][0], flags=pflags)
             if e: e[2].record()
             mla.decode(cache, ml.layer, *L["qd"], L["bt_d"], L["ctx_d"], scale=ml.scale,
                        w_uk=L["w"][0], w_uv=L["w"][1], window=ml.window, out=L["dout"],
@@ -399,7 +403,7 @@ def main_mixed(args):
         "config": {"workload": "mixed step: 8 x 512-token chunks + 120 decode requests per layer, "
                                "4 layers, windows (128, 0, 128, 0)",
                    "heads": d.H, "kv_lora_rank": d.R, "qk_rope": d.Dr, "page_size": d.page_size,
-                   "attended_pairs": pairs},
+                   "attended_pairs": pairs, "prefill_form": args.prefill_form},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
                      "kernel": "whole step (prefill dominates the flops)"},

@@ -93,6 +93,12 @@ typedef struct {
 
 /* Flags for mla_attn.flags (testing and comparison only). */
 #define MLA_FLAG_GENERIC_KERNELS 1u /* use the plain (non-MFMA) kernels for every shape */
+/* mla_prefill_chunk form: absorbed (latent-space attention, as decode) or
+ * expanded (keys and values up-projected per head through W_UK / W_UV into
+ * the workspace, [CHUNK] "Future work"); without either flag the library
+ * picks one (see mla_prefill_chunk). */
+#define MLA_FLAG_PREFILL_ABSORBED 2u
+#define MLA_FLAG_PREFILL_EXPANDED 4u
 
 /*
  * Per-call attention parameters.
@@ -285,6 +291,18 @@ size_t mla_prefill_workspace_size(const mla_cache* cache, const mla_attn* attn, 
  *   total_q_tokens, max_q_len : host values
  *   out    : bf16 [total_q_tokens][num_heads][v_head_dim or kv_lora_rank]
  *   lse_or_null : fp32 [total_q_tokens][num_heads] or NULL
+ * Two forms compute the same result.  Absorbed: each query row is a decode
+ * item of the latent-space kernels.  Expanded ([CHUNK] "Future work"): the
+ * keys the chunk's rows can see are up-projected per head through W_UK and
+ * W_UV (kv_b_proj) into the workspace, in passes of at most 2048 keys sized so
+ * that one pass of all requests fits 512 MiB, and attended with q_nope (128)
+ * + q_pe (64) against [W_UK c ; k_pe], values W_UV c (128); pass results are
+ * merged by log-sum-exp.  The expanded form needs w_uk and w_uv, qk_rope_dim
+ * 64, qk_nope_dim = v_head_dim = 128 and kv_lora_rank a multiple of 64.
+ * MLA_FLAG_PREFILL_ABSORBED / _EXPANDED choose; without a flag the expanded
+ * form runs for windowed calls (window > 0) whose chunks average at least 64
+ * rows, the absorbed one otherwise.  mla_prefill_workspace_size returns the
+ * chosen form's size (the same attn flags must be passed to both calls).
  */
 mla_status mla_prefill_chunk(const mla_cache* cache, int32_t layer_idx, const mla_attn* attn,
                              const void* q_nope, int64_t q_nope_stride_t, int64_t q_nope_stride_h,

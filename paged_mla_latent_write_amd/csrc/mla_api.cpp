@@ -179,6 +179,75 @@ bool make_sparse_layout(const mla_cache* c, const mla_attn* a, int64_t num_q, in
   return true;
 }
 
+// One layer of the cache as the kernels see it.
+CacheView layer_view(const mla_cache* cache, int32_t layer_idx) {
+  const int R = cache->kv_lora_rank;
+  const int64_t layer_elems =
+      static_cast<int64_t>(cache->num_pages) * cache->page_size * (R + cache->qk_rope_dim);
+  CacheView kv;
+  kv.data = static_cast<const char*>(cache->data) + layer_idx * layer_elems * elem_bytes(cache->dtype);
+  kv.scale = cache->dtype == MLA_KV_FP8_E4M3
+                 ? cache->scale + static_cast<int64_t>(layer_idx) * cache->num_pages * cache->page_size
+                 : nullptr;
+  kv.dtype = cache->dtype == MLA_KV_BF16 ? mla::kKvBf16 : mla::kKvFp8;
+  kv.num_pages = cache->num_pages;
+  kv.page_size = cache->page_size;
+  kv.page_shift = __builtin_ctz(static_cast<unsigned>(cache->page_size));
+  kv.R = R;
+  kv.Dr = cache->qk_rope_dim;
+  kv.D = R + cache->qk_rope_dim;
+  return kv;
+}
+
+// Expanded-form prefill workspace: one pass's up-projected keys and values,
+// and the running per-(row, head) output state across passes.
+struct XLayout {
+  int32_t ck = 0;  // keys per pass
+  size_t k_exp = 0, v_exp = 0, kpe = 0, o_acc = 0, m_acc = 0, l_acc = 0, total = 0;
+};
+
+constexpr size_t kXPassBudget = size_t{512} << 20;
+
+XLayout make_xlayout(const mla_attn* a, int64_t batch, int64_t total_q) {
+  XLayout X;
+  const int64_t H = a->num_heads;
+  const int64_t B = std::max<int64_t>(batch, 1);
+  const size_t per_key = sizeof(uint16_t) * (H * 256 + 64);  // K and V of every head, and the rope part
+  const int64_t fit = static_cast<int64_t>(kXPassBudget / (per_key * B)) / 128 * 128;
+  X.ck = static_cast<int32_t>(std::min<int64_t>(mla::kXCk, std::max<int64_t>(128, fit)));
+  size_t off = 0;
+  X.k_exp = off;
+  off = align_up(off + sizeof(uint16_t) * B * H * X.ck * 128);
+  X.v_exp = off;
+  off = align_up(off + sizeof(uint16_t) * B * H * 128 * X.ck);
+  X.kpe = off;
+  off = align_up(off + sizeof(uint16_t) * B * X.ck * 64);
+  X.o_acc = off;
+  off = align_up(off + sizeof(float) * total_q * H * 128);
+  X.m_acc = off;
+  off = align_up(off + sizeof(float) * total_q * H);
+  X.l_acc = off;
+  off = align_up(off + sizeof(float) * total_q * H);
+  X.total = off;
+  return X;
+}
+
+// Which form mla_prefill_chunk runs.  The expanded one needs both weights and
+// a shape its kernels take; it runs when asked for, or, without a flag, for
+// windowed calls whose chunks average at least 64 rows: there it does a small
+// up-projection (chunk + window keys) instead of per-row latent outputs
+// (measured on the mixed step's window-128 layer: 0.66 ms against 1.15 ms).
+// Full-attention prefill stays absorbed unless asked for (13.9 ms against
+// 9.1 ms on the mixed step's full layers).
+bool prefill_route_expanded(const mla_cache* c, const mla_attn* a, int32_t batch, int32_t total_q) {
+  if (a->flags & (MLA_FLAG_GENERIC_KERNELS | MLA_FLAG_PREFILL_ABSORBED)) return false;
+  if (!a->w_uk || !a->w_uv) return false;
+  const CacheView kv = layer_view(c, 0);
+  if (!mla::prefill_expanded_supported(kv, a->num_heads, a->qk_nope_dim, a->v_head_dim)) return false;
+  if (a->flags & MLA_FLAG_PREFILL_EXPANDED) return true;
+  return a->window > 0 && static_cast<int64_t>(total_q) >= 64 * static_cast<int64_t>(batch);
+}
+
 template <typename T>
 T* at(void* base, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(base) + off);
@@ -446,6 +515,86 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
   return to_status(e);
 }
 
+// Expanded-form prefill: per request, passes of up to kXCk visible keys, each
+// an up-projection launch and an attention launch that merges into the
+// running state (no host sync: the device reads lengths and row ranges).
+mla_status run_prefill_expanded(const mla_cache* cache, int32_t layer_idx, const mla_attn* attn,
+                                const void* q_nope, int64_t qn_st, int64_t qn_sh, const void* q_pe,
+                                int64_t qp_st, int64_t qp_sh, const int32_t* qsl, int32_t total_q,
+                                int32_t max_q_len, const int32_t* block_tables, int32_t max_blocks,
+                                const int32_t* context_lens, int32_t batch, void* out,
+                                float* lse_or_null, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (layer_idx < 0 || layer_idx >= cache->num_layers) return MLA_ERR_INVALID_ARGUMENT;
+  if (batch < 0 || max_blocks <= 0) return MLA_ERR_INVALID_ARGUMENT;
+  if (batch == 0 || total_q == 0) return MLA_OK;
+  if (!q_nope || !q_pe || !qsl || !block_tables || !context_lens || !out)
+    return MLA_ERR_INVALID_ARGUMENT;
+  const int64_t max_ctx64 = static_cast<int64_t>(max_blocks) * cache->page_size;
+  if (max_ctx64 > (1ll << 30)) return MLA_ERR_UNSUPPORTED;
+  const auto aligned16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const CacheView kv = layer_view(cache, layer_idx);
+  if (!aligned16(q_nope) || !aligned16(q_pe) || qn_st % 8 || qn_sh % 8 || qp_st % 8 || qp_sh % 8 ||
+      !aligned16(attn->w_uk) || !aligned16(attn->w_uv) || !aligned16(kv.data) || !aligned16(out))
+    return MLA_ERR_UNSUPPORTED;
+  const XLayout X = make_xlayout(attn, batch, total_q);
+  if (!workspace || workspace_bytes < X.total) return MLA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MLA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (debug_check_enabled()) {
+    const mla_status st = debug_check_attention(mla::kPlanPrefill, cache, block_tables, max_blocks,
+                                                context_lens, batch, qsl, total_q, max_q_len, s);
+    if (st != MLA_OK) return st;
+  }
+  if (max_q_len == 0) return MLA_OK;
+  mla::XPassArgs a;
+  memset(&a, 0, sizeof(a));
+  a.kv = kv;
+  a.block_tables = block_tables;
+  a.max_blocks = max_blocks;
+  a.max_ctx = max_ctx64;
+  a.context_lens = context_lens;
+  a.query_start_loc = qsl;
+  a.window = attn->window;
+  a.H = attn->num_heads;
+  a.total_q = total_q;
+  a.w_uk = static_cast<const uint16_t*>(attn->w_uk);
+  a.w_uv = static_cast<const uint16_t*>(attn->w_uv);
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.qn_st = qn_st;
+  a.qn_sh = qn_sh;
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.qp_st = qp_st;
+  a.qp_sh = qp_sh;
+  a.scale_log2 = attn->scale * 1.4426950408889634f;
+  a.k_exp = at<uint16_t>(workspace, X.k_exp);
+  a.v_expT = at<uint16_t>(workspace, X.v_exp);
+  a.kpe = at<uint16_t>(workspace, X.kpe);
+  a.o_acc = at<float>(workspace, X.o_acc);
+  a.m_acc = at<float>(workspace, X.m_acc);
+  a.l_acc = at<float>(workspace, X.l_acc);
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse_or_null;
+  // the most keys one request's rows can see
+  const int64_t need = attn->window > 0
+                           ? std::min<int64_t>(max_ctx64, static_cast<int64_t>(max_q_len) + attn->window - 1)
+                           : max_ctx64;
+  a.batch = batch;
+  a.ck = X.ck;
+  const int npass = static_cast<int>((need + X.ck - 1) / X.ck);
+  if (attn->kernel_events[0] &&
+      hipEventRecord(static_cast<hipEvent_t>(attn->kernel_events[0]), s) != hipSuccess)
+    return MLA_ERR_HIP;
+  for (int j = 0; j < npass; ++j) {
+    a.pass = j;
+    if (mla::launch_prefill_expanded_pass(a, max_q_len, s) != hipSuccess) return MLA_ERR_HIP;
+  }
+  if (attn->kernel_events[1] &&
+      hipEventRecord(static_cast<hipEvent_t>(attn->kernel_events[1]), s) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -637,6 +786,8 @@ size_t mla_prefill_workspace_size(const mla_cache* cache, const mla_attn* attn, 
   if (check_cache(cache) != MLA_OK || check_attn(attn) != MLA_OK || batch < 0 ||
       total_q_tokens < 0 || max_blocks_per_seq <= 0)
     return 0;
+  if (prefill_route_expanded(cache, attn, batch, total_q_tokens))
+    return make_xlayout(attn, batch, total_q_tokens).total;
   Layout L;
   if (!make_layout(cache, attn, total_q_tokens, &L)) return 0;
   return L.total;
@@ -663,6 +814,12 @@ mla_status mla_prefill_chunk(const mla_cache* cache, int32_t layer_idx, const ml
                              int32_t batch, void* out, float* lse_or_null, void* workspace,
                              size_t workspace_bytes, void* stream) {
   if (total_q_tokens < 0 || max_q_len < 0) return MLA_ERR_INVALID_ARGUMENT;
+  if (check_cache(cache) == MLA_OK && check_attn(attn) == MLA_OK &&
+      prefill_route_expanded(cache, attn, batch, total_q_tokens))
+    return run_prefill_expanded(cache, layer_idx, attn, q_nope, q_nope_stride_t, q_nope_stride_h,
+                                q_pe, q_pe_stride_t, q_pe_stride_h, query_start_loc, total_q_tokens,
+                                max_q_len, block_tables, max_blocks_per_seq, context_lens, batch,
+                                out, lse_or_null, workspace, workspace_bytes, stream);
   return run_attention(mla::kPlanPrefill, cache, layer_idx, attn, q_nope, q_nope_stride_t,
                        q_nope_stride_h, q_pe, q_pe_stride_t, q_pe_stride_h, query_start_loc,
                        total_q_tokens, block_tables, max_blocks_per_seq, context_lens, batch,

@@ -117,6 +117,38 @@ struct CompactArgs {
   int32_t* out_bt;               // [items][rows_per_item / kCompactPage] identity block table
 };
 
+// Expanded-form chunked prefill (prefill_expanded.hip): one pass covers up to
+// `ck` keys (a multiple of 128, at most kXCk) of every request; the launch's
+// last grid dimension runs over the requests.
+constexpr int kXCk = 2048;
+struct XPassArgs {
+  CacheView kv;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  int64_t max_ctx;
+  const int32_t* context_lens;
+  const int32_t* query_start_loc;
+  int32_t batch, pass, ck, window, H;
+  int32_t total_q;         // rows of q / out / state (a row past it is never touched)
+  const uint16_t* w_uk;    // [H][128][R]
+  const uint16_t* w_uv;    // [H][128][R]
+  const uint16_t* q_nope;  // [Tq][H][128] (strides)
+  int64_t qn_st, qn_sh;
+  const uint16_t* q_pe;    // [Tq][H][64] (strides)
+  int64_t qp_st, qp_sh;
+  float scale_log2;
+  uint16_t* k_exp;         // [batch][H][ck][128]
+  uint16_t* v_expT;        // [batch][H][128][ck]
+  uint16_t* kpe;           // [batch][ck][64]
+  float* o_acc;            // [Tq][H][128] running (unnormalised) output
+  float* m_acc;            // [Tq][H] running maximum (log2 units)
+  float* l_acc;            // [Tq][H] running sum
+  uint16_t* out;           // [Tq][H][128]
+  float* lse;              // [Tq][H] or null
+};
+bool prefill_expanded_supported(const CacheView& kv, int32_t H, int32_t Dn, int32_t Dv);
+hipError_t launch_prefill_expanded_pass(const XPassArgs& a, int32_t max_q_len, hipStream_t s);
+
 // ---- launchers (each returns the launch's hipGetLastError) ----
 hipError_t launch_write_kv(void* cache_layer, float* scale_layer, int32_t dtype, int64_t num_slots,
                            int32_t R, int32_t Dr, const uint16_t* c_kv, int64_t c_stride,

@@ -34,6 +34,8 @@ MLA_ERR_HIP = 4
 MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3 = 1
 MLA_FLAG_GENERIC_KERNELS = 1
+MLA_FLAG_PREFILL_ABSORBED = 2
+MLA_FLAG_PREFILL_EXPANDED = 4
 
 EXPORTED = ("mla_write_kv", "mla_write_kv_fused", "mla_decode_workspace_size", "mla_decode", "mla_decode_noalloc",
             "mla_decode_combine", "mla_prefill_workspace_size", "mla_prefill_chunk",

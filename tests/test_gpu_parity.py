@@ -403,6 +403,39 @@ def test_prefill_small(mla, window, flags):
     check_prefill(mla, case, flags=flags, label=f" w={window}")
 
 
+@pytest.mark.parametrize("window", [0, 3, 64])
+def test_prefill_expanded_small(mla, window):
+    """The expanded form (keys and values up-projected per head) on the same
+    ragged chunks as the absorbed form's test, including a one-row chunk."""
+    say(f"prefill expanded small window={window}")
+    d = W.Dims(H=16, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
+    case = W.prefill_case(d, [0, 5, 100, 64], [7, 1, 70, 33], seed=800 + window, window=window,
+                          sharp=True)
+    check_prefill(mla, case, flags=mla.MLA_FLAG_PREFILL_EXPANDED, label=f" expanded w={window}")
+
+
+@pytest.mark.parametrize("kv", [O.KV_BF16, O.KV_FP8])
+@pytest.mark.parametrize("window", [0, 128])
+def test_prefill_expanded_multi_pass(mla, kv, window):
+    """Contexts longer than one 2048-key pass (the running state is merged
+    across passes), chunks longer than a 128-row block, 128 heads."""
+    say(f"prefill expanded multi-pass kv={kv} window={window}")
+    d = W.Dims(H=128, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
+    case = W.prefill_case(d, [4500, 0, 2047], [300, 130, 2], seed=850 + window, window=window,
+                          sharp=True, kv_dtype=kv)
+    check_prefill(mla, case, flags=mla.MLA_FLAG_PREFILL_EXPANDED, label=f" expanded {kv} w={window}")
+
+
+def test_prefill_expanded_equals_absorbed_on_gpu(mla):
+    """Both forms of the same call agree to the tolerance."""
+    say("prefill expanded vs absorbed")
+    d = W.Dims(H=32, R=512, Dr=64, Dn=128, Dv=128, page_size=32)
+    case = W.prefill_case(d, [1000, 77], [200, 64], seed=870, sharp=True)
+    a, _ = check_prefill(mla, case, flags=mla.MLA_FLAG_PREFILL_ABSORBED, label=" absorbed")
+    e, _ = check_prefill(mla, case, flags=mla.MLA_FLAG_PREFILL_EXPANDED, label=" expanded")
+    assert np.max(np.abs(bf16_host_f64(a) - bf16_host_f64(e))) < 2e-2
+
+
 def test_prefill_tiny_dims(mla):
     say("prefill tiny dims")
     case = W.prefill_case(W.TINY_DIMS, [10, 0], [27, 5], seed=810, sharp=True,
@@ -471,9 +504,13 @@ def mixed_step(mla):
         dout, dlse = mla.decode(cache, ml.layer, dev_bf16(ml.q_nope_d), dev_bf16(ml.q_pe_d),
                                 bt[P:].contiguous(), ctx[P:].contiguous(), scale=ml.scale,
                                 w_uk=w_uk, w_uv=w_uv, window=ml.window)
+        xout, xlse = mla.prefill_chunk(cache, ml.layer, dev_bf16(ml.q_nope_p), dev_bf16(ml.q_pe_p),
+                                       dev(ml.query_start_loc), 512, bt[:P].contiguous(),
+                                       ctx[:P].contiguous(), scale=ml.scale, w_uk=w_uk, w_uv=w_uv,
+                                       window=ml.window, flags=mla.MLA_FLAG_PREFILL_EXPANDED)
         torch.cuda.synchronize()
         results.append((bf16_host_f64(pout), plse.cpu().numpy(), bf16_host_f64(dout),
-                        dlse.cpu().numpy()))
+                        dlse.cpu().numpy(), bf16_host_f64(xout), xlse.cpu().numpy()))
     del cache
     torch.cuda.empty_cache()
     return layers, results
@@ -485,7 +522,7 @@ def test_mixed_step_full_size(mla, mixed_step, layer):
     every 8th prefill row of each chunk plus its last row (520 of 4096)."""
     layers, results = mixed_step
     ml = layers[layer]
-    pout, plse, dout, dlse = results[layer]
+    pout, plse, dout, dlse, xout, xlse = results[layer]
     say(f"mixed step layer {layer}: oracle")
     d = ml.dims
     P = ml.n_prefill
@@ -499,6 +536,8 @@ def test_mixed_step_full_size(mla, mixed_step, layer):
                                    ml.scale, ml.window, rows=rows)
     assert_close(pout[rows], ref[rows], BF16_TOL, f"mixed L{layer} prefill ({len(rows)} rows)")
     assert_lse_close(plse[rows], ref_lse[rows], LSE_ATOL[O.KV_BF16], f"mixed L{layer} prefill lse")
+    assert_close(xout[rows], ref[rows], BF16_TOL, f"mixed L{layer} expanded prefill")
+    assert_lse_close(xlse[rows], ref_lse[rows], LSE_ATOL[O.KV_BF16], f"mixed L{layer} expanded lse")
     dref, dref_lse = O.decode(hc, hs, O.KV_BF16, 0, ml.q_nope_d, ml.q_pe_d, ml.block_tables[P:],
                               ml.context_lens[P:], ml.w_uk, ml.w_uv, ml.scale, ml.window)
     assert_close(dout, dref, BF16_TOL, f"mixed L{layer} decode (all 120)")
