@@ -294,10 +294,11 @@ size_t mla_prefill_workspace_size(const mla_cache* cache, const mla_attn* attn, 
  * Two forms compute the same result.  Absorbed: each query row is a decode
  * item of the latent-space kernels.  Expanded ([CHUNK] "Future work"): the
  * keys the chunk's rows can see are up-projected per head through W_UK and
- * W_UV (kv_b_proj) into the workspace, in passes of at most 2048 keys sized so
- * that one pass of all requests fits 512 MiB, and attended with q_nope (128)
- * + q_pe (64) against [W_UK c ; k_pe], values W_UV c (128); pass results are
- * merged by log-sum-exp.  The expanded form needs w_uk and w_uv, qk_rope_dim
+ * W_UV (kv_b_proj) into the workspace and attended with q_nope (128) + q_pe
+ * (64) against [W_UK c ; k_pe], values W_UV c (128).  The up-projected keys
+ * take at most 1.25 GiB of workspace: requests go in groups whose visible
+ * ranges all fit, or, for a range longer than that, one at a time in passes
+ * whose results are merged by log-sum-exp.  The expanded form needs w_uk and w_uv, qk_rope_dim
  * 64, qk_nope_dim = v_head_dim = 128 and kv_lora_rank a multiple of 64.
  * MLA_FLAG_PREFILL_ABSORBED / _EXPANDED choose; without a flag the expanded
  * form runs for windowed calls (window > 0) whose chunks average at least 64

@@ -199,35 +199,53 @@ CacheView layer_view(const mla_cache* cache, int32_t layer_idx) {
   return kv;
 }
 
-// Expanded-form prefill workspace: one pass's up-projected keys and values,
-// and the running per-(row, head) output state across passes.
+// Expanded-form prefill workspace: the up-projected keys and values of one
+// launch pair (a group of requests, or one request's pass), and, when a
+// request's visible range needs several passes, the running per-(row, head)
+// output state.  The keys' and values' share is bounded by kXBudget.
 struct XLayout {
-  int32_t ck = 0;  // keys per pass
+  int32_t ck = 0;     // keys per pass (a multiple of 256)
+  int32_t group = 0;  // requests per launch pair
+  int32_t npass = 0;  // passes per request
   size_t k_exp = 0, v_exp = 0, kpe = 0, o_acc = 0, m_acc = 0, l_acc = 0, total = 0;
 };
 
-constexpr size_t kXPassBudget = size_t{512} << 20;
+constexpr size_t kXBudget = size_t{1280} << 20;
 
-XLayout make_xlayout(const mla_attn* a, int64_t batch, int64_t total_q) {
+// `need` bounds the keys one request's rows can see: the context, or, with a
+// window, the chunk plus the window (total_q_tokens bounds the chunk, so the
+// size query, which has no max_q_len, agrees with the call).
+XLayout make_xlayout(const mla_attn* a, int64_t batch, int64_t total_q, int64_t max_ctx) {
   XLayout X;
   const int64_t H = a->num_heads;
   const int64_t B = std::max<int64_t>(batch, 1);
+  const int64_t need = std::max<int64_t>(
+      1, a->window > 0 ? std::min<int64_t>(max_ctx, total_q + a->window - 1) : max_ctx);
   const size_t per_key = sizeof(uint16_t) * (H * 256 + 64);  // K and V of every head, and the rope part
-  const int64_t fit = static_cast<int64_t>(kXPassBudget / (per_key * B)) / 128 * 128;
-  X.ck = static_cast<int32_t>(std::min<int64_t>(mla::kXCk, std::max<int64_t>(128, fit)));
+  const int64_t ck_full = (need + 255) / 256 * 256;
+  if (static_cast<size_t>(ck_full) * per_key <= kXBudget) {
+    X.ck = static_cast<int32_t>(ck_full);
+    X.group = static_cast<int32_t>(std::min<int64_t>(B, kXBudget / (ck_full * per_key)));
+    X.npass = 1;
+  } else {
+    X.ck = static_cast<int32_t>(std::max<int64_t>(256, static_cast<int64_t>(kXBudget / per_key) / 256 * 256));
+    X.group = 1;
+    X.npass = static_cast<int32_t>((need + X.ck - 1) / X.ck);
+  }
   size_t off = 0;
   X.k_exp = off;
-  off = align_up(off + sizeof(uint16_t) * B * H * X.ck * 128);
+  off = align_up(off + sizeof(uint16_t) * X.group * H * X.ck * 128);
   X.v_exp = off;
-  off = align_up(off + sizeof(uint16_t) * B * H * 128 * X.ck);
+  off = align_up(off + sizeof(uint16_t) * X.group * H * 128 * X.ck);
   X.kpe = off;
-  off = align_up(off + sizeof(uint16_t) * B * X.ck * 64);
+  off = align_up(off + sizeof(uint16_t) * X.group * X.ck * 64);
+  const int64_t st_rows = X.npass > 1 ? total_q : 0;
   X.o_acc = off;
-  off = align_up(off + sizeof(float) * total_q * H * 128);
+  off = align_up(off + sizeof(float) * st_rows * H * 128);
   X.m_acc = off;
-  off = align_up(off + sizeof(float) * total_q * H);
+  off = align_up(off + sizeof(float) * st_rows * H);
   X.l_acc = off;
-  off = align_up(off + sizeof(float) * total_q * H);
+  off = align_up(off + sizeof(float) * st_rows * H);
   X.total = off;
   return X;
 }
@@ -236,8 +254,8 @@ XLayout make_xlayout(const mla_attn* a, int64_t batch, int64_t total_q) {
 // a shape its kernels take; it runs when asked for, or, without a flag, for
 // windowed calls whose chunks average at least 64 rows: there it does a small
 // up-projection (chunk + window keys) instead of per-row latent outputs
-// (measured on the mixed step's window-128 layer: 0.66 ms against 1.15 ms).
-// Full-attention prefill stays absorbed unless asked for (13.9 ms against
+// (measured on the mixed step's window-128 layer: 0.61 ms against 1.15 ms).
+// Full-attention prefill stays absorbed unless asked for (9.6 ms against
 // 9.1 ms on the mixed step's full layers).
 bool prefill_route_expanded(const mla_cache* c, const mla_attn* a, int32_t batch, int32_t total_q) {
   if (a->flags & (MLA_FLAG_GENERIC_KERNELS | MLA_FLAG_PREFILL_ABSORBED)) return false;
@@ -515,7 +533,7 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
   return to_status(e);
 }
 
-// Expanded-form prefill: per request, passes of up to kXCk visible keys, each
+// Expanded-form prefill: per group of requests (or per request, in passes),
 // an up-projection launch and an attention launch that merges into the
 // running state (no host sync: the device reads lengths and row ranges).
 mla_status run_prefill_expanded(const mla_cache* cache, int32_t layer_idx, const mla_attn* attn,
@@ -537,7 +555,7 @@ mla_status run_prefill_expanded(const mla_cache* cache, int32_t layer_idx, const
   if (!aligned16(q_nope) || !aligned16(q_pe) || qn_st % 8 || qn_sh % 8 || qp_st % 8 || qp_sh % 8 ||
       !aligned16(attn->w_uk) || !aligned16(attn->w_uv) || !aligned16(kv.data) || !aligned16(out))
     return MLA_ERR_UNSUPPORTED;
-  const XLayout X = make_xlayout(attn, batch, total_q);
+  const XLayout X = make_xlayout(attn, batch, total_q, max_ctx64);
   if (!workspace || workspace_bytes < X.total) return MLA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MLA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -575,19 +593,17 @@ mla_status run_prefill_expanded(const mla_cache* cache, int32_t layer_idx, const
   a.l_acc = at<float>(workspace, X.l_acc);
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse_or_null;
-  // the most keys one request's rows can see
-  const int64_t need = attn->window > 0
-                           ? std::min<int64_t>(max_ctx64, static_cast<int64_t>(max_q_len) + attn->window - 1)
-                           : max_ctx64;
-  a.batch = batch;
   a.ck = X.ck;
-  const int npass = static_cast<int>((need + X.ck - 1) / X.ck);
   if (attn->kernel_events[0] &&
       hipEventRecord(static_cast<hipEvent_t>(attn->kernel_events[0]), s) != hipSuccess)
     return MLA_ERR_HIP;
-  for (int j = 0; j < npass; ++j) {
-    a.pass = j;
-    if (mla::launch_prefill_expanded_pass(a, max_q_len, s) != hipSuccess) return MLA_ERR_HIP;
+  for (int32_t b0 = 0; b0 < batch; b0 += X.group) {
+    a.b0 = b0;
+    a.batch = std::min(X.group, batch - b0);
+    for (int j = 0; j < X.npass; ++j) {
+      a.pass = j;
+      if (mla::launch_prefill_expanded_pass(a, max_q_len, s) != hipSuccess) return MLA_ERR_HIP;
+    }
   }
   if (attn->kernel_events[1] &&
       hipEventRecord(static_cast<hipEvent_t>(attn->kernel_events[1]), s) != hipSuccess)
@@ -787,7 +803,8 @@ size_t mla_prefill_workspace_size(const mla_cache* cache, const mla_attn* attn, 
       total_q_tokens < 0 || max_blocks_per_seq <= 0)
     return 0;
   if (prefill_route_expanded(cache, attn, batch, total_q_tokens))
-    return make_xlayout(attn, batch, total_q_tokens).total;
+    return make_xlayout(attn, batch, total_q_tokens,
+                        static_cast<int64_t>(max_blocks_per_seq) * cache->page_size).total;
   Layout L;
   if (!make_layout(cache, attn, total_q_tokens, &L)) return 0;
   return L.total;

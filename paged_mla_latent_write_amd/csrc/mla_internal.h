@@ -117,10 +117,9 @@ struct CompactArgs {
   int32_t* out_bt;               // [items][rows_per_item / kCompactPage] identity block table
 };
 
-// Expanded-form chunked prefill (prefill_expanded.hip): one pass covers up to
-// `ck` keys (a multiple of 128, at most kXCk) of every request; the launch's
-// last grid dimension runs over the requests.
-constexpr int kXCk = 2048;
+// Expanded-form chunked prefill (prefill_expanded.hip): one launch pair
+// covers up to `ck` keys (a multiple of 256) of requests b0 .. b0 + batch - 1;
+// the launch's last grid dimension runs over those requests.
 struct XPassArgs {
   CacheView kv;
   const int32_t* block_tables;
@@ -128,7 +127,7 @@ struct XPassArgs {
   int64_t max_ctx;
   const int32_t* context_lens;
   const int32_t* query_start_loc;
-  int32_t batch, pass, ck, window, H;
+  int32_t b0, batch, pass, ck, window, H;
   int32_t total_q;         // rows of q / out / state (a row past it is never touched)
   const uint16_t* w_uk;    // [H][128][R]
   const uint16_t* w_uv;    // [H][128][R]
@@ -140,7 +139,7 @@ struct XPassArgs {
   uint16_t* k_exp;         // [batch][H][ck][128]
   uint16_t* v_expT;        // [batch][H][128][ck]
   uint16_t* kpe;           // [batch][ck][64]
-  float* o_acc;            // [Tq][H][128] running (unnormalised) output
+  float* o_acc;            // [Tq][H][128] running (unnormalised) output (several passes only)
   float* m_acc;            // [Tq][H] running maximum (log2 units)
   float* l_acc;            // [Tq][H] running sum
   uint16_t* out;           // [Tq][H][128]

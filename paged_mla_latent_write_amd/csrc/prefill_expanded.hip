@@ -12,10 +12,10 @@
 // pair instead of 2 H (2R + Dr), plus 2 H R (Dn + Dv) per key for the
 // up-projection.
 //
-// The keys a request's rows can see, [lo, n), are processed in passes of up to
-// ck tokens, every request of the call in the same launch (the pass length
-// bounds the workspace: ck is chosen so that all requests' up-projected keys
-// and values of one pass fit 512 MiB, at most 2048):
+// The keys a request's rows can see, [lo, n), are up-projected into a
+// workspace bounded by 1.25 GiB: when the longest such range fits, a launch
+// pair covers whole ranges of as many requests as fit (one pass, no running
+// state); otherwise requests go one at a time in passes of ck keys, merged:
 //   kv_expand_kernel   K_exp[h][j][0:128] = W_UK[h] c_{k0+j},
 //                      V_expT[h][0:128][j] = W_UV[h] c_{k0+j},
 //                      kpe[j][0:64] = r_{k0+j}, all bf16 (fp8 caches: the
@@ -72,17 +72,26 @@ __device__ __forceinline__ bool pass_range(const XPassArgs& a, int b, int64_t* n
 // Up-projection of one pass's keys (a gathered GEMM: tokens x R times R x 128)
 // ---------------------------------------------------------------------------
 
-constexpr int kGTok = 128;                 // tokens per workgroup tile
-constexpr int kGN = 128;                   // output columns per tile (one head's K or V)
+constexpr int kGTok = 256;                 // tokens per workgroup tile
+constexpr int kGThreads = 512;             // 8 waves: 4 token quarters x (K, V)
+constexpr int kGN = 256;                   // output columns per tile: one head's K (128) and V (128)
 constexpr int kGK = 64;                    // R per LDS stage
 constexpr int kGPitch = kGK * 2 + 16;      // bytes per LDS row
 
-__global__ __launch_bounds__(256) void kv_expand_kernel(XPassArgs a) {
+// V_expT keeps each 16-key group with its second and third quads swapped
+// (keys 4..7 after 8..11): the attention kernel's MFMA reads the eight keys
+// of a lane's P fragment (keys 4g..4g+3 and 8+4g..8+4g+3 of the group, lane
+// half g) as one contiguous 16-byte run.
+__device__ __forceinline__ int vperm(int j) {
+  const int q = (j >> 2) & 3;
+  return (q == 1 || q == 2) ? (j ^ 12) : j;
+}
+
+__global__ __launch_bounds__(kGThreads, 1) void kv_expand_kernel(XPassArgs a) {
   __shared__ __attribute__((aligned(16))) char As[kGTok * kGPitch];
   __shared__ __attribute__((aligned(16))) char Bs[kGN * kGPitch];
   __shared__ float tok_scale[kGTok];
-  const int b = blockIdx.z >> 1;
-  const bool is_v = (blockIdx.z & 1) != 0;
+  const int bz = blockIdx.z, b = a.b0 + bz;
   int64_t n, m, k0, ntok;
   if (!pass_range(a, b, &n, &m, &k0, &ntok)) return;
   const int j0 = blockIdx.x * kGTok;
@@ -96,29 +105,37 @@ __global__ __launch_bounds__(256) void kv_expand_kernel(XPassArgs a) {
   const bool fp8 = kv.dtype == kKvFp8;
   const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
   const unsigned last_page = static_cast<unsigned>(kv.num_pages - 1);
-  const uint16_t* W = (is_v ? a.w_uv : a.w_uk) + static_cast<int64_t>(h) * kGN * R;
-  uint16_t* k_exp = a.k_exp + static_cast<int64_t>(b) * a.H * ck * kXDn;
-  uint16_t* v_expT = a.v_expT + static_cast<int64_t>(b) * a.H * kXDv * ck;
-  uint16_t* kpe = a.kpe + static_cast<int64_t>(b) * ck * kXDr;
+  // B rows 0..127: W_UK[h] rows, 128..255: W_UV[h] rows
+  const uint16_t* Wk = a.w_uk + static_cast<int64_t>(h) * kXDn * R;
+  const uint16_t* Wv = a.w_uv + static_cast<int64_t>(h) * kXDv * R;
+  uint16_t* k_exp = a.k_exp + static_cast<int64_t>(bz) * a.H * ck * kXDn;
+  uint16_t* v_expT = a.v_expT + static_cast<int64_t>(bz) * a.H * kXDv * ck;
+  uint16_t* kpe = a.kpe + static_cast<int64_t>(bz) * ck * kXDr;
 
-  // this thread's A rows (4 per thread: row = (t + 256 q) / 8, chunk (t % 8)
-  // for bf16; 2 per thread for fp8) and their cache rows
   auto cache_row = [&](int j) -> int64_t {
     const int64_t tok = k0 + min(j, static_cast<int>(ntok) - 1);
     const unsigned pg = min(static_cast<unsigned>(bt[tok >> kv.page_shift]), last_page);
     return static_cast<int64_t>(pg) * kv.page_size + (tok & (kv.page_size - 1));
   };
+  // cache rows of this thread's A chunks (fixed over the stages)
+  int64_t arow[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = fp8 ? ((t + kGThreads * q) >> 2) : ((t + kGThreads * q) >> 3);
+    arow[q] = (fp8 && q >= 2) ? 0 : cache_row(j0 + r);
+  }
   if (t < kGTok) {
     const int j = j0 + t;
     tok_scale[t] = (fp8 && j < ntok) ? kv.scale[cache_row(j)] : 1.0f;
   }
 
-  f32x16 acc[2][2];
+  // wave tile: 64 tokens x 128 columns (all K or all V)
+  const int tm = wave >> 1, tn = wave & 1;  // tm 0..3
+  f32x16 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) acc[i][jj] = f32x16{};
-  const int tm = wave >> 1, tn = wave & 1;
+    for (int jj = 0; jj < 4; ++jj) acc[i][jj] = f32x16{};
 
   // The next stage's global loads are issued before this stage's MFMAs and
   // land in registers; they are stored to LDS after the stage.
@@ -128,44 +145,43 @@ __global__ __launch_bounds__(256) void kv_expand_kernel(XPassArgs a) {
     if (!fp8) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int idx = t + 256 * q;
+        const int idx = t + kGThreads * q;
         const int r = idx >> 3, c = idx & 7;
-        const int j = j0 + r;
         i16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (j < ntok)
-          v = *reinterpret_cast<const i16x8*>(static_cast<const uint16_t*>(kv.data) + cache_row(j) * kv.D + kc + 8 * c);
+        if (j0 + r < ntok)
+          v = *reinterpret_cast<const i16x8*>(static_cast<const uint16_t*>(kv.data) + arow[q] * kv.D + kc + 8 * c);
         ra[q] = v;
       }
     } else {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const int idx = t + 256 * q;
+        const int idx = t + kGThreads * q;
         const int r = idx >> 2, c = idx & 3;
-        const int j = j0 + r;
         uint4 codes = make_uint4(0, 0, 0, 0);
-        if (j < ntok)
-          codes = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(kv.data) + cache_row(j) * kv.D + kc + 16 * c);
+        if (j0 + r < ntok)
+          codes = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(kv.data) + arow[q] * kv.D + kc + 16 * c);
         rc[q] = codes;
       }
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int idx = t + 256 * q;
+      const int idx = t + kGThreads * q;
       const int r = idx >> 3, c = idx & 7;
-      rb[q] = *reinterpret_cast<const i16x8*>(W + static_cast<int64_t>(r) * R + kc + 8 * c);
+      const uint16_t* W = r < kXDn ? Wk + static_cast<int64_t>(r) * R : Wv + static_cast<int64_t>(r - kXDn) * R;
+      rb[q] = *reinterpret_cast<const i16x8*>(W + kc + 8 * c);
     }
   };
   auto store_stage = [&]() {
     if (!fp8) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int idx = t + 256 * q;
+        const int idx = t + kGThreads * q;
         *reinterpret_cast<i16x8*>(As + (idx >> 3) * kGPitch + (idx & 7) * 16) = ra[q];
       }
     } else {
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const int idx = t + 256 * q;
+        const int idx = t + kGThreads * q;
         const int r = idx >> 2, c = idx & 3;
         const uint32_t w4[4] = {rc[q].x, rc[q].y, rc[q].z, rc[q].w};
         i16x8 lo, hi;
@@ -181,7 +197,7 @@ __global__ __launch_bounds__(256) void kv_expand_kernel(XPassArgs a) {
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int idx = t + 256 * q;
+      const int idx = t + kGThreads * q;
       *reinterpret_cast<i16x8*>(Bs + (idx >> 3) * kGPitch + (idx & 7) * 16) = rb[q];
     }
   };
@@ -192,36 +208,37 @@ __global__ __launch_bounds__(256) void kv_expand_kernel(XPassArgs a) {
     if (kc + kGK < R) load_stage(kc + kGK);  // in flight during this stage's MFMAs
 #pragma unroll
     for (int ks = 0; ks < kGK / 16; ++ks) {
-      i16x8 af[2], bf[2];
+      i16x8 af[2], bf[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < 2; ++i)
         af[i] = *reinterpret_cast<const i16x8*>(As + (64 * tm + 32 * i + n32) * kGPitch + (16 * ks + 8 * g) * 2);
-        bf[i] = *reinterpret_cast<const i16x8*>(Bs + (64 * tn + 32 * i + n32) * kGPitch + (16 * ks + 8 * g) * 2);
-      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        bf[jj] = *reinterpret_cast<const i16x8*>(Bs + (128 * tn + 32 * jj + n32) * kGPitch + (16 * ks + 8 * g) * 2);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = mfma(af[i], bf[jj], acc[i][jj]);
+        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = mfma(af[i], bf[jj], acc[i][jj]);
     }
     __syncthreads();
   }
 
   // epilogue: element e of acc[i][jj] is token 64 tm + 32 i + 8 (e / 4) + 4 g + e % 4,
-  // column d = 64 tn + 32 jj + n32
+  // column d = 32 jj + n32 of the wave's K (tn = 0) or V (tn = 1) block
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-      const int d = 64 * tn + 32 * jj + n32;
+    for (int jj = 0; jj < 4; ++jj) {
+      const int d = 32 * jj + n32;
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         const int r = 64 * tm + 32 * i + 8 * e4 + 4 * g;  // tile-local token of element 4 e4
         uint16_t v[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = f32_to_bf16(acc[i][jj][4 * e4 + e] * tok_scale[r + e]);
-        if (is_v) {
-          // V_expT[h][d][j]: four consecutive tokens, one 8-byte store
-          uint16_t* dst = v_expT + (static_cast<int64_t>(h) * kXDv + d) * ck + j0 + r;
+        if (tn == 1) {
+          // V_expT[h][d][vperm(j)]: four consecutive tokens (a quad), one 8-byte store
+          uint16_t* dst = v_expT + (static_cast<int64_t>(h) * kXDv + d) * ck + vperm(j0 + r);
           *reinterpret_cast<uint2*>(dst) = make_uint2(v[0] | (static_cast<uint32_t>(v[1]) << 16),
                                                       v[2] | (static_cast<uint32_t>(v[3]) << 16));
         } else {
@@ -233,8 +250,8 @@ __global__ __launch_bounds__(256) void kv_expand_kernel(XPassArgs a) {
     }
   }
   // the rope part of the keys, shared by every head (written once)
-  if (h == 0 && !is_v) {
-    for (int idx = t; idx < kGTok * kXDr; idx += 256) {
+  if (h == 0) {
+    for (int idx = t; idx < kGTok * kXDr; idx += kGThreads) {
       const int r = idx / kXDr, c = idx % kXDr;
       const int j = j0 + r;
       uint16_t v = 0;
@@ -262,12 +279,25 @@ constexpr int kAVPitch = kAT * 2 + 16;         // bytes per LDS V^T row (80)
 constexpr float kRescaleSlack = 8.0f;          // log2 units
 
 __global__ __launch_bounds__(256, 2) void attn_expanded_kernel(XPassArgs a) {
-  __shared__ __attribute__((aligned(16))) char Ks[2][kAT * kAKPitch];
-  __shared__ __attribute__((aligned(16))) char Vs[2][kXDv * kAVPitch];
-  const int b = blockIdx.z;
+  __shared__ __attribute__((aligned(16))) char Ks[3][kAT * kAKPitch];
+  __shared__ __attribute__((aligned(16))) char Vs[3][kXDv * kAVPitch];
+  // XCD-aware numbering: workgroups are dispatched round-robin over the 8
+  // XCDs (each with its own L2).  The row blocks of one (request, head) read
+  // the same key and value tiles, so they are made the consecutive
+  // workgroups of one XCD (k-th workgroup on XCD x: group (k / nrb) * 8 + x,
+  // row block k % nrb), while consecutive groups still go to different XCDs.
+  const int nrb = gridDim.x;
+  const int groups = gridDim.y * gridDim.z;
+  const int lin = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  int rb = blockIdx.x, grp = blockIdx.y + gridDim.y * blockIdx.z;
+  if (groups % 8 == 0) {
+    const int x = lin % 8, k = lin / 8;
+    grp = (k / nrb) * 8 + x;
+    rb = k % nrb;
+  }
+  const int h = grp % gridDim.y, bz = grp / gridDim.y, b = a.b0 + bz;
   int64_t n, m, k0, ntok;
   if (!pass_range(a, b, &n, &m, &k0, &ntok)) return;
-  const int rb = blockIdx.x, h = blockIdx.y;
   if (static_cast<int64_t>(rb) * 128 >= m) return;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int g = lane >> 5, n32 = lane & 31;
@@ -300,9 +330,9 @@ __global__ __launch_bounds__(256, 2) void attn_expanded_kernel(XPassArgs a) {
   }
 
   // tile loads: 5 chunks of 16 B per thread (K_exp 512, kpe 256, V^T 512)
-  const uint16_t* kexp_h = a.k_exp + (static_cast<int64_t>(b) * a.H + h) * ck * kXDn;
-  const uint16_t* vexp_h = a.v_expT + (static_cast<int64_t>(b) * a.H + h) * kXDv * ck;
-  const uint16_t* kpe_b = a.kpe + static_cast<int64_t>(b) * ck * kXDr;
+  const uint16_t* kexp_h = a.k_exp + (static_cast<int64_t>(bz) * a.H + h) * ck * kXDn;
+  const uint16_t* vexp_h = a.v_expT + (static_cast<int64_t>(bz) * a.H + h) * kXDv * ck;
+  const uint16_t* kpe_b = a.kpe + static_cast<int64_t>(bz) * ck * kXDr;
   i16x8 ld[5];
   auto load_tile = [&](int tile) {
     const int j0 = tile * kAT;
@@ -342,20 +372,36 @@ __global__ __launch_bounds__(256, 2) void attn_expanded_kernel(XPassArgs a) {
   float m_ref = -INFINITY, l_sum = 0.f;
   const float c = a.scale_log2;
 
+  // S^T = K Q^T (keys x rows) of the tile in buffer `buf`
+  auto scores = [&](int buf) {
+    f32x16 sc = f32x16{};
+    const char* kb = Ks[buf] + n32 * kAKPitch + 16 * g;
+#pragma unroll
+    for (int st = 0; st < kXDq / 16; ++st) sc = mfma(*reinterpret_cast<const i16x8*>(kb + 32 * st), qf[st], sc);
+    return sc;
+  };
+
+  // Software pipeline over three LDS buffers (tile t in buffer t mod 3): the
+  // scores of tile t + 1 are issued on the matrix cores before the softmax of
+  // tile t runs on the vector ALUs, and tile t + 2 is loaded meanwhile.
   if (tile_lo < tile_hi) {
     load_tile(tile_lo);
     store_tile(0);
   }
+  if (tile_lo + 1 < tile_hi) {
+    load_tile(tile_lo + 1);
+    store_tile(1);
+  }
   __syncthreads();
+  f32x16 s_cur = tile_lo < tile_hi ? scores(0) : f32x16{};
   for (int tile = tile_lo; tile < tile_hi; ++tile) {
-    const int buf = (tile - tile_lo) & 1;
-    const bool more = tile + 1 < tile_hi;
-    if (more) load_tile(tile + 1);  // in flight during this tile's math
-    // S^T = K Q^T (keys x rows)
-    f32x16 s = f32x16{};
-    const char* kb = Ks[buf] + n32 * kAKPitch + 16 * g;
-#pragma unroll
-    for (int st = 0; st < kXDq / 16; ++st) s = mfma(*reinterpret_cast<const i16x8*>(kb + 32 * st), qf[st], s);
+    const int i = tile - tile_lo;
+    const int cur = i % 3, nxt = (i + 1) % 3, far = (i + 2) % 3;
+    const bool has_next = tile + 1 < tile_hi, has_far = tile + 2 < tile_hi;
+    if (has_far) load_tile(tile + 2);  // in flight during this tile's math
+    f32x16 s_next = f32x16{};
+    if (has_next) s_next = scores(nxt);
+    f32x16 s = s_cur;
     // scale, mask, tile maximum (a row's 32 keys sit in lanes n32 and n32 + 32)
     const int64_t tile_key = k0 + static_cast<int64_t>(tile) * kAT;
     const bool full = row_ok && tile_key + kAT - 1 <= P + r_lo + 32 * wave &&  // every row of the wave sees the whole tile
@@ -388,31 +434,32 @@ __global__ __launch_bounds__(256, 2) void attn_expanded_kernel(XPassArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
     }
-    i16x8 pb[2];
+    // p = 2^(s - m_ref) <= 2^8 (v_exp_f32; masked keys give exp2(-inf) = 0),
+    // rounded to bf16 by the hardware conversion (nearest even)
+    bf16x8 pb[2];
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;  // a row with nothing visible yet
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float p = s[e] == -INFINITY ? 0.f : exp2f(s[e] - m_ref);
+      const float p = __builtin_amdgcn_exp2f(s[e] - m_use);
       l_sum += p;
-      pb[e >> 3][e & 7] = static_cast<short>(f32_to_bf16(p));
+      pb[e >> 3][e & 7] = static_cast<__bf16>(p);
     }
     // O^T += V^T P^T; MFMA k-slot 8 g + j of key half kk is key 16 kk + 4 g + j
-    // (j < 4) or 16 kk + 8 + 4 g + (j - 4): the keys this lane's P registers hold
-    const char* vb = Vs[buf] + n32 * kAVPitch + 8 * g;
+    // (j < 4) or 16 kk + 8 + 4 g + (j - 4): the keys this lane's P registers
+    // hold, which the quad-swapped V^T columns 16 kk + 8 g .. + 7 hold in order
+    const char* vb = Vs[cur] + n32 * kAVPitch + 16 * g;
 #pragma unroll
     for (int db = 0; db < kXDv / 32; ++db) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const char* row = vb + 32 * db * kAVPitch + 32 * kk;
-        const i16x4 lo = *reinterpret_cast<const i16x4*>(row);
-        const i16x4 hi = *reinterpret_cast<const i16x4*>(row + 16);
-        const i16x8 af = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[db] = mfma(af, pb[kk], o[db]);
-      }
+      for (int kk = 0; kk < 2; ++kk)
+        o[db] = mfma(*reinterpret_cast<const i16x8*>(vb + 32 * db * kAVPitch + 32 * kk),
+                     __builtin_bit_cast(i16x8, pb[kk]), o[db]);
     }
-    // the other buffer was last read in the previous tile, before the barrier
-    // that ended it, so it can be refilled now
-    if (more) store_tile(buf ^ 1);
+    // buffer `far` last held tile t - 1, whose values were read before the
+    // barrier that ended the previous step
+    if (has_far) store_tile(far);
     __syncthreads();
+    s_cur = s_next;
   }
 
   // merge with the previous passes and store
@@ -468,11 +515,13 @@ __global__ __launch_bounds__(256, 2) void attn_expanded_kernel(XPassArgs a) {
 }  // namespace
 
 bool prefill_expanded_supported(const CacheView& kv, int32_t H, int32_t Dn, int32_t Dv) {
+  // (the pass length is a multiple of the up-projection's token tile)
+  static_assert(kGTok == 256, "pass lengths are rounded to 256 keys");
   return kv.Dr == kXDr && kv.R % kGK == 0 && Dn == kXDn && Dv == kXDv && H >= 1 && H <= 1024;
 }
 
 hipError_t launch_prefill_expanded_pass(const XPassArgs& a, int32_t max_q_len, hipStream_t s) {
-  hipLaunchKernelGGL(kv_expand_kernel, dim3(a.ck / kGTok, a.H, 2 * a.batch), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(kv_expand_kernel, dim3(a.ck / kGTok, a.H, a.batch), dim3(kGThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_expanded_kernel, dim3((max_q_len + 127) / 128, a.H, a.batch), dim3(256), 0, s, a);

@@ -426,6 +426,15 @@ def test_prefill_expanded_multi_pass(mla, kv, window):
     check_prefill(mla, case, flags=mla.MLA_FLAG_PREFILL_EXPANDED, label=f" expanded {kv} w={window}")
 
 
+def test_prefill_expanded_passes_merged(mla):
+    """A context whose up-projected keys exceed the expanded form's 1.25 GiB
+    workspace share (24000 keys x 128 heads) runs in two merged passes."""
+    say("prefill expanded, two passes")
+    d = W.Dims(H=128, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
+    case = W.prefill_case(d, [23850, 100], [150, 40], seed=880, sharp=True)
+    check_prefill(mla, case, flags=mla.MLA_FLAG_PREFILL_EXPANDED, label=" expanded 2 passes")
+
+
 def test_prefill_expanded_equals_absorbed_on_gpu(mla):
     """Both forms of the same call agree to the tolerance."""
     say("prefill expanded vs absorbed")
@@ -477,9 +486,10 @@ def mixed_rows(ml):
 def mixed_step(mla):
     """The whole mixed step at full size, as the serving step runs it: one
     4-layer cache holding every layer's population, then per layer the write
-    of the step's 4216 new tokens, the prefill of the 8 chunks and the decode
-    of the 120 single-token requests.  Returns the layers and their outputs
-    (host copies)."""
+    of the step's 4216 new tokens, the prefill of the 8 chunks (in the
+    absorbed form, and again in the expanded form) and the decode of the 120
+    single-token requests.  Returns the layers and their outputs (host
+    copies)."""
     from concurrent.futures import ThreadPoolExecutor
 
     say("mixed step: generating 4 layers")
@@ -500,7 +510,7 @@ def mixed_step(mla):
         pout, plse = mla.prefill_chunk(cache, ml.layer, dev_bf16(ml.q_nope_p), dev_bf16(ml.q_pe_p),
                                        dev(ml.query_start_loc), 512, bt[:P].contiguous(),
                                        ctx[:P].contiguous(), scale=ml.scale, w_uk=w_uk, w_uv=w_uv,
-                                       window=ml.window)
+                                       window=ml.window, flags=mla.MLA_FLAG_PREFILL_ABSORBED)
         dout, dlse = mla.decode(cache, ml.layer, dev_bf16(ml.q_nope_d), dev_bf16(ml.q_pe_d),
                                 bt[P:].contiguous(), ctx[P:].contiguous(), scale=ml.scale,
                                 w_uk=w_uk, w_uv=w_uv, window=ml.window)
