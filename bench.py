@@ -388,8 +388,8 @@ def main_mixed(args):
         per_layer[f"L{li}"] = {"window": L["ml"].window, "write_ms": float(med[0]),
                                "prefill_ms": float(med[1]), "decode_ms": float(med[2]),
                                "prefill_pairs": pre, "decode_tokens": dec,
-                               "prefill_tflops": pre * 2 * d.H * (2 * d.R + d.Dr) / (med[1] * 1e-3) / 1e12,
-                               "decode_gbs": dec * d.D * 2 / (med[2] * 1e-3) / 1e9}
+                               "prefill_tflops": float(pre * 2 * d.H * (2 * d.R + d.Dr) / (med[1] * 1e-3) / 1e12),
+                               "decode_gbs": float(dec * d.D * 2 / (med[2] * 1e-3) / 1e9)}
         print(f"[bench] mixed L{li}: {per_layer[f'L{li}']}", file=sys.stderr, flush=True)
     pairs = sum(sum(L["pairs"]) for L in layers)
     flops = pairs * 2 * d.H * (2 * d.R + d.Dr)

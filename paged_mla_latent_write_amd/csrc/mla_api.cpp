@@ -213,14 +213,16 @@ struct XLayout {
 constexpr size_t kXBudget = size_t{1280} << 20;
 
 // `need` bounds the keys one request's rows can see: the context, or, with a
-// window, the chunk plus the window (total_q_tokens bounds the chunk, so the
-// size query, which has no max_q_len, agrees with the call).
-XLayout make_xlayout(const mla_attn* a, int64_t batch, int64_t total_q, int64_t max_ctx) {
+// window, the chunk (at most q_bound rows) plus the window.  The size query
+// has no max_q_len and bounds the chunk by total_q; the call uses max_q_len
+// when that layout fits the workspace it is given.
+XLayout make_xlayout(const mla_attn* a, int64_t batch, int64_t total_q, int64_t max_ctx,
+                     int64_t q_bound) {
   XLayout X;
   const int64_t H = a->num_heads;
   const int64_t B = std::max<int64_t>(batch, 1);
   const int64_t need = std::max<int64_t>(
-      1, a->window > 0 ? std::min<int64_t>(max_ctx, total_q + a->window - 1) : max_ctx);
+      1, a->window > 0 ? std::min<int64_t>(max_ctx, q_bound + a->window - 1) : max_ctx);
   const size_t per_key = sizeof(uint16_t) * (H * 256 + 64);  // K and V of every head, and the rope part
   const int64_t ck_full = (need + 255) / 256 * 256;
   if (static_cast<size_t>(ck_full) * per_key <= kXBudget) {
@@ -555,7 +557,8 @@ mla_status run_prefill_expanded(const mla_cache* cache, int32_t layer_idx, const
   if (!aligned16(q_nope) || !aligned16(q_pe) || qn_st % 8 || qn_sh % 8 || qp_st % 8 || qp_sh % 8 ||
       !aligned16(attn->w_uk) || !aligned16(attn->w_uv) || !aligned16(kv.data) || !aligned16(out))
     return MLA_ERR_UNSUPPORTED;
-  const XLayout X = make_xlayout(attn, batch, total_q, max_ctx64);
+  XLayout X = make_xlayout(attn, batch, total_q, max_ctx64, max_q_len);
+  if (X.total > workspace_bytes) X = make_xlayout(attn, batch, total_q, max_ctx64, total_q);
   if (!workspace || workspace_bytes < X.total) return MLA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0) return MLA_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -804,7 +807,8 @@ size_t mla_prefill_workspace_size(const mla_cache* cache, const mla_attn* attn, 
     return 0;
   if (prefill_route_expanded(cache, attn, batch, total_q_tokens))
     return make_xlayout(attn, batch, total_q_tokens,
-                        static_cast<int64_t>(max_blocks_per_seq) * cache->page_size).total;
+                        static_cast<int64_t>(max_blocks_per_seq) * cache->page_size, total_q_tokens)
+        .total;
   Layout L;
   if (!make_layout(cache, attn, total_q_tokens, &L)) return 0;
   return L.total;
