@@ -45,7 +45,6 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a, int hpb) 
   float* al_s = l_s + hpb;           // [hpb]
 
   const int64_t g = blockIdx.x;
-  if (a.redo_only && a.redo_only[g] == 0) return;
   const int64_t t0 = a.wg_tile[g], t1 = a.wg_tile[g + 1];
   if (t0 >= t1) return;
   // head blocks: one per grid row (the grid may also have fewer rows)

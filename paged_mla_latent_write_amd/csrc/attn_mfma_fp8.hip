@@ -1,6 +1,6 @@
 // Split-KV paged latent attention over an fp8 (E4M3) latent cache on CDNA4
 // matrix cores (gfx950), for the MLA latent shape kv_lora_rank 512 +
-// qk_rope 64 with up to 128 query heads.
+// qk_rope 64 with up to 128 query heads and pages of at least 16 tokens.
 //
 // What it computes is the bf16 kernel's (attn_mfma.hip) with the cache read as
 // dequantised values: token t holds E4M3 codes x_t[0..575] and one fp32 scale
@@ -13,27 +13,27 @@
 //
 // Design (one workgroup of four waves per compute unit, wave w owns heads
 // [32w, 32w + 32), as in the bf16 kernel):
-//  * a 32-token tile is 18 KiB of codes + 128 B of scales.  It is copied
-//    HBM -> LDS with global_load_lds (no VGPR staging) into one of four
-//    staging buffers, two tiles ahead of the compute: five copies per wave
-//    (18 of codes, one of scales that waves 2 and 3 both issue).
-//  * one step later the whole workgroup converts the staged codes once into a
-//    bf16 tile (the layout and swizzle of the bf16 kernel's tiles), so the
-//    four waves do not each convert the keys they all read.  Two bf16 tiles
-//    alternate: tile t + 1 is converted during tile t's values step, between
-//    its MFMAs (each lane its five 16-code chunks, destinations from a table
-//    in LDS), and published by the barrier that starts step t + 1.
-//  * S^T = K Q^T and O^T += V^T P^T run on v_mfma_f32_32x32x16_bf16 as two
-//    hand-scheduled blocks per tile (attn_mfma_fp8_asm.inc, generated): K and
-//    V^T fragments (ds_read_b128, ds_read_b64_tr_b16) stream through a ring of
-//    registers a few MFMAs ahead, Q and the 512 x 32 accumulator sit in the
-//    registers the bf16 kernel reserves for them (the compiler is limited to
-//    the rest); the scales and the softmax run in C++ between the blocks.
-//  * online softmax in base 2 against a reference maximum fixed by each
-//    segment's first tile, so the accumulators are never rescaled (the blocks
-//    hold no rescale step).  Probabilities up to 2^64 stay far inside fp32; a
-//    score beyond that flags the workgroup, whose range the generic kernel
-//    then recomputes exactly (redo).
+//  * a 32-token tile is 18 KiB of codes + 128 B of scales.  Lane i of the
+//    workgroup owns the tile's 16-byte code chunks i, i + 256, ...: it copies
+//    them HBM -> LDS (global_load_lds, no VGPR staging) into one of two
+//    staging buffers, three tiles ahead of the compute, and it alone converts
+//    them to bf16 (exact), so a staging buffer is refilled as soon as its owner
+//    has read it, with no barrier.  Waves 2 and 3 copy the scales into one of
+//    four 1 KiB scale slots (lanes 8-63 repeat lanes 0-7 into the slot's pad).
+//  * three bf16 tile buffers (the bf16 kernel's layout and swizzle): step n
+//    reads the keys of tile n and the values of tile n - 1 and writes tile
+//    n + 1, which the barrier ending the step publishes.
+//  * each step is one generated block (attn_mfma_fp8_asm.inc): S^T = K Q^T of
+//    tile n on v_mfma_f32_32x32x16_bf16 with the conversion of tile n + 1 and
+//    the copies of tile n + 3 between its MFMAs, then O^T += V^T P^T of tile
+//    n - 1 with the softmax of tile n (per-token scales, mask, reference
+//    maximum, exp2, P * s_t rounded to bf16) between its MFMAs.  Q and the
+//    512 x 32 accumulator sit in registers the compiler does not allocate.
+//  * online softmax in base 2 against a reference maximum that moves up (with
+//    a rescale of the accumulators) only when a tile's maximum passes it by
+//    more than 16: the accumulators are rarely rescaled.
+// With pages of 16 tokens a tile spans two pages, and the copies are issued
+// by the C++ code after each block instead of inside it.
 #include <math.h>
 
 #include "device_utils.h"
@@ -42,18 +42,29 @@
 namespace mla {
 namespace {
 
-// Q (v62-v205), the accumulators (a0-a255) and the register ring: load_q,
-// zero_q and store_acc from the bf16 kernel's blocks, and the fp8 kernel's own
-// scores and values blocks
+// Operands of one tile step's block.
+struct Fp8Step {
+  uint32_t cs;      // tile n + 1's codes: staging buffer + 16 tid (this lane's first chunk)
+  uint32_t cs4;     // this lane's fifth chunk (its fourth again when it has none)
+  uint32_t ct;      // this lane's row of the conversion table
+  uint32_t sc;      // tile n's scale slot + 16 g
+  uint32_t cp;      // 1: the block issues the copies of tile n + 3
+  uint32_t m0b;     // LDS destination of the first code copy (+ 4 KiB per copy)
+  uint32_t m04;     // LDS destination of the fifth copy
+  const char* sb;   // the copied tile's first code row
+  const char* sb4;  // base of the fifth copy (codes, or the tile's 32 scales)
+  uint32_t o0;      // this lane's byte offset from sb of its first chunk (16 tid)
+  uint32_t o4;      // and of its fifth copy from sb4
+};
+
+// Q (v62-v205), the accumulators (a0-a255), the register ring: load_q,
+// zero_q, store_acc, rescale_acc and tile_prefetch_k from the bf16 kernel's
+// blocks, and the fp8 kernel's tile blocks
 #include "attn_mfma_asm.inc"
 #include "attn_mfma_fp8_asm.inc"
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kR = 512;
@@ -62,10 +73,9 @@ constexpr int kRowBytes = kD * 2;              // 1152: one bf16 row in LDS
 constexpr int kTileBytes = kTile * kRowBytes;  // 36864
 constexpr int kCodeRow = kD;                   // 576: one fp8 row
 constexpr int kCodeBytes = kTile * kCodeRow;   // 18432
-constexpr int kStageBytes = kCodeBytes + 4 * kTile;  // codes + 32 fp32 scales
 constexpr int kCodeChunks = kCodeBytes / 16;   // 1152 16-byte chunks
 constexpr int kCopies = 5;                     // copy instructions per wave per tile
-constexpr float kSlack = 64.0f;                // reference slack (log2 units)
+constexpr int kScaleSlot = 1024;               // 64 lanes x 16 B (the first 128 B are the tile's)
 
 #define LDS_PTR(T) __attribute__((address_space(3))) T*
 #define CONST_PTR(T) const __attribute__((address_space(4))) T*
@@ -82,9 +92,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// 16-byte copy HBM -> LDS: lane i's bytes land at lds_base + 16 i (inactive
-// lanes copy nothing).  Inline assembly keeps the compiler from draining the
-// copies with conservative waits; the kernel waits explicitly.
+// 16-byte copy HBM -> LDS: lane i's bytes land at lds_base + 16 i.  Inline
+// assembly keeps the compiler from draining the copies with conservative
+// waits; the kernel waits explicitly.
 __device__ __forceinline__ void lds_dma_16(const void* gptr, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
                :
@@ -105,71 +115,105 @@ __device__ __forceinline__ int advance_item(const Meta& m, int num_items, int it
   return item;
 }
 
-// Copy tile `tile` (owned by `item`) into a staging buffer: codes chunk c
-// (token c / 36, bytes 16 (c % 36)) at byte 16 c, the 32 scales after them.
-// Tokens outside the visible range load a clamped (valid) token's codes; their
-// scores are masked and their scales zeroed before use.
-__device__ __forceinline__ void copy_tile(const AttnArgs& a, const Meta& m, int item, int64_t tile,
-                                          uint32_t stage, int wave, int lane_in) {
-  // (an opaque copy of the lane index: the per-lane address arithmetic below is
-  // then recomputed per tile rather than hoisted out of the tile loop, where it
-  // would hold ~15 registers)
-  int lane = lane_in;
-  asm volatile("" : "+v"(lane));
+// Where a tile's rows are: its first token, the item's visible range, and
+// the pages of its first and (pages of 16 tokens) second half.
+struct TileLoc {
+  int tok0, vlo, vhi;
+  unsigned pg0, pg1;
+};
+
+__device__ __forceinline__ TileLoc locate(const AttnArgs& a, const Meta& m, int item, int64_t tile) {
+  TileLoc L;
   const int b = m.item_b[item];
-  const int vlo = m.item_lo[item], vhi = m.item_hi[item];
-  const int tok0 = ((vlo >> 5) + static_cast<int>(tile - m.tile_start[item])) * kTile;
+  L.vlo = m.item_lo[item];
+  L.vhi = m.item_hi[item];
+  L.tok0 = ((L.vlo >> 5) + static_cast<int>(tile - m.tile_start[item])) * kTile;
   CONST_PTR(int32_t) bt = m.block_tables + static_cast<int64_t>(b) * a.max_blocks;
+  const unsigned last_page = static_cast<unsigned>(a.kv.num_pages - 1);
+  const int blk0 = L.tok0 >> a.kv.page_shift;
+  L.pg0 = min(static_cast<unsigned>(bt[blk0]), last_page);
+  L.pg1 = L.pg0;
+  // (the second entry is read only if it holds a visible token: the block
+  // table is read up to ceil(n / page_size) entries)
+  if (a.kv.page_size < kTile && L.tok0 + a.kv.page_size < L.vhi)
+    L.pg1 = min(static_cast<unsigned>(bt[blk0 + 1]), last_page);
+  return L;
+}
+
+// Token and byte of this lane's copy k: chunk c = tid + 256 k is token c / 36,
+// bytes 16 (c % 36).  Tokens outside the visible range load a visible token's
+// codes (clamped); their scores are masked and their P * s_t zeroed.
+__device__ __forceinline__ int clamp_tok(const TileLoc& L, int t) {
+  int pos = L.tok0 + t;
+  pos = pos < L.vlo ? L.vlo : pos;
+  return pos >= L.vhi ? L.vhi - 1 : pos;
+}
+
+// This lane's five copies of a tile (any page size): codes into its chunks of
+// the staging buffer, or (waves 2 and 3, fifth copy) the 32 scales into the
+// scale slot.
+__device__ __forceinline__ void copy_tile(const AttnArgs& a, const TileLoc& L, uint32_t stage, uint32_t sslot,
+                                          int wave, int tid_in) {
+  // (an opaque copy of the thread index: the address arithmetic below is then
+  // recomputed per tile rather than hoisted out of the tile loop)
+  int tid = tid_in;
+  asm volatile("" : "+v"(tid));
   const int ps = a.kv.page_size;
   const int psh = a.kv.page_shift;
-  const unsigned last_page = static_cast<unsigned>(a.kv.num_pages - 1);
-  // one page for page sizes >= 32, two of 16 (the second read only if it holds
-  // a visible token: the block table is read up to ceil(n / ps) entries)
-  const int blk0 = tok0 >> psh;
-  const unsigned pg0 = min(static_cast<unsigned>(bt[blk0]), last_page);
-  unsigned pg1 = pg0;
-  if (ps < kTile && tok0 + ps < vhi) pg1 = min(static_cast<unsigned>(bt[blk0 + 1]), last_page);
+  const int blk0 = L.tok0 >> psh;
   const char* codes = static_cast<const char*>(a.kv.data);
-#pragma unroll
-  for (int k = 0; k < kCopies - 1; ++k) {
-    const int s = wave + 4 * k;  // slots 0..15
-    const int c = 64 * s + lane;
+  // (one copy at a time: few registers live, the compiler has only v0-v53)
+#pragma unroll 1
+  for (int k = 0; k < kCopies; ++k) {
+    if (k == kCopies - 1 && wave >= 2) break;
+    const int c = tid + 256 * k;
     const int t = c / 36, p = c - 36 * (c / 36);
-    int pos = tok0 + t;
-    pos = pos < vlo ? vlo : pos;
-    pos = pos >= vhi ? vhi - 1 : pos;
-    const int in_page = pos - (blk0 << psh);
-    const unsigned pg = in_page >= ps ? pg1 : pg0;
+    const int in_page = clamp_tok(L, t) - (blk0 << psh);
+    const unsigned pg = in_page >= ps ? L.pg1 : L.pg0;
     const int off = in_page >= ps ? in_page - ps : in_page;
-    lds_dma_16(codes + ((static_cast<int64_t>(pg) << psh) + off) * kCodeRow + 16 * p, stage + 1024 * s);
+    lds_dma_16(codes + ((static_cast<int64_t>(pg) << psh) + off) * kCodeRow + 16 * p,
+               stage + 1024 * (k < 4 ? wave + 4 * k : 16 + wave));
   }
-  if (wave < 2) {  // slots 16, 17
-    const int s = 16 + wave;
-    const int c = 64 * s + lane;
-    const int t = c / 36, p = c - 36 * (c / 36);
-    int pos = tok0 + t;
-    pos = pos < vlo ? vlo : pos;
-    pos = pos >= vhi ? vhi - 1 : pos;
-    const int in_page = pos - (blk0 << psh);
-    const unsigned pg = in_page >= ps ? pg1 : pg0;
+  if (wave >= 2) {
+    // scales of tokens 4 (lane % 8) .. + 3 (one page: 4 | page size)
+    const int in_page = L.tok0 + 4 * (tid & 7) - (blk0 << psh);
+    const unsigned pg = in_page >= ps ? L.pg1 : L.pg0;
     const int off = in_page >= ps ? in_page - ps : in_page;
-    lds_dma_16(codes + ((static_cast<int64_t>(pg) << psh) + off) * kCodeRow + 16 * p, stage + 1024 * s);
-  } else if (lane < 8) {
-    // scales of tokens 4 lane .. 4 lane + 3 (one page: 4 | ps), issued by waves
-    // 2 and 3 alike so that every wave has five copies per tile
-    const int in_page = tok0 + 4 * lane - (blk0 << psh);
-    const unsigned pg = in_page >= ps ? pg1 : pg0;
-    const int off = in_page >= ps ? in_page - ps : in_page;
-    lds_dma_16(a.kv.scale + (static_cast<int64_t>(pg) << psh) + off, stage + kCodeBytes);
+    lds_dma_16(a.kv.scale + (static_cast<int64_t>(pg) << psh) + off, sslot);
   }
 }
 
-// Convert a staged tile's codes into a bf16 tile (row t: 72 chunks of 8
-// values, chunk j at slot (j & ~7) | ((j & 7) ^ swz(t))).  Thread i handles
-// 16-code chunks i, i + 256, ...
-__device__ __forceinline__ void convert_tile(LDS_PTR(const char) stage, LDS_PTR(char) tile) {
-  int tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));  // (not hoisted out of the tile loop, as in copy_tile)
+// Wave-uniform values as the scalar operands of the blocks.
+// (the builtin returns int: each half goes through uint32_t before it is
+// widened, or a low half with bit 31 set would sign-extend over the high one)
+__device__ __forceinline__ uint32_t uni(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(v));
+}
+__device__ __forceinline__ const char* uni(const void* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint64_t lo = uni(static_cast<uint32_t>(v));
+  const uint64_t hi = uni(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const char*>(lo | (hi << 32));
+}
+
+// The same copies as operands of a block, for a tile that lies in one page
+// (pages of at least one tile) and wholly inside its item's visible range:
+// this lane's chunk k is at sb + 16 (tid + 256 k).
+__device__ __forceinline__ void copy_desc(Fp8Step& f, const AttnArgs& a, const TileLoc& L, uint32_t stage,
+                                          uint32_t sslot, int wave) {
+  const int64_t row0 = (static_cast<int64_t>(L.pg0) << a.kv.page_shift) + (L.tok0 & (a.kv.page_size - 1));
+  f.sb = uni(static_cast<const char*>(a.kv.data) + row0 * kCodeRow);
+  f.sb4 = wave < 2 ? f.sb : uni(a.kv.scale + row0);
+  f.m0b = uni(stage + 1024 * wave);
+  f.m04 = uni(wave < 2 ? stage + 1024 * (16 + wave) : sslot);
+}
+
+// Convert this lane's chunks of a staged tile (chunk c = tid + 256 j) into the
+// bf16 tile: row t holds 72 chunks of 8 values, chunk j at slot
+// (j & ~7) | ((j & 7) ^ swz(t)).
+__device__ __forceinline__ void convert_own(uint32_t stage, uint32_t tile, int tid_in) {
+  int tid = tid_in;
+  asm volatile("" : "+v"(tid));
   for (int c = tid; c < kCodeChunks; c += 256) {
     const int t = c / 36, m2 = c - 36 * (c / 36);
     const i32x4 v = *reinterpret_cast<LDS_PTR(const i32x4)>(stage + 16 * c);
@@ -196,87 +240,102 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(kCompilerVgp
     const int32_t* __restrict__ block_tables) {
   const Meta m{(CONST_PTR(int32_t))item_b, (CONST_PTR(int32_t))item_lo, (CONST_PTR(int32_t))item_hi,
                (CONST_PTR(int32_t))tile_start, (CONST_PTR(int32_t))block_tables};
-  __shared__ __attribute__((aligned(1024))) char lds_tile[2][kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char lds_stage[4][kStageBytes];
-  // this thread's five conversion chunks (see convert_tile): entry j holds the
-  // two 16-byte destinations of chunk tid + 256 j in a bf16 tile (low and high
-  // 16 bits); a thread with no fifth chunk repeats its fourth
-  __shared__ __attribute__((aligned(16))) uint32_t conv_tab[256][8];
+  __shared__ __attribute__((aligned(1024))) char lds_tile[3][kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_stage[2][kCodeBytes];
+  __shared__ __attribute__((aligned(1024))) char lds_scale[4][kScaleSlot];
+  // thread i's entry j: the two 16-byte destinations (low and high 16 bits)
+  // in a bf16 tile of its chunk i + 256 j; a thread with no fifth chunk
+  // repeats its fourth
+  __shared__ __attribute__((aligned(16))) uint32_t conv_tab[256 * 5];
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5;
   const int n32 = lane & 31;
   const int head = wave * 32 + n32;
   const bool head_ok = head < a.H;
+  // with fewer than 128 heads the surplus waves still copy and convert their
+  // chunks of every tile, but skip the arithmetic
   const bool wave_active = wave * 32 < a.H;
 
-  const int64_t wg = blockIdx.x;
+  // consecutive ranges (which mostly share an item, and so its queries) run
+  // on the same XCD
+  const int64_t wg = (gridDim.x & 7) == 0 ? (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3)
+                                          : blockIdx.x;
   const int64_t t0 = a.wg_tile[wg], t1 = a.wg_tile[wg + 1];
-  __shared__ int wg_overflow;
-  if (threadIdx.x == 0) wg_overflow = 0;
-  if (t0 >= t1) {
-    if (threadIdx.x == 0) a.redo[wg] = 0;
-    return;
-  }
-  bool overflow = false;
+  if (t0 >= t1) return;
   const int ntiles = static_cast<int>(t1 - t0);
   const int first_item = advance_item(m, a.num_items, a.wg_item[wg], t0);
+  const bool direct = a.kv.page_size >= kTile;  // a tile lies in one page
+  // this lane's offsets of its first chunk and of its fifth copy (codes, or
+  // waves 2 and 3: the scales, lane % 8 repeating over the slot's pad)
+  const uint32_t o0 = 16 * tid;
+  const uint32_t o4 = wave < 2 ? 16 * (tid + 1024) : 16 * (tid & 7);
 
-  LDS_PTR(char) tiles[2];
-  LDS_PTR(char) stages[4];
-  tiles[0] = (LDS_PTR(char))(&lds_tile[0][0]);
-  tiles[1] = (LDS_PTR(char))(&lds_tile[1][0]);
-#pragma unroll
-  for (int u = 0; u < 4; ++u) stages[u] = (LDS_PTR(char))(&lds_stage[u][0]);
-  auto stage_addr = [&](int u) { return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stages[u & 3])); };
+  const uint32_t tile_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&lds_tile[0][0]));
+  const uint32_t stage_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&lds_stage[0][0]));
+  const uint32_t scale_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&lds_scale[0][0]));
+  auto tbuf = [&](int i) { return tile_base + static_cast<uint32_t>(i * kTileBytes); };
+  auto stage = [&](int n) { return stage_base + static_cast<uint32_t>((n & 1) * kCodeBytes); };
+  auto sslot = [&](int n) { return scale_base + static_cast<uint32_t>((n & 3) * kScaleSlot); };
 
   // lane-constant LDS offsets (as in the bf16 kernel)
   const int y = g ^ swz(n32);
-  int koff[4];
+  uint32_t koff[4], kcur[4], voff[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) koff[j] = n32 * kRowBytes + (((2 * j) ^ y) << 4);
-  const int q = lane >> 4, jj = lane & 15, rr = jj >> 2, c4 = jj & 3;
-  const int xs = (2 * (q & 1) + (c4 >> 1)) ^ (4 * (rr >> 1)) ^ g;
-  const int vbase = (4 * g + rr) * kRowBytes + 8 * (c4 & 1);
-  const int voff_even = vbase + (xs << 4);
-  const int voff_odd = vbase + ((4 ^ xs) << 4);
-  const int voff_even_h = vbase + 8 * kRowBytes + ((2 ^ xs) << 4);
-  const int voff_odd_h = vbase + 8 * kRowBytes + ((6 ^ xs) << 4);
-
-  // ---- copy cursor: tiles 0, 1, 2 ahead of the loop ----
-  int l_item = first_item;
-  int64_t l_tile = t0;
-  auto copy_next = [&](int slot) {
-    l_item = advance_item(m, a.num_items, l_item, l_tile);
-    copy_tile(a, m, l_item, l_tile, stage_addr(slot), wave, lane);
-    ++l_tile;
-  };
-  for (int p = 0; p < 3; ++p)
-    if (p < ntiles) copy_next(p);
-  // tile 0 landed (the copies of tiles 1 and 2 may still be in flight)
-  if (ntiles >= 3) wait_vmcnt<2 * kCopies>();
-  else if (ntiles == 2) wait_vmcnt<kCopies>();
-  else wait_vmcnt<0>();
-  __syncthreads();
-  convert_tile(stages[0], tiles[0]);
   {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int j = 0; j < 5; ++j) {
-      int c = tid + 256 * j;
-      if (c >= kCodeChunks) c -= 256;
-      const int t = c / 36, m2 = c - 36 * (c / 36);
-      const int j0 = 2 * m2, j1 = 2 * m2 + 1;
-      const int p0 = (j0 & ~7) | ((j0 & 7) ^ swz(t)), p1 = (j1 & ~7) | ((j1 & 7) ^ swz(t));
-      conv_tab[tid][j] = static_cast<uint32_t>(t * kRowBytes + 16 * p0) |
-                         (static_cast<uint32_t>(t * kRowBytes + 16 * p1) << 16);
-    }
+    const int q = lane >> 4, jj = lane & 15, rr = jj >> 2, c4 = jj & 3;
+    const int xs = (2 * (q & 1) + (c4 >> 1)) ^ (4 * (rr >> 1)) ^ g;
+    const int vbase = (4 * g + rr) * kRowBytes + 8 * (c4 & 1);
+    voff[0] = vbase + (xs << 4);
+    voff[1] = vbase + ((4 ^ xs) << 4);
+    voff[2] = vbase + 8 * kRowBytes + ((2 ^ xs) << 4);
+    voff[3] = vbase + 8 * kRowBytes + ((6 ^ xs) << 4);
   }
 
-  zero_q();  // lanes of heads >= H keep zero queries
+  // ---- copy cursor: tile tn + 3 is copied in step tn; past the range's end
+  // the last tile is copied again (so that every step has five copies per
+  // wave, and the waits count the same) ----
+  int l_item = first_item;
+  int64_t l_tile = t0;
+  auto next_loc = [&]() {
+    const int64_t tile = l_tile < t1 ? l_tile : t1 - 1;
+    l_item = advance_item(m, a.num_items, l_item, tile);
+    ++l_tile;
+    return locate(a, m, l_item, tile);
+  };
+  {
+    const TileLoc L0 = next_loc();
+    copy_tile(a, L0, stage(0), sslot(0), wave, tid);
+    const TileLoc L1 = next_loc();
+    copy_tile(a, L1, stage(1), sslot(1), wave, tid);
+  }
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    int c = tid + 256 * j;
+    if (c >= kCodeChunks) c -= 256;
+    const int t = c / 36, m2 = c - 36 * (c / 36);
+    const int j0 = 2 * m2, j1 = 2 * m2 + 1;
+    const int p0 = (j0 & ~7) | ((j0 & 7) ^ swz(t)), p1 = (j1 & ~7) | ((j1 & 7) ^ swz(t));
+    conv_tab[tid * 5 + j] = static_cast<uint32_t>(t * kRowBytes + 16 * p0) |
+                            (static_cast<uint32_t>(t * kRowBytes + 16 * p1) << 16);
+  }
+  wait_vmcnt<kCopies>();  // this lane's chunks of tile 0 (and the scales) have landed
+  convert_own(stage(0), tbuf(0), tid);
+  {
+    const TileLoc L2 = next_loc();  // (after this lane's reads of tile 0's chunks)
+    copy_tile(a, L2, stage(2), sslot(2), wave, tid);
+  }
+  __syncthreads();  // tile 0 converted, its scales in place
+  zero_q();         // lanes of heads >= H keep zero queries
+  if (wave_active) tile_prefetch_k(kcur, koff, tbuf(0));
 
+  const uint32_t tab = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&conv_tab[0])) + 20 * tid;
+  const float c = a.scale_log2;
   int tn = 0;
+  int ib = 0;  // tile buffer of tile tn
   int c_item = first_item;
   int64_t ctile = t0;
   while (ctile < t1) {
@@ -293,91 +352,85 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(kCompilerVgp
     const int tok_first = ((vlo >> 5) + static_cast<int>(seg_begin - item_ts)) * kTile;
 
     for (int64_t tt = seg_begin; tt < seg_end; ++tt, ++tn) {
-      // tile tn + 1 has landed once at most the copies of tile tn + 2 remain
-      if (tn + 2 < ntiles) wait_vmcnt<kCopies>();
-      else wait_vmcnt<0>();
-      __syncthreads();  // tile tn + 1 staged; tile tn converted; buffers of tn - 1 free
-      if (tn + 3 < ntiles) copy_next(tn + 3);
-      // the next tile's conversion: inside this tile's values step (below)
-      // in the waves that compute, here in the others
-      const bool conv_next = tn + 1 < ntiles;
-      if (conv_next && !wave_active) convert_tile(stages[(tn + 1) & 3], tiles[(tn + 1) & 1]);
-      LDS_PTR(char) buf = tiles[tn & 1];
-      LDS_PTR(const float) scl = (LDS_PTR(const float))(stages[tn & 3] + kCodeBytes);
+      const int ibn = ib == 2 ? 0 : ib + 1;
+      const int ibp = ib == 0 ? 2 : ib - 1;
+      const uint32_t tail = tn + 1 < ntiles ? 1u : 0u;
+      const TileLoc L = next_loc();           // tile tn + 3
+      const uint32_t cstage = stage(tn + 1);  // tile tn + 1's codes, then tile tn + 3's
+      const uint32_t cslot = sslot(tn + 3);
+      if (!wave_active) {
+        wait_vmcnt<kCopies>();
+        convert_own(cstage, tbuf(ibn), tid);
+        copy_tile(a, L, cstage, cslot, wave, tid);
+        if (tail) __syncthreads();
+        ib = ibn;
+        continue;
+      }
+      Fp8Step f;
+      f.cs = cstage + 16 * tid;
+      f.cs4 = f.cs + (tid < kCodeChunks - 1024 ? 16384u : 12288u);
+      f.ct = tab;
+      f.sc = sslot(tn) + 16 * g;
+      f.o0 = o0;
+      f.o4 = o4;
+      // copies inside the block for a tile in one page and wholly visible;
+      // else (pages of 16 tokens, a tile at an item's edge) after it
+      const bool in_block = direct && L.tok0 >= L.vlo && L.tok0 + kTile <= L.vhi;
+      if (in_block) {
+        f.cp = 1;
+        copy_desc(f, a, L, cstage, cslot, wave);
+      } else {
+        f.cp = 0;
+        f.m0b = f.m04 = 0;
+        f.sb = f.sb4 = uni(a.kv.data);
+      }
+      const uint32_t tl = uni(tail);
       const int tok0 = tok_first + static_cast<int>(tt - seg_begin) * kTile;
-
-      if (wave_active) {
-        const uint32_t bbase = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(buf));
-        const uint32_t kcur[4] = {bbase + static_cast<uint32_t>(koff[0]), bbase + static_cast<uint32_t>(koff[1]),
-                                  bbase + static_cast<uint32_t>(koff[2]), bbase + static_cast<uint32_t>(koff[3])};
-        float s[16];
-        fp8_scores(kcur, s);
-        // per-token scale, mask, scale to log2 units; P * s_t as bf16 pairs
-        // (element i of the lane's 16 is the low half of pair i / 2 when i is
-        // even), the B operand of the values MFMAs.  The scales are read again
-        // rather than held across the exponentials.  Tokens outside the
-        // visible range (only in a tile that is not wholly inside it) get a
-        // score of -inf and a scale of zero: their staged scale may be anything.
-        const bool partial = !(tok0 >= vlo && tok0 + kTile <= vhi);  // uniform
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const f32x4 sv = *reinterpret_cast<LDS_PTR(const f32x4)>(scl + 8 * i4 + 4 * g);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s[4 * i4 + e] *= sv[e] * a.scale_log2;
+      const bool masked = !(tok0 >= vlo && tok0 + kTile <= vhi);
+      // masked tiles: element i of a lane is visible iff lo <= 8 (i / 4) + i % 4 < hi
+      const int lo = vlo - tok0 - 4 * g, hi = vhi - tok0 - 4 * g;
+      const uint32_t bs = uni(tbuf(ib)), bp = uni(tbuf(ibp)), bn = uni(tbuf(ibn));
+      const bool first = tt == seg_begin, last = tt == seg_end - 1;
+      uint32_t vn[4];  // the tile's own values addresses when it ends the segment
+      if (first) {
+        if (!last) {
+          if (masked) fp8_first_tail_m1(kcur, koff, voff, bs, bp, bn, tl, c, m_ref, l_sum, f, lo, hi);
+          else fp8_first_tail_m0(kcur, koff, voff, bs, bp, bn, tl, c, m_ref, l_sum, f);
+          if (!in_block) copy_tile(a, L, cstage, cslot, wave, tid);
+        } else {  // one-tile segment: its own values step follows
+          if (masked) fp8_first_lastv_m1(kcur, koff, voff, bs, bs, bn, tl, c, m_ref, l_sum, f, vn, voff, lo, hi);
+          else fp8_first_lastv_m0(kcur, koff, voff, bs, bs, bn, tl, c, m_ref, l_sum, f, vn, voff);
+          if (!in_block) copy_tile(a, L, cstage, cslot, wave, tid);
+          fp8_last_pv_f1(kcur, koff, vn, bn, tl);
         }
-        if (partial) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int tok = tok0 + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (tok < vlo || tok >= vhi) s[i] = -INFINITY;
+      } else {
+        float fac;       // 2^(old - new) when the tile moved this lane's reference, else 1
+        uint64_t moved;  // lanes whose reference moved
+        const bool fpv = tt - 1 == seg_begin;  // first values step of the segment: O starts at 0
+        if (!last) {
+          if (fpv) {
+            if (masked) fp8_step_tail_f1_m1(kcur, koff, voff, bs, bp, bn, tl, c, m_ref, l_sum, f, fac, moved, lo, hi);
+            else fp8_step_tail_f1_m0(kcur, koff, voff, bs, bp, bn, tl, c, m_ref, l_sum, f, fac, moved);
+          } else {
+            if (masked) fp8_step_tail_f0_m1(kcur, koff, voff, bs, bp, bn, tl, c, m_ref, l_sum, f, fac, moved, lo, hi);
+            else fp8_step_tail_f0_m0(kcur, koff, voff, bs, bp, bn, tl, c, m_ref, l_sum, f, fac, moved);
           }
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, s[i]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        if (tt == seg_begin) m_ref = tmax;
-        else if (tmax > m_ref + kSlack) overflow = true;
-        uint32_t pb[8];
-        float psum = 0.f;
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          f32x4 sv = *reinterpret_cast<LDS_PTR(const f32x4)>(scl + 8 * i4 + 4 * g);
-          if (partial) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int tok = tok0 + 8 * i4 + 4 * g + e;
-              if (tok < vlo || tok >= vhi) sv[e] = 0.f;
-            }
-          }
-#pragma unroll
-          for (int e = 0; e < 4; e += 2) {
-            const int i = 4 * i4 + e;
-            const float p0 = __builtin_amdgcn_exp2f(s[i] - m_ref);
-            const float p1 = __builtin_amdgcn_exp2f(s[i + 1] - m_ref);
-            psum += p0 + p1;
-            const bf16x2 pk = {static_cast<__bf16>(p0 * sv[e]), static_cast<__bf16>(p1 * sv[e + 1])};  // RNE
-            pb[i >> 1] = __builtin_bit_cast(uint32_t, pk);
-          }
-        }
-        l_sum += psum;
-        const uint32_t vcur[4] = {bbase + static_cast<uint32_t>(voff_even), bbase + static_cast<uint32_t>(voff_odd),
-                                  bbase + static_cast<uint32_t>(voff_even_h),
-                                  bbase + static_cast<uint32_t>(voff_odd_h)};
-        if (conv_next) {
-          const uint32_t tid = threadIdx.x;
-          const uint32_t cs = stage_addr(tn + 1) + 16 * tid;
-          const uint32_t cs4 = cs + (tid < kCodeChunks - 1024 ? 16384u : 12288u);
-          const uint32_t ct = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&conv_tab[0][0])) + 32 * tid;
-          const uint32_t tb = __builtin_amdgcn_readfirstlane(
-              static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tiles[(tn + 1) & 1])));
-          if (tt == seg_begin) fp8_values_conv_f1(vcur, pb, cs, cs4, ct, tb);
-          else fp8_values_conv_f0(vcur, pb, cs, cs4, ct, tb);
+          if (moved) rescale_acc(fac);  // rare: a score far above the reference
+          if (!in_block) copy_tile(a, L, cstage, cslot, wave, tid);
         } else {
-          if (tt == seg_begin) fp8_values_f1(vcur, pb);
-          else fp8_values_f0(vcur, pb);
+          if (fpv) {
+            if (masked) fp8_step_lastv_f1_m1(kcur, koff, voff, bs, bp, bn, tl, c, m_ref, l_sum, f, fac, moved, vn, voff, lo, hi);
+            else fp8_step_lastv_f1_m0(kcur, koff, voff, bs, bp, bn, tl, c, m_ref, l_sum, f, fac, moved, vn, voff);
+          } else {
+            if (masked) fp8_step_lastv_f0_m1(kcur, koff, voff, bs, bp, bn, tl, c, m_ref, l_sum, f, fac, moved, vn, voff, lo, hi);
+            else fp8_step_lastv_f0_m0(kcur, koff, voff, bs, bp, bn, tl, c, m_ref, l_sum, f, fac, moved, vn, voff);
+          }
+          if (moved) rescale_acc(fac);  // before the tile's own values step
+          if (!in_block) copy_tile(a, L, cstage, cslot, wave, tid);
+          fp8_last_pv_f0(kcur, koff, vn, bn, tl);
         }
       }
+      ib = ibn;
     }
     ctile = seg_end;
 
@@ -405,9 +458,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(kCompilerVgp
       }
     }
   }
-  if (__any(overflow) && lane == 0) wg_overflow = 1;
-  __syncthreads();
-  if (threadIdx.x == 0) a.redo[wg] = wg_overflow;
+  // the copies issued past the range's end land before the workgroup's LDS
+  // is released
+  wait_vmcnt<0>();
 }
 
 }  // namespace

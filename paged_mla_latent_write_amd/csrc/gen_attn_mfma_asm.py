@@ -237,6 +237,18 @@ def s_part(st, dma, copy_p, prefetch_v):
                 st.add(f"v_lshrrev_b32 v{TMP_DMA}, 16, %[l{d // 2}]")
 
 
+def emit_ops(st, ops):
+    """Adds a list of operations: plain lines, ("R", line, tag) for an LDS read
+    the Stream tracks, ("W", tag) for a wait until that read has landed."""
+    for op in ops:
+        if isinstance(op, str):
+            st.add(op)
+        elif op[0] == "R":
+            st.lds(op[1], op[2])
+        else:
+            st.wait_for(op[1])
+
+
 def pv_part(st, first_pv, vops, p_regs, prefetched, end_v=False, smem=None, early_tail=None):
     """O^T += V^T P^T (fragments from %[v0..v3], this lane's read offsets plus
     the buffer base %[bp]; P in p_regs), with the VALU list vops interleaved
@@ -271,10 +283,10 @@ def pv_part(st, first_pv, vops, p_regs, prefetched, end_v=False, smem=None, earl
         if i == 1 and vops:
             st.add("s_nop 7", "s_nop 7", "s_nop 4")  # score results of the last k-steps
         if i >= 2:
-            st.add(*vops[vi:vi + per])
+            emit_ops(st, vops[vi:vi + per])
             vi += per
         if end_v and i == 32 - NF:
-            st.add(*vops[vi:])
+            emit_ops(st, vops[vi:])
             vi = len(vops)
             st.add(*[f"v_add_u32 %[vn{j}], %[bs], %[vo{j}]" for j in range(4)])
         if early_tail is not None and i == early_tail:
@@ -297,7 +309,7 @@ def pv_part(st, first_pv, vops, p_regs, prefetched, end_v=False, smem=None, earl
             off = 128 * (mt2 >> 1) + 1152 * 16 * j2
             st.lds(f"ds_read_b64_tr_b16 {vring2(i % NF, 0)}, {rl} offset:{off}", ("N", i % NF))
             st.lds(f"ds_read_b64_tr_b16 {vring2(i % NF, 1)}, {rh} offset:{off}", ("N", i % NF))
-    st.add(*vops[vi:])
+    emit_ops(st, vops[vi:])
     st.add(*[f"v_sub_u32 %[v{j}], %[v{j}], %[bp]" for j in range(4)])
 
 
@@ -608,105 +620,270 @@ def pv_rest(st, first_pv, p_regs, vregs):
             v_reads(st, i + NF, vregs)
 
 
-def emit_fp8():
-    """The matrix-core steps of the fp8-cache kernel (attn_mfma_fp8.hip), which
-    converts each tile to bf16 in LDS first (the bf16 kernel's layout): the
-    scores and the values of one tile as two blocks, each with its LDS
-    fragments pipelined through the ring as in the blocks above; the per-token
-    scales and the softmax stay in the kernel's C++ between them.  Q and the
-    accumulators use the registers of the blocks above (load_q, zero_q and
-    store_acc come from attn_mfma_asm.inc)."""
-    o = ["// Generated by gen_attn_mfma_asm.py --fp8; do not edit by hand.", ""]
-    # scores S^T = K Q^T of the tile whose bf16 rows are at %[k0..k3] (this
-    # lane's K row offsets plus the buffer base); the 16 results leave in s[]
-    st = Stream()
-    for i in range(NF):
-        k_read(st, i)
+# ---------------------------------------------------------------------------
+# The fp8-cache kernel (attn_mfma_fp8.hip).  Its tile step is the bf16 step
+# above (scores of tile n; values of tile n - 1 with the softmax of tile n
+# between their MFMAs) on bf16 tiles the workgroup converts from the staged
+# E4M3 codes, plus, between the scores MFMAs,
+#   * the conversion of tile n + 1: this lane's five 16-code chunks of the
+#     staging buffer (%[cs] + 4096 j, the fifth at %[cs4]), eight codes at a
+#     time, to bf16 rows of the next tile buffer (%[bn] plus the two 16-bit
+#     offsets of entry j of this lane's table row %[ct]);
+#   * the copies of tile n + 3 into the staging buffer just converted, each
+#     lane to its own chunks (so no other wave reads them): five
+#     global_load_lds from %[sb] / %[sb4], LDS rows from %[m0b] (+ 4 KB per
+#     copy) / %[m04]; skipped when %[cp] is 0 (the caller then copies);
+# and in the softmax the per-token scales of tile n (%[sc]: its 32 fp32 scales
+# + 16 g): the scores are multiplied by them before the tile maximum, and P
+# after the row sum, before it is rounded to bf16.
+# Registers: during the scores the conversion uses v224-v231 (the previous P
+# has moved to v54-v61 after the first MFMA) and v206/v207; in the softmax the
+# scale groups go to v224-v227 / v228-v231, where P is written only at its end.
+FP8_CA, FP8_CB, FP8_OUT = PN, PN + 2, PN + 4
+FP8_SA, FP8_SB = PN, PN + 4
+FP8_ADR, FP8_TAB = T0, T1
+FP8_COPIES = 5                     # copies per wave per tile
+FP8_HALVES = [(j, h) for j in range(5) for h in range(2)]
+FP8_HALF_AT = {3 + 2 * i: jh for i, jh in enumerate(FP8_HALVES)}  # scores MFMA -> half chunk
+FP8_COPY_AT = 23                   # the copies follow this scores MFMA
+FP8_SCALE_AT = 27                  # the first two scale groups are read after this one
+
+
+def fp8_code_read(st, j, h):
+    x = FP8_CA if h == 0 else FP8_CB
+    src = f"%[cs4] offset:{8 * h}" if j == 4 else f"%[cs] offset:{4096 * j + 8 * h}"
+    st.lds(f"ds_read_b64 v[{x}:{x + 1}], {src}", ("C", j, h))
+
+
+def fp8_tab_read(st, j):
+    st.lds(f"ds_read_b32 v{FP8_TAB}, %[ct] offset:{4 * j}", ("T", j))
+
+
+def fp8_half(st, j, h, prev):
+    """Eight codes of chunk j (half h): four packed conversions (exact: every
+    E4M3 value is a bf16 value), the read of the same half of chunk j + 1 into
+    the freed code registers, and a 16-byte LDS write."""
+    x = FP8_CA if h == 0 else FP8_CB
+    st.wait_for(("C", j, h))
+    if prev is not None:
+        st.wait_for(("W",) + prev)  # the previous write has read the values and the address
+    for k in range(4):
+        sel = " op_sel:[1,0,0]" if k % 2 else ""
+        st.add(f"v_cvt_scalef32_pk_bf16_fp8 v{FP8_OUT + k}, v{x + k // 2}, 1.0{sel}")
+    if j < 4:
+        fp8_code_read(st, j + 1, h)
+    if h == 0:
+        st.wait_for(("T", j))
+        st.add(f"v_and_b32 v{FP8_ADR}, 0xffff, v{FP8_TAB}")
+    else:
+        st.add(f"v_lshrrev_b32 v{FP8_ADR}, 16, v{FP8_TAB}")
+        if j < 4:
+            fp8_tab_read(st, j + 1)
+    st.add(f"v_add_u32 v{FP8_ADR}, %[bn], v{FP8_ADR}")
+    st.lds(f"ds_write_b128 v{FP8_ADR}, v[{FP8_OUT}:{FP8_OUT + 3}]", ("W", j, h))
+
+
+def fp8_copies(st):
+    """The copies of a tile lying wholly in one page and inside its item's
+    visible range: this lane's chunk k is at %[sb] + %[o0] + 4096 k (the
+    offsets formed in v224-v228, free once the last conversion write has
+    read them); the fifth copy reads %[sb4] + %[o4]."""
+    st.wait_for(("W",) + FP8_HALVES[-1])
+    st.add("s_cmp_eq_u32 %[cp], 0", "s_cbranch_scc1 5f", "s_mov_b32 m0, %[m0b]")
+    for k in range(4):
+        st.add(f"v_add_u32 v{PN + k}, {4096 * k}, %[o0]")
+    for k in range(4):
+        if k:
+            st.add("s_add_u32 m0, m0, 0x1000")
+        st.add("s_nop 0", f"global_load_lds_dwordx4 v{PN + k}, %[sb] offset:0")
+    st.add("s_mov_b32 m0, %[m04]", "s_nop 0", "global_load_lds_dwordx4 %[o4], %[sb4] offset:0", "5:")
+
+
+def fp8_scale_read(st, g, p):
+    b = FP8_SA if g % 2 == 0 else FP8_SB
+    st.lds(f"ds_read_b128 v[{b}:{b + 3}], %[sc] offset:{32 * g}", ("S", g, p))
+
+
+def s_part_fp8(st, copy_p, prefetch_v):
+    """Scores of tile n with the conversion of tile n + 1, the copies of tile
+    n + 3 and the reads of the first two scale groups of tile n interleaved.
+    copy_p and prefetch_v as in s_part."""
+    if prefetch_v:
+        st.add(*[f"v_add_u32 %[v{j}], %[bp], %[v{j}]" for j in range(4)])
+    prev = None
     for k in range(36):
         st.wait_pair("K", k, 36)
         st.add(f"v_mfma_f32_32x32x16_bf16 {s_chain(k)}, {ring4(k)}, {q(k)}, {'0' if k == 0 else s_chain(k)}")
+        if k == 0:
+            if copy_p:
+                st.add(*[f"v_mov_b32 v{P_BASE + j}, v{PN + j}" for j in range(8)])
+            # tile n + 1 has landed once only the copies of tile n + 2 remain
+            st.add(f"s_waitcnt vmcnt({FP8_COPIES})")
+            fp8_code_read(st, 0, 0)
+            fp8_code_read(st, 0, 1)
+            fp8_tab_read(st, 0)
         if k + NF < 36:
             k_read(st, k + NF)
-    st.add("s_nop 7", "s_nop 7", "s_nop 4")  # the last MFMA's results must have landed
-    st.add(*[f"v_mov_b32 %[s{i}], v{SS + i}" for i in range(16)])
-    outs = [", ".join(f'[s{i}] "=v"(s[{i}])' for i in range(16))]
-    o += block("fp8_scores", ["const uint32_t (&kcur)[4]", "float (&s)[16]"], st.lines, outs,
-               ['[k0] "v"(kcur[0]), [k1] "v"(kcur[1]), [k2] "v"(kcur[2]), [k3] "v"(kcur[3])'])
-    # values O^T += V^T P^T of the same tile (%[v0..v3]: this lane's transposed
-    # read offsets plus the buffer base; P as eight registers of bf16 pairs);
-    # f1: the segment's first tile, whose MFMAs start the accumulators at zero
-    for first in (0, 1):
-        st = Stream()
-        st.add(*[f"v_mov_b32 v{P_BASE + j}, %[p{j}]" for j in range(8)])
-        st.add("s_nop 1")  # P written by VALU just before the MFMAs read it
-        for i in range(NF):
-            v_reads(st, i)
-        for i in range(32):
-            mt, j = PV_ORDER[i]
-            st.wait_pair("V", i, 32)
-            src_c = "0" if (first and j == 0) else acc(mt)
-            st.add(f"v_mfma_f32_32x32x16_bf16 {acc(mt)}, {vring4(i)}, {P_FIXED[j]}, {src_c}")
-            if i + NF < 32:
-                v_reads(st, i + NF)
-        ins = ['[v0] "v"(vcur[0]), [v1] "v"(vcur[1]), [v2] "v"(vcur[2]), [v3] "v"(vcur[3])',
-               ", ".join(f'[p{j}] "v"(p[{j}])' for j in range(8))]
-        o += block(f"fp8_values_f{first}", ["const uint32_t (&vcur)[4]", "const uint32_t (&p)[8]"], st.lines,
-                   [], ins)
-    # the same values step with the next tile's conversion interleaved: this
-    # lane's five 16-code chunks of the staged tile (%[cs] + 4096 j, the fifth
-    # at %[cs4]) become bf16 rows of the next tile buffer (%[tb] plus the two
-    # 16-bit offsets of the lane's entry j in the table at %[ct]).  The score
-    # and P registers are free during the values step and hold the table
-    # entries (v208-v215), two code buffers (v216-v223) and the converted
-    # values (v224-v231); the block waits for its LDS writes before it ends,
-    # since the caller's barrier publishes the converted tile.
-    D, C, OUT = SS, SS + 8, PN
-    CONV_AT = [3, 9, 15, 21, 26]  # the MFMA after which chunk j is converted
-    for first in (0, 1):
-        st = Stream()
-        st.add(*[f"v_mov_b32 v{P_BASE + j}, %[p{j}]" for j in range(8)])
-        st.lds(f"ds_read_b128 v[{D}:{D + 3}], %[ct] offset:0", ("D", 0))
-        st.lds(f"ds_read_b128 v[{D + 4}:{D + 7}], %[ct] offset:16", ("D", 1))
+        elif prefetch_v:
+            v_reads(st, (k - VSLOT) % NF)
+        if k in FP8_HALF_AT:
+            fp8_half(st, *FP8_HALF_AT[k], prev)
+            prev = FP8_HALF_AT[k]
+        if k == FP8_COPY_AT:
+            fp8_copies(st)
+        if k == FP8_SCALE_AT:
+            st.wait_for(("W",) + prev)
+            fp8_scale_read(st, 0, 1)
+            fp8_scale_read(st, 1, 1)
 
-        def code_read(j):
-            b = C + 4 * (j % 2)
-            src = "%[cs4] offset:0" if j == 4 else f"%[cs] offset:{4096 * j}"
-            st.lds(f"ds_read_b128 v[{b}:{b + 3}], {src}", ("C", j))
 
-        code_read(0)
-        code_read(1)
-        for i in range(NF):
-            v_reads(st, i)
-        for i in range(32):
-            mt, j = PV_ORDER[i]
-            st.wait_pair("V", i, 32)
-            src_c = "0" if (first and j == 0) else acc(mt)
-            st.add(f"v_mfma_f32_32x32x16_bf16 {acc(mt)}, {vring4(i)}, {P_FIXED[j]}, {src_c}")
-            if i + NF < 32:
-                v_reads(st, i + NF)
-            if i in CONV_AT:
-                c = CONV_AT.index(i)
-                b = C + 4 * (c % 2)
-                st.wait_for(("C", c))
-                st.wait_for(("D", 1 if c >= 4 else 0))
-                if c > 0:
-                    st.wait_for(("W", c - 1))  # its writes have read OUT, T0 and T1
-                for k in range(4):
-                    st.add(f"v_cvt_scalef32_pk_bf16_fp8 v{OUT + 2 * k}, v{b + k}, 1.0",
-                           f"v_cvt_scalef32_pk_bf16_fp8 v{OUT + 2 * k + 1}, v{b + k}, 1.0 op_sel:[1,0,0]")
-                if c + 2 <= 4:
-                    code_read(c + 2)  # into the buffer the conversions just read
-                st.add(f"v_and_b32 v{T0}, 0xffff, v{D + c}", f"v_add_u32 v{T0}, %[tb], v{T0}",
-                       f"v_lshrrev_b32 v{T1}, 16, v{D + c}", f"v_add_u32 v{T1}, %[tb], v{T1}")
-                st.lds(f"ds_write_b128 v{T0}, v[{OUT}:{OUT + 3}]", ("W", c))
-                st.lds(f"ds_write_b128 v{T1}, v[{OUT + 4}:{OUT + 7}]", ("W", c))
-        st.wait_all()
-        ins = ['[v0] "v"(vcur[0]), [v1] "v"(vcur[1]), [v2] "v"(vcur[2]), [v3] "v"(vcur[3])',
-               ", ".join(f'[p{j}] "v"(p[{j}])' for j in range(8)),
-               '[cs] "v"(cs), [cs4] "v"(cs4), [ct] "v"(ct), [tb] "s"(tb)']
-        o += block(f"fp8_values_conv_f{first}",
-                   ["const uint32_t (&vcur)[4]", "const uint32_t (&p)[8]", "uint32_t cs", "uint32_t cs4",
-                    "uint32_t ct", "uint32_t tb"], st.lines, [], ins)
+def softmax_fp8(first, masked):
+    """The softmax of one tile of the fp8 kernel (scores in v208-v223, scale
+    groups 0 and 1 already read): as softmax_ops, with each score multiplied by
+    its token's scale first and each probability by it after the row sum;
+    leaves P (bf16 pairs) in v224-v231.  Masked tokens get a score of -inf
+    and a P times scale of 0 (their staged scale may be anything)."""
+    s = [f"v{SS + i}" for i in range(16)]
+    buf = [FP8_SA, FP8_SB, FP8_SA, FP8_SB]
+    ops = []
+
+    def read(g, p):
+        ops.append(("R", f"ds_read_b128 v[{buf[g]}:{buf[g] + 3}], %[sc] offset:{32 * g}", ("S", g, p)))
+
+    def mask(i, fill):
+        e = 8 * (i >> 2) + (i & 3)
+        return [f"v_cmp_ge_i32 vcc, {e}, %[lo]", f"v_cndmask_b32 {s[i]}, {fill}, {s[i]}, vcc",
+                f"v_cmp_lt_i32 vcc, {e}, %[hi]", f"v_cndmask_b32 {s[i]}, {fill}, {s[i]}, vcc"]
+
+    max_ops = [[f"v_max3_f32 v{T0}, {s[0]}, {s[1]}, {s[2]}", f"v_max_f32 v{T0}, v{T0}, {s[3]}"]]
+    max_ops += [[f"v_max3_f32 v{T0}, v{T0}, {s[4 * g]}, {s[4 * g + 1]}",
+                 f"v_max3_f32 v{T0}, v{T0}, {s[4 * g + 2]}, {s[4 * g + 3]}"] for g in (1, 2, 3)]
+    if masked:
+        ops.append(f"v_mov_b32 v{T1}, {NEG_INF}")
+    for g in range(4):
+        ops.append(("W", ("S", g, 1)))
+        ops += [f"v_mul_f32 {s[4 * g + e]}, v{buf[g] + e}, {s[4 * g + e]}" for e in range(4)]
+        if g < 2:
+            read(g + 2, 1)
+        if masked:
+            for e in range(4):
+                ops += mask(4 * g + e, f"v{T1}")
+        ops += max_ops[g]
+    read(0, 2)
+    read(1, 2)
+    ops += [f"v_mov_b32 v{T1}, v{T0}", "s_nop 1", f"v_permlane32_swap_b32 v{T1}, v{T1}", "s_nop 1",
+            f"v_max_f32 v{T0}, v{T0}, v{T1}", f"v_mul_f32 v{T0}, %[c], v{T0}"]
+    if first:
+        ops.append(f"v_mov_b32 %[mref], v{T0}")
+    else:
+        # the reference move of softmax_ops
+        ops += [f"v_add_f32 v{T1}, {SLACK}, %[mref]",
+                f"v_cmp_gt_f32 %[mv], v{T0}, v{T1}",
+                f"v_sub_f32 v{T1}, %[mref], v{T0}",
+                f"v_exp_f32 v{T1}, v{T1}",
+                "s_nop 0",
+                f"v_cndmask_b32 %[fac], 1.0, v{T1}, %[mv]",
+                f"v_cndmask_b32 %[mref], %[mref], v{T0}, %[mv]",
+                "v_mul_f32 %[lsum], %[lsum], %[fac]"]
+    ops += [f"v_fma_f32 {s[i]}, {s[i]}, %[c], -%[mref]" for i in range(16)]
+    for g in range(4):
+        ops += [f"v_exp_f32 {s[4 * g + e]}, {s[4 * g + e]}" for e in range(4)]
+        ops.append("s_nop 0")
+        if g == 0:
+            ops += [f"v_add_f32 v{T1}, {s[0]}, {s[1]}", f"v_add_f32 v{T1}, v{T1}, {s[2]}",
+                    f"v_add_f32 v{T1}, v{T1}, {s[3]}"]
+        else:
+            ops += [f"v_add_f32 v{T1}, v{T1}, {s[4 * g + e]}" for e in range(4)]
+        ops.append(("W", ("S", g, 2)))
+        ops += [f"v_mul_f32 {s[4 * g + e]}, v{buf[g] + e}, {s[4 * g + e]}" for e in range(4)]
+        if g < 2:
+            read(g + 2, 2)
+        if masked:
+            for e in range(4):
+                ops += mask(4 * g + e, "0")
+        ops += [f"v_cvt_pk_bf16_f32 {s[4 * g]}, {s[4 * g]}, {s[4 * g + 1]}",
+                f"v_cvt_pk_bf16_f32 {s[4 * g + 2]}, {s[4 * g + 2]}, {s[4 * g + 3]}"]
+    ops.append(f"v_add_f32 %[lsum], %[lsum], v{T1}")
+    ops += [f"v_mov_b32 v{PN + 2 * g + h}, {s[4 * g + 2 * h]}" for g in range(4) for h in range(2)]
+    return ops
+
+
+def fp8_tail(st):
+    """Wait for this wave's LDS operations (the converted tile n + 1 among
+    them), pass the workgroup barrier that publishes it, and read its first K
+    fragments into the ring (%[k0..k3] = %[ko0..ko3] + %[bn]); %[tail] = 0: no
+    next tile."""
+    st.wait_all()
+    st.add("s_cmp_eq_u32 %[tail], 0", "s_cbranch_scc1 9f", "s_barrier")
+    st.add(*[f"v_add_u32 %[k{j}], %[bn], %[ko{j}]" for j in range(4)])
+    for i in range(NF):
+        st.add(f"ds_read_b128 {ring4(i)}, %[k{i % 4}] offset:{128 * (i // 4)}")
+    st.add("9:")
+
+
+FP8_IN = ('[cs] "v"(f.cs), [cs4] "v"(f.cs4), [ct] "v"(f.ct), [sc] "v"(f.sc), [cp] "s"(f.cp), '
+          '[m0b] "s"(f.m0b), [m04] "s"(f.m04), [sb] "s"(f.sb), [sb4] "s"(f.sb4), [o0] "v"(f.o0), '
+          '[o4] "v"(f.o4)')
+
+
+def emit_fp8():
+    """The tile blocks of the fp8-cache kernel (names as the bf16 kernel's:
+    fp8_{step,first}_{tail,lastv}[_f{first values step}]_m{masked}, and
+    fp8_last_pv_f*); Q and the accumulators use the registers of the bf16
+    blocks (load_q, zero_q, store_acc, rescale_acc and tile_prefetch_k come
+    from attn_mfma_asm.inc)."""
+    o = ["// Generated by gen_attn_mfma_asm.py --fp8; do not edit by hand.", ""]
+    for kind in ("step", "first"):
+        for end in ("tail", "lastv"):
+            for first_pv in ((0, 1) if kind == "step" else (0,)):
+                for masked in (0, 1):
+                    args = ["uint32_t (&kcur)[4]", "const uint32_t (&koff)[4]", "uint32_t (&voff)[4]",
+                            "uint32_t bs", "uint32_t bp", "uint32_t bn", "uint32_t tail", "float c",
+                            "float& mref", "float& lsum", "const Fp8Step& f"]
+                    ins = ['[bs] "s"(bs), [bp] "s"(bp), [bn] "s"(bn), [tail] "s"(tail), [c] "s"(c)', KOFF_IN,
+                           FP8_IN]
+                    outs = [STATS, KCUR, VOFF]
+                    if kind == "step":
+                        args += ["float& fac", "uint64_t& moved"]
+                        outs.append(FAC)
+                    if end == "lastv":
+                        args += ["uint32_t (&vn)[4]", "const uint32_t (&vo)[4]"]
+                        outs.append('[vn0] "=&v"(vn[0]), [vn1] "=&v"(vn[1]), [vn2] "=&v"(vn[2]), [vn3] "=&v"(vn[3])')
+                        ins.append('[vo0] "v"(vo[0]), [vo1] "v"(vo[1]), [vo2] "v"(vo[2]), [vo3] "v"(vo[3])')
+                    if masked:
+                        args += ["int lo", "int hi"]
+                        ins.append('[lo] "v"(lo), [hi] "v"(hi)')
+                    st = Stream()
+                    st.queue = [("K", i) for i in range(NF)]
+                    if kind == "step":
+                        s_part_fp8(st, True, True)
+                        pv_part(st, first_pv, softmax_fp8(False, masked), P_FIXED, True, end == "lastv")
+                    else:
+                        s_part_fp8(st, False, end == "lastv")
+                        st.add("s_nop 7", "s_nop 7", "s_nop 4")  # score results of the last k-steps
+                        emit_ops(st, softmax_fp8(True, masked))
+                        if end == "lastv":
+                            st.add(*[f"v_sub_u32 %[v{j}], %[v{j}], %[bp]" for j in range(4)])
+                            st.add(*[f"v_add_u32 %[vn{j}], %[bs], %[vo{j}]" for j in range(4)])
+                    if end == "tail":
+                        fp8_tail(st)
+                    name = f"fp8_{kind}_{end}" + (f"_f{first_pv}" if kind == "step" else "") + f"_m{masked}"
+                    o += block(name, args, st.lines, outs, ins, ', "m0", "scc"')
+    # the segment's last values step (as tile_last_pv), then the fp8 tail
+    for first_pv in (0, 1):
+        st = Stream()
+        order = [(k - VSLOT) % NF for k in range(36 - NF, 36)] if first_pv else [i % NF for i in range(32 - NF, 32)]
+        st.queue = [("V", f) for f in order for _ in range(2)]
+        st.add("s_nop 1")  # P was written by VALU at the end of the previous block
+        pv_rest(st, first_pv, P_NEW, ("%[vn0]", "%[vn1]", "%[vn2]", "%[vn3]"))
+        fp8_tail(st)
+        o += block(f"fp8_last_pv_f{first_pv}",
+                   ["uint32_t (&kcur)[4]", "const uint32_t (&koff)[4]", "const uint32_t (&vn)[4]", "uint32_t bn",
+                    "uint32_t tail"],
+                   st.lines, [KCUR],
+                   ['[bn] "s"(bn), [tail] "s"(tail)', KOFF_IN,
+                    '[vn0] "v"(vn[0]), [vn1] "v"(vn[1]), [vn2] "v"(vn[2]), [vn3] "v"(vn[3])'],
+                   ', "scc"')
     return "\n".join(o)
 
 

@@ -80,8 +80,7 @@ struct Layout {
   int G = 0;
   size_t q_lat = 0, o_lat = 0, lse = 0, o_scale = 0, item_b = 0, item_lo = 0, item_hi = 0,
          tile_start = 0, wg_tile = 0, wg_item = 0, item_wg = 0, part_o = 0, part_lse = 0,
-         part_scale = 0, redo = 0,
-         total = 0;
+         part_scale = 0, total = 0;
 };
 
 // Returns false when the number of workgroups cannot be determined.
@@ -122,8 +121,6 @@ bool make_layout(const mla_cache* c, const mla_attn* a, int64_t num_items, Layou
   off = align_up(off + sizeof(float) * 2 * G * H);
   L->part_scale = off;
   off = align_up(off + sizeof(float) * 2 * G * H);
-  L->redo = off;
-  off = align_up(off + sizeof(int32_t) * G);
   L->total = off;
   return true;
 }
@@ -481,8 +478,6 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
   a.part_o = at<float>(workspace, L.part_o);
   a.part_lse = at<float>(workspace, L.part_lse);
   a.part_scale = at<float>(workspace, L.part_scale);
-  a.redo = at<int32_t>(workspace, L.redo);
-  a.redo_only = nullptr;
 
   // (the MFMA kernel takes the tile maximum on unscaled scores: scale > 0)
   const bool use_mfma = !generic && mla::mfma_attn_supported(kv, H) && attn->scale > 0.f &&
@@ -497,15 +492,7 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
                             (qp_sh % 8 == 0) && aligned16(q_lat) && aligned16(q_pe) &&
                             aligned16(kv.scale);
   if (use_mfma_fp8) {
-    // the fp8 kernel, then an exact recompute of any workgroup whose scores
-    // jumped past its reference by more than 2^64 (no workgroup does on
-    // ordinary inputs; the launch then returns at once)
     e = mla::launch_attn_mfma_fp8(a, s);
-    if (e == hipSuccess) {
-      a.redo_only = a.redo;
-      e = mla::launch_attn_generic(a, s);
-      a.redo_only = nullptr;
-    }
   } else {
     e = use_mfma ? mla::launch_attn_mfma(a, s) : mla::launch_attn_generic(a, s);
   }

@@ -73,11 +73,6 @@ struct AttnArgs {
   float* part_o;          // [2G][H][R] fp32 partials (cut items)
   float* part_lse;        // [2G][H]
   float* part_scale;      // [2G][H]
-  // fp8 MFMA kernel: per workgroup, 1 when a score passed its segment's
-  // reference maximum by more than 2^64 (the generic kernel then recomputes
-  // that workgroup's range exactly), else 0
-  int32_t* redo;          // [G]
-  const int32_t* redo_only;  // generic kernel: non-null = only workgroups with redo_only[g] != 0
 };
 
 // Compute units of the current device (cached per device; -1 on error).

@@ -33,7 +33,31 @@ def test_fp8_include_matches_generator():
 
 def test_fp8_blocks_wait_for_their_lds_reads():
     n, problems = _load("check_attn_mfma_asm").check((CSRC / "attn_mfma_fp8_asm.inc").read_text())
-    assert n == 5 and not problems, problems[:5]
+    assert n == 14 and not problems, problems[:5]
+
+
+def test_checker_catches_a_conversion_before_its_codes_landed():
+    # plant a mistake: drop the waits of one fp8 block's scores half (the
+    # conversions then read code registers whose LDS reads are in flight)
+    text = (CSRC / "attn_mfma_fp8_asm.inc").read_text()
+    start = text.index("void fp8_step_tail_f0_m0(")
+    cut = text.index("v_mfma_f32_32x32x16_bf16 v[208:223], v[232:235], v[86:89]", start)
+    planted = text[:start] + text[start:cut].replace("s_waitcnt lgkmcnt(", "s_nop 0 // (") + text[cut:]
+    n, problems = _load("check_attn_mfma_asm").check(planted)
+    assert any("VALU use of a register whose LDS read has not landed" in p for p in problems)
+
+
+def test_checker_catches_a_write_source_overwritten_too_early():
+    # plant a mistake: a conversion overwrites the values the previous
+    # half's LDS write may still be reading
+    text = (CSRC / "attn_mfma_fp8_asm.inc").read_text()
+    start = text.index("void fp8_step_tail_f0_m0(")
+    first = text.index("ds_write_b128 v206", start)
+    nxt = text.index("v_cvt_scalef32_pk_bf16_fp8", first)
+    wait = text.rindex("s_waitcnt lgkmcnt(", first, nxt)
+    planted = text[:wait] + "s_nop 0 // (" + text[wait + len("s_waitcnt lgkmcnt("):]
+    n, problems = _load("check_attn_mfma_asm").check(planted)
+    assert any("LDS write still reads" in p for p in problems)
 
 
 def test_blocks_wait_for_their_lds_reads():

@@ -320,11 +320,11 @@ def test_decode_mfma_partly_filled_waves(mla, kv, H):
 
 
 @pytest.mark.parametrize("G", [1, 2])
-def test_decode_fp8_score_jump_is_recomputed(mla, G):
+def test_decode_fp8_score_jump_moves_the_reference(mla, G):
     """fp8 cache: a key whose score passes its segment's first-tile maximum by
-    about 2^97 (log2 units) makes the matrix-core kernel hand the workgroup's
-    range to the exact recompute; the output is still the oracle's (the
-    needle's latent)."""
+    about 2^97 (log2 units) moves the matrix-core kernel's reference maximum
+    up, with a rescale of the accumulators; the output is still the oracle's
+    (the needle's latent)."""
     say(f"decode fp8 score jump G={G}")
     d = W.Dims(H=32, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
     case = W.custom(d, [300, 41], seed=740, kv_dtype=O.KV_FP8)
