@@ -352,6 +352,39 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(kCompilerVgp
     const int tok_first = ((vlo >> 5) + static_cast<int>(seg_begin - item_ts)) * kTile;
 
     for (int64_t tt = seg_begin; tt < seg_end; ++tt, ++tn) {
+      // The common case -- a tile inside the segment (not its first, second
+      // or last) whose copy three tiles ahead is a wholly visible tile of the
+      // same item, in one page -- runs as one statement that loops over those
+      // tiles (fp8_hot_loop), reading the copies' block-table entries itself.
+      if (wave_active && direct && tt - 1 > seg_begin) {
+        const int64_t hot_end = min(min(seg_end - 1, item_te - 4), t1 - 3);
+        if (tt < hot_end) {
+          const int steps = static_cast<int>(hot_end - tt);
+          l_item = advance_item(m, a.num_items, l_item, l_tile);  // the loop's first copy: tile tn + 3
+          const TileLoc L = locate(a, m, l_item, l_tile);
+          const int b = m.item_b[l_item];
+          const int32_t* bt_row = block_tables + static_cast<int64_t>(b) * a.max_blocks;
+          int tok = L.tok0;
+          int32_t pg = static_cast<int32_t>(L.pg0);
+          uint32_t n = uni(static_cast<uint32_t>(steps));
+          uint32_t bs = uni(tbuf(ib)), bp = uni(tbuf(ib == 0 ? 2 : ib - 1)), bn = uni(tbuf(ib == 2 ? 0 : ib + 1));
+          uint32_t cs = stage(tn + 1) + 16 * tid;
+          uint32_t cs4 = cs + (tid < kCodeChunks - 1024 ? 16384u : 12288u);
+          uint32_t ds = uni(stage(tn + 2) - stage(tn + 1));
+          uint32_t scb = uni(sslot(tn));
+          uint32_t sc = scb + 16 * g;
+          uint32_t m0b = uni(stage(tn + 3) + 1024 * wave);
+          fp8_hot_loop(kcur, koff, voff, c, m_ref, l_sum, bs, bp, bn, n, cs, cs4, tab, ds, sc, scb, 16 * g,
+                       uni(scale_base), uni(scale_base + 4 * kScaleSlot), m0b, uni(wave >= 2 ? 1u : 0u), o0, o4,
+                       tok, pg, uni(a.kv.data), reinterpret_cast<const float*>(uni(a.kv.scale)),
+                       reinterpret_cast<const int32_t*>(uni(bt_row)), uni(static_cast<uint32_t>(a.kv.page_shift)),
+                       uni(static_cast<uint32_t>(a.kv.page_size - 1)), uni(static_cast<uint32_t>(a.kv.num_pages - 1)));
+          l_tile += steps;
+          tt += steps;
+          tn += steps;
+          ib = (ib + steps) % 3;
+        }
+      }
       const int ibn = ib == 2 ? 0 : ib + 1;
       const int ibp = ib == 0 ? 2 : ib - 1;
       const uint32_t tail = tn + 1 < ntiles ? 1u : 0u;

@@ -102,7 +102,7 @@ def check(text):
     for name, body in blocks:
         lines = [ln.strip().strip('"').replace("\\n", "") for ln in body.split("\n")]
         starts_with_ring = name.startswith(("tile_step", "tile_first", "tile_last_pv", "tile_hot", "fp8_step",
-                                            "fp8_first", "fp8_last_pv"))
+                                            "fp8_first", "fp8_last_pv", "fp8_hot"))
         live = set(range(ring, 256)) if starts_with_ring else set()
         if "1:" in lines and "s_cbranch_scc1 1b" in lines:
             # a loop: its reads still in flight at the back edge carry into

@@ -249,7 +249,7 @@ def emit_ops(st, ops):
             st.wait_for(op[1])
 
 
-def pv_part(st, first_pv, vops, p_regs, prefetched, end_v=False, smem=None, early_tail=None):
+def pv_part(st, first_pv, vops, p_regs, prefetched, end_v=False, smem=None, early_tail=None, fp8=False):
     """O^T += V^T P^T (fragments from %[v0..v3], this lane's read offsets plus
     the buffer base %[bp]; P in p_regs), with the VALU list vops interleaved
     between the MFMAs (they read the scores, so they start after 21 wait
@@ -264,7 +264,9 @@ def pv_part(st, first_pv, vops, p_regs, prefetched, end_v=False, smem=None, earl
     wait for the next tile's copy, pass the barrier and read the next tile's
     first K fragments into the ring slots freed so far and then after each
     remaining MFMA, so the next scores step starts on landed fragments
-    (order: EARLY_TAIL_ORDER)."""
+    (order: EARLY_TAIL_ORDER).  fp8: the early tail waits for no copy (the
+    barrier publishes the tile this wave converted), and every operation of
+    vops is issued before it."""
     if not prefetched:
         st.add(*[f"v_add_u32 %[v{j}], %[bp], %[v{j}]" for j in range(4)])
         for i in range(NF):
@@ -291,8 +293,14 @@ def pv_part(st, first_pv, vops, p_regs, prefetched, end_v=False, smem=None, earl
             st.add(*[f"v_add_u32 %[vn{j}], %[bs], %[vo{j}]" for j in range(4)])
         if early_tail is not None and i == early_tail:
             assert early_tail >= 32 - NF
-            st.wait_all()
-            st.add(f"s_waitcnt vmcnt({COPY_LOADS})", "s_barrier")
+            if fp8:
+                emit_ops(st, vops[vi:])
+                vi = len(vops)
+                st.wait_all()
+                st.add("s_barrier")
+            else:
+                st.wait_all()
+                st.add(f"s_waitcnt vmcnt({COPY_LOADS})", "s_barrier")
             st.add(*[f"v_add_u32 %[k{j}], %[bn], %[ko{j}]" for j in range(4)])
         if early_tail is not None and i >= early_tail:
             # the slots freed by MFMAs 32 - NF .. i get no more values
@@ -683,20 +691,26 @@ def fp8_half(st, j, h, prev):
     st.lds(f"ds_write_b128 v{FP8_ADR}, v[{FP8_OUT}:{FP8_OUT + 3}]", ("W", j, h))
 
 
-def fp8_copies(st):
+def fp8_copies(st, hot=False):
     """The copies of a tile lying wholly in one page and inside its item's
     visible range: this lane's chunk k is at %[sb] + %[o0] + 4096 k (the
-    offsets formed in v224-v228, free once the last conversion write has
-    read them); the fifth copy reads %[sb4] + %[o4]."""
+    offsets formed in v224-v227, free once the last conversion write has
+    read them); the fifth copy reads %[sb4] + %[o4].  hot: the bases are
+    s[96:97] and s[94:95] (formed by the hot loop), and there is no skip."""
     st.wait_for(("W",) + FP8_HALVES[-1])
-    st.add("s_cmp_eq_u32 %[cp], 0", "s_cbranch_scc1 5f", "s_mov_b32 m0, %[m0b]")
+    sb, sb4 = ("s[96:97]", "s[94:95]") if hot else ("%[sb]", "%[sb4]")
+    if not hot:
+        st.add("s_cmp_eq_u32 %[cp], 0", "s_cbranch_scc1 5f")
+    st.add("s_mov_b32 m0, %[m0b]")
     for k in range(4):
         st.add(f"v_add_u32 v{PN + k}, {4096 * k}, %[o0]")
     for k in range(4):
         if k:
             st.add("s_add_u32 m0, m0, 0x1000")
-        st.add("s_nop 0", f"global_load_lds_dwordx4 v{PN + k}, %[sb] offset:0")
-    st.add("s_mov_b32 m0, %[m04]", "s_nop 0", "global_load_lds_dwordx4 %[o4], %[sb4] offset:0", "5:")
+        st.add("s_nop 0", f"global_load_lds_dwordx4 v{PN + k}, {sb} offset:0")
+    st.add("s_mov_b32 m0, %[m04]", "s_nop 0", f"global_load_lds_dwordx4 %[o4], {sb4} offset:0")
+    if not hot:
+        st.add("5:")
 
 
 def fp8_scale_read(st, g, p):
@@ -704,10 +718,11 @@ def fp8_scale_read(st, g, p):
     st.lds(f"ds_read_b128 v[{b}:{b + 3}], %[sc] offset:{32 * g}", ("S", g, p))
 
 
-def s_part_fp8(st, copy_p, prefetch_v):
+def s_part_fp8(st, copy_p, prefetch_v, hot=False):
     """Scores of tile n with the conversion of tile n + 1, the copies of tile
     n + 3 and the reads of the first two scale groups of tile n interleaved.
-    copy_p and prefetch_v as in s_part."""
+    copy_p and prefetch_v as in s_part.  hot: the copy's bases are formed
+    here (see fp8_hot_loop), and %[tok] then moves on to the next copy."""
     if prefetch_v:
         st.add(*[f"v_add_u32 %[v{j}], %[bp], %[v{j}]" for j in range(4)])
     prev = None
@@ -729,8 +744,28 @@ def s_part_fp8(st, copy_p, prefetch_v):
         if k in FP8_HALF_AT:
             fp8_half(st, *FP8_HALF_AT[k], prev)
             prev = FP8_HALF_AT[k]
+        if hot and k == 1:
+            # row of the copied tile's first token: page (clamped) * page
+            # size + in-page position; its codes and its scales
+            st.add("s_min_u32 %[t0], %[pg], %[np1]", "s_lshl_b32 %[t0], %[t0], %[psh]",
+                   "s_and_b32 %[t1], %[tok], %[pmask]", "s_add_u32 %[t0], %[t0], %[t1]",
+                   f"s_mul_i32 s96, %[t0], {ROW_BYTES // 2}", f"s_mul_hi_u32 s97, %[t0], {ROW_BYTES // 2}",
+                   "s_add_u32 s96, s96, s98", "s_addc_u32 s97, s97, s99",
+                   "s_lshl_b32 %[t1], %[t0], 2", "s_lshr_b32 %[t0], %[t0], 30",
+                   "s_add_u32 s94, s92, %[t1]", "s_addc_u32 s95, s93, %[t0]",
+                   "s_cmp_eq_u32 %[w2], 0", "s_cselect_b64 s[94:95], s[96:97], s[94:95]")
+        if hot and k == 2:
+            # fifth copy's LDS rows: the codes' last slots (waves 0, 1) or
+            # the scale slot of tile n + 3, the one before tile n's (waves 2, 3)
+            st.add("s_add_u32 %[t1], %[scb], 0xc00", "s_cmp_ge_u32 %[t1], %[scend]",
+                   "s_cselect_b32 %[t0], 0x1000, 0", "s_sub_u32 %[t1], %[t1], %[t0]",
+                   "s_add_u32 %[t0], %[m0b], 0x4000", "s_cmp_eq_u32 %[w2], 0",
+                   "s_cselect_b32 %[m04], %[t0], %[t1]")
         if k == FP8_COPY_AT:
-            fp8_copies(st)
+            fp8_copies(st, hot)
+        if hot and k == FP8_COPY_AT + 1:
+            st.add("s_add_u32 %[tok], %[tok], 32", "s_lshr_b32 %[pgo], %[tok], %[psh]",
+                   "s_lshl_b32 %[pgo], %[pgo], 2")
         if k == FP8_SCALE_AT:
             st.wait_for(("W",) + prev)
             fp8_scale_read(st, 0, 1)
@@ -826,6 +861,59 @@ FP8_IN = ('[cs] "v"(f.cs), [cs4] "v"(f.cs4), [ct] "v"(f.ct), [sc] "v"(f.sc), [cp
           '[o4] "v"(f.o4)')
 
 
+def fp8_hot_loop():
+    """The common fp8 tile step, repeated %[n] times in one statement (tiles
+    in the middle of a segment whose copy three tiles ahead is a wholly
+    visible tile of the same item): the step of fp8_step_tail_f0_m0 with the
+    copy's page read by the loop itself (block-table entry %[pgo] of %[bt],
+    loaded during the values MFMAs for the next pass), the copy's bases formed
+    in s[96:97] (codes: %[data], kept in s[98:99]) and s[94:95] (scales:
+    %[scl], kept in s[92:93]; waves 0 and 1 take the codes' base), an early
+    tail (barrier before the last four values MFMAs, as tile_hot_loop), the
+    rare rescale out of line, and the rotation of the tile buffers (bp, bs,
+    bn), the staging buffer (%[cs], %[cs4], %[m0b] move by %[ds], whose sign
+    alternates) and the scale slot (%[scb] steps by 1 KiB from %[scbase] to
+    %[scend] and wraps; %[sc] = %[scb] + %[g16])."""
+    st = Stream()
+    st.queue = [("K", k) for k in EARLY_TAIL_ORDER]
+    st.add("s_mov_b64 s[98:99], %[data]", "s_mov_b64 s[92:93], %[scl]", "s_waitcnt lgkmcnt(0)", "1:")
+    s_part_fp8(st, True, True, hot=True)
+    pv_part(st, False, softmax_fp8(False, False), P_FIXED, True, False, "s_load_dword %[pg], %[bt], %[pgo]",
+            early_tail=EARLY_TAIL, fp8=True)
+    st.add("s_cmp_lg_u64 %[mv], 0", "s_cbranch_scc1 3f",
+           "2:",
+           "s_mov_b32 %[t0], %[bp]", "s_mov_b32 %[bp], %[bs]", "s_mov_b32 %[bs], %[bn]", "s_mov_b32 %[bn], %[t0]",
+           "v_add_u32 %[cs], %[ds], %[cs]", "v_add_u32 %[cs4], %[ds], %[cs4]", "s_add_u32 %[m0b], %[m0b], %[ds]",
+           "s_sub_u32 %[ds], 0, %[ds]",
+           "s_add_u32 %[scb], %[scb], 0x400", "s_cmp_eq_u32 %[scb], %[scend]",
+           "s_cselect_b32 %[scb], %[scbase], %[scb]", "v_add_u32 %[sc], %[scb], %[g16]",
+           "s_sub_u32 %[n], %[n], 1", "s_cmp_lg_u32 %[n], 0", "s_cbranch_scc1 1b",
+           "s_branch 4f",
+           "3:")
+    st.add(*rescale_lines())
+    # the K fragments in flight leave in the loop's order; the blocks after it
+    # assume index order, so they are waited for here
+    st.add("s_branch 2b", "4:", "s_waitcnt lgkmcnt(0)")
+    args = ["uint32_t (&kcur)[4]", "const uint32_t (&koff)[4]", "uint32_t (&voff)[4]", "float c",
+            "float& mref", "float& lsum", "uint32_t& bs", "uint32_t& bp", "uint32_t& bn", "uint32_t& n",
+            "uint32_t& cs", "uint32_t& cs4", "uint32_t ct", "uint32_t& ds", "uint32_t& sc", "uint32_t& scb",
+            "uint32_t g16", "uint32_t scbase", "uint32_t scend", "uint32_t& m0b", "uint32_t w2", "uint32_t o0",
+            "uint32_t o4", "int& tok", "int32_t& pg", "const char* data", "const float* scl", "const int32_t* bt",
+            "uint32_t psh", "uint32_t pmask", "uint32_t np1"]
+    outs = [STATS, KCUR, VOFF, FAC,
+            '[bs] "+s"(bs), [bp] "+s"(bp), [bn] "+s"(bn), [n] "+s"(n), [ds] "+s"(ds), [scb] "+s"(scb), '
+            '[m0b] "+s"(m0b), [tok] "+s"(tok), [pg] "+s"(pg)',
+            '[cs] "+v"(cs), [cs4] "+v"(cs4), [sc] "+v"(sc)',
+            '[t0] "=&s"(t0), [t1] "=&s"(t1), [pgo] "=&s"(pgo), [m04] "=&s"(m04)']
+    ins = ['[c] "s"(c), [ct] "v"(ct), [g16] "v"(g16), [scbase] "s"(scbase), [scend] "s"(scend), [w2] "s"(w2), '
+           '[o0] "v"(o0), [o4] "v"(o4), [data] "s"(data), [scl] "s"(scl), [bt] "s"(bt), [psh] "s"(psh), '
+           '[pmask] "s"(pmask), [np1] "s"(np1)',
+           KOFF_IN]
+    return block("fp8_hot_loop", args, st.lines, outs, ins,
+                 ', "m0", "scc", "s92", "s93", "s94", "s95", "s96", "s97", "s98", "s99"',
+                 locals_="  float fac;\n  uint64_t moved;\n  uint32_t t0, t1, pgo, m04;\n")
+
+
 def emit_fp8():
     """The tile blocks of the fp8-cache kernel (names as the bf16 kernel's:
     fp8_{step,first}_{tail,lastv}[_f{first values step}]_m{masked}, and
@@ -869,6 +957,7 @@ def emit_fp8():
                         fp8_tail(st)
                     name = f"fp8_{kind}_{end}" + (f"_f{first_pv}" if kind == "step" else "") + f"_m{masked}"
                     o += block(name, args, st.lines, outs, ins, ', "m0", "scc"')
+    o += fp8_hot_loop()
     # the segment's last values step (as tile_last_pv), then the fp8 tail
     for first_pv in (0, 1):
         st = Stream()
