@@ -299,10 +299,11 @@ size_t mla_prefill_workspace_size(const mla_cache* cache, const mla_attn* attn, 
  * take at most 1.25 GiB of workspace: requests go in groups whose visible
  * ranges all fit, or, for a range longer than that, one at a time in passes
  * whose results are merged by log-sum-exp.  The expanded form needs w_uk and w_uv, qk_rope_dim
- * 64, qk_nope_dim = v_head_dim = 128 and kv_lora_rank a multiple of 64.
+ * 64, qk_nope_dim = v_head_dim = 128, kv_lora_rank a multiple of 64 and scale > 0
+ * (otherwise the absorbed form runs, flag or not).
  * MLA_FLAG_PREFILL_ABSORBED / _EXPANDED choose; without a flag the expanded
- * form runs for windowed calls (window > 0) whose chunks average at least 64
- * rows, the absorbed one otherwise.  mla_prefill_workspace_size returns the
+ * form runs for calls whose chunks average at least 64 rows, the absorbed one
+ * otherwise.  mla_prefill_workspace_size returns the
  * chosen form's size (the same attn flags must be passed to both calls).
  */
 mla_status mla_prefill_chunk(const mla_cache* cache, int32_t layer_idx, const mla_attn* attn,

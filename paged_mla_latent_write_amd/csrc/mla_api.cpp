@@ -259,10 +259,11 @@ XLayout make_xlayout(const mla_attn* a, int64_t batch, int64_t total_q, int64_t 
 bool prefill_route_expanded(const mla_cache* c, const mla_attn* a, int32_t batch, int32_t total_q) {
   if (a->flags & (MLA_FLAG_GENERIC_KERNELS | MLA_FLAG_PREFILL_ABSORBED)) return false;
   if (!a->w_uk || !a->w_uv) return false;
+  if (!(a->scale > 0.f)) return false;  // (the kernel scales the tile maximum of the raw scores)
   const CacheView kv = layer_view(c, 0);
   if (!mla::prefill_expanded_supported(kv, a->num_heads, a->qk_nope_dim, a->v_head_dim)) return false;
   if (a->flags & MLA_FLAG_PREFILL_EXPANDED) return true;
-  return a->window > 0 && static_cast<int64_t>(total_q) >= 64 * static_cast<int64_t>(batch);
+  return static_cast<int64_t>(total_q) >= 64 * static_cast<int64_t>(batch);
 }
 
 template <typename T>

@@ -87,22 +87,58 @@ __device__ __forceinline__ int vperm(int j) {
   return (q == 1 || q == 2) ? (j ^ 12) : j;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Two fp32 values as a bf16 pair (hardware conversion, nearest even).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+constexpr int kGKRow = kXDn * 2 + 16;      // bytes per LDS row of a K wave's output tile (transpose)
+constexpr int kGSlots = (kGTok + kGN) * (kGPitch / 16);  // 16-byte LDS slots of one stage (A then B rows)
+constexpr int kGDma = kGSlots / kGThreads;               // copies per thread per stage (9)
+static_assert(kGSlots % kGThreads == 0 && kGTok * (kGPitch / 16) % 64 == 0, "stage copies");
+
+// 16-byte copy HBM -> LDS: lane i's bytes land at lds_base + 16 i.  Inline
+// assembly keeps the compiler from draining the copies with conservative
+// waits; the kernel waits explicitly.
+__device__ __forceinline__ void lds_dma_16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_base)), "v"(gptr)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(n) with lgkmcnt and expcnt left unconstrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <bool kFp8>
 __global__ __launch_bounds__(kGThreads, 1) void kv_expand_kernel(XPassArgs a) {
-  __shared__ __attribute__((aligned(16))) char As[kGTok * kGPitch];
-  __shared__ __attribute__((aligned(16))) char Bs[kGN * kGPitch];
-  __shared__ float tok_scale[kGTok];
-  const int bz = blockIdx.z, b = a.b0 + bz;
+  // A (tokens) and B (weight rows) of a stage (bf16 caches: two stages, the
+  // copies of stage s + 2 in flight during stage s); after the last stage
+  // the same memory holds the K waves' output tiles for the transposed store
+  constexpr int kStages = kFp8 ? 1 : 2;
+  __shared__ __attribute__((aligned(16))) char smem[kStages * (kGTok + kGN) * kGPitch];
+  __shared__ float tok_scale[kFp8 ? kGTok : 1];
+  char* const As = smem;
+  char* const Bs = smem + kGTok * kGPitch;
+  const int tile = blockIdx.x, h = blockIdx.y, bz = blockIdx.z;
+  const int b = a.b0 + bz;
   int64_t n, m, k0, ntok;
   if (!pass_range(a, b, &n, &m, &k0, &ntok)) return;
-  const int j0 = blockIdx.x * kGTok;
+  const int j0 = tile * kGTok;
   if (j0 >= ntok) return;
-  const int h = blockIdx.y;
   const int ck = a.ck;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int g = lane >> 5, n32 = lane & 31;
   const CacheView& kv = a.kv;
   const int R = kv.R;
-  const bool fp8 = kv.dtype == kKvFp8;
   const int32_t* bt = a.block_tables + static_cast<int64_t>(b) * a.max_blocks;
   const unsigned last_page = static_cast<unsigned>(kv.num_pages - 1);
   // B rows 0..127: W_UK[h] rows, 128..255: W_UV[h] rows
@@ -117,18 +153,7 @@ __global__ __launch_bounds__(kGThreads, 1) void kv_expand_kernel(XPassArgs a) {
     const unsigned pg = min(static_cast<unsigned>(bt[tok >> kv.page_shift]), last_page);
     return static_cast<int64_t>(pg) * kv.page_size + (tok & (kv.page_size - 1));
   };
-  // cache rows of this thread's A chunks (fixed over the stages)
-  int64_t arow[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = fp8 ? ((t + kGThreads * q) >> 2) : ((t + kGThreads * q) >> 3);
-    arow[q] = (fp8 && q >= 2) ? 0 : cache_row(j0 + r);
-  }
-  if (t < kGTok) {
-    const int j = j0 + t;
-    tok_scale[t] = (fp8 && j < ntok) ? kv.scale[cache_row(j)] : 1.0f;
-  }
-
+  const char* cache = static_cast<const char*>(kv.data);
   // wave tile: 64 tokens x 128 columns (all K or all V)
   const int tm = wave >> 1, tn = wave & 1;  // tm 0..3
   f32x16 acc[2][4];
@@ -136,117 +161,176 @@ __global__ __launch_bounds__(kGThreads, 1) void kv_expand_kernel(XPassArgs a) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) acc[i][jj] = f32x16{};
-
-  // The next stage's global loads are issued before this stage's MFMAs and
-  // land in registers; they are stored to LDS after the stage.
-  i16x8 ra[4], rb[4];
-  uint4 rc[2];
-  auto load_stage = [&](int kc) {
-    if (!fp8) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int idx = t + kGThreads * q;
-        const int r = idx >> 3, c = idx & 7;
-        i16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (j0 + r < ntok)
-          v = *reinterpret_cast<const i16x8*>(static_cast<const uint16_t*>(kv.data) + arow[q] * kv.D + kc + 8 * c);
-        ra[q] = v;
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int idx = t + kGThreads * q;
-        const int r = idx >> 2, c = idx & 3;
-        uint4 codes = make_uint4(0, 0, 0, 0);
-        if (j0 + r < ntok)
-          codes = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(kv.data) + arow[q] * kv.D + kc + 16 * c);
-        rc[q] = codes;
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int idx = t + kGThreads * q;
-      const int r = idx >> 3, c = idx & 7;
-      const uint16_t* W = r < kXDn ? Wk + static_cast<int64_t>(r) * R : Wv + static_cast<int64_t>(r - kXDn) * R;
-      rb[q] = *reinterpret_cast<const i16x8*>(W + kc + 8 * c);
-    }
-  };
-  auto store_stage = [&]() {
-    if (!fp8) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int idx = t + kGThreads * q;
-        *reinterpret_cast<i16x8*>(As + (idx >> 3) * kGPitch + (idx & 7) * 16) = ra[q];
-      }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int idx = t + kGThreads * q;
-        const int r = idx >> 2, c = idx & 3;
-        const uint32_t w4[4] = {rc[q].x, rc[q].y, rc[q].z, rc[q].w};
-        i16x8 lo, hi;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          // E4M3 -> bf16 is exact (3 mantissa bits, exponent range inside bf16's)
-          lo[e] = static_cast<short>(__float_as_uint(e4m3_to_f32((w4[e >> 2] >> (8 * (e & 3))) & 0xFF)) >> 16);
-          hi[e] = static_cast<short>(__float_as_uint(e4m3_to_f32((w4[2 + (e >> 2)] >> (8 * (e & 3))) & 0xFF)) >> 16);
-        }
-        *reinterpret_cast<i16x8*>(As + r * kGPitch + c * 32) = lo;
-        *reinterpret_cast<i16x8*>(As + r * kGPitch + c * 32 + 16) = hi;
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int idx = t + kGThreads * q;
-      *reinterpret_cast<i16x8*>(Bs + (idx >> 3) * kGPitch + (idx & 7) * 16) = rb[q];
-    }
-  };
-  load_stage(0);
-  for (int kc = 0; kc < R; kc += kGK) {
-    store_stage();
-    __syncthreads();
-    if (kc + kGK < R) load_stage(kc + kGK);  // in flight during this stage's MFMAs
+  // the MFMAs of one stage on the LDS rows at As / Bs
+  auto stage_mfma = [&](const char* as, const char* bs) {
 #pragma unroll
     for (int ks = 0; ks < kGK / 16; ++ks) {
       i16x8 af[2], bf[4];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const i16x8*>(As + (64 * tm + 32 * i + n32) * kGPitch + (16 * ks + 8 * g) * 2);
+        af[i] = *reinterpret_cast<const i16x8*>(as + (64 * tm + 32 * i + n32) * kGPitch + (16 * ks + 8 * g) * 2);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
-        bf[jj] = *reinterpret_cast<const i16x8*>(Bs + (128 * tn + 32 * jj + n32) * kGPitch + (16 * ks + 8 * g) * 2);
+        bf[jj] = *reinterpret_cast<const i16x8*>(bs + (128 * tn + 32 * jj + n32) * kGPitch + (16 * ks + 8 * g) * 2);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) acc[i][jj] = mfma(af[i], bf[jj], acc[i][jj]);
     }
-    __syncthreads();
+  };
+
+  if constexpr (!kFp8) {
+    // Stage slot z (16 bytes; 9 per 144-byte row: 8 of data, one of pad)
+    // of the A rows then the B rows is filled by thread z % 512, copy z / 512
+    // (each wave's copy covers 64 consecutive slots).  Pad slots repeat the
+    // row's last chunk; token rows past the pass's keys repeat its last row
+    // (finite values, never attended).
+    const char* dsrc[kGDma];
+#pragma unroll
+    for (int k = 0; k < kGDma; ++k) {
+      const int z = kGThreads * k + t;
+      const int zr = z < kGTok * 9 ? z : z - kGTok * 9;
+      const int r = zr / 9, cc = min(zr - 9 * r, 7);
+      if (z < kGTok * 9)
+        dsrc[k] = cache + cache_row(j0 + r) * kv.D * 2 + 16 * cc;
+      else
+        dsrc[k] = reinterpret_cast<const char*>(r < kXDn ? Wk + static_cast<int64_t>(r) * R
+                                                         : Wv + static_cast<int64_t>(r - kXDn) * R) + 16 * cc;
+    }
+    const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem)) + 1024 * wave;
+    auto issue = [&](int kc, int buf) {
+#pragma unroll
+      for (int k = 0; k < kGDma; ++k)
+        lds_dma_16(dsrc[k] + 2 * kc, lds0 + buf * ((kGTok + kGN) * kGPitch) + 16 * kGThreads * k);
+    };
+    const int nst = R / kGK;
+    issue(0, 0);
+    if (nst > 1) issue(kGK, 1);
+    for (int st = 0; st < nst; ++st) {
+      if (st + 1 < nst) wait_vmcnt<kGDma>();  // this thread's copies of stage st have landed
+      else wait_vmcnt<0>();
+      __syncthreads();  // and every thread's
+      const char* base = smem + (st & 1) * ((kGTok + kGN) * kGPitch);
+      stage_mfma(base, base + kGTok * kGPitch);
+      __syncthreads();  // every wave is done with this buffer
+      if (st + 2 < nst) issue((st + 2) * kGK, st & 1);
+    }
+  } else {
+    // fp8 caches: the next stage's loads land in registers during this
+    // stage's MFMAs; the codes are converted on their way to LDS.  This
+    // thread's A chunks (16 codes of a token row per stage; rows past the
+    // pass's keys load zeros) and B chunks, as pointers fixed over the stages.
+    constexpr int kAq = kGTok * 4 / kGThreads;  // 16-code A chunks per thread (2)
+    constexpr int kBq = kGN * 8 / kGThreads;    // 8-value B chunks per thread (4)
+    const char* asrc[kAq];
+    bool aok[kAq];
+#pragma unroll
+    for (int q = 0; q < kAq; ++q) {
+      const int idx = t + kGThreads * q;
+      const int r = idx >> 2, c = idx & 3;
+      asrc[q] = cache + cache_row(j0 + r) * kv.D + 16 * c;
+      aok[q] = j0 + r < ntok;
+    }
+    const uint16_t* bsrc[kBq];
+#pragma unroll
+    for (int q = 0; q < kBq; ++q) {
+      const int idx = t + kGThreads * q;
+      const int r = idx >> 3, c = idx & 7;
+      bsrc[q] = (r < kXDn ? Wk + static_cast<int64_t>(r) * R : Wv + static_cast<int64_t>(r - kXDn) * R) + 8 * c;
+    }
+    if (t < kGTok) {
+      const int j = j0 + t;
+      tok_scale[t] = j < ntok ? kv.scale[cache_row(j)] : 0.0f;
+    }
+    i32x4 ra[kAq];
+    i16x8 rb[kBq];
+    auto load_stage = [&](int kc) {
+#pragma unroll
+      for (int q = 0; q < kAq; ++q) {
+        i32x4 v = {0, 0, 0, 0};
+        if (aok[q]) v = *reinterpret_cast<const i32x4*>(asrc[q] + kc);
+        ra[q] = v;
+      }
+#pragma unroll
+      for (int q = 0; q < kBq; ++q) rb[q] = *reinterpret_cast<const i16x8*>(bsrc[q] + kc);
+    };
+    auto store_stage = [&]() {
+#pragma unroll
+      for (int q = 0; q < kAq; ++q) {
+        // 16 E4M3 codes -> 16 bf16 values (exact: every E4M3 value is a bf16 value)
+        const int idx = t + kGThreads * q;
+        const int r = idx >> 2, c = idx & 3;
+        i32x4 lo, hi;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          lo[2 * w] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ra[q][w], 1.0f, false));
+          lo[2 * w + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ra[q][w], 1.0f, true));
+          hi[2 * w] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ra[q][w + 2], 1.0f, false));
+          hi[2 * w + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ra[q][w + 2], 1.0f, true));
+        }
+        *reinterpret_cast<i32x4*>(As + r * kGPitch + c * 32) = lo;
+        *reinterpret_cast<i32x4*>(As + r * kGPitch + c * 32 + 16) = hi;
+      }
+#pragma unroll
+      for (int q = 0; q < kBq; ++q) {
+        const int idx = t + kGThreads * q;
+        *reinterpret_cast<i16x8*>(Bs + (idx >> 3) * kGPitch + (idx & 7) * 16) = rb[q];
+      }
+    };
+    load_stage(0);
+    for (int kc = 0; kc < R; kc += kGK) {
+      store_stage();
+      __syncthreads();
+      if (kc + kGK < R) load_stage(kc + kGK);  // in flight during this stage's MFMAs
+      stage_mfma(As, Bs);
+      __syncthreads();
+    }
   }
 
   // epilogue: element e of acc[i][jj] is token 64 tm + 32 i + 8 (e / 4) + 4 g + e % 4,
   // column d = 32 jj + n32 of the wave's K (tn = 0) or V (tn = 1) block
+  auto val = [&](int i, int jj, int e, int r) {
+    const float x = acc[i][jj][e];
+    return kFp8 ? x * tok_scale[r] : x;
+  };
+  if (tn == 1) {
+    // V_expT[h][d][vperm(j)]: four consecutive tokens (a quad), one 8-byte store
+    uint16_t* vrow = v_expT + static_cast<int64_t>(h) * kXDv * ck + j0;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 2; ++i) {
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int d = 32 * jj + n32;
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d = 32 * jj + n32;
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int r = 64 * tm + 32 * i + 8 * e4 + 4 * g;  // tile-local token of element 4 e4
-        uint16_t v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = f32_to_bf16(acc[i][jj][4 * e4 + e] * tok_scale[r + e]);
-        if (tn == 1) {
-          // V_expT[h][d][vperm(j)]: four consecutive tokens (a quad), one 8-byte store
-          uint16_t* dst = v_expT + (static_cast<int64_t>(h) * kXDv + d) * ck + vperm(j0 + r);
-          *reinterpret_cast<uint2*>(dst) = make_uint2(v[0] | (static_cast<uint32_t>(v[1]) << 16),
-                                                      v[2] | (static_cast<uint32_t>(v[3]) << 16));
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            k_exp[(static_cast<int64_t>(h) * ck + j0 + r + e) * kXDn + d] = v[e];
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int r = 64 * tm + 32 * i + 8 * e4 + 4 * g;  // tile-local token of element 4 e4
+          *reinterpret_cast<uint2*>(vrow + static_cast<int64_t>(d) * ck + vperm(r)) =
+              make_uint2(pack_bf16(val(i, jj, 4 * e4, r), val(i, jj, 4 * e4 + 1, r + 1)),
+                         pack_bf16(val(i, jj, 4 * e4 + 2, r + 2), val(i, jj, 4 * e4 + 3, r + 3)));
         }
       }
+    }
+  } else {
+    // K_exp[h][j][d]: the wave's 64 x 128 tile goes through LDS (token rows)
+    // so that each lane stores 16 contiguous bytes of a row
+    char* kt = smem + tm * (64 * kGKRow);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int rl = 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);  // wave-local token
+          *reinterpret_cast<__bf16*>(kt + rl * kGKRow + (32 * jj + n32) * 2) =
+              static_cast<__bf16>(val(i, jj, e, 64 * tm + rl));
+        }
+    uint16_t* krow = k_exp + (static_cast<int64_t>(h) * ck + j0 + 64 * tm) * kXDn;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int c = lane + 64 * k;  // 16-byte chunk: token c / 16, columns 8 (c % 16) ..
+      const int rl = c >> 4, cc = c & 15;
+      *reinterpret_cast<i32x4*>(krow + rl * kXDn + 8 * cc) =
+          *reinterpret_cast<const i32x4*>(kt + rl * kGKRow + 16 * cc);
     }
   }
   // the rope part of the keys, shared by every head (written once)
@@ -257,7 +341,7 @@ __global__ __launch_bounds__(kGThreads, 1) void kv_expand_kernel(XPassArgs a) {
       uint16_t v = 0;
       if (j < ntok) {
         const int64_t row = cache_row(j);
-        if (!fp8) {
+        if (!kFp8) {
           v = static_cast<const uint16_t*>(kv.data)[row * kv.D + R + c];
         } else {
           const uint8_t code = static_cast<const uint8_t*>(kv.data)[row * kv.D + R + c];
@@ -329,40 +413,43 @@ __global__ __launch_bounds__(256, 2) void attn_expanded_kernel(XPassArgs a) {
     qf[s] = *reinterpret_cast<const i16x8*>(src);
   }
 
-  // tile loads: 5 chunks of 16 B per thread (K_exp 512, kpe 256, V^T 512)
+  // tile loads: 5 chunks of 16 B per thread (K_exp 512, kpe 256, V^T 512);
+  // chunk q of tile `tile` is at src[q] + j0 * stride(q) elements, j0 = 32 tile
   const uint16_t* kexp_h = a.k_exp + (static_cast<int64_t>(bz) * a.H + h) * ck * kXDn;
   const uint16_t* vexp_h = a.v_expT + (static_cast<int64_t>(bz) * a.H + h) * kXDv * ck;
   const uint16_t* kpe_b = a.kpe + static_cast<int64_t>(bz) * ck * kXDr;
+  const uint16_t* src[5];
+  uint32_t dst[5];  // byte offsets in a K / V buffer
+#pragma unroll
+  for (int q = 0; q < 5; ++q) {
+    const int idx = t + 256 * q;
+    if (q < 2) {  // K_exp: key idx / 16, chunk idx % 16
+      src[q] = kexp_h + (idx >> 4) * kXDn + 8 * (idx & 15);
+      dst[q] = (idx >> 4) * kAKPitch + 16 * (idx & 15);
+    } else if (q == 2) {  // kpe: key (idx - 512) / 8, chunk % 8
+      const int k = idx - 512;
+      src[q] = kpe_b + (k >> 3) * kXDr + 8 * (k & 7);
+      dst[q] = (k >> 3) * kAKPitch + kXDn * 2 + 16 * (k & 7);
+    } else {  // V^T: row (idx - 768) / 4, chunk % 4
+      const int k = idx - 768;
+      src[q] = vexp_h + static_cast<int64_t>(k >> 2) * ck + 8 * (k & 3);
+      dst[q] = (k >> 2) * kAVPitch + 16 * (k & 3);
+    }
+  }
   i16x8 ld[5];
   auto load_tile = [&](int tile) {
-    const int j0 = tile * kAT;
+    const int64_t j0 = static_cast<int64_t>(tile) * kAT;
 #pragma unroll
     for (int q = 0; q < 5; ++q) {
-      const int idx = t + 256 * q;
-      if (idx < 512) {  // K_exp: key idx / 16, chunk idx % 16
-        ld[q] = *reinterpret_cast<const i16x8*>(kexp_h + static_cast<int64_t>(j0 + (idx >> 4)) * kXDn + 8 * (idx & 15));
-      } else if (idx < 768) {  // kpe: key (idx - 512) / 8, chunk % 8
-        const int k = idx - 512;
-        ld[q] = *reinterpret_cast<const i16x8*>(kpe_b + static_cast<int64_t>(j0 + (k >> 3)) * kXDr + 8 * (k & 7));
-      } else {  // V^T: row (idx - 768) / 4, chunk % 4
-        const int k = idx - 768;
-        ld[q] = *reinterpret_cast<const i16x8*>(vexp_h + static_cast<int64_t>(k >> 2) * ck + j0 + 8 * (k & 3));
-      }
+      const int64_t stride = q < 2 ? kXDn : (q == 2 ? kXDr : 1);
+      ld[q] = *reinterpret_cast<const i16x8*>(src[q] + j0 * stride);
     }
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int q = 0; q < 5; ++q) {
-      const int idx = t + 256 * q;
-      if (idx < 512) {
-        *reinterpret_cast<i16x8*>(Ks[buf] + (idx >> 4) * kAKPitch + 16 * (idx & 15)) = ld[q];
-      } else if (idx < 768) {
-        const int k = idx - 512;
-        *reinterpret_cast<i16x8*>(Ks[buf] + (k >> 3) * kAKPitch + kXDn * 2 + 16 * (k & 7)) = ld[q];
-      } else {
-        const int k = idx - 768;
-        *reinterpret_cast<i16x8*>(Vs[buf] + (k >> 2) * kAVPitch + 16 * (k & 3)) = ld[q];
-      }
+      char* base = q < 3 ? Ks[buf] : Vs[buf];
+      *reinterpret_cast<i16x8*>(base + dst[q]) = ld[q];
     }
   };
 
@@ -370,7 +457,7 @@ __global__ __launch_bounds__(256, 2) void attn_expanded_kernel(XPassArgs a) {
 #pragma unroll
   for (int db = 0; db < kXDv / 32; ++db) o[db] = f32x16{};
   float m_ref = -INFINITY, l_sum = 0.f;
-  const float c = a.scale_log2;
+  const float c = a.scale_log2;  // > 0 (the host routes other scales to the absorbed form)
 
   // S^T = K Q^T (keys x rows) of the tile in buffer `buf`
   auto scores = [&](int buf) {
@@ -380,6 +467,11 @@ __global__ __launch_bounds__(256, 2) void attn_expanded_kernel(XPassArgs a) {
     for (int st = 0; st < kXDq / 16; ++st) sc = mfma(*reinterpret_cast<const i16x8*>(kb + 32 * st), qf[st], sc);
     return sc;
   };
+  // the keys of this lane's row inside [k0, k0 + ntok): key <= pos, and with a
+  // window key > pos - window; as tile-relative bounds lo <= key - tile_key < hi
+  const int64_t vis_hi = row_ok ? min(pos + 1, k0 + ntok) : k0;
+  const int64_t vis_lo = a.window > 0 ? pos - a.window + 1 : INT64_MIN / 2;
+  auto clamp32 = [](int64_t x) { return static_cast<int>(min(max(x, int64_t{0}), int64_t{kAT})); };
 
   // Software pipeline over three LDS buffers (tile t in buffer t mod 3): the
   // scores of tile t + 1 are issued on the matrix cores before the softmax of
@@ -394,32 +486,29 @@ __global__ __launch_bounds__(256, 2) void attn_expanded_kernel(XPassArgs a) {
   }
   __syncthreads();
   f32x16 s_cur = tile_lo < tile_hi ? scores(0) : f32x16{};
+  int cur = 0, nxt = 1, far = 2;
   for (int tile = tile_lo; tile < tile_hi; ++tile) {
-    const int i = tile - tile_lo;
-    const int cur = i % 3, nxt = (i + 1) % 3, far = (i + 2) % 3;
     const bool has_next = tile + 1 < tile_hi, has_far = tile + 2 < tile_hi;
     if (has_far) load_tile(tile + 2);  // in flight during this tile's math
     f32x16 s_next = f32x16{};
     if (has_next) s_next = scores(nxt);
     f32x16 s = s_cur;
-    // scale, mask, tile maximum (a row's 32 keys sit in lanes n32 and n32 + 32)
+    // mask (tiles the lane's row does not wholly see), tile maximum of the
+    // raw scores (a row's 32 keys sit in lanes n32 and n32 + 32; the scale
+    // is positive, so it is applied to the maximum)
     const int64_t tile_key = k0 + static_cast<int64_t>(tile) * kAT;
-    const bool full = row_ok && tile_key + kAT - 1 <= P + r_lo + 32 * wave &&  // every row of the wave sees the whole tile
-                      tile_key + kAT <= k0 + ntok &&
-                      (a.window <= 0 || tile_key > P + r_lo + 32 * wave + 31 - a.window);
-    float mx = -INFINITY;
+    const int lo = clamp32(vis_lo - tile_key), hi = clamp32(vis_hi - tile_key);
+    if (__ballot(lo != 0 || hi != kAT) != 0) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float x = s[e] * c;
-      if (!full) {
-        const int64_t key = tile_key + 8 * (e >> 2) + 4 * g + (e & 3);
-        const bool vis = row_ok && key <= pos && key < k0 + ntok && (a.window <= 0 || key > pos - a.window);
-        x = vis ? x : -INFINITY;
+      for (int e = 0; e < 16; ++e) {
+        const int off = 8 * (e >> 2) + 4 * g + (e & 3);
+        s[e] = (off >= lo && off < hi) ? s[e] : -INFINITY;
       }
-      s[e] = x;
-      mx = fmaxf(mx, x);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+    for (int e = 3; e < 16; ++e) mx = fmaxf(mx, s[e]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
     // move the reference when this tile's maximum passes it by the slack
     // (always on a row's first visible tile: the reference starts at -inf)
     const bool move = mx > m_ref + kRescaleSlack;
@@ -434,16 +523,19 @@ __global__ __launch_bounds__(256, 2) void attn_expanded_kernel(XPassArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
     }
-    // p = 2^(s - m_ref) <= 2^8 (v_exp_f32; masked keys give exp2(-inf) = 0),
-    // rounded to bf16 by the hardware conversion (nearest even)
-    bf16x8 pb[2];
+    // p = 2^(s c - m_ref) <= 2^8 (v_exp_f32; masked keys give exp2(-inf) = 0),
+    // rounded to bf16 pairs by the hardware conversion (nearest even)
     const float m_use = m_ref == -INFINITY ? 0.f : m_ref;  // a row with nothing visible yet
+    uint32_t pk[8];
+    float psum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float p = __builtin_amdgcn_exp2f(s[e] - m_use);
-      l_sum += p;
-      pb[e >> 3][e & 7] = static_cast<__bf16>(p);
+    for (int e = 0; e < 16; e += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[e], c, -m_use));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[e + 1], c, -m_use));
+      psum += p0 + p1;
+      pk[e >> 1] = pack_bf16(p0, p1);
     }
+    l_sum += psum;
     // O^T += V^T P^T; MFMA k-slot 8 g + j of key half kk is key 16 kk + 4 g + j
     // (j < 4) or 16 kk + 8 + 4 g + (j - 4): the keys this lane's P registers
     // hold, which the quad-swapped V^T columns 16 kk + 8 g .. + 7 hold in order
@@ -451,15 +543,22 @@ __global__ __launch_bounds__(256, 2) void attn_expanded_kernel(XPassArgs a) {
 #pragma unroll
     for (int db = 0; db < kXDv / 32; ++db) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+      for (int kk = 0; kk < 2; ++kk) {
+        const i32x4 pv = {static_cast<int>(pk[4 * kk]), static_cast<int>(pk[4 * kk + 1]),
+                          static_cast<int>(pk[4 * kk + 2]), static_cast<int>(pk[4 * kk + 3])};
         o[db] = mfma(*reinterpret_cast<const i16x8*>(vb + 32 * db * kAVPitch + 32 * kk),
-                     __builtin_bit_cast(i16x8, pb[kk]), o[db]);
+                     __builtin_bit_cast(i16x8, pv), o[db]);
+      }
     }
     // buffer `far` last held tile t - 1, whose values were read before the
     // barrier that ended the previous step
     if (has_far) store_tile(far);
     __syncthreads();
     s_cur = s_next;
+    const int tmp = cur;
+    cur = nxt;
+    nxt = far;
+    far = tmp;
   }
 
   // merge with the previous passes and store
@@ -521,7 +620,11 @@ bool prefill_expanded_supported(const CacheView& kv, int32_t H, int32_t Dn, int3
 }
 
 hipError_t launch_prefill_expanded_pass(const XPassArgs& a, int32_t max_q_len, hipStream_t s) {
-  hipLaunchKernelGGL(kv_expand_kernel, dim3(a.ck / kGTok, a.H, a.batch), dim3(kGThreads), 0, s, a);
+  const dim3 grid(a.ck / kGTok, a.H, a.batch);
+  if (a.kv.dtype == kKvFp8)
+    hipLaunchKernelGGL(kv_expand_kernel<true>, grid, dim3(kGThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(kv_expand_kernel<false>, grid, dim3(kGThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_expanded_kernel, dim3((max_q_len + 127) / 128, a.H, a.batch), dim3(256), 0, s, a);
