@@ -2,9 +2,12 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3]
 
-A step is one decode step of the whole hot path for a batch: mla_write_kv of
-the batch's newest tokens (write-then-attend) followed by mla_decode (absorb,
-device-side split plan, split-KV attention, combine, up-projection).  Inputs
+A step is one decode step of the whole hot path for a batch: one
+mla_decode_write call, which writes the batch's newest tokens into the cache
+(write-then-attend; extra workgroups of the absorb launch do it) and then
+decodes (absorb, device-side split plan, split-KV attention, combine,
+up-projection).  The index-list workload keeps mla_write_kv followed by
+mla_sparse_attention.  Inputs
 are seeded synthetic data with the V3 shape (128 heads, kv_lora_rank 512 +
 qk_rope 64, page size 64, batch 64, contexts uniform in [1024, 32768],
 shuffled block tables), resident in HBM before the timed region.
@@ -525,15 +528,15 @@ def main():
         b.record()
 
     def step(ev=None):
-        mla.write_kv(cache, case.layer, new_c, new_r, new_slots)
         if sparse:
+            mla.write_kv(cache, case.layer, new_c, new_r, new_slots)
             mla.sparse_attention(cache, case.layer, q_nope, q_pe, lists, bt, ctx, scale=case.scale,
                                  w_uk=w_uk, w_uv=w_uv, window=case.window, out=out, lse=lse,
                                  workspace=ws, flags=flags, kernel_events=ev)
         else:
             mla.decode(cache, case.layer, q_nope, q_pe, bt, ctx, scale=case.scale, w_uk=w_uk,
                        w_uv=w_uv, window=case.window, out=out, lse=lse, workspace=ws, flags=flags,
-                       kernel_events=ev)
+                       kernel_events=ev, new_tokens=(new_c, new_r, new_slots))
 
     protocol = None
     if args.protocol_steps > 0:
@@ -616,8 +619,8 @@ def main():
             "v_head": d.Dv, "page_size": d.page_size,
             "context_lens": f"{int(case.context_lens.min())}..{int(case.context_lens.max())}",
             "attended_tokens": tokens, "kv_cache": case.kv_dtype,
-            "step": "mla_write_kv(batch newest tokens) + "
-                    + ("mla_sparse_attention" if sparse else "mla_decode"),
+            "step": ("mla_write_kv(batch newest tokens) + mla_sparse_attention" if sparse
+                     else "mla_decode_write(batch newest tokens written, then the decode)"),
             "kernels": "generic" if args.generic else "default",
         },
         "step_hbm_gbs": (kv_bytes + fixed_bytes) / step_s / 1e9,

@@ -234,6 +234,32 @@ mla_status mla_decode(const mla_cache* cache, int32_t layer_idx, const mla_attn*
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_decode_write - mla_write_kv of the step's new tokens followed by
+ * mla_decode, as one call ([SHIM] "Root causes" item 2: a decode step writes
+ * its tokens before attending over them).  The write arguments are
+ * mla_write_kv's (c_kv, c_kv_row_stride, k_pe, k_pe_row_stride,
+ * slot_mapping, num_tokens: same meaning, layout, checks and errors), the
+ * rest are mla_decode's; the results (cache contents, out, lse) are those of
+ * the two calls in order on the same stream.  When the decode runs the
+ * matrix-core absorb (w_uk given, the MFMA shapes), the tokens are written by
+ * extra workgroups of that first launch, beside the absorb and the split
+ * plan, which saves the write's own launch; otherwise a write launch runs
+ * first.  Workspace: mla_decode_workspace_size.  A call whose arguments are
+ * invalid enqueues nothing (neither the write nor the decode).  batch 0 writes
+ * only.
+ */
+mla_status mla_decode_write(const mla_cache* cache, int32_t layer_idx, const mla_attn* attn,
+                            const void* c_kv, int64_t c_kv_row_stride,
+                            const void* k_pe, int64_t k_pe_row_stride,
+                            const int64_t* slot_mapping, int32_t num_tokens,
+                            const void* q_nope, int64_t q_nope_stride_b, int64_t q_nope_stride_h,
+                            const void* q_pe, int64_t q_pe_stride_b, int64_t q_pe_stride_h,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t batch,
+                            void* out, float* lse_or_null,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * mla_decode_noalloc - mla_decode without a caller workspace, for callers that
  * cannot allocate device memory (code under graph capture, tight serving
  * loops, harnesses that forbid allocation).  Same arguments, results and

@@ -25,6 +25,7 @@
 #include "device_utils.h"
 #include "mla_internal.h"
 #include "plan_device.h"
+#include "write_device.h"
 
 namespace mla {
 namespace {
@@ -50,19 +51,25 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const uint16_t* __rest
                                                           const uint16_t* __restrict__ w_uk,
                                                           int32_t Nq, int32_t H, int32_t Dn,
                                                           int32_t R, uint16_t* __restrict__ q_lat,
-                                                          PlanArgs pa) {
+                                                          PlanArgs pa, TokenWrite tw) {
   __shared__ __attribute__((aligned(16))) char wt[kAbsMaxDn * kAbsPitch];
   __shared__ __attribute__((aligned(16))) char qs[32 * MT * kAbsQPitch];
   static_assert((256 + 1 + 2 * kPlanLds) * 4 <= kAbsMaxDn * kAbsPitch, "plan LDS fits the staging buffer");
   if (blockIdx.x * kAbsCols >= R) {
-    // the extra column of workgroups: one computes the split plan, in the
-    // staging buffer's LDS (pa.plan.G == 0: no plan asked for)
-    if (blockIdx.y == 0 && blockIdx.z == 0 && pa.plan.G > 0) {
+    // the extra columns of workgroups: the first computes the split plan, in
+    // the staging buffer's LDS (pa.plan.G == 0: no plan asked for); the next
+    // write the new tokens, one wavefront per token (tw.T == 0: none)
+    const int planned = pa.plan.G > 0 ? 1 : 0;
+    const int id = (blockIdx.x - R / kAbsCols) * gridDim.y * gridDim.z + blockIdx.y + gridDim.y * blockIdx.z;
+    if (id < planned) {
       int32_t* l = reinterpret_cast<int32_t*>(wt);
       plan_items_body<256>(l, l + 256, l + 257, l + 257 + kPlanLds, pa.mode, pa.batch, pa.num_items,
                            pa.context_lens, pa.query_start_loc, pa.window, pa.max_ctx,
                            pa.plan.item_b, pa.plan.item_lo, pa.plan.item_hi, pa.plan.tile_start,
                            pa.plan.G, pa.plan.wg_tile, pa.plan.wg_item, pa.plan.item_wg);
+    } else {
+      const int64_t tok = static_cast<int64_t>(id - planned) * 4 + (threadIdx.x >> 6);
+      if (tok < tw.T) write_token(tw, tok, threadIdx.x & 63);
     }
     return;
   }
@@ -477,19 +484,24 @@ hipError_t launch_combine_up_project(const AttnArgs& a, const uint16_t* w_uv, in
 
 hipError_t launch_absorb_mfma(const uint16_t* q_nope, int64_t st, int64_t sh, const uint16_t* w_uk,
                               int32_t num_items, int32_t H, int32_t Dn, int32_t R, uint16_t* q_lat,
-                              const PlanArgs* plan, hipStream_t s) {
+                              const PlanArgs* plan, const TokenWrite* write, hipStream_t s) {
   PlanArgs pa{};
   if (plan) pa = *plan;  // else pa.plan.G == 0: no plan
+  TokenWrite tw{};
+  if (write) tw = *write;  // else tw.T == 0: nothing to write
   const int mt = pick_mt(num_items);
   // the W_UK block (Dn x 128 columns) is staged once per workgroup: at most
   // ~2048 workgroups in all, so large item counts loop over several blocks
   const int nblk = (num_items + 32 * mt - 1) / (32 * mt);
   const int gz = std::max(1, std::min(nblk, std::max(1, 2048 / std::max(1, (R / kAbsCols) * H))));
-  const dim3 grid(R / kAbsCols + (plan ? 1 : 0), H, gz);
+  // extra columns: the plan's workgroup, then one per four new tokens
+  const int64_t extra = (plan ? 1 : 0) + (static_cast<int64_t>(tw.T) + 3) / 4;
+  const int64_t per_col = static_cast<int64_t>(H) * gz;
+  const dim3 grid(R / kAbsCols + static_cast<int>((extra + per_col - 1) / per_col), H, gz);
   switch (mt) {
-    case 1: hipLaunchKernelGGL(absorb_mfma_kernel<1>, grid, dim3(256), 0, s, q_nope, st, sh, w_uk, num_items, H, Dn, R, q_lat, pa); break;
-    case 2: hipLaunchKernelGGL(absorb_mfma_kernel<2>, grid, dim3(256), 0, s, q_nope, st, sh, w_uk, num_items, H, Dn, R, q_lat, pa); break;
-    default: hipLaunchKernelGGL(absorb_mfma_kernel<4>, grid, dim3(256), 0, s, q_nope, st, sh, w_uk, num_items, H, Dn, R, q_lat, pa); break;
+    case 1: hipLaunchKernelGGL(absorb_mfma_kernel<1>, grid, dim3(256), 0, s, q_nope, st, sh, w_uk, num_items, H, Dn, R, q_lat, pa, tw); break;
+    case 2: hipLaunchKernelGGL(absorb_mfma_kernel<2>, grid, dim3(256), 0, s, q_nope, st, sh, w_uk, num_items, H, Dn, R, q_lat, pa, tw); break;
+    default: hipLaunchKernelGGL(absorb_mfma_kernel<4>, grid, dim3(256), 0, s, q_nope, st, sh, w_uk, num_items, H, Dn, R, q_lat, pa, tw); break;
   }
   return hipGetLastError();
 }

@@ -368,7 +368,7 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
                          const int32_t* block_tables, int32_t max_blocks,
                          const int32_t* context_lens, int32_t batch, int32_t max_q_len,
                          void* out, float* lse_or_null, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+                         void* stream, const mla::TokenWrite* tw = nullptr) {
   mla_status st = check_cache(cache);
   if (st != MLA_OK) return st;
   if ((st = check_attn(attn)) != MLA_OK) return st;
@@ -429,13 +429,20 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
                          static_cast<int32_t>(max_ctx64), plan};
   bool planned = false;  // the MFMA absorb launch computes the plan too
 
+  const bool absorb_mfma = attn->w_uk && !generic && mla::absorb_mfma_supported(attn->qk_nope_dim, R) &&
+                           aligned16(q_nope) && aligned16(attn->w_uk) && qn_st % 8 == 0 && qn_sh % 8 == 0;
+  if (tw && tw->T > 0 && !absorb_mfma) {
+    // new tokens to write, and no absorb launch to carry them: a write launch first
+    e = mla::launch_write_kv(tw->cache, tw->scale, tw->dtype, tw->num_slots, tw->R, tw->Dr, tw->c_kv,
+                             tw->c_stride, tw->k_pe, tw->k_stride, tw->slots, tw->T, s);
+    if (e != hipSuccess) return MLA_ERR_HIP;
+  }
   if (attn->w_uk) {
     uint16_t* ql = at<uint16_t>(workspace, L.q_lat);
-    const bool mfma = !generic && mla::absorb_mfma_supported(attn->qk_nope_dim, R) &&
-                      aligned16(q_nope) && aligned16(attn->w_uk) && qn_st % 8 == 0 && qn_sh % 8 == 0;
+    const bool mfma = absorb_mfma;
     e = mfma ? mla::launch_absorb_mfma(static_cast<const uint16_t*>(q_nope), qn_st, qn_sh,
                                        static_cast<const uint16_t*>(attn->w_uk), num_items, H,
-                                       attn->qk_nope_dim, R, ql, &pa, s)
+                                       attn->qk_nope_dim, R, ql, &pa, tw, s)
              : mla::launch_absorb(static_cast<const uint16_t*>(q_nope), qn_st, qn_sh,
                                   static_cast<const uint16_t*>(attn->w_uk), num_items, H,
                                   attn->qk_nope_dim, R, ql, s);
@@ -619,31 +626,45 @@ const char* mla_status_string(mla_status status) {
 
 const char* mla_version(void) { return "paged-mla-gfx950 0.1"; }
 
-mla_status mla_write_kv(const mla_cache* cache, int32_t layer_idx, const void* c_kv,
-                        int64_t c_kv_row_stride, const void* k_pe, int64_t k_pe_row_stride,
-                        const int64_t* slot_mapping, int32_t num_tokens, void* stream) {
+// mla_write_kv's argument checks (and, with MLA_DEBUG_CHECK, its slot check);
+// on success *w describes the write (w->T == 0: nothing to write).
+static mla_status prepare_write(const mla_cache* cache, int32_t layer_idx, const void* c_kv, int64_t c_kv_row_stride,
+                         const void* k_pe, int64_t k_pe_row_stride, const int64_t* slot_mapping,
+                         int32_t num_tokens, hipStream_t s, mla::TokenWrite* w) {
   mla_status st = check_cache(cache);
   if (st != MLA_OK) return st;
   if (layer_idx < 0 || layer_idx >= cache->num_layers || num_tokens < 0)
     return MLA_ERR_INVALID_ARGUMENT;
+  memset(w, 0, sizeof(*w));
   if (num_tokens == 0) return MLA_OK;
   if (!c_kv || !slot_mapping || (cache->qk_rope_dim > 0 && !k_pe)) return MLA_ERR_INVALID_ARGUMENT;
   if (c_kv_row_stride < cache->kv_lora_rank || k_pe_row_stride < cache->qk_rope_dim)
     return MLA_ERR_INVALID_ARGUMENT;
   if (debug_check_enabled()) {
-    st = debug_check_slots(cache, slot_mapping, num_tokens, static_cast<hipStream_t>(stream));
+    st = debug_check_slots(cache, slot_mapping, num_tokens, s);
     if (st != MLA_OK) return st;
   }
   const int64_t slots = static_cast<int64_t>(cache->num_pages) * cache->page_size;
   const int64_t D = cache->kv_lora_rank + cache->qk_rope_dim;
   void* layer = static_cast<char*>(cache->data) + layer_idx * slots * D * elem_bytes(cache->dtype);
   float* scale = cache->dtype == MLA_KV_FP8_E4M3 ? cache->scale + layer_idx * slots : nullptr;
-  const hipError_t e = mla::launch_write_kv(
-      layer, scale, cache->dtype == MLA_KV_BF16 ? mla::kKvBf16 : mla::kKvFp8, slots,
-      cache->kv_lora_rank, cache->qk_rope_dim, static_cast<const uint16_t*>(c_kv), c_kv_row_stride,
-      static_cast<const uint16_t*>(k_pe), k_pe_row_stride, slot_mapping, num_tokens,
-      static_cast<hipStream_t>(stream));
-  return to_status(e);
+  *w = mla::make_token_write(layer, scale, cache->dtype == MLA_KV_BF16 ? mla::kKvBf16 : mla::kKvFp8, slots,
+                             cache->kv_lora_rank, cache->qk_rope_dim, static_cast<const uint16_t*>(c_kv),
+                             c_kv_row_stride, static_cast<const uint16_t*>(k_pe), k_pe_row_stride,
+                             slot_mapping, num_tokens);
+  return MLA_OK;
+}
+
+mla_status mla_write_kv(const mla_cache* cache, int32_t layer_idx, const void* c_kv,
+                        int64_t c_kv_row_stride, const void* k_pe, int64_t k_pe_row_stride,
+                        const int64_t* slot_mapping, int32_t num_tokens, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  mla::TokenWrite w;
+  const mla_status st =
+      prepare_write(cache, layer_idx, c_kv, c_kv_row_stride, k_pe, k_pe_row_stride, slot_mapping, num_tokens, s, &w);
+  if (st != MLA_OK || w.T == 0) return st;
+  return to_status(mla::launch_write_kv(w.cache, w.scale, w.dtype, w.num_slots, w.R, w.Dr, w.c_kv, w.c_stride,
+                                        w.k_pe, w.k_stride, w.slots, w.T, s));
 }
 
 mla_status mla_write_kv_fused(const mla_cache* cache, int32_t layer_idx, const void* c_kv,
@@ -812,6 +833,31 @@ mla_status mla_decode(const mla_cache* cache, int32_t layer_idx, const mla_attn*
                        q_nope_stride_h, q_pe, q_pe_stride_b, q_pe_stride_h, nullptr, batch,
                        block_tables, max_blocks_per_seq, context_lens, batch, 1, out, lse_or_null,
                        workspace, workspace_bytes, stream);
+}
+
+mla_status mla_decode_write(const mla_cache* cache, int32_t layer_idx, const mla_attn* attn,
+                            const void* c_kv, int64_t c_kv_row_stride, const void* k_pe,
+                            int64_t k_pe_row_stride, const int64_t* slot_mapping, int32_t num_tokens,
+                            const void* q_nope, int64_t q_nope_stride_b, int64_t q_nope_stride_h,
+                            const void* q_pe, int64_t q_pe_stride_b, int64_t q_pe_stride_h,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t batch, void* out, float* lse_or_null,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  mla::TokenWrite w;
+  mla_status st =
+      prepare_write(cache, layer_idx, c_kv, c_kv_row_stride, k_pe, k_pe_row_stride, slot_mapping, num_tokens, s, &w);
+  if (st != MLA_OK) return st;
+  if (batch < 0) return MLA_ERR_INVALID_ARGUMENT;
+  if ((st = check_attn(attn)) != MLA_OK) return st;
+  // nothing to decode: the write alone
+  if (batch == 0 && w.T > 0)
+    return to_status(mla::launch_write_kv(w.cache, w.scale, w.dtype, w.num_slots, w.R, w.Dr, w.c_kv, w.c_stride,
+                                          w.k_pe, w.k_stride, w.slots, w.T, s));
+  return run_attention(mla::kPlanDecode, cache, layer_idx, attn, q_nope, q_nope_stride_b,
+                       q_nope_stride_h, q_pe, q_pe_stride_b, q_pe_stride_h, nullptr, batch,
+                       block_tables, max_blocks_per_seq, context_lens, batch, 1, out, lse_or_null,
+                       workspace, workspace_bytes, stream, &w);
 }
 
 mla_status mla_prefill_chunk(const mla_cache* cache, int32_t layer_idx, const mla_attn* attn,

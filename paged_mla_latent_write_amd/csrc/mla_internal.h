@@ -196,14 +196,34 @@ hipError_t launch_up_project(const float* o_lat, const float* o_scale, const uin
 hipError_t launch_latent_out(const float* o_lat, const float* o_scale, int32_t num_items, int32_t H,
                              int32_t R, uint16_t* out, hipStream_t s);
 
+// New tokens of one layer for mla_write_kv's per-token write (write_device.h).
+struct TokenWrite {
+  void* cache;          // the layer's rows [num_slots][R + Dr] (bf16 or E4M3 codes)
+  float* scale;         // the layer's fp32 scales [num_slots] (fp8), else null
+  int64_t num_slots;
+  const uint16_t* c_kv;
+  int64_t c_stride;
+  const uint16_t* k_pe;
+  int64_t k_stride;
+  const int64_t* slots;
+  int32_t dtype;        // kKvBf16 / kKvFp8
+  int32_t R, Dr;
+  int32_t T;            // tokens (0: nothing to write)
+  int32_t vec;          // bf16: 16-byte copies (R, Dr, strides multiples of 8, rows 16-byte aligned)
+};
+TokenWrite make_token_write(void* cache_layer, float* scale_layer, int32_t dtype, int64_t num_slots, int32_t R,
+                            int32_t Dr, const uint16_t* c_kv, int64_t c_stride, const uint16_t* k_pe,
+                            int64_t k_stride, const int64_t* slots, int32_t num_tokens);
+
 // Matrix-core versions of the two per-head projections (head_gemm.hip).
 bool absorb_mfma_supported(int32_t Dn, int32_t R);
 bool up_project_mfma_supported(int32_t R, int32_t Dv);
 // With `plan` non-null the same launch also computes the split plan, in one
-// extra workgroup.
+// extra workgroup; with `write` non-null (and write->T > 0) further extra
+// workgroups write those tokens into the cache, one wavefront per token.
 hipError_t launch_absorb_mfma(const uint16_t* q_nope, int64_t st, int64_t sh, const uint16_t* w_uk,
                               int32_t num_items, int32_t H, int32_t Dn, int32_t R, uint16_t* q_lat,
-                              const PlanArgs* plan, hipStream_t s);
+                              const PlanArgs* plan, const TokenWrite* write, hipStream_t s);
 hipError_t launch_up_project_mfma(const float* o_lat, const float* o_scale, const uint16_t* w_uv,
                                   int32_t num_items, int32_t H, int32_t R, int32_t Dv, uint16_t* out,
                                   hipStream_t s);

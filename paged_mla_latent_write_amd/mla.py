@@ -37,7 +37,8 @@ MLA_FLAG_GENERIC_KERNELS = 1
 MLA_FLAG_PREFILL_ABSORBED = 2
 MLA_FLAG_PREFILL_EXPANDED = 4
 
-EXPORTED = ("mla_write_kv", "mla_write_kv_fused", "mla_decode_workspace_size", "mla_decode", "mla_decode_noalloc",
+EXPORTED = ("mla_write_kv", "mla_write_kv_fused", "mla_decode_workspace_size", "mla_decode", "mla_decode_write",
+            "mla_decode_noalloc",
             "mla_decode_combine", "mla_prefill_workspace_size", "mla_prefill_chunk",
             "mla_sparse_workspace_size", "mla_sparse_attention",
             "mla_status_string", "mla_version")
@@ -86,6 +87,8 @@ _write_kv_fused = _sig("mla_write_kv_fused", _I32, _CP, _I32, _P, _I64, _P, _I64
 _decode_ws = _sig("mla_decode_workspace_size", _SZ, _CP, _AP, _I32, _I32)
 _decode = _sig("mla_decode", _I32, _CP, _I32, _AP, _P, _I64, _I64, _P, _I64, _I64, _P, _I32, _P,
                _I32, _P, _P, _P, _SZ, _P)
+_decode_write = _sig("mla_decode_write", _I32, _CP, _I32, _AP, _P, _I64, _P, _I64, _P, _I32, _P, _I64, _I64,
+                     _P, _I64, _I64, _P, _I32, _P, _I32, _P, _P, _P, _SZ, _P)
 _decode_noalloc = _sig("mla_decode_noalloc", _I32, _CP, _I32, _AP, _P, _I64, _I64, _P, _I64, _I64, _P,
                       _I32, _P, _I32, _P, _P, _P)
 _combine = _sig("mla_decode_combine", _I32, _P, _P, _I32, _I32, _I32, _I32, _P, _P, _P)
@@ -258,10 +261,8 @@ def _check_outputs(out, lse, shape):
               f"lse must be contiguous fp32 {shape[:2]}")
 
 
-def write_kv(cache: KVCache, layer_idx: int, c_kv: torch.Tensor, k_pe: torch.Tensor,
-             slot_mapping: torch.Tensor, stream=None):
-    """Scatter rows [c_kv | k_pe] (bf16 [T, R], [T, Dr], unit inner stride)
-    into layer `layer_idx` at slot_mapping (int64 [T]; negative = pad row)."""
+def _check_write(cache, c_kv, k_pe, slot_mapping):
+    """mla_write_kv's host-known argument checks; returns the token count."""
     _need(c_kv.dtype == torch.bfloat16 and k_pe.dtype == torch.bfloat16, "c_kv and k_pe must be bf16")
     _need(slot_mapping.dtype == torch.int64 and slot_mapping.dim() == 1, "slot_mapping: int64 [T]")
     _need(c_kv.dim() == 2 and c_kv.shape[1] == cache.kv_lora_rank and c_kv.stride(-1) == 1,
@@ -272,6 +273,14 @@ def write_kv(cache: KVCache, layer_idx: int, c_kv: torch.Tensor, k_pe: torch.Ten
     _need(k_pe.shape[0] == T and slot_mapping.numel() == T and slot_mapping.is_contiguous(),
           "c_kv, k_pe and slot_mapping must have the same number of tokens")
     _same_device(cache.data, c_kv, k_pe, slot_mapping)
+    return T
+
+
+def write_kv(cache: KVCache, layer_idx: int, c_kv: torch.Tensor, k_pe: torch.Tensor,
+             slot_mapping: torch.Tensor, stream=None):
+    """Scatter rows [c_kv | k_pe] (bf16 [T, R], [T, Dr], unit inner stride)
+    into layer `layer_idx` at slot_mapping (int64 [T]; negative = pad row)."""
+    T = _check_write(cache, c_kv, k_pe, slot_mapping)
     st = cache.struct()
     _check(_write_kv(ctypes.byref(st), layer_idx, _ptr(c_kv), c_kv.stride(0), _ptr(k_pe),
                      k_pe.stride(0), _ptr(slot_mapping), T, _stream(stream)), "mla_write_kv")
@@ -337,15 +346,20 @@ class Workspace:
 
 def decode(cache: KVCache, layer_idx: int, q_nope, q_pe, block_tables, context_lens, *, scale,
            w_uk=None, w_uv=None, window=0, out=None, lse=None, want_lse=True, workspace=None,
-           num_workgroups=0, flags=0, kernel_events=None, stream=None):
+           num_workgroups=0, flags=0, kernel_events=None, stream=None, new_tokens=None):
     """Absorbed split-KV decode.  q_nope bf16 [B, H, Dn] (or [B, H, R] latent when
     w_uk is None), q_pe bf16 [B, H, Dr]; block_tables int32 [B, max_blocks];
-    context_lens int32 [B].  Returns (out bf16 [B, H, Dv or R], lse fp32 [B, H])."""
+    context_lens int32 [B].  Returns (out bf16 [B, H, Dv or R], lse fp32 [B, H]).
+    new_tokens = (c_kv, k_pe, slot_mapping), as write_kv's arguments: the
+    step's tokens are written first, in the same call (mla_decode_write)."""
     B, H = int(q_nope.shape[0]), int(q_nope.shape[1])
     dn, dv = _check_heads(cache, q_nope, q_pe, w_uk, w_uv)
     _check_tables(block_tables, context_lens, B)
     _check_outputs(out, lse, (B, H, dv))
     _same_device(cache.data, q_nope, q_pe, w_uk, w_uv, block_tables, context_lens, out, lse)
+    if new_tokens is not None:
+        c_kv, k_pe, slots = new_tokens
+        T = _check_write(cache, c_kv, k_pe, slots)
     attn = _attn_struct(H, dn, dv, w_uk, w_uv, scale, window, num_workgroups, flags, kernel_events)
     st = cache.struct()
     max_blocks = int(block_tables.shape[1])
@@ -368,6 +382,12 @@ def decode(cache: KVCache, layer_idx: int, q_nope, q_pe, block_tables, context_l
     _keep_alive_on(stream, *fresh)
     qs_b, qs_h = _row_strides(q_nope)
     ps_b, ps_h = _row_strides(q_pe)
+    if new_tokens is not None:
+        _check(_decode_write(ctypes.byref(st), layer_idx, ctypes.byref(attn), _ptr(c_kv), c_kv.stride(0),
+                             _ptr(k_pe), k_pe.stride(0), _ptr(slots), T, _ptr(q_nope), qs_b, qs_h,
+                             _ptr(q_pe), ps_b, ps_h, _ptr(block_tables), max_blocks, _ptr(context_lens), B,
+                             _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)), "mla_decode_write")
+        return out, lse
     _check(_decode(ctypes.byref(st), layer_idx, ctypes.byref(attn), _ptr(q_nope), qs_b, qs_h,
                    _ptr(q_pe), ps_b, ps_h, _ptr(block_tables), max_blocks, _ptr(context_lens), B,
                    _ptr(out), _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)), "mla_decode")

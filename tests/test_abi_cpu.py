@@ -120,6 +120,23 @@ def test_argument_validation_without_device():
                         P(1), None, P(0x10000), 1 << 30, None) == mla.MLA_ERR_INVALID_ARGUMENT
     assert mla._prefill(byref(c), 0, byref(a), P(1), 1, 1, P(1), 1, 1, P(1), -1, 5, P(1), 4, P(1), 2,
                         P(1), None, P(0x10000), 1 << 30, None) == mla.MLA_ERR_INVALID_ARGUMENT
+    # decode_write: the write's errors, then the decode's, all before any launch
+    def dw(batch=4, T=4, ws=None, ws_bytes=0, c_kv=P(1), c_stride=512, attn=a, layer=0):
+        return mla._decode_write(byref(c), layer, byref(attn), c_kv, c_stride, P(1), 64, P(1), T, P(1),
+                                 128 * 16, 128, P(1), 64 * 16, 64, P(1), 4, P(1), batch, P(1), None, ws,
+                                 ws_bytes, None)
+
+    assert dw(c_kv=None) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert dw(c_stride=100) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert dw(layer=2) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert dw(T=-1) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert dw(batch=-1) == mla.MLA_ERR_INVALID_ARGUMENT
+    assert dw(batch=0, T=0) == mla.MLA_OK
+    assert dw(batch=0, attn=_attn(mla, num_heads=0)) == mla.MLA_ERR_INVALID_ARGUMENT
+    # valid tokens, no workspace for the decode: neither runs
+    assert dw(ws=None) == mla.MLA_ERR_WORKSPACE
+    assert dw(ws=P(0x10000), ws_bytes=need - 1) == mla.MLA_ERR_WORKSPACE
+    assert dw(T=0, ws=None) == mla.MLA_ERR_WORKSPACE
     # combine
     assert mla._combine(P(1), P(1), 2, 0, 4, 8, P(1), P(1), None) == mla.MLA_OK
     assert mla._combine(None, P(1), 2, 1, 4, 8, P(1), P(1), None) == mla.MLA_ERR_INVALID_ARGUMENT
@@ -202,3 +219,5 @@ def test_binding_rejects_mismatched_shapes():
                     (torch.zeros(3, R, **bf), torch.zeros(3, Dr, **bf), slots.to(torch.int32))):
         with pytest.raises(ValueError):
             mla.write_kv(cache, 0, c, r, s)
+        with pytest.raises(ValueError):
+            dec(new_tokens=(c, r, s))
