@@ -63,6 +63,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP8_MFMA_PEAK_TFLOPS = 5000.0
 METRIC = "paged MLA decode attended-KV-tokens/s + HBM GB/s % peak, V3 shape bf16"
 
 
@@ -78,6 +79,9 @@ def parse():
     p.add_argument("--event-every", type=int, default=4,
                    help="time the attention kernel with HIP events on every n-th timed step")
     p.add_argument("--generic", action="store_true", help="force the plain (non-MFMA) kernels")
+    p.add_argument("--fp8-mfma", action="store_true",
+                   help="fp8 caches: queries and probabilities in E4M3 on the fp8 matrix cores "
+                        "(approximate; MLA_FLAG_FP8_MFMA)")
     p.add_argument("--protocol-steps", type=int, default=300,
                    help="steps of the per-step protocol (512 MB cache-evicting write between steps, "
                         "median/min from HIP events), run before the timed loop; 0 skips it")
@@ -515,6 +519,8 @@ def main():
     lse = torch.empty((B, d.H), dtype=torch.float32, device=dev)
     ws = mla.Workspace()
     flags = mla.MLA_FLAG_GENERIC_KERNELS if args.generic else 0
+    if args.fp8_mfma and fp8:
+        flags |= mla.MLA_FLAG_FP8_MFMA
     K = args.steps
     # The attention kernel is timed by a pair of HIP events on every
     # args.event_every-th timed step: each recorded pair leaves ~12 us of idle
@@ -582,11 +588,14 @@ def main():
     traffic_bytes = None if (args.generic or fp8) else measured_traffic(args.workload)
     traffic = None if traffic_bytes is None else traffic_bytes / (kern_ms * 1e-3) / 1e9
     tflops = flops / (kern_ms * 1e-3) / 1e12
-    if flops / kv_bytes > BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
-        # past the bf16 ridge (the fp8 cache: 580 B per token for the same
-        # bf16-MFMA flops): the matrix cores bind
-        roofline = {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": tflops / BF16_MFMA_PEAK_TFLOPS, "traffic": None,
+    # the matrix-core peak of the arithmetic the kernel runs (fp8 for the
+    # fp8-MFMA path, else bf16)
+    mfma_peak = FP8_MFMA_PEAK_TFLOPS if (args.fp8_mfma and fp8) else BF16_MFMA_PEAK_TFLOPS
+    if flops / kv_bytes > mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9):
+        # past the ridge (the fp8 cache on bf16 matrix cores: 580 B per token
+        # for the same flops): the matrix cores bind
+        roofline = {"bound": "mfma", "achieved": tflops, "peak": mfma_peak, "unit": "TFLOP/s",
+                    "frac": tflops / mfma_peak, "traffic": None,
                     "kernel": "split-KV attention", "kernel_ms": kern_ms,
                     "alg_flops_per_launch": flops, "hbm_gbs": achieved,
                     "hbm_frac": achieved / HBM_PEAK_GBS}
@@ -621,7 +630,9 @@ def main():
             "attended_tokens": tokens, "kv_cache": case.kv_dtype,
             "step": ("mla_write_kv(batch newest tokens) + mla_sparse_attention" if sparse
                      else "mla_decode_write(batch newest tokens written, then the decode)"),
-            "kernels": "generic" if args.generic else "default",
+            "kernels": ("generic" if args.generic else
+                        "fp8 matrix cores (E4M3 queries and probabilities)" if (args.fp8_mfma and fp8)
+                        else "default"),
         },
         "step_hbm_gbs": (kv_bytes + fixed_bytes) / step_s / 1e9,
         "step_tflops": flops / step_s / 1e12,

@@ -9,6 +9,7 @@
  *   [CHUNK]   "[Attention] MLA with chunked prefill"
  *   [UNIFIED] "[unified-memory] Let Kimi-Linear use the paged MLA attention
  *             backends"
+ *   [DSV4]    "Support dsv4 model"
  *
  * Conventions for every entry point
  *   - Pointers are DEVICE pointers unless marked (host).  Descriptor structs
@@ -99,6 +100,18 @@ typedef struct {
  * picks one (see mla_prefill_chunk). */
 #define MLA_FLAG_PREFILL_ABSORBED 2u
 #define MLA_FLAG_PREFILL_EXPANDED 4u
+/* fp8 E4M3 caches (kv_lora_rank 512, qk_rope_dim 64, up to 128 heads): run
+ * the scores and the values on the fp8 matrix cores, reading the cache codes
+ * as stored ([UNIFIED] "Validation": the fp8_e4m3 cache rows; [DSV4] "Model
+ * Architecture and Inference": packed FP8 KV).  The queries enter as a
+ * two-term E4M3 expansion (hi + lo, one scale per head) and the
+ * probabilities as E4M3 with a power-of-two scale per head and step, so the
+ * result approximates the exact softmax over the dequantised cache (errors
+ * against the exact result: well inside max-abs 0.1 and rel-L2 3e-2 on the
+ * tested inputs, against ~2e-3 for the default path, which is exact up to
+ * rounding).  Absorbed-form decode and prefill; ignored for bf16 caches and
+ * other shapes. */
+#define MLA_FLAG_FP8_MFMA 8u
 
 /*
  * Per-call attention parameters.

@@ -499,7 +499,13 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
                             (ql_st % 8 == 0) && (ql_sh % 8 == 0) && (qp_st % 8 == 0) &&
                             (qp_sh % 8 == 0) && aligned16(q_lat) && aligned16(q_pe) &&
                             aligned16(kv.scale);
-  if (use_mfma_fp8) {
+  const bool use_f8mfma = (attn->flags & MLA_FLAG_FP8_MFMA) != 0 && !generic &&
+                         mla::f8mfma_attn_supported(kv, H) && (ql_st % 8 == 0) && (ql_sh % 8 == 0) &&
+                         (qp_st % 8 == 0) && (qp_sh % 8 == 0) && aligned16(q_lat) && aligned16(q_pe) &&
+                         aligned16(kv.scale);
+  if (use_f8mfma) {
+    e = mla::launch_attn_f8mfma(a, s);
+  } else if (use_mfma_fp8) {
     e = mla::launch_attn_mfma_fp8(a, s);
   } else {
     e = use_mfma ? mla::launch_attn_mfma(a, s) : mla::launch_attn_generic(a, s);

@@ -182,6 +182,9 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
 // R 512, Dr 64, H <= 128).
 bool mfma_fp8_attn_supported(const CacheView& kv, int32_t H);
 hipError_t launch_attn_mfma_fp8(const AttnArgs& a, hipStream_t s);
+// fp8 caches on the fp8 matrix cores (queries and probabilities quantised).
+bool f8mfma_attn_supported(const CacheView& kv, int32_t H);
+hipError_t launch_attn_f8mfma(const AttnArgs& a, hipStream_t s);
 
 hipError_t launch_combine_segments(const AttnArgs& a, hipStream_t s);
 

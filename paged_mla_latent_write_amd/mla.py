@@ -36,6 +36,7 @@ MLA_KV_FP8_E4M3 = 1
 MLA_FLAG_GENERIC_KERNELS = 1
 MLA_FLAG_PREFILL_ABSORBED = 2
 MLA_FLAG_PREFILL_EXPANDED = 4
+MLA_FLAG_FP8_MFMA = 8
 
 EXPORTED = ("mla_write_kv", "mla_write_kv_fused", "mla_decode_workspace_size", "mla_decode", "mla_decode_write",
             "mla_decode_noalloc",

@@ -49,6 +49,15 @@ def test_header_compiles_as_c():
     assert r.returncode == 0, r.stderr
 
 
+def test_flags_match_the_header():
+    from paged_mla_latent_write_amd import mla
+    text = open(HEADER).read()
+    for name in ("MLA_FLAG_GENERIC_KERNELS", "MLA_FLAG_PREFILL_ABSORBED", "MLA_FLAG_PREFILL_EXPANDED",
+                 "MLA_FLAG_FP8_MFMA"):
+        m = re.search(rf"#define {name} (\d+)u", text)
+        assert m and int(m.group(1)) == getattr(mla, name), name
+
+
 def test_status_strings_and_version():
     from paged_mla_latent_write_amd import mla
     assert mla.status_string(0) == "MLA_OK"

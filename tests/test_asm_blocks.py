@@ -144,3 +144,29 @@ def test_compiler_code_leaves_reserved_registers_alone(src):
     top, agprs = _compiler_registers(src)
     assert top < gen.Q_BASE, f"{src}: compiler code uses v{top} (queries start at v{gen.Q_BASE})"
     assert agprs == 0, f"{src}: compiler code references accumulator registers"
+
+
+def test_fp8_matrix_core_kernel_keeps_its_registers():
+    """The fp8-MFMA attention kernel holds 16 accumulator tiles (all 256
+    accumulation registers) and its score accumulators in VGPRs: the compiled
+    kernel must fit without spilling to scratch, and its score MFMAs must
+    accumulate in VGPRs (not in the accumulation registers the values use)."""
+    import re
+    import shutil
+    import tempfile
+
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not Path(hipcc).exists():
+        pytest.skip("hipcc not available")
+    with tempfile.TemporaryDirectory() as d:
+        out = Path(d) / "k.s"
+        subprocess.run([hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
+                        "-Xclang", "-packed-fp32-ops", "-I", str(CSRC), "-I", str(CSRC.parents[1] / "include"),
+                        "-x", "hip", "--cuda-device-only", "-S", str(CSRC / "attn_f8mfma.hip"), "-o", str(out)],
+                       check=True, capture_output=True)
+        text = out.read_text()
+    scratch = [int(v) for v in re.findall(r"; ScratchSize: (\d+)", text)]
+    assert scratch and max(scratch) == 0, f"scratch use {scratch}"
+    assert "scratch_store" not in text and "scratch_load" not in text
+    assert re.search(r"v_mfma_f32_32x32x64_f8f6f4 v\[", text), "score MFMAs do not accumulate in VGPRs"
+    assert len(re.findall(r"v_mfma_scale_f32_32x32x64_f8f6f4 a\[", text)) >= 16, "values MFMAs not in AGPRs"

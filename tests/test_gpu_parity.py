@@ -173,18 +173,21 @@ def test_decode_v3_full_size(mla, sharp):
     check_decode(mla, W.v3(sharp=sharp))
 
 
+@pytest.mark.parametrize("f8mfma", [False, True])
 @pytest.mark.parametrize("sharp", [False, True])
-def test_decode_v3fp8_full_size(mla, v3fp8_population, sharp):
-    """V3 shape over the fp8 cache, every one of the 128 requests compared."""
-    say(f"decode v3fp8 sharp={sharp}")
+def test_decode_v3fp8_full_size(mla, v3fp8_population, sharp, f8mfma):
+    """V3 shape over the fp8 cache, every one of the 128 requests compared;
+    also with the fp8 matrix cores (queries and probabilities in E4M3)."""
+    say(f"decode v3fp8 sharp={sharp} f8mfma={f8mfma}")
     base, cache, hcache = v3fp8_population
     case = W.v3fp8(sharp=sharp)
     assert np.array_equal(case.ctx_slots, base.ctx_slots)
     assert np.array_equal(case.ctx_c_kv[::4096], base.ctx_c_kv[::4096])
-    out, lse = gpu_decode(mla, case, cache)
+    out, lse = gpu_decode(mla, case, cache, flags=mla.MLA_FLAG_FP8_MFMA if f8mfma else 0)
     ref, ref_lse = oracle_decode(case, hcache)
-    assert_close(bf16_host_f64(out), ref, FP8_TOL, f"v3fp8 sharp={sharp} out")
-    assert_lse_close(lse.cpu().numpy(), ref_lse, LSE_ATOL[O.KV_FP8], f"v3fp8 sharp={sharp} lse")
+    tag = f"v3fp8 sharp={sharp} f8mfma={f8mfma}"
+    assert_close(bf16_host_f64(out), ref, FP8_TOL, f"{tag} out")
+    assert_lse_close(lse.cpu().numpy(), ref_lse, LSE_ATOL[O.KV_FP8], f"{tag} lse")
 
 
 @pytest.mark.parametrize("G", [1, 3, 7, 1000])
@@ -344,6 +347,86 @@ def test_decode_fp8_score_jump_moves_the_reference(mla, G):
     assert_close(bf16_host_f64(out), ref, FP8_TOL, f"fp8 jump G={G}")
     assert_lse_close(lse.cpu().numpy(), ref_lse, LSE_ATOL[case.kv_dtype], f"fp8 jump G={G} lse")
     assert np.max(np.abs(bf16_host_f64(out)[0] - c_j[None, :])) < 2e-2
+
+
+# ---------------------------------------------------------------------------
+# fp8 matrix cores (MLA_FLAG_FP8_MFMA): queries as a two-term E4M3 expansion,
+# probabilities in E4M3; an approximation held to the fp8 cache's tolerance
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("ps", [16, 32, 64, 128])
+def test_decode_f8mfma_page_sizes(mla, ps):
+    """Ragged contexts (64-token step edges, one-token and multi-page
+    requests) over every page size, sharp queries, one and seven workgroups
+    (contexts cut at odd tiles: half-masked steps)."""
+    say(f"decode f8mfma ps={ps}")
+    d = W.Dims(H=128, R=512, Dr=64, Dn=128, Dv=128, page_size=ps)
+    case = W.custom(d, [1, 31, 32, 33, 63, 64, 65, 700, 2049], seed=1710 + ps, kv_dtype=O.KV_FP8, sharp=True)
+    f = mla.MLA_FLAG_FP8_MFMA
+    check_decode(mla, case, flags=f, label=f" f8mfma ps={ps}")
+    check_decode(mla, case, flags=f, num_workgroups=7, label=f" f8mfma ps={ps} G=7")
+
+
+@pytest.mark.parametrize("sharp", [False, True])
+@pytest.mark.parametrize("window", [1, 33, 500])
+def test_decode_f8mfma_window(mla, window, sharp):
+    say(f"decode f8mfma window={window} sharp={sharp}")
+    d = W.Dims(H=64, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
+    case = W.custom(d, [40, 700, 2049], seed=1730 + window, kv_dtype=O.KV_FP8, window=window, sharp=sharp)
+    check_decode(mla, case, flags=mla.MLA_FLAG_FP8_MFMA, label=f" f8mfma w={window}")
+
+
+@pytest.mark.parametrize("H", [16, 40, 100])
+def test_decode_f8mfma_partly_filled_waves(mla, H):
+    """Head counts that leave waves partly filled or empty (those still copy
+    their share of every step); forced partitions put items in split slots."""
+    say(f"decode f8mfma H={H}")
+    d = W.Dims(H=H, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
+    case = W.custom(d, [1, 33, 700, 2049], seed=1750 + H, kv_dtype=O.KV_FP8, sharp=True)
+    f = mla.MLA_FLAG_FP8_MFMA
+    check_decode(mla, case, flags=f, label=f" f8mfma H={H}")
+    check_decode(mla, case, flags=f, num_workgroups=5, label=f" f8mfma H={H} G=5")
+
+
+@pytest.mark.parametrize("G", [1, 2])
+@pytest.mark.parametrize("gap", [25.0, 70.0])
+def test_decode_f8mfma_score_jump(mla, G, gap):
+    """A key whose score passes its segment's first-step maximum by ~36
+    octaves (the reference moves and later weights are scaled up through the
+    matrix instruction's operand scale) or by ~97 (past 64 octaves the old
+    contributions are dropped and the units restart): the output is still
+    the oracle's, the needle's latent."""
+    say(f"decode f8mfma score jump gap={gap} G={G}")
+    d = W.Dims(H=32, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
+    case = W.custom(d, [300, 41], seed=740, kv_dtype=O.KV_FP8)
+    cache = populate_device(mla, case)
+    hc, hs = host_cache(case)
+    X = O.gather_latent(hc, hs, case.kv_dtype, 0, case.block_tables[0], int(case.context_lens[0]))
+    j = 260  # step 4 of request 0: not the first step of its segment with one or two workgroups
+    c_j = X[j, :d.R]
+    q_lat = np.zeros((2, d.H, d.R))
+    q_lat[0] = gap / (case.scale * (c_j @ c_j)) * c_j
+    q_bits = W.f32_to_bf16_bits(q_lat.astype(np.float32))
+    out, lse = mla.decode(cache, 0, dev_bf16(q_bits), dev_bf16(case.q_pe), dev(case.block_tables),
+                          dev(case.context_lens), scale=case.scale, num_workgroups=G,
+                          flags=mla.MLA_FLAG_FP8_MFMA)
+    torch.cuda.synchronize()
+    ref, ref_lse = O.decode(hc, hs, case.kv_dtype, 0, q_bits, case.q_pe, case.block_tables,
+                            case.context_lens, None, None, case.scale, 0)
+    assert_close(bf16_host_f64(out), ref, FP8_TOL, f"f8mfma jump gap={gap} G={G}")
+    assert_lse_close(lse.cpu().numpy(), ref_lse, LSE_ATOL[case.kv_dtype], f"f8mfma jump gap={gap} G={G} lse")
+    assert np.max(np.abs(bf16_host_f64(out)[0] - c_j[None, :])) < 5e-2
+
+
+@pytest.mark.parametrize("window", [0, 64])
+def test_prefill_f8mfma(mla, window):
+    """Absorbed-form prefill rows over an fp8 cache on the fp8 matrix cores."""
+    say(f"prefill f8mfma window={window}")
+    d = W.Dims(H=128, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
+    case = W.prefill_case(d, [0, 5, 100, 640], [7, 1, 70, 33], seed=1800 + window, window=window,
+                          sharp=True, kv_dtype=O.KV_FP8)
+    check_prefill(mla, case, flags=mla.MLA_FLAG_FP8_MFMA | mla.MLA_FLAG_PREFILL_ABSORBED,
+                  label=f" f8mfma w={window}")
 
 
 # ---------------------------------------------------------------------------
