@@ -81,9 +81,12 @@ __global__ __launch_bounds__(256) void combine_segments_kernel(AttnArgs a) {
         l[j] = live ? a.part_lse[slot * H + h] : -INFINITY;
         sc[j] = live ? a.part_scale[slot * H + h] : 0.f;
         if (live) {
-          const float4* src = reinterpret_cast<const float4*>(a.part_o + (slot * H + h) * R + r0);
-          x0[j] = src[0];
-          x1[j] = src[1];
+          // 8 bf16 partial values (low half first in each word)
+          const uint4 v = *reinterpret_cast<const uint4*>(a.part_o + (slot * H + h) * R + r0);
+          x0[j] = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                              __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
+          x1[j] = make_float4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xFFFF0000u),
+                              __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xFFFF0000u));
         } else {
           x0[j] = x1[j] = make_float4(0.f, 0.f, 0.f, 0.f);
         }

@@ -281,6 +281,13 @@ __device__ __forceinline__ float half_max(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Two floats as packed bf16 (round to nearest even), the first in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ __forceinline__ float bf16_bits_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
 
 // One k-step of one 32-token block's scores: s += K hi, then s += K lo (two
@@ -713,27 +720,35 @@ __global__ __launch_bounds__(256, 1) void attn_f8mfma_kernel(AttnArgs a, const i
     // ---- segment done: the unnormalised accumulator, lse and 1/l ----
     const float l_tot = wave_active ? l_sum + __shfl_xor(l_sum, 32, 64) : 1.f;
     if (wave_active && head_ok) {
+      // (a complete item's row is fp32 o_lat; a split item's partial is bf16)
       const bool complete = (seg_begin == item_ts) && (seg_end == item_te);
-      float* o_dst;
       float* lse_dst;
       float* scl_dst;
       if (complete) {
-        o_dst = a.o_lat + (static_cast<int64_t>(c_item) * a.H) * kR;
+        float* orow = a.o_lat + (static_cast<int64_t>(c_item) * a.H + head) * kR + 4 * g;
         lse_dst = a.lse + static_cast<int64_t>(c_item) * a.H;
         scl_dst = a.o_scale + static_cast<int64_t>(c_item) * a.H;
+#pragma unroll
+        for (int rb = 0; rb < kRBlocks; ++rb) {
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            *reinterpret_cast<f32x4*>(orow + 32 * rb + 8 * jj) =
+                f32x4{acc[rb][4 * jj], acc[rb][4 * jj + 1], acc[rb][4 * jj + 2], acc[rb][4 * jj + 3]};
+        }
       } else {
         const int64_t slot = (item_ts < t0) ? 2 * wg : 2 * wg + 1;
-        o_dst = a.part_o + (slot * a.H) * kR;
+        uint16_t* prow = a.part_o + (slot * a.H + head) * kR + 4 * g;
         lse_dst = a.part_lse + slot * a.H;
         scl_dst = a.part_scale + slot * a.H;
-      }
-      float* orow = o_dst + static_cast<int64_t>(head) * kR + 4 * g;
 #pragma unroll
-      for (int rb = 0; rb < kRBlocks; ++rb) {
+        for (int rb = 0; rb < kRBlocks; ++rb) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          *reinterpret_cast<f32x4*>(orow + 32 * rb + 8 * jj) =
-              f32x4{acc[rb][4 * jj], acc[rb][4 * jj + 1], acc[rb][4 * jj + 2], acc[rb][4 * jj + 3]};
+          for (int jj = 0; jj < 4; ++jj)
+            *reinterpret_cast<i32x2*>(prow + 32 * rb + 8 * jj) =
+                i32x2{static_cast<int>(pack_bf16(acc[rb][4 * jj], acc[rb][4 * jj + 1])),
+                      static_cast<int>(pack_bf16(acc[rb][4 * jj + 2], acc[rb][4 * jj + 3]))};
+          __builtin_amdgcn_sched_barrier(0);  // (one tile at a time: few registers live)
+        }
       }
       if (g == 0) {
         lse_dst[head] = (m_base + log2f(l_tot)) * kLn2;

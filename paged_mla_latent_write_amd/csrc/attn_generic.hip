@@ -146,8 +146,10 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a, int hpb) 
       }
     }
 
+    // (a complete item's row is fp32 o_lat; a split item's partial is bf16)
     const bool complete = (t == ts) && (seg_end == te);
-    float* o_dst;
+    float* o_dst = nullptr;
+    uint16_t* p_dst = nullptr;
     float* lse_dst;
     float* scl_dst;
     if (complete) {
@@ -156,14 +158,18 @@ __global__ __launch_bounds__(256) void attn_generic_kernel(AttnArgs a, int hpb) 
       scl_dst = a.o_scale + static_cast<int64_t>(i) * a.H + h0;
     } else {
       const int64_t slot = (ts < t0) ? 2 * g : 2 * g + 1;
-      o_dst = a.part_o + (slot * a.H + h0) * R;
+      p_dst = a.part_o + (slot * a.H + h0) * R;
       lse_dst = a.part_lse + slot * a.H + h0;
       scl_dst = a.part_scale + slot * a.H + h0;
     }
 #pragma unroll
     for (int k = 0; k < kMaxAcc; ++k) {
       const int idx = tid + 256 * k;
-      if (idx < nh * R) o_dst[idx] = acc[k] / l_s[idx / R];
+      if (idx < nh * R) {
+        const float v = acc[k] / l_s[idx / R];
+        if (complete) o_dst[idx] = v;
+        else p_dst[idx] = f32_to_bf16(v);
+      }
     }
     if (tid < nh) {
       lse_dst[tid] = (m_s[tid] + log2f(l_s[tid])) * kLn2;

@@ -469,8 +469,10 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
     // ---- segment done: the unnormalised accumulator, lse and 1/l
     // (no arithmetic on the accumulator registers: consumers apply 1/l)
     const float l_tot = wave_active ? l_sum + __shfl_xor(l_sum, 32, 64) : 1.f;
+    // (a complete item's row is fp32 o_lat; a split item's partial is bf16)
     const bool complete = (seg_begin == item_ts) && (seg_end == item_te);
-    float* o_dst;
+    float* o_dst = nullptr;
+    uint16_t* p_dst = nullptr;
     float* lse_dst;
     float* scl_dst;
     if (complete) {
@@ -479,7 +481,7 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
       scl_dst = a.o_scale + static_cast<int64_t>(c_item) * a.H;
     } else {
       const int64_t slot = (item_ts < t0) ? 2 * wg : 2 * wg + 1;
-      o_dst = a.part_o + (slot * a.H) * kR;
+      p_dst = a.part_o + (slot * a.H) * kR;
       lse_dst = a.part_lse + slot * a.H;
       scl_dst = a.part_scale + slot * a.H;
     }
@@ -495,12 +497,19 @@ __global__ __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_num_vgpr(kCompile
       const uint32_t reg_a = lds_base + ((tn - 2) & 3) * kTileBytes + wave * kLoads * 1024;
       const uint32_t reg_b = lds_base + ((tn - 1) & 3) * kTileBytes + wave * kLoads * 1024;
       const uint32_t w_off = n32 * 272 + 16 * g;
-      const uint32_t r_off = (lane >> 4) * 272 + (lane & 15) * 16;
-      store_acc_lds(reinterpret_cast<char*>(o_dst + static_cast<int64_t>(wave * 32) * kR),
-                    (lane >> 4) * 2048 + (lane & 15) * 16, reg_a + w_off, reg_b + w_off, reg_a + r_off,
-                    reg_b + r_off);
+      if (complete) {
+        const uint32_t r_off = (lane >> 4) * 272 + (lane & 15) * 16;
+        store_acc_lds(reinterpret_cast<char*>(o_dst + static_cast<int64_t>(wave * 32) * kR),
+                      (lane >> 4) * 2048 + (lane & 15) * 16, reg_a + w_off, reg_b + w_off, reg_a + r_off,
+                      reg_b + r_off);
+      } else {
+        const uint32_t r_off = (lane >> 3) * 272 + (lane & 7) * 32;
+        store_acc_lds_bf16(p_dst + static_cast<int64_t>(wave * 32) * kR, (lane >> 3) * 1024 + (lane & 7) * 16,
+                           reg_a + w_off, reg_b + w_off, reg_a + r_off, reg_b + r_off);
+      }
     } else if (wave_active && head_ok) {
-      store_acc(o_dst + static_cast<int64_t>(head) * kR + 4 * g);
+      if (complete) store_acc(o_dst + static_cast<int64_t>(head) * kR + 4 * g);
+      else store_acc_bf16(p_dst + static_cast<int64_t>(head) * kR + 4 * g);
     }
     if (wave_active && head_ok && g == 0) {
       lse_dst[head] = (m_ref + log2f(l_tot)) * kLn2;

@@ -469,8 +469,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(kCompilerVgp
 
     // ---- segment done: the unnormalised accumulator, lse and 1/l ----
     const float l_tot = wave_active ? l_sum + __shfl_xor(l_sum, 32, 64) : 1.f;
+    // (a complete item's row is fp32 o_lat; a split item's partial is bf16)
     const bool complete = (seg_begin == item_ts) && (seg_end == item_te);
-    float* o_dst;
+    float* o_dst = nullptr;
+    uint16_t* p_dst = nullptr;
     float* lse_dst;
     float* scl_dst;
     if (complete) {
@@ -479,12 +481,13 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(kCompilerVgp
       scl_dst = a.o_scale + static_cast<int64_t>(c_item) * a.H;
     } else {
       const int64_t slot = (item_ts < t0) ? 2 * wg : 2 * wg + 1;
-      o_dst = a.part_o + (slot * a.H) * kR;
+      p_dst = a.part_o + (slot * a.H) * kR;
       lse_dst = a.part_lse + slot * a.H;
       scl_dst = a.part_scale + slot * a.H;
     }
     if (wave_active && head_ok) {
-      store_acc(o_dst + static_cast<int64_t>(head) * kR + 4 * g);
+      if (complete) store_acc(o_dst + static_cast<int64_t>(head) * kR + 4 * g);
+      else store_acc_bf16(p_dst + static_cast<int64_t>(head) * kR + 4 * g);
       if (g == 0) {
         lse_dst[head] = (m_ref + log2f(l_tot)) * kLn2;
         scl_dst[head] = 1.0f / l_tot;

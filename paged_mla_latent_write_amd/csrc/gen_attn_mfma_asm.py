@@ -444,6 +444,41 @@ def store_acc_lds():
                  ['[base] "s"(base), [soff] "v"(soff), [wa] "v"(wa), [wb] "v"(wb), [ra] "v"(ra), [rb] "v"(rb)'])
 
 
+def store_acc_lds_bf16():
+    """store_acc_lds for a split item's partial row: the same LDS staging of
+    fp32 accumulators, read back eight values per lane (two reads of one
+    row), rounded to bf16 (v_cvt_pk_bf16_f32, nearest even) and stored as
+    128-byte row pieces of the wave's bf16 rows [head][512] at %[base]
+    (%[soff] = 1024 (lane / 8) + 16 (lane % 8), %[ra] / %[rb] = block +
+    272 (lane / 8) + 32 (lane % 8)).  Temporaries: the query registers."""
+    L = ["s_nop 7", "s_nop 7", "s_nop 4"]  # the last MFMA results must have landed
+    OFF = Q_BASE  # v62-v65: store offsets of the four row groups
+    L += [f"v_add_u32 v{OFF + i}, {8192 * i}, %[soff]" for i in range(4)]
+    for r in range(8):
+        wa, ra = ("%[wa]", "%[ra]") if r % 2 == 0 else ("%[wb]", "%[rb]")
+        T = Q_BASE + 8 + 64 * (r % 2)  # 32 accumulator values, then 32 read back
+        for m in range(2):
+            mt = 2 * r + m
+            for a4 in range(4):
+                t = T + 16 * m + 4 * a4
+                L += [f"v_accvgpr_read_b32 v{t + e}, a{16 * mt + 4 * a4 + e}" for e in range(4)]
+                L.append(f"ds_write_b128 {wa}, v[{t}:{t + 3}] offset:{128 * m + 32 * a4}")
+        rd = T + 32
+        for i in range(8):
+            # store s reads row 8 s + lane / 8: chunks 2 (lane % 8) and + 1
+            L.append(f"ds_read_b128 v[{rd + 4 * i}:{rd + 4 * i + 3}], {ra} offset:{2176 * (i // 2) + 16 * (i % 2)}")
+        for s4 in range(4):
+            # LDS operations of one wave complete in order: reads 2 s and 2 s + 1
+            # have landed once at most the 6 - 2 s later ones are outstanding
+            L.append(f"s_waitcnt lgkmcnt({6 - 2 * s4})")
+            d = rd + 8 * s4
+            L += [f"v_cvt_pk_bf16_f32 v{d + w}, v{d + 2 * w}, v{d + 2 * w + 1}" for w in range(4)]
+            L.append(f"global_store_dwordx4 v{OFF + s4}, v[{d}:{d + 3}], %[base] offset:{128 * r}")
+    return block("store_acc_lds_bf16", ["uint16_t* base", "uint32_t soff", "uint32_t wa", "uint32_t wb",
+                                        "uint32_t ra", "uint32_t rb"], L, [],
+                 ['[base] "s"(base), [soff] "v"(soff), [wa] "v"(wa), [wb] "v"(wb), [ra] "v"(ra), [rb] "v"(rb)'])
+
+
 def rescale_lines():
     """Scale this lane's accumulators by %[fac] (rare: after a reference move);
     temporaries: the score registers (P of the tile is in v224-v231, the next
@@ -609,8 +644,21 @@ def emit():
             L.append(f"global_store_dwordx4 %[orow], v[{r}:{r + 3}], off offset:{4 * (32 * mt + 8 * a4)}")
             n += 1
     o += block("store_acc", ["float* orow"], L, [], ['[orow] "v"(orow)'])
+    # the same as bf16 (a split item's partial row): orow includes 4 g
+    L = ["s_nop 7", "s_nop 7", "s_nop 4"]
+    n = 0
+    for mt in range(16):
+        for a4 in range(4):
+            r = SS + 4 * (n % 6)
+            L += [f"v_accvgpr_read_b32 v{r + e}, a{16 * mt + 4 * a4 + e}" for e in range(4)]
+            L.append(f"v_cvt_pk_bf16_f32 v{r}, v{r}, v{r + 1}")
+            L.append(f"v_cvt_pk_bf16_f32 v{r + 1}, v{r + 2}, v{r + 3}")
+            L.append(f"global_store_dwordx2 %[orow], v[{r}:{r + 1}], off offset:{2 * (32 * mt + 8 * a4)}")
+            n += 1
+    o += block("store_acc_bf16", ["uint16_t* orow"], L, [], ['[orow] "v"(orow)'])
     o += block("rescale_acc", ["float fac"], rescale_lines(), [], ['[fac] "v"(fac)'])
     o += store_acc_lds()
+    o += store_acc_lds_bf16()
     o += hot_loop()
     return "\n".join(o)
 

@@ -322,7 +322,7 @@ __global__ __launch_bounds__(kCupThreads) void combine_up_project_kernel(AttnArg
       } else if (g0 >= 0) {
         for (int gb = g0; gb <= g1; gb += SB) {
           float l[SB], sc[SB];
-          float4 x[SB][kE];
+          uint2 x[SB][kE];  // 4 bf16 partial values each (low half first)
 #pragma unroll
           for (int p = 0; p < SB; ++p) {
             const int gg = gb + p;
@@ -333,11 +333,11 @@ __global__ __launch_bounds__(kCupThreads) void combine_up_project_kernel(AttnArg
             const int64_t slot = (gg == g0) ? 2 * gg + 1 : 2 * gg;
             const float lp = in ? a.part_lse[slot * H + h] : -INFINITY;
             sc[p] = in ? a.part_scale[slot * H + h] : 0.f;
-            const float4* src = reinterpret_cast<const float4*>(a.part_o + (slot * H + h) * R);
+            const uint2* src = reinterpret_cast<const uint2*>(a.part_o + (slot * H + h) * R);
 #pragma unroll
             for (int e = 0; e < kE; ++e) {
               const int c = 4 * j + 4 * kTpi * e;
-              x[p][e] = (in && c < R) ? src[c >> 2] : make_float4(0.f, 0.f, 0.f, 0.f);
+              x[p][e] = (in && c < R) ? src[c >> 2] : make_uint2(0u, 0u);
             }
             l[p] = live ? lp : -INFINITY;
           }
@@ -359,10 +359,10 @@ __global__ __launch_bounds__(kCupThreads) void combine_up_project_kernel(AttnArg
             const float w = e_l * sc[p];
 #pragma unroll
             for (int e = 0; e < kE; ++e) {
-              acc[e].x = fmaf(w, x[p][e].x, acc[e].x);
-              acc[e].y = fmaf(w, x[p][e].y, acc[e].y);
-              acc[e].z = fmaf(w, x[p][e].z, acc[e].z);
-              acc[e].w = fmaf(w, x[p][e].w, acc[e].w);
+              acc[e].x = fmaf(w, __uint_as_float(x[p][e].x << 16), acc[e].x);
+              acc[e].y = fmaf(w, __uint_as_float(x[p][e].x & 0xFFFF0000u), acc[e].y);
+              acc[e].z = fmaf(w, __uint_as_float(x[p][e].y << 16), acc[e].z);
+              acc[e].w = fmaf(w, __uint_as_float(x[p][e].y & 0xFFFF0000u), acc[e].w);
             }
           }
         }

@@ -116,7 +116,7 @@ bool make_layout(const mla_cache* c, const mla_attn* a, int64_t num_items, Layou
   L->item_wg = off;
   off = align_up(off + sizeof(int32_t) * 2 * num_items);
   L->part_o = off;
-  off = align_up(off + sizeof(float) * 2 * G * H * R);
+  off = align_up(off + sizeof(uint16_t) * 2 * G * H * R);  // bf16 partials
   L->part_lse = off;
   off = align_up(off + sizeof(float) * 2 * G * H);
   L->part_scale = off;
@@ -483,7 +483,7 @@ mla_status run_attention(int mode, const mla_cache* cache, int32_t layer_idx, co
   a.o_lat = at<float>(workspace, L.o_lat);
   a.lse = lse_or_null ? lse_or_null : at<float>(workspace, L.lse);
   a.o_scale = at<float>(workspace, L.o_scale);
-  a.part_o = at<float>(workspace, L.part_o);
+  a.part_o = at<uint16_t>(workspace, L.part_o);
   a.part_lse = at<float>(workspace, L.part_lse);
   a.part_scale = at<float>(workspace, L.part_scale);
 

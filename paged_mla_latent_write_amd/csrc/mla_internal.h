@@ -70,7 +70,7 @@ struct AttnArgs {
   float* o_lat;           // [Nq][H][R] fp32 (complete items)
   float* lse;             // [Nq][H] fp32 natural log (complete items)
   float* o_scale;         // [Nq][H]
-  float* part_o;          // [2G][H][R] fp32 partials (cut items)
+  uint16_t* part_o;       // [2G][H][R] bf16 partials (cut items; unnormalised, RNE)
   float* part_lse;        // [2G][H]
   float* part_scale;      // [2G][H]
 };
