@@ -464,16 +464,27 @@ __global__ __launch_bounds__(256, 1) void attn_f8mfma_kernel(AttnArgs a, const i
           }
         }
       }
-      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+      amax = half_max(amax);
       const float sq = amax > 0.f ? amax / 448.f : 1.f;
       const float inv = amax > 0.f ? 448.f / amax : 1.f;
       qscale = sq * c_log2;
+      // (the rows are re-read three k-steps ahead of their conversion, so the
+      // loads' latency overlaps the conversions)
+      constexpr int kQAhead = 3;
+      i32x4 ring[kQAhead][4];
+      auto qload = [&](int ks) {
+        const i32x4* src = reinterpret_cast<const i32x4*>(qrow(ks));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ring[ks % kQAhead][u] = head_ok ? src[u] : i32x4{0, 0, 0, 0};
+      };
+#pragma unroll
+      for (int ks = 0; ks < kQAhead; ++ks) qload(ks);
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) {
         i32x4 raw[4];
-        const i32x4* src = reinterpret_cast<const i32x4*>(qrow(ks));
 #pragma unroll
-        for (int u = 0; u < 4; ++u) raw[u] = head_ok ? src[u] : i32x4{0, 0, 0, 0};
+        for (int u = 0; u < 4; ++u) raw[u] = ring[ks % kQAhead][u];
+        if (ks + kQAhead < kKSteps) qload(ks + kQAhead);
         i32x8 hi, lo;
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
@@ -719,9 +730,15 @@ __global__ __launch_bounds__(256, 1) void attn_f8mfma_kernel(AttnArgs a, const i
 
     // ---- segment done: the unnormalised accumulator, lse and 1/l ----
     const float l_tot = wave_active ? l_sum + __shfl_xor(l_sum, 32, 64) : 1.f;
+    // (a complete item's row is fp32 o_lat; a split item's partial is bf16)
+    const bool complete = (seg_begin == item_ts) && (seg_end == item_te);
+    // A partial goes to bf16 through LDS: each lane's accumulators are
+    // written to a private 64-byte slot of the lo-code region and read back
+    // for the conversion (read directly, the compiler stages all 256
+    // accumulation registers through VGPRs and moves them around the step
+    // loop).  Every wave is past its last reads of the lo codes here.
+    if (!complete) __syncthreads();
     if (wave_active && head_ok) {
-      // (a complete item's row is fp32 o_lat; a split item's partial is bf16)
-      const bool complete = (seg_begin == item_ts) && (seg_end == item_te);
       float* lse_dst;
       float* scl_dst;
       if (complete) {
@@ -740,14 +757,20 @@ __global__ __launch_bounds__(256, 1) void attn_f8mfma_kernel(AttnArgs a, const i
         uint16_t* prow = a.part_o + (slot * a.H + head) * kR + 4 * g;
         lse_dst = a.part_lse + slot * a.H;
         scl_dst = a.part_scale + slot * a.H;
+        const uint32_t stg = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds_qlo)) + 64 * tid;
 #pragma unroll
         for (int rb = 0; rb < kRBlocks; ++rb) {
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj)
+            *reinterpret_cast<LDS_PTR(f32x4)>(stg + 16 * jj) =
+                f32x4{acc[rb][4 * jj], acc[rb][4 * jj + 1], acc[rb][4 * jj + 2], acc[rb][4 * jj + 3]};
+          asm volatile("" ::: "memory");  // (a real round trip: no forwarding of the stored registers)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const f32x4 v = *reinterpret_cast<LDS_PTR(const f32x4)>(stg + 16 * jj);
             *reinterpret_cast<i32x2*>(prow + 32 * rb + 8 * jj) =
-                i32x2{static_cast<int>(pack_bf16(acc[rb][4 * jj], acc[rb][4 * jj + 1])),
-                      static_cast<int>(pack_bf16(acc[rb][4 * jj + 2], acc[rb][4 * jj + 3]))};
-          __builtin_amdgcn_sched_barrier(0);  // (one tile at a time: few registers live)
+                i32x2{static_cast<int>(pack_bf16(v[0], v[1])), static_cast<int>(pack_bf16(v[2], v[3]))};
+          }
         }
       }
       if (g == 0) {
