@@ -32,6 +32,8 @@
 // and passes past a request's context return at once.
 #include <math.h>
 
+#include <type_traits>
+
 #include "device_utils.h"
 #include "mla_internal.h"
 
@@ -75,8 +77,10 @@ __device__ __forceinline__ bool pass_range(const XPassArgs& a, int b, int64_t* n
 constexpr int kGTok = 256;                 // tokens per workgroup tile
 constexpr int kGThreads = 512;             // 8 waves: 4 token quarters x (K, V)
 constexpr int kGN = 256;                   // output columns per tile: one head's K (128) and V (128)
-constexpr int kGK = 64;                    // R per LDS stage
-constexpr int kGPitch = kGK * 2 + 16;      // bytes per LDS row
+// bf16 caches: R in 32-wide stages, three LDS buffers (copies of stage s + 2
+// issued during stage s's MFMAs); fp8 caches: 64-wide stages, one buffer
+constexpr int kGK = 32, kGPitch = kGK * 2 + 16, kGBufs = 3;
+constexpr int kGK8 = 64, kGPitch8 = kGK8 * 2 + 16;
 
 // V_expT keeps each 16-key group with its second and third quads swapped
 // (keys 4..7 after 8..11): the attention kernel's MFMA reads the eight keys
@@ -96,10 +100,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-constexpr int kGKRow = kXDn * 2 + 16;      // bytes per LDS row of a K wave's output tile (transpose)
-constexpr int kGSlots = (kGTok + kGN) * (kGPitch / 16);  // 16-byte LDS slots of one stage (A then B rows)
-constexpr int kGDma = kGSlots / kGThreads;               // copies per thread per stage (9)
-static_assert(kGSlots % kGThreads == 0 && kGTok * (kGPitch / 16) % 64 == 0, "stage copies");
+constexpr int kGRowSlots = kGPitch / 16;   // 16-byte LDS slots per row (4 of data, one of pad)
+constexpr int kGSlots = (kGTok + kGN) * kGRowSlots;  // slots of one stage (A then B rows)
+constexpr int kGDma = kGSlots / kGThreads;            // copies per thread per stage (5)
+constexpr int kGStageBytes = (kGTok + kGN) * kGPitch;
+static_assert(kGSlots % kGThreads == 0, "stage copies");
 
 // 16-byte copy HBM -> LDS: lane i's bytes land at lds_base + 16 i.  Inline
 // assembly keeps the compiler from draining the copies with conservative
@@ -120,14 +125,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 template <bool kFp8>
 __global__ __launch_bounds__(kGThreads, 1) void kv_expand_kernel(XPassArgs a) {
-  // A (tokens) and B (weight rows) of a stage (bf16 caches: two stages, the
-  // copies of stage s + 2 in flight during stage s); after the last stage
-  // the same memory holds the K waves' output tiles for the transposed store
-  constexpr int kStages = kFp8 ? 1 : 2;
-  __shared__ __attribute__((aligned(16))) char smem[kStages * (kGTok + kGN) * kGPitch];
+  // A (tokens) and B (weight rows) of the stages
+  constexpr int kSmem = kFp8 ? (kGTok + kGN) * kGPitch8 : kGBufs * kGStageBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
   __shared__ float tok_scale[kFp8 ? kGTok : 1];
-  char* const As = smem;
-  char* const Bs = smem + kGTok * kGPitch;
   const int tile = blockIdx.x, h = blockIdx.y, bz = blockIdx.z;
   const int b = a.b0 + bz;
   int64_t n, m, k0, ntok;
@@ -161,65 +162,102 @@ __global__ __launch_bounds__(kGThreads, 1) void kv_expand_kernel(XPassArgs a) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) acc[i][jj] = f32x16{};
-  // the MFMAs of one stage on the LDS rows at As / Bs
-  auto stage_mfma = [&](const char* as, const char* bs) {
+  // The MFMAs of k-step ks of a stage on the LDS rows at as / bs (rows of
+  // kP bytes).  V waves compute tokens x dims (a lane ends with four
+  // consecutive tokens of one dim: a piece of a V^T row); K waves compute
+  // dims x tokens (four consecutive dims of one token: a piece of a K row).
+  auto kstep_mfma = [&](auto kt, auto pitch_c, int ks, const char* as, const char* bs) {
+    constexpr bool kK = decltype(kt)::value;
+    constexpr int kP = decltype(pitch_c)::value;
+    i16x8 af[2], bf[4];
 #pragma unroll
-    for (int ks = 0; ks < kGK / 16; ++ks) {
-      i16x8 af[2], bf[4];
+    for (int i = 0; i < 2; ++i)
+      af[i] = *reinterpret_cast<const i16x8*>(as + (64 * tm + 32 * i + n32) * kP + (16 * ks + 8 * g) * 2);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const i16x8*>(as + (64 * tm + 32 * i + n32) * kGPitch + (16 * ks + 8 * g) * 2);
+    for (int jj = 0; jj < 4; ++jj)
+      bf[jj] = *reinterpret_cast<const i16x8*>(bs + (128 * tn + 32 * jj + n32) * kP + (16 * ks + 8 * g) * 2);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
-        bf[jj] = *reinterpret_cast<const i16x8*>(bs + (128 * tn + 32 * jj + n32) * kGPitch + (16 * ks + 8 * g) * 2);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[i][jj] = mfma(af[i], bf[jj], acc[i][jj]);
-    }
+        acc[i][jj] = kK ? mfma(bf[jj], af[i], acc[i][jj]) : mfma(af[i], bf[jj], acc[i][jj]);
   };
 
   if constexpr (!kFp8) {
-    // Stage slot z (16 bytes; 9 per 144-byte row: 8 of data, one of pad)
-    // of the A rows then the B rows is filled by thread z % 512, copy z / 512
-    // (each wave's copy covers 64 consecutive slots).  Pad slots repeat the
-    // row's last chunk; token rows past the pass's keys repeat its last row
-    // (finite values, never attended).
+    // Stage slot z (16 bytes; 5 per 80-byte row: 4 of data, one of pad) of
+    // the A rows then the B rows is filled by thread z % 512, copy z / 512
+    // (each wave's copy covers 64 consecutive slots, so lane i's bytes land
+    // at the copy's base + 16 i).  Pad slots repeat the row's last chunk;
+    // token rows past the pass's keys repeat its last row (finite values,
+    // never attended).  The block-table loads go out together (each lane
+    // loads for every token copy, whatever its slot holds).
+    constexpr int kACopies = (kGTok * kGRowSlots + kGThreads - 1) / kGThreads;  // copies with token rows (3)
+    int64_t tok[kACopies];
+    unsigned pg[kACopies];
+#pragma unroll
+    for (int k = 0; k < kACopies; ++k) {
+      const int z = kGThreads * k + t;
+      const int r = (z < kGTok * kGRowSlots ? z : z - kGTok * kGRowSlots) / kGRowSlots;
+      tok[k] = k0 + min(j0 + r, static_cast<int>(ntok) - 1);
+      pg[k] = static_cast<unsigned>(bt[tok[k] >> kv.page_shift]);
+    }
+    // (opaque: the compiler may not sink a load into the branch that uses it)
+#pragma unroll
+    for (int k = 0; k < kACopies; ++k) asm volatile("" : "+v"(pg[k]));
     const char* dsrc[kGDma];
 #pragma unroll
     for (int k = 0; k < kGDma; ++k) {
       const int z = kGThreads * k + t;
-      const int zr = z < kGTok * 9 ? z : z - kGTok * 9;
-      const int r = zr / 9, cc = min(zr - 9 * r, 7);
-      if (z < kGTok * 9)
-        dsrc[k] = cache + cache_row(j0 + r) * kv.D * 2 + 16 * cc;
-      else
-        dsrc[k] = reinterpret_cast<const char*>(r < kXDn ? Wk + static_cast<int64_t>(r) * R
-                                                         : Wv + static_cast<int64_t>(r - kXDn) * R) + 16 * cc;
+      const bool is_a = z < kGTok * kGRowSlots;
+      const int zr = is_a ? z : z - kGTok * kGRowSlots;
+      const int r = zr / kGRowSlots, cc = min(zr - kGRowSlots * r, kGRowSlots - 2);
+      const char* wp = reinterpret_cast<const char*>(r < kXDn ? Wk + static_cast<int64_t>(r) * R
+                                                             : Wv + static_cast<int64_t>(r - kXDn) * R) + 16 * cc;
+      if (k < kACopies) {
+        const int64_t row = static_cast<int64_t>(min(pg[k], last_page)) * kv.page_size +
+                            (tok[k] & (kv.page_size - 1));
+        dsrc[k] = is_a ? cache + row * kv.D * 2 + 16 * cc : wp;
+      } else {
+        dsrc[k] = wp;
+      }
     }
     const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem)) + 1024 * wave;
-    auto issue = [&](int kc, int buf) {
+    // copies [k_lo, k_hi) of stage st into its buffer
+    auto issue = [&](int st, int k_lo, int k_hi) {
 #pragma unroll
       for (int k = 0; k < kGDma; ++k)
-        lds_dma_16(dsrc[k] + 2 * kc, lds0 + buf * ((kGTok + kGN) * kGPitch) + 16 * kGThreads * k);
+        if (k >= k_lo && k < k_hi)
+          lds_dma_16(dsrc[k] + 2 * kGK * st, lds0 + (st % kGBufs) * kGStageBytes + 16 * kGThreads * k);
     };
     const int nst = R / kGK;
-    issue(0, 0);
-    if (nst > 1) issue(kGK, 1);
-    for (int st = 0; st < nst; ++st) {
-      if (st + 1 < nst) wait_vmcnt<kGDma>();  // this thread's copies of stage st have landed
-      else wait_vmcnt<0>();
-      __syncthreads();  // and every thread's
-      const char* base = smem + (st & 1) * ((kGTok + kGN) * kGPitch);
-      stage_mfma(base, base + kGTok * kGPitch);
-      __syncthreads();  // every wave is done with this buffer
-      if (st + 2 < nst) issue((st + 2) * kGK, st & 1);
-    }
+    issue(0, 0, kGDma);
+    if (nst > 1) issue(1, 0, kGDma);
+    auto stages = [&](auto kt) {
+      for (int st = 0; st < nst; ++st) {
+        // this thread's copies of stage st have landed (stage st + 1's may not)
+        if (st + 1 < nst) wait_vmcnt<kGDma>();
+        else wait_vmcnt<0>();
+        // every thread's have, and every wave is done with stage st - 1's
+        // buffer, which stage st + 2's copies (issued between this stage's
+        // MFMAs) refill
+        __syncthreads();
+        const char* base = smem + (st % kGBufs) * kGStageBytes;
+        const bool more = st + 2 < nst;
+        if (more) issue(st + 2, 0, 3);
+        kstep_mfma(kt, std::integral_constant<int, kGPitch>{}, 0, base, base + kGTok * kGPitch);
+        if (more) issue(st + 2, 3, kGDma);
+        kstep_mfma(kt, std::integral_constant<int, kGPitch>{}, 1, base, base + kGTok * kGPitch);
+      }
+    };
+    if (tn == 1) stages(std::false_type{});
+    else stages(std::true_type{});
   } else {
     // fp8 caches: the next stage's loads land in registers during this
     // stage's MFMAs; the codes are converted on their way to LDS.  This
     // thread's A chunks (16 codes of a token row per stage; rows past the
     // pass's keys load zeros) and B chunks, as pointers fixed over the stages.
+    char* const As = smem;
+    char* const Bs = smem + kGTok * kGPitch8;
     constexpr int kAq = kGTok * 4 / kGThreads;  // 16-code A chunks per thread (2)
     constexpr int kBq = kGN * 8 / kGThreads;    // 8-value B chunks per thread (4)
     const char* asrc[kAq];
@@ -268,33 +306,45 @@ __global__ __launch_bounds__(kGThreads, 1) void kv_expand_kernel(XPassArgs a) {
           hi[2 * w] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ra[q][w + 2], 1.0f, false));
           hi[2 * w + 1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ra[q][w + 2], 1.0f, true));
         }
-        *reinterpret_cast<i32x4*>(As + r * kGPitch + c * 32) = lo;
-        *reinterpret_cast<i32x4*>(As + r * kGPitch + c * 32 + 16) = hi;
+        *reinterpret_cast<i32x4*>(As + r * kGPitch8 + c * 32) = lo;
+        *reinterpret_cast<i32x4*>(As + r * kGPitch8 + c * 32 + 16) = hi;
       }
 #pragma unroll
       for (int q = 0; q < kBq; ++q) {
         const int idx = t + kGThreads * q;
-        *reinterpret_cast<i16x8*>(Bs + (idx >> 3) * kGPitch + (idx & 7) * 16) = rb[q];
+        *reinterpret_cast<i16x8*>(Bs + (idx >> 3) * kGPitch8 + (idx & 7) * 16) = rb[q];
       }
     };
     load_stage(0);
-    for (int kc = 0; kc < R; kc += kGK) {
+    for (int kc = 0; kc < R; kc += kGK8) {
       store_stage();
       __syncthreads();
-      if (kc + kGK < R) load_stage(kc + kGK);  // in flight during this stage's MFMAs
-      stage_mfma(As, Bs);
+      if (kc + kGK8 < R) load_stage(kc + kGK8);  // in flight during this stage's MFMAs
+      if (tn == 1) {
+#pragma unroll
+        for (int ks = 0; ks < kGK8 / 16; ++ks)
+          kstep_mfma(std::false_type{}, std::integral_constant<int, kGPitch8>{}, ks, As, Bs);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < kGK8 / 16; ++ks)
+          kstep_mfma(std::true_type{}, std::integral_constant<int, kGPitch8>{}, ks, As, Bs);
+      }
       __syncthreads();
     }
   }
 
-  // epilogue: element e of acc[i][jj] is token 64 tm + 32 i + 8 (e / 4) + 4 g + e % 4,
-  // column d = 32 jj + n32 of the wave's K (tn = 0) or V (tn = 1) block
-  auto val = [&](int i, int jj, int e, int r) {
-    const float x = acc[i][jj][e];
-    return kFp8 ? x * tok_scale[r] : x;
+  // epilogue: 16-byte stores, 16 per lane.  V waves: element e of
+  // acc[i][jj] is token 64 tm + 32 i + 8 (e / 4) + 4 g + e % 4 of dim
+  // 32 jj + n32.  With V^T's quad order a lane's quads e4 = 2p and 2p + 1
+  // (tokens 16 p + 4 g + 0..3 and + 8..11) are adjacent in memory.  K waves:
+  // element e is dim 32 jj + 8 (e / 4) + 4 g + e % 4 of token 64 tm + 32 i +
+  // n32; a swap of lanes l + 32 and l (dims 4..7 for 8..11) gives lane half 0
+  // dims 16 p + 0..7 and half 1 dims 16 p + 8..15.
+  auto quad = [&](int i, int jj, int e4, float sc0, float sc1, float sc2, float sc3) -> uint2 {
+    return make_uint2(pack_bf16(acc[i][jj][4 * e4] * sc0, acc[i][jj][4 * e4 + 1] * sc1),
+                      pack_bf16(acc[i][jj][4 * e4 + 2] * sc2, acc[i][jj][4 * e4 + 3] * sc3));
   };
   if (tn == 1) {
-    // V_expT[h][d][vperm(j)]: four consecutive tokens (a quad), one 8-byte store
     uint16_t* vrow = v_expT + static_cast<int64_t>(h) * kXDv * ck + j0;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -302,53 +352,70 @@ __global__ __launch_bounds__(kGThreads, 1) void kv_expand_kernel(XPassArgs a) {
       for (int jj = 0; jj < 4; ++jj) {
         const int d = 32 * jj + n32;
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int r = 64 * tm + 32 * i + 8 * e4 + 4 * g;  // tile-local token of element 4 e4
-          *reinterpret_cast<uint2*>(vrow + static_cast<int64_t>(d) * ck + vperm(r)) =
-              make_uint2(pack_bf16(val(i, jj, 4 * e4, r), val(i, jj, 4 * e4 + 1, r + 1)),
-                         pack_bf16(val(i, jj, 4 * e4 + 2, r + 2), val(i, jj, 4 * e4 + 3, r + 3)));
+        for (int p = 0; p < 2; ++p) {
+          const int r = 64 * tm + 32 * i + 16 * p + 4 * g;  // tile-local token of quad e4 = 2 p
+          float sc[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sc[e] = kFp8 ? tok_scale[r + (e < 4 ? e : e + 4)] : 1.0f;
+          const uint2 q0 = quad(i, jj, 2 * p, sc[0], sc[1], sc[2], sc[3]);
+          const uint2 q1 = quad(i, jj, 2 * p + 1, sc[4], sc[5], sc[6], sc[7]);
+          *reinterpret_cast<uint4*>(vrow + static_cast<int64_t>(d) * ck + vperm(r)) =
+              make_uint4(q0.x, q0.y, q1.x, q1.y);
         }
       }
     }
   } else {
-    // K_exp[h][j][d]: the wave's 64 x 128 tile goes through LDS (token rows)
-    // so that each lane stores 16 contiguous bytes of a row
-    char* kt = smem + tm * (64 * kGKRow);
+    uint16_t* krow = k_exp + (static_cast<int64_t>(h) * ck + j0) * kXDn;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
+      const int r = 64 * tm + 32 * i + n32;  // tile-local token
+      const float sc = kFp8 ? tok_scale[r] : 1.0f;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
+      for (int jj = 0; jj < 4; ++jj) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int rl = 32 * i + 8 * (e >> 2) + 4 * g + (e & 3);  // wave-local token
-          *reinterpret_cast<__bf16*>(kt + rl * kGKRow + (32 * jj + n32) * 2) =
-              static_cast<__bf16>(val(i, jj, e, 64 * tm + rl));
-        }
-    uint16_t* krow = k_exp + (static_cast<int64_t>(h) * ck + j0 + 64 * tm) * kXDn;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int c = lane + 64 * k;  // 16-byte chunk: token c / 16, columns 8 (c % 16) ..
-      const int rl = c >> 4, cc = c & 15;
-      *reinterpret_cast<i32x4*>(krow + rl * kXDn + 8 * cc) =
-          *reinterpret_cast<const i32x4*>(kt + rl * kGKRow + 16 * cc);
-    }
-  }
-  // the rope part of the keys, shared by every head (written once)
-  if (h == 0) {
-    for (int idx = t; idx < kGTok * kXDr; idx += kGThreads) {
-      const int r = idx / kXDr, c = idx % kXDr;
-      const int j = j0 + r;
-      uint16_t v = 0;
-      if (j < ntok) {
-        const int64_t row = cache_row(j);
-        if (!kFp8) {
-          v = static_cast<const uint16_t*>(kv.data)[row * kv.D + R + c];
-        } else {
-          const uint8_t code = static_cast<const uint8_t*>(kv.data)[row * kv.D + R + c];
-          v = f32_to_bf16(e4m3_to_f32(code) * kv.scale[row]);
+        for (int p = 0; p < 2; ++p) {
+          const uint2 qa = quad(i, jj, 2 * p, sc, sc, sc, sc);      // dims 16 p + 4 g + 0..3
+          const uint2 qb = quad(i, jj, 2 * p + 1, sc, sc, sc, sc);  // dims 16 p + 8 + 4 g + 0..3
+          const auto sx = __builtin_amdgcn_permlane32_swap(qa.x, qb.x, false, false);
+          const auto sy = __builtin_amdgcn_permlane32_swap(qa.y, qb.y, false, false);
+          // half 0: [own qa, partner's qa] = dims 16 p + 0..7; half 1:
+          // [partner's qb, own qb] = dims 16 p + 8..15
+          *reinterpret_cast<uint4*>(krow + static_cast<int64_t>(r) * kXDn + 32 * jj + 16 * p + 8 * g) =
+              make_uint4(sx[0], sy[0], sx[1], sy[1]);
         }
       }
-      kpe[static_cast<int64_t>(j) * kXDr + c] = v;
+    }
+  }
+  // the rope part of the keys, shared by every head (written once): 8-value
+  // chunks, four per thread; tokens past the pass's keys get zeros
+  if (h == 0) {
+    constexpr int kQ = kGTok * (kXDr / 8) / kGThreads;
+    int64_t row[kQ];
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) row[q] = cache_row(j0 + ((t + kGThreads * q) >> 3));
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const int c = t + kGThreads * q, r = c >> 3, part = c & 7;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (j0 + r < ntok) {
+        if constexpr (!kFp8) {
+          v = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(kv.data) + row[q] * kv.D + R + 8 * part);
+        } else {
+          const uint2 codes =
+              *reinterpret_cast<const uint2*>(static_cast<const uint8_t*>(kv.data) + row[q] * kv.D + R + 8 * part);
+          const float sc = kv.scale[row[q]];
+          uint32_t w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t word = e < 2 ? codes.x : codes.y;
+            const int sh = 16 * (e & 1);
+            w[e] = static_cast<uint32_t>(f32_to_bf16(e4m3_to_f32((word >> sh) & 0xFF) * sc)) |
+                   (static_cast<uint32_t>(f32_to_bf16(e4m3_to_f32((word >> (sh + 8)) & 0xFF) * sc)) << 16);
+          }
+          v = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      }
+      *reinterpret_cast<uint4*>(kpe + static_cast<int64_t>(j0 + r) * kXDr + 8 * part) = v;
     }
   }
 }
@@ -616,7 +683,7 @@ __global__ __launch_bounds__(256, 2) void attn_expanded_kernel(XPassArgs a) {
 bool prefill_expanded_supported(const CacheView& kv, int32_t H, int32_t Dn, int32_t Dv) {
   // (the pass length is a multiple of the up-projection's token tile)
   static_assert(kGTok == 256, "pass lengths are rounded to 256 keys");
-  return kv.Dr == kXDr && kv.R % kGK == 0 && Dn == kXDn && Dv == kXDv && H >= 1 && H <= 1024;
+  return kv.Dr == kXDr && kv.R % kGK8 == 0 && Dn == kXDn && Dv == kXDv && H >= 1 && H <= 1024;
 }
 
 hipError_t launch_prefill_expanded_pass(const XPassArgs& a, int32_t max_q_len, hipStream_t s) {
