@@ -527,11 +527,24 @@ __global__ __launch_bounds__(256, 2) void attn_expanded_kernel(XPassArgs a) {
   const float c = a.scale_log2;  // > 0 (the host routes other scales to the absorbed form)
 
   // S^T = K Q^T (keys x rows) of the tile in buffer `buf`
+  // (the key fragments are read six at a time, so that the MFMAs do not
+  // each wait for their own LDS read)
   auto scores = [&](int buf) {
     f32x16 sc = f32x16{};
     const char* kb = Ks[buf] + n32 * kAKPitch + 16 * g;
 #pragma unroll
-    for (int st = 0; st < kXDq / 16; ++st) sc = mfma(*reinterpret_cast<const i16x8*>(kb + 32 * st), qf[st], sc);
+    for (int s0 = 0; s0 < kXDq / 16; s0 += 6) {
+      i16x8 kf[6];
+#pragma unroll
+      for (int u = 0; u < 6; ++u) kf[u] = *reinterpret_cast<const i16x8*>(kb + 32 * (s0 + u));
+#pragma unroll
+      for (int u = 0; u < 6; ++u) sc = mfma(kf[u], qf[s0 + u], sc);
+    }
+    // (the order above, kept by the scheduler: six LDS reads, six MFMAs)
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
     return sc;
   };
   // the keys of this lane's row inside [k0, k0 + ntok): key <= pos, and with a
@@ -560,6 +573,16 @@ __global__ __launch_bounds__(256, 2) void attn_expanded_kernel(XPassArgs a) {
     f32x16 s_next = f32x16{};
     if (has_next) s_next = scores(nxt);
     f32x16 s = s_cur;
+    // this tile's V^T fragments, read before the softmax so that they land
+    // during it
+    i16x8 vf[kXDv / 32][2];
+    {
+      const char* vb = Vs[cur] + n32 * kAVPitch + 16 * g;
+#pragma unroll
+      for (int db = 0; db < kXDv / 32; ++db)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) vf[db][kk] = *reinterpret_cast<const i16x8*>(vb + 32 * db * kAVPitch + 32 * kk);
+    }
     // mask (tiles the lane's row does not wholly see), tile maximum of the
     // raw scores (a row's 32 keys sit in lanes n32 and n32 + 32; the scale
     // is positive, so it is applied to the maximum)
@@ -575,7 +598,12 @@ __global__ __launch_bounds__(256, 2) void attn_expanded_kernel(XPassArgs a) {
     float mx = fmaxf(fmaxf(s[0], s[1]), s[2]);
 #pragma unroll
     for (int e = 3; e < 16; ++e) mx = fmaxf(mx, s[e]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * c;
+    {
+      // (the other half of the row's keys sits in lane l ^ 32: a lane swap,
+      // no LDS round trip)
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * c;
+    }
     // move the reference when this tile's maximum passes it by the slack
     // (always on a row's first visible tile: the reference starts at -inf)
     const bool move = mx > m_ref + kRescaleSlack;
@@ -606,15 +634,13 @@ __global__ __launch_bounds__(256, 2) void attn_expanded_kernel(XPassArgs a) {
     // O^T += V^T P^T; MFMA k-slot 8 g + j of key half kk is key 16 kk + 4 g + j
     // (j < 4) or 16 kk + 8 + 4 g + (j - 4): the keys this lane's P registers
     // hold, which the quad-swapped V^T columns 16 kk + 8 g .. + 7 hold in order
-    const char* vb = Vs[cur] + n32 * kAVPitch + 16 * g;
 #pragma unroll
     for (int db = 0; db < kXDv / 32; ++db) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const i32x4 pv = {static_cast<int>(pk[4 * kk]), static_cast<int>(pk[4 * kk + 1]),
                           static_cast<int>(pk[4 * kk + 2]), static_cast<int>(pk[4 * kk + 3])};
-        o[db] = mfma(*reinterpret_cast<const i16x8*>(vb + 32 * db * kAVPitch + 32 * kk),
-                     __builtin_bit_cast(i16x8, pv), o[db]);
+        o[db] = mfma(vf[db][kk], __builtin_bit_cast(i16x8, pv), o[db]);
       }
     }
     // buffer `far` last held tile t - 1, whose values were read before the
