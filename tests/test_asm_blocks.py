@@ -178,3 +178,48 @@ def test_fp8_matrix_core_kernel_keeps_its_registers():
     assert re.search(r"Depth=2", text), "no nested loop found (the check would be vacuous)"
     assert re.search(r"v_mfma_f32_32x32x64_f8f6f4 v\[", text), "score MFMAs do not accumulate in VGPRs"
     assert len(re.findall(r"v_mfma_scale_f32_32x32x64_f8f6f4 a\[", text)) >= 16, "values MFMAs not in AGPRs"
+
+
+def _kernel_loop_scratch(src, kernel_substr):
+    """Scratch accesses inside loops (any depth) of one kernel of a source
+    file, from the compiler's own loop annotations."""
+    import re
+    import shutil
+    import tempfile
+
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not Path(hipcc).exists():
+        pytest.skip("hipcc not available")
+    with tempfile.TemporaryDirectory() as d:
+        out = Path(d) / "k.s"
+        subprocess.run([hipcc, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature",
+                        "-Xclang", "-packed-fp32-ops", "-I", str(CSRC), "-I", str(CSRC.parents[1] / "include"),
+                        "-x", "hip", "--cuda-device-only", "-S", str(CSRC / src), "-o", str(out)],
+                       check=True, capture_output=True)
+        text = out.read_text()
+    found, loops, in_loop_scratch, depth, inside = False, 0, 0, 0, False
+    for ln in text.splitlines():
+        m = re.match(r"^(_Z\w+):", ln)
+        if m:
+            inside = kernel_substr in m.group(1)
+            found |= inside
+            depth = 0
+            continue
+        if not inside:
+            continue
+        if re.match(r"^\.LBB\d+_\d+:", ln) or re.match(r"^; %bb\.\d+:", ln):
+            m = re.search(r"Depth=(\d+)", ln)
+            depth = int(m.group(1)) if m else 0
+            loops += depth > 0
+        elif depth >= 1 and re.search(r"\bscratch_(load|store)", ln):
+            in_loop_scratch += 1
+    assert found, f"no kernel matching {kernel_substr} in {src}"
+    assert loops > 0, "no loop found (the check would be vacuous)"
+    return in_loop_scratch
+
+
+@pytest.mark.parametrize("kernel", ["kv_expand_kernelILb0E", "kv_expand_kernelILb1E", "attn_expanded_kernel"])
+def test_expanded_prefill_kernels_do_not_spill_in_loops(kernel):
+    """The expanded-form prefill kernels keep their accumulators and staging
+    in registers: no scratch traffic inside their stage / tile loops."""
+    assert _kernel_loop_scratch("prefill_expanded.hip", kernel) == 0
