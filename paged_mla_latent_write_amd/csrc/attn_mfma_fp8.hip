@@ -14,12 +14,15 @@
 // Design (one workgroup of four waves per compute unit, wave w owns heads
 // [32w, 32w + 32), as in the bf16 kernel):
 //  * a 32-token tile is 18 KiB of codes + 128 B of scales.  Lane i of the
-//    workgroup owns the tile's 16-byte code chunks i, i + 256, ...: it copies
-//    them HBM -> LDS (global_load_lds, no VGPR staging) into one of two
-//    staging buffers, three tiles ahead of the compute, and it alone converts
-//    them to bf16 (exact), so a staging buffer is refilled as soon as its owner
-//    has read it, with no barrier.  Waves 2 and 3 copy the scales into one of
-//    four 1 KiB scale slots (lanes 8-63 repeat lanes 0-7 into the slot's pad).
+//    workgroup copies the tile's 16-byte code chunks i, i + 256, ... HBM ->
+//    LDS (global_load_lds, no VGPR staging) into one of two staging buffers,
+//    three tiles ahead of the compute, so that wave w fills the 1 KiB spans
+//    w, w + 4, ... of the buffer.  The wave alone converts its spans to bf16
+//    (exact), lane l taking the span's 8-byte halves l and 64 + l, so a
+//    staging buffer is refilled as soon as its owner wave has read it, with
+//    no barrier, and the conversion's LDS reads and writes are free of bank
+//    conflicts.  Waves 2 and 3 copy the scales into one of four 1 KiB scale
+//    slots (lanes 8-63 repeat lanes 0-7 into the slot's pad).
 //  * three bf16 tile buffers (the bf16 kernel's layout and swizzle): step n
 //    reads the keys of tile n and the values of tile n - 1 and writes tile
 //    n + 1, which the barrier ending the step publishes.
@@ -44,8 +47,8 @@ namespace {
 
 // Operands of one tile step's block.
 struct Fp8Step {
-  uint32_t cs;      // tile n + 1's codes: staging buffer + 16 tid (this lane's first chunk)
-  uint32_t cs4;     // this lane's fifth chunk (its fourth again when it has none)
+  uint32_t cs;      // tile n + 1's codes: staging buffer + 1024 wave + 8 lane (first span, half 0)
+  uint32_t cs4;     // the same in the wave's fifth span (its fourth again when it has none)
   uint32_t ct;      // this lane's row of the conversion table
   uint32_t sc;      // tile n's scale slot + 16 g
   uint32_t cp;      // 1: the block issues the copies of tile n + 3
@@ -243,9 +246,9 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(kCompilerVgp
   __shared__ __attribute__((aligned(1024))) char lds_tile[3][kTileBytes];
   __shared__ __attribute__((aligned(1024))) char lds_stage[2][kCodeBytes];
   __shared__ __attribute__((aligned(1024))) char lds_scale[4][kScaleSlot];
-  // thread i's entry j: the two 16-byte destinations (low and high 16 bits)
-  // in a bf16 tile of its chunk i + 256 j; a thread with no fifth chunk
-  // repeats its fourth
+  // thread i's entry j: the 16-byte destinations in a bf16 tile (low and
+  // high 16 bits) of the 8-byte halves lane and 64 + lane of its wave's span
+  // j; the waves with no fifth span repeat their fourth
   __shared__ __attribute__((aligned(16))) uint32_t conv_tab[256 * 5];
 
   const int tid = threadIdx.x;
@@ -272,6 +275,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(kCompilerVgp
   // waves 2 and 3: the scales, lane % 8 repeating over the slot's pad)
   const uint32_t o0 = 16 * tid;
   const uint32_t o4 = wave < 2 ? 16 * (tid + 1024) : 16 * (tid & 7);
+  // this lane's first code half in a staging buffer, for the conversion
+  const uint32_t cofs = 1024 * wave + 8 * lane;
 
   const uint32_t tile_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&lds_tile[0][0]));
   const uint32_t stage_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&lds_stage[0][0]));
@@ -312,15 +317,18 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(kCompilerVgp
     const TileLoc L1 = next_loc();
     copy_tile(a, L1, stage(1), sslot(1), wave, tid);
   }
+  // (half u of the tile -- bytes 8u.. of the codes -- is bf16 chunk u % 72 of
+  // row u / 72, at its swizzled slot)
+  auto half_dest = [](int u) {
+    const int t = u / 72, jc = u - 72 * (u / 72);
+    const int p = (jc & ~7) | ((jc & 7) ^ swz(t));
+    return static_cast<uint32_t>(t * kRowBytes + 16 * p);
+  };
 #pragma unroll
   for (int j = 0; j < 5; ++j) {
-    int c = tid + 256 * j;
-    if (c >= kCodeChunks) c -= 256;
-    const int t = c / 36, m2 = c - 36 * (c / 36);
-    const int j0 = 2 * m2, j1 = 2 * m2 + 1;
-    const int p0 = (j0 & ~7) | ((j0 & 7) ^ swz(t)), p1 = (j1 & ~7) | ((j1 & 7) ^ swz(t));
-    conv_tab[tid * 5 + j] = static_cast<uint32_t>(t * kRowBytes + 16 * p0) |
-                            (static_cast<uint32_t>(t * kRowBytes + 16 * p1) << 16);
+    const int span = j < 4 ? wave + 4 * j : (wave < 2 ? 16 + wave : wave + 12);
+    const int u = 128 * span + lane;
+    conv_tab[tid * 5 + j] = half_dest(u) | (half_dest(u + 64) << 16);
   }
   wait_vmcnt<kCopies>();  // this lane's chunks of tile 0 (and the scales) have landed
   convert_own(stage(0), tbuf(0), tid);
@@ -368,8 +376,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(kCompilerVgp
           int32_t pg = static_cast<int32_t>(L.pg0);
           uint32_t n = uni(static_cast<uint32_t>(steps));
           uint32_t bs = uni(tbuf(ib)), bp = uni(tbuf(ib == 0 ? 2 : ib - 1)), bn = uni(tbuf(ib == 2 ? 0 : ib + 1));
-          uint32_t cs = stage(tn + 1) + 16 * tid;
-          uint32_t cs4 = cs + (tid < kCodeChunks - 1024 ? 16384u : 12288u);
+          uint32_t cs = stage(tn + 1) + cofs;
+          uint32_t cs4 = cs + (wave < 2 ? 16384u : 12288u);
           uint32_t ds = uni(stage(tn + 2) - stage(tn + 1));
           uint32_t scb = uni(sslot(tn));
           uint32_t sc = scb + 16 * g;
@@ -400,8 +408,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_num_vgpr(kCompilerVgp
         continue;
       }
       Fp8Step f;
-      f.cs = cstage + 16 * tid;
-      f.cs4 = f.cs + (tid < kCodeChunks - 1024 ? 16384u : 12288u);
+      f.cs = cstage + cofs;
+      f.cs4 = f.cs + (wave < 2 ? 16384u : 12288u);
       f.ct = tab;
       f.sc = sslot(tn) + 16 * g;
       f.o0 = o0;

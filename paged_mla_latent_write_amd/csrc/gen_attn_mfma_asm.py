@@ -681,10 +681,14 @@ def pv_rest(st, first_pv, p_regs, vregs):
 # above (scores of tile n; values of tile n - 1 with the softmax of tile n
 # between their MFMAs) on bf16 tiles the workgroup converts from the staged
 # E4M3 codes, plus, between the scores MFMAs,
-#   * the conversion of tile n + 1: this lane's five 16-code chunks of the
-#     staging buffer (%[cs] + 4096 j, the fifth at %[cs4]), eight codes at a
-#     time, to bf16 rows of the next tile buffer (%[bn] plus the two 16-bit
-#     offsets of entry j of this lane's table row %[ct]);
+#   * the conversion of tile n + 1: the wave's five 1 KiB spans of the
+#     staging buffer (the ones its own copies filled), eight codes at a time:
+#     lane l converts the 8-byte halves l and 64 + l of span j (%[cs] + 4096 j
+#     + 512 h, the fifth span at %[cs4]) to bf16 rows of the next tile buffer
+#     (%[bn] plus the two 16-bit offsets of entry j of this lane's table row
+#     %[ct]); consecutive lanes read consecutive 8-byte halves and write
+#     consecutive 16-byte bf16 chunks (permuted within 128-byte groups by the
+#     swizzle), so neither access has a bank conflict;
 #   * the copies of tile n + 3 into the staging buffer just converted, each
 #     lane to its own chunks (so no other wave reads them): five
 #     global_load_lds from %[sb] / %[sb4], LDS rows from %[m0b] (+ 4 KB per
@@ -707,7 +711,7 @@ FP8_SCALE_AT = 27                  # the first two scale groups are read after t
 
 def fp8_code_read(st, j, h):
     x = FP8_CA if h == 0 else FP8_CB
-    src = f"%[cs4] offset:{8 * h}" if j == 4 else f"%[cs] offset:{4096 * j + 8 * h}"
+    src = f"%[cs4] offset:{512 * h}" if j == 4 else f"%[cs] offset:{4096 * j + 512 * h}"
     st.lds(f"ds_read_b64 v[{x}:{x + 1}], {src}", ("C", j, h))
 
 
@@ -716,8 +720,8 @@ def fp8_tab_read(st, j):
 
 
 def fp8_half(st, j, h, prev):
-    """Eight codes of chunk j (half h): four packed conversions (exact: every
-    E4M3 value is a bf16 value), the read of the same half of chunk j + 1 into
+    """Eight codes of span j (half h): four packed conversions (exact: every
+    E4M3 value is a bf16 value), the read of the same half of span j + 1 into
     the freed code registers, and a 16-byte LDS write."""
     x = FP8_CA if h == 0 else FP8_CB
     st.wait_for(("C", j, h))
