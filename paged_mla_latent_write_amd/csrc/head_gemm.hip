@@ -273,7 +273,11 @@ constexpr int kCupThreads = 512;
 // SB: partial rows of one item loaded together.  SB = 1 is the low-register
 // form for large item counts (prefill): phase 2 then loads its W_UV fragments
 // eight k-steps at a time instead of all before the barrier, so that two
-// workgroups fit on a compute unit.  IPW: items per workgroup, 32 or (grids
+// workgroups fit on a compute unit.  Decode grids of at most one workgroup
+// per compute unit take SB = 8, so that the partial rows of most items (a
+// long context is cut across four to six workgroups) arrive in one round
+// trip; larger decode grids take SB = 4 (on 512 workgroups of items cut
+// across two or three workgroups each, SB = 8 measured 20 % slower).  IPW: items per workgroup, 32 or (grids
 // smaller than the chip: few heads and requests) 4, merged by 128 threads each
 // with up to SB = 16 segments per round trip; the up-projection's MFMA rows
 // past those items are computed and discarded.
@@ -475,6 +479,9 @@ hipError_t launch_combine_up_project(const AttnArgs& a, const uint16_t* w_uv, in
   } else if (blocks32 * a.H < cus) {  // fewer workgroups than compute units
     hipLaunchKernelGGL((combine_up_project_kernel<16, 4>), dim3((a.num_items + 3) / 4, a.H), dim3(kCupThreads), 0,
                        s, a, w_uv, Dv, out);
+  } else if (blocks32 * a.H <= cus) {  // one workgroup per compute unit: the register-heavy form
+    hipLaunchKernelGGL((combine_up_project_kernel<8, 32>), dim3(blocks32, a.H), dim3(kCupThreads), 0, s, a, w_uv,
+                       Dv, out);
   } else {
     hipLaunchKernelGGL((combine_up_project_kernel<4, 32>), dim3(blocks32, a.H), dim3(kCupThreads), 0, s, a, w_uv,
                        Dv, out);
@@ -491,9 +498,12 @@ hipError_t launch_absorb_mfma(const uint16_t* q_nope, int64_t st, int64_t sh, co
   if (write) tw = *write;  // else tw.T == 0: nothing to write
   const int mt = pick_mt(num_items);
   // the W_UK block (Dn x 128 columns) is staged once per workgroup: at most
-  // ~2048 workgroups in all, so large item counts loop over several blocks
+  // ~2048 workgroups in all, so large item counts loop over several blocks;
+  // decode-sized batches (one or two blocks) take one workgroup per W_UK
+  // block, which reads it from memory once (measured faster than two
+  // workgroups each reading it for half the items)
   const int nblk = (num_items + 32 * mt - 1) / (32 * mt);
-  const int gz = std::max(1, std::min(nblk, std::max(1, 2048 / std::max(1, (R / kAbsCols) * H))));
+  const int gz = nblk <= 2 ? 1 : std::max(1, std::min(nblk, std::max(1, 2048 / std::max(1, (R / kAbsCols) * H))));
   // extra columns: the plan's workgroup, then one per four new tokens
   const int64_t extra = (plan ? 1 : 0) + (static_cast<int64_t>(tw.T) + 3) / 4;
   const int64_t per_col = static_cast<int64_t>(H) * gz;
