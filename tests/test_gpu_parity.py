@@ -199,17 +199,20 @@ def test_decode_forced_partitions(mla, G):
     check_decode(mla, case, num_workgroups=G, label=f" G={G}")
 
 
+@pytest.mark.parametrize("B", [40, 72])
 @pytest.mark.parametrize("G", [1, 3, 7, 1000])
-def test_decode_forced_partitions_wide_batch(mla, G):
-    """128 heads and 40 requests: enough 32-item blocks x heads to fill the
-    chip, so the combine runs its 32-items-per-workgroup form, whose merge of
-    cut items (several rounds of segments, empty ranges, both partial slots of
-    a workgroup) is then checked in full."""
-    say(f"decode forced G={G}, 128 heads x 40 requests")
+def test_decode_forced_partitions_wide_batch(mla, G, B):
+    """128 heads and 40 or 72 requests: enough 32-item blocks x heads to fill
+    the chip, so the combine runs its 32-items-per-workgroup forms -- up to
+    eight segments per round trip with 256 workgroups (40 requests: as many
+    as a 256-CU chip has compute units), four with 384 (72 requests) -- whose
+    merge of cut items (several rounds of segments, empty ranges, both
+    partial slots of a workgroup) is then checked in full."""
+    say(f"decode forced G={G}, 128 heads x {B} requests")
     d = W.Dims(H=128, R=512, Dr=64, Dn=128, Dv=128, page_size=64)
-    ctx = [1, 31, 32, 33, 64, 65, 700, 2049] * 5
-    case = W.custom(d, ctx, seed=210 + G, sharp=True)
-    check_decode(mla, case, num_workgroups=G, label=f" G={G} B=40")
+    ctx = [1, 31, 32, 33, 64, 65, 700, 2049] * (B // 8)
+    case = W.custom(d, ctx, seed=210 + G + (0 if B == 40 else 100), sharp=True)
+    check_decode(mla, case, num_workgroups=G, label=f" G={G} B={B}")
 
 
 @pytest.mark.parametrize("G", [1, 7, 1000])
