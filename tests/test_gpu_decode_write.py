@@ -151,3 +151,30 @@ def test_decode_write_with_no_requests_writes_only(mla):
         torch.cuda.synchronize()
         caches.append(cache_bits(cache)[0])
     assert np.array_equal(caches[0], caches[1])
+
+
+@pytest.mark.parametrize("kv", [O.KV_BF16, O.KV_FP8])
+def test_decode_write_two_item_blocks(mla, kv):
+    """48 requests: the absorb launch's workgroups each take two 32-item
+    blocks of one W_UK column block, beside the plan's and the new tokens'
+    workgroups; the result is still write-then-decode's, and the oracle's."""
+    ctx = [1, 31, 33, 700, 2049, 64, 3000, 5] * 6
+    say(f"decode_write kv={kv} B={len(ctx)}")
+    case = W.custom(DIMS, ctx, seed=1230, kv_dtype=kv, num_layers=2, layer=1, sharp=True)
+    step = step_tokens(case, [1] * len(ctx), n_pads=2, seed=1231)
+    kw = dict(w_uk=dev_bf16(case.w_uk), w_uv=dev_bf16(case.w_uv))
+    (ca, oa, la), (cb, ob, lb) = run_both(mla, case, step, **kw)
+    assert np.array_equal(ca[0], cb[0]), f"{int((ca[0] != cb[0]).sum())} cache elements differ"
+    assert np.array_equal(oa, ob), f"{int((oa != ob).sum())} outputs differ"
+    assert np.array_equal(la, lb)
+    hc = np.full((2, case.num_pages, DIMS.page_size, DIMS.D),
+                 W.BF16_NAN if kv == O.KV_BF16 else W.E4M3_NAN,
+                 dtype=np.uint16 if kv == O.KV_BF16 else np.uint8)
+    hs = np.full((2, case.num_pages, DIMS.page_size), np.nan, dtype=np.float32)
+    old, _ = step["split"]
+    O.write_kv(hc, hs, 1, case.ctx_c_kv[old], case.ctx_k_pe[old], case.ctx_slots[old], kv)
+    O.write_kv(hc, hs, 1, step["c"], step["r"], step["s"], kv)
+    ref, _ = O.decode(hc, hs, kv, 1, case.q_nope, case.q_pe, case.block_tables, case.context_lens,
+                      case.w_uk, case.w_uv, case.scale, 0)
+    assert_close(O.bf16_bits_to_f64(ob), ref, FP8_TOL if kv == O.KV_FP8 else BF16_TOL,
+                 f"decode_write kv={kv} B={len(ctx)}")
