@@ -7,7 +7,9 @@ mla_decode_write call, which writes the batch's newest tokens into the cache
 (write-then-attend; extra workgroups of the absorb launch do it) and then
 decodes (absorb, device-side split plan, split-KV attention, combine,
 up-projection).  The index-list workload keeps mla_write_kv followed by
-mla_sparse_attention.  Inputs
+mla_sparse_attention; the write workload (--workload write) times
+mla_write_kv_fused (RMSNorm + RoPE + cache write) on 262 144 tokens, with
+mla_write_kv beside it.  Inputs
 are seeded synthetic data with the V3 shape (128 heads, kv_lora_rank 512 +
 qk_rope 64, page size 64, batch 64, contexts uniform in [1024, 32768],
 shuffled block tables), resident in HBM before the timed region.
@@ -72,7 +74,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=100)
-    p.add_argument("--workload", default="v3", choices=["v3", "v3fp8", "v2lite", "mixed", "v3sparse"])
+    p.add_argument("--workload", default="v3", choices=["v3", "v3fp8", "v2lite", "mixed", "v3sparse", "write"])
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="CPU time budget for the oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -470,6 +472,148 @@ def cpu_baseline_mixed(L, budget_s):
                       f"{elapsed:.1f} s)"}, err
 
 
+WRITE_METRIC = "fused RMSNorm + RoPE latent cache write (mla_write_kv_fused) tokens/s, prefill-sized batch"
+WRITE_TOKENS = 262144
+
+
+def write_bytes_per_token(d, fp8):
+    """Algorithmic HBM bytes of one written token: the latent and rope rows
+    read (bf16), its slot and position (int64), and the cache row written
+    (bf16 values, or E4M3 codes and an fp32 scale).  The norm weight and the
+    cos/sin table rows are shared by every token and stay in the caches."""
+    return 2 * (d.R + d.Dr) + 8 + 8 + (d.D + 4 if fp8 else 2 * d.D)
+
+
+def main_write(args):
+    """f3 at a prefill-sized batch: one mla_write_kv_fused call of 262 144
+    tokens (RMSNorm over the 512-wide latent, interleaved RoPE over the 64-wide
+    rope part, then the cache write) per step, into a bf16 cache (the line's
+    value) and an fp8 E4M3 cache; mla_write_kv of the same rows timed beside
+    it.  About 600 MB move per bf16 call, more than the 256 MB Infinity Cache,
+    so back-to-back calls stream from HBM."""
+    import torch
+
+    from paged_mla_latent_write_amd import mla
+    from paged_mla_latent_write_amd import workloads as W
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    d = W.MLA_DIMS_128
+    T = WRITE_TOKENS
+    fc = W.fused_write_case(d, T, seed=7)
+    print(f"[bench] write: {T} tokens generated", file=sys.stderr, flush=True)
+
+    def bf16(u16):
+        return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def i(x):
+        return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+    c_kv, k_pe, slots, pos = bf16(fc.c_kv), bf16(fc.k_pe), i(fc.slots), i(fc.positions)
+    w, cs = bf16(fc.norm_weight), i(fc.cos_sin)
+    caches = {kv: mla.KVCache.empty(1, fc.num_pages, d.page_size, d.R, d.Dr, fp8=(kv == "fp8_e4m3"))
+              for kv in ("bf16", "fp8_e4m3")}
+
+    def fused(kv):
+        mla.write_kv_fused(caches[kv], 0, c_kv, k_pe, slots, positions=pos, norm_weight=w, eps=fc.eps,
+                           cos_sin=cs, interleaved=True)
+
+    def plain(kv):
+        mla.write_kv(caches[kv], 0, c_kv, k_pe, slots)
+
+    K = args.steps
+
+    def timed(fn):
+        """Warm-up, then K calls back to back (wall clock between two
+        synchronisations) with every call also between its own HIP events on
+        the stream it is launched on; returns (ms per step, event stats)."""
+        for _ in range(args.warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall * 1e3 / K, stats_ms([a.elapsed_time(b) for a, b in ev])
+
+    res = {}
+    for kv in ("bf16", "fp8_e4m3"):
+        for name, fn in (("fused", fused), ("plain", plain)):
+            res[(kv, name)] = timed(lambda: fn(kv))
+            ms, ev = res[(kv, name)]
+            print(f"[bench] write {name} {kv}: {ms:.4f} ms/step, kernel median {ev['median']:.4f} ms",
+                  file=sys.stderr, flush=True)
+
+    def roof(kv, name):
+        ms, ev = res[(kv, name)]
+        nbytes = T * write_bytes_per_token(d, kv == "fp8_e4m3")
+        gbs = nbytes / (ev["mean"] * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": gbs / HBM_PEAK_GBS, "traffic": None, "kernel": f"{name} write, {kv} cache",
+                "kernel_ms": ev["mean"], "kernel_ms_stats": ev, "alg_bytes_per_launch": nbytes,
+                "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3)}
+
+    ms = res[("bf16", "fused")][0]
+    line = {
+        "metric": WRITE_METRIC,
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32 arithmetic, bf16 cache",
+        "data": "synthetic (seeded; N(0,1) latent and rope rows, norm weight 1 + 0.1 N(0,1), "
+                "positions uniform in [0, 40000), slots a random permutation of the pages)",
+        "config": {"workload": f"fused latent write: {T} tokens, R {d.R} + Dr {d.Dr}, page size "
+                               f"{d.page_size}, RMSNorm (eps {fc.eps}) + interleaved RoPE",
+                   "tokens": T, "kv_lora_rank": d.R, "qk_rope": d.Dr, "page_size": d.page_size},
+        "roofline": roof("bf16", "fused"),
+        "plain_write_bf16": roof("bf16", "plain"),
+        "fused_write_fp8": roof("fp8_e4m3", "fused"),
+        "plain_write_fp8": roof("fp8_e4m3", "plain"),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import mla_oracle as O
+
+        fused("bf16")
+        torch.cuda.synchronize()
+        got = caches["bf16"].data[0].view(torch.int16).cpu().numpy().view(np.uint16)
+        hc = np.zeros((1, fc.num_pages, d.page_size, d.D), dtype=np.uint16)
+        hs = np.ones((1, fc.num_pages, d.page_size), dtype=np.float32)
+        done, elapsed, chunk = 0, 0.0, 4096
+        while done < T and (elapsed < args.cpu_seconds or done == 0):
+            sl = slice(done, min(T, done + chunk))
+            t0 = time.perf_counter()
+            O.write_kv_fused(hc, hs, 0, fc.c_kv[sl], fc.k_pe[sl], fc.slots[sl], fc.positions[sl],
+                             fc.norm_weight, fc.eps, fc.cos_sin, True, O.KV_BF16)
+            elapsed += time.perf_counter() - t0
+            done = sl.stop
+        s = fc.slots[:done]
+        pg, off = s // d.page_size, s % d.page_size
+        ref = O.bf16_bits_to_f64(hc[0][pg, off])
+        gpu = O.bf16_bits_to_f64(got[pg, off])
+        model, affinity = host_info()
+        line["cpu_baseline"] = {
+            "value": done / elapsed, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "cpu_model": model, "cores_available": affinity,
+            "sample": f"fp64 numpy oracle write_kv_fused (bf16 cache) on the first {done} of {T} tokens "
+                      f"({elapsed:.1f} s)"}
+        line["parity_sample"] = {
+            "max_abs": float(np.max(np.abs(gpu - ref))),
+            "rel_l2": float(np.linalg.norm(gpu - ref) / np.linalg.norm(ref)),
+            "bf16_values_differing": float(np.mean(hc[0][pg, off] != got[pg, off]))}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -478,6 +622,8 @@ def main():
         sys.exit(2)
     if args.workload == "mixed":
         return main_mixed(args)
+    if args.workload == "write":
+        return main_write(args)
     import torch
 
     from paged_mla_latent_write_amd import mla

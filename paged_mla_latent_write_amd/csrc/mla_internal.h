@@ -212,7 +212,7 @@ struct TokenWrite {
   int32_t dtype;        // kKvBf16 / kKvFp8
   int32_t R, Dr;
   int32_t T;            // tokens (0: nothing to write)
-  int32_t vec;          // bf16: 16-byte copies (R, Dr, strides multiples of 8, rows 16-byte aligned)
+  int32_t vec;          // 16-byte row chunks (R, Dr, strides multiples of 8, rows 16-byte aligned; fp8: R + Dr <= 1024)
 };
 TokenWrite make_token_write(void* cache_layer, float* scale_layer, int32_t dtype, int64_t num_slots, int32_t R,
                             int32_t Dr, const uint16_t* c_kv, int64_t c_stride, const uint16_t* k_pe,

@@ -36,12 +36,107 @@ __global__ __launch_bounds__(256) void write_kv_kernel(TokenWrite w) {
 //           from the input row, angle i of the token's position in the table
 // Each result is rounded to bf16 (nearest even), then written exactly as
 // write_kv writes a bf16 row: a bit copy, or the per-token E4M3 quantisation.
+
+// The same token in the 16-byte chunk layout (lane l: the row's 8-element
+// chunks l and l + 64, chunk c < R / 8 of the latent, else of the rope part;
+// R and Dr multiples of 8, Dr of 16 for half-split pairs, R + Dr <= 1024,
+// rows, weight and table 16-byte aligned): one 16-byte load per chunk, its
+// norm weights in one more, an interleaved pair inside one chunk (a
+// half-split pair's partner chunk is loaded whole), and one 16- (bf16) or
+// 8-byte (E4M3) store, where the lane-strided form moves 2 bytes (1 for a
+// code) per lane and access.  The arithmetic is the lane-strided form's; only
+// the order of the sum of squares differs.
+template <bool kFp8>
+__device__ __forceinline__ void fused_token_chunks(void* __restrict__ cache, float* __restrict__ scale_out,
+                                                   int64_t s, int32_t R, int32_t Dr,
+                                                   const uint16_t* __restrict__ src_c,
+                                                   const uint16_t* __restrict__ src_r, const KvTransform& tf,
+                                                   int64_t i, int lane) {
+  const int rc = R >> 3, nc = (R + Dr) >> 3;
+  float v[2][8];
+  load_row_chunks(src_c, src_r, rc, nc, lane, v);
+  if (tf.norm_weight != nullptr) {
+    float ss = 0.f;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      if (lane + 64 * q < rc)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ss = fmaf(v[q][e], v[q][e], ss);
+    const float r = 1.0f / sqrtf(wave_sum(ss) / static_cast<float>(R) + tf.eps);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int c = lane + 64 * q;
+      if (c < rc) {
+        float wf[8];
+        unpack_bf16x8(reinterpret_cast<const uint4*>(tf.norm_weight)[c], wf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[q][e] = bf16_to_f32(f32_to_bf16(v[q][e] * r * wf[e]));
+      }
+    }
+  }
+  if (tf.cos_sin != nullptr) {
+    const int64_t pos = min(max(tf.positions[i], int64_t{0}), static_cast<int64_t>(tf.max_position - 1));
+    const float* cs = tf.cos_sin + pos * Dr;
+    const int h = Dr >> 1;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int c = lane + 64 * q;
+      if (c >= rc && c < nc) {
+        const int j0 = 8 * (c - rc);  // first rope element of the chunk
+        float y[8];
+        if (tf.interleaved) {
+          // pairs (j0 + 2p, j0 + 2p + 1), angle j0 / 2 + p
+          const float4 co = *reinterpret_cast<const float4*>(cs + j0 / 2);
+          const float4 si = *reinterpret_cast<const float4*>(cs + h + j0 / 2);
+          const float cf[4] = {co.x, co.y, co.z, co.w}, sf[4] = {si.x, si.y, si.z, si.w};
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const float a = v[q][2 * p], b = v[q][2 * p + 1];
+            y[2 * p] = a * cf[p] - b * sf[p];
+            y[2 * p + 1] = b * cf[p] + a * sf[p];
+          }
+        } else {
+          // pairs (u, u + h): the chunk lies wholly in one half (h % 8 == 0)
+          const bool first = j0 < h;
+          const int f0 = first ? j0 : j0 - h;
+          float xp[8];
+          unpack_bf16x8(reinterpret_cast<const uint4*>(src_r)[(first ? j0 + h : j0 - h) >> 3], xp);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float cf = cs[f0 + e], sf = cs[h + f0 + e];
+            y[e] = first ? v[q][e] * cf - xp[e] * sf : v[q][e] * cf + xp[e] * sf;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[q][e] = bf16_to_f32(f32_to_bf16(y[e]));
+      }
+    }
+  }
+  const int D = R + Dr;
+  if constexpr (!kFp8) {
+    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(cache) + s * D);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int c = lane + 64 * q;
+      if (c < nc) {
+        uint32_t w[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          w[k] = (__float_as_uint(v[q][2 * k]) >> 16) | (__float_as_uint(v[q][2 * k + 1]) & 0xFFFF0000u);
+        dst[c] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+    }
+  } else {
+    store_fp8_chunks(static_cast<uint8_t*>(cache) + s * D, scale_out, s, nc, v, lane);
+  }
+}
+
 template <bool kFp8>
 __global__ __launch_bounds__(256) void write_kv_fused_kernel(
     void* __restrict__ cache, float* __restrict__ scale_out, int64_t num_slots, int32_t R,
     int32_t Dr, const uint16_t* __restrict__ c_kv, int64_t c_stride,
     const uint16_t* __restrict__ k_pe, int64_t k_stride, const int64_t* __restrict__ slots,
-    int32_t T, KvTransform tf) {
+    int32_t T, KvTransform tf, int32_t vec) {
   const int lane = threadIdx.x & 63;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + (threadIdx.x >> 6);
   if (i >= T) return;
@@ -50,6 +145,10 @@ __global__ __launch_bounds__(256) void write_kv_fused_kernel(
   const int D = R + Dr;
   const uint16_t* src_c = c_kv + i * c_stride;
   const uint16_t* src_r = k_pe + i * k_stride;
+  if (vec) {
+    fused_token_chunks<kFp8>(cache, scale_out, s, R, Dr, src_c, src_r, tf, i, lane);
+    return;
+  }
   constexpr int kMaxPerLane = 16;  // D <= 1024
   float v[kMaxPerLane];
   float ss = 0.f;
@@ -132,12 +231,18 @@ hipError_t launch_write_kv_fused(void* cache_layer, float* scale_layer, int32_t 
                                  hipStream_t s) {
   const dim3 grid((num_tokens + kWavesPerBlock - 1) / kWavesPerBlock);
   const dim3 block(64 * kWavesPerBlock);
+  const auto aligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  // the 16-byte chunk layout when the shapes and pointers allow it
+  const int32_t vec = (R % 8 == 0) && (Dr % 8 == 0) && R + Dr <= 1024 && (c_stride % 8 == 0) &&
+                      (k_stride % 8 == 0) && aligned(cache_layer) && aligned(c_kv) && aligned(k_pe) &&
+                      (tf.norm_weight == nullptr || aligned(tf.norm_weight)) &&
+                      (tf.cos_sin == nullptr || (aligned(tf.cos_sin) && (tf.interleaved || Dr % 16 == 0)));
   if (dtype == kKvBf16) {
     hipLaunchKernelGGL(write_kv_fused_kernel<false>, grid, block, 0, s, cache_layer, nullptr,
-                       num_slots, R, Dr, c_kv, c_stride, k_pe, k_stride, slots, num_tokens, tf);
+                       num_slots, R, Dr, c_kv, c_stride, k_pe, k_stride, slots, num_tokens, tf, vec);
   } else {
     hipLaunchKernelGGL(write_kv_fused_kernel<true>, grid, block, 0, s, cache_layer, scale_layer,
-                       num_slots, R, Dr, c_kv, c_stride, k_pe, k_stride, slots, num_tokens, tf);
+                       num_slots, R, Dr, c_kv, c_stride, k_pe, k_stride, slots, num_tokens, tf, vec);
   }
   return hipGetLastError();
 }
@@ -159,8 +264,8 @@ TokenWrite make_token_write(void* cache_layer, float* scale_layer, int32_t dtype
   w.R = R;
   w.Dr = Dr;
   w.T = num_tokens;
-  w.vec = dtype == kKvBf16 && (R % 8 == 0) && (Dr % 8 == 0) && (c_stride % 8 == 0) && (k_stride % 8 == 0) &&
-          aligned(cache_layer) && aligned(c_kv) && aligned(k_pe);
+  w.vec = (R % 8 == 0) && (Dr % 8 == 0) && (c_stride % 8 == 0) && (k_stride % 8 == 0) && aligned(cache_layer) &&
+          aligned(c_kv) && aligned(k_pe) && (dtype == kKvBf16 || R + Dr <= 1024);
   return w;
 }
 

@@ -34,9 +34,22 @@ def mla():
     return m
 
 
-def gpu_fused(mla, fc, kv, *, norm=True, rope=True, interleaved=True, layer=1, num_layers=2):
+def offset_bf16(bits):
+    """bf16 rows [T, n] as a view 8 bytes into the rows of a wider device
+    tensor: not 16-byte aligned, so the write kernels take their
+    lane-strided form (element j of a row in lane j % 64) instead of the
+    16-byte chunk form."""
+    T, n = bits.shape
+    wide = np.zeros((T, n + 8), dtype=np.uint16)
+    wide[:, 4:4 + n] = bits
+    return dev_bf16(wide)[:, 4:4 + n]
+
+
+def gpu_fused(mla, fc, kv, *, norm=True, rope=True, interleaved=True, layer=1, num_layers=2,
+              unaligned=False):
     cache = new_device_cache(mla, num_layers, fc.num_pages, fc.dims, kv)
-    mla.write_kv_fused(cache, layer, dev_bf16(fc.c_kv), dev_bf16(fc.k_pe), dev(fc.slots),
+    c_kv = offset_bf16(fc.c_kv) if unaligned else dev_bf16(fc.c_kv)
+    mla.write_kv_fused(cache, layer, c_kv, dev_bf16(fc.k_pe), dev(fc.slots),
                        positions=dev(fc.positions), norm_weight=dev_bf16(fc.norm_weight) if norm else None,
                        eps=fc.eps, cos_sin=dev(fc.cos_sin) if rope else None, interleaved=interleaved)
     torch.cuda.synchronize()
@@ -83,11 +96,14 @@ def fp32_slack(fc, interleaved):
     return np.concatenate([np.zeros((x.shape[0], d.R)), 2.0 ** -22 * mag], axis=1)
 
 
+# unaligned: the latent rows handed over 8 bytes off 16-byte alignment (the
+# kernels' lane-strided form); else aligned (their 16-byte chunk form)
+@pytest.mark.parametrize("unaligned", [False, True])
 @pytest.mark.parametrize("interleaved", [True, False])
-def test_fused_write_bf16(mla, interleaved):
-    say(f"fused write bf16 interleaved={interleaved}")
+def test_fused_write_bf16(mla, interleaved, unaligned):
+    say(f"fused write bf16 interleaved={interleaved} unaligned={unaligned}")
     fc = W.fused_write_case(D512, 4096, seed=1200 + interleaved, pad_every=9, c_std=2.0)
-    got = bf16_host_bits(gpu_fused(mla, fc, O.KV_BF16, interleaved=interleaved).data)
+    got = bf16_host_bits(gpu_fused(mla, fc, O.KV_BF16, interleaved=interleaved, unaligned=unaligned).data)
     hc, _ = oracle_fused(fc, O.KV_BF16, interleaved=interleaved)
     live = fc.slots >= 0
     # rows the call must not touch: other layer, pad rows, unused slots
@@ -110,10 +126,11 @@ def test_fused_write_bf16(mla, interleaved):
     assert frac <= 1e-3
 
 
-def test_fused_write_fp8(mla):
-    say("fused write fp8")
+@pytest.mark.parametrize("unaligned", [False, True])
+def test_fused_write_fp8(mla, unaligned):
+    say(f"fused write fp8 unaligned={unaligned}")
     fc = W.fused_write_case(D512, 4096, seed=1210, pad_every=11, c_std=2.0)
-    cache = gpu_fused(mla, fc, O.KV_FP8)
+    cache = gpu_fused(mla, fc, O.KV_FP8, unaligned=unaligned)
     codes = cache.data.cpu().numpy()
     scl = cache.scale.cpu().numpy()
     hc, hs = oracle_fused(fc, O.KV_FP8)
@@ -147,6 +164,28 @@ def test_fused_write_without_transform_is_plain_write(mla, kv):
     assert torch.equal(a.data.view(torch.uint8), b.data.view(torch.uint8))
     if kv == O.KV_FP8:
         assert torch.equal(a.scale.view(torch.int32), b.scale.view(torch.int32))
+
+
+@pytest.mark.parametrize("kv", [O.KV_BF16, O.KV_FP8])
+def test_write_forms_bit_identical(mla, kv):
+    """The plain write in its lane-strided form (latent rows off 16-byte
+    alignment) and in its 16-byte chunk form, and the fused write without
+    transforms in the lane-strided form: the same bytes and scales (the E4M3
+    row rule depends on no order of operations)."""
+    say(f"write forms {kv}")
+    fc = W.fused_write_case(D512, 900, seed=1240, pad_every=7, c_std=3.0)
+    caches = []
+    for unaligned in (False, True):
+        cache = new_device_cache(mla, 2, fc.num_pages, fc.dims, kv)
+        c_kv = offset_bf16(fc.c_kv) if unaligned else dev_bf16(fc.c_kv)
+        mla.write_kv(cache, 1, c_kv, dev_bf16(fc.k_pe), dev(fc.slots))
+        caches.append(cache)
+    caches.append(gpu_fused(mla, fc, kv, norm=False, rope=False, unaligned=True))
+    torch.cuda.synchronize()
+    for c in caches[1:]:
+        assert torch.equal(caches[0].data.view(torch.uint8), c.data.view(torch.uint8))
+        if kv == O.KV_FP8:
+            assert torch.equal(caches[0].scale.view(torch.int32), c.scale.view(torch.int32))
 
 
 def test_decode_over_a_fused_written_cache(mla):
