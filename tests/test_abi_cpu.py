@@ -167,6 +167,25 @@ def test_bench_refuses_more_than_one_gpu():
     assert "one GPU" in msg["error"]
 
 
+def test_bench_write_bytes_per_token():
+    """The write workload's roofline counts, per token at the MLA shape, the
+    bf16 latent and rope rows read (2 x 576 B), its int64 slot and position
+    (16 B) and the cache row written: 1152 B of bf16, or 576 codes and a 4-byte
+    scale."""
+    import importlib.util
+    from pathlib import Path
+
+    from paged_mla_latent_write_amd import workloads as W
+
+    spec = importlib.util.spec_from_file_location("bench_mod", Path(__file__).resolve().parents[1] / "bench.py")
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    d = W.MLA_DIMS_128
+    assert (d.R, d.Dr) == (512, 64)
+    assert bench.write_bytes_per_token(d, False) == 1152 + 16 + 1152
+    assert bench.write_bytes_per_token(d, True) == 1152 + 16 + 580
+
+
 def test_binding_rejects_mismatched_shapes():
     """The binding checks every host-known shape before it calls the ABI: a
     short block table or context_lens, queries whose head count or width
