@@ -46,6 +46,32 @@ __global__ __launch_bounds__(256) void write_kv_kernel(TokenWrite w) {
 // 8-byte (E4M3) store, where the lane-strided form moves 2 bytes (1 for a
 // code) per lane and access.  The arithmetic is the lane-strided form's; only
 // the order of the sum of squares differs.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Eight values rounded to bf16, nearest even, and back to fp32: the packed
+// hardware convert, two values per instruction (measured equal to
+// f32_to_bf16 on every non-NaN input tried, subnormals, ties and overflow
+// included); a group holding a NaN takes f32_to_bf16 itself, so a NaN becomes
+// 0x7FC0 as in the lane-strided form.
+__device__ __forceinline__ void round_bf16x8(float (&v)[8]) {
+  bool nan = false;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) nan |= v[e] != v[e];
+  if (nan) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = bf16_to_f32(f32_to_bf16(v[e]));
+    return;
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f32x2_t p = {v[2 * k], v[2 * k + 1]};
+    const uint32_t u = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2_t));
+    v[2 * k] = __uint_as_float(u << 16);
+    v[2 * k + 1] = __uint_as_float(u & 0xFFFF0000u);
+  }
+}
+
 template <bool kFp8>
 __device__ __forceinline__ void fused_token_chunks(void* __restrict__ cache, float* __restrict__ scale_out,
                                                    int64_t s, int32_t R, int32_t Dr,
@@ -70,7 +96,8 @@ __device__ __forceinline__ void fused_token_chunks(void* __restrict__ cache, flo
         float wf[8];
         unpack_bf16x8(reinterpret_cast<const uint4*>(tf.norm_weight)[c], wf);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[q][e] = bf16_to_f32(f32_to_bf16(v[q][e] * r * wf[e]));
+        for (int e = 0; e < 8; ++e) v[q][e] = v[q][e] * r * wf[e];
+        round_bf16x8(v[q]);
       }
     }
   }
@@ -107,8 +134,9 @@ __device__ __forceinline__ void fused_token_chunks(void* __restrict__ cache, flo
             y[e] = first ? v[q][e] * cf - xp[e] * sf : v[q][e] * cf + xp[e] * sf;
           }
         }
+        round_bf16x8(y);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[q][e] = bf16_to_f32(f32_to_bf16(y[e]));
+        for (int e = 0; e < 8; ++e) v[q][e] = y[e];
       }
     }
   }
