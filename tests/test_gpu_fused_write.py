@@ -188,6 +188,31 @@ def test_write_forms_bit_identical(mla, kv):
             assert torch.equal(caches[0].scale.view(torch.int32), c.scale.view(torch.int32))
 
 
+def test_fused_write_nan_rows(mla):
+    """NaN inputs (with payloads and either sign): a NaN in a row's latent
+    makes its whole normalised latent NaN (the sum of squares is NaN), a NaN
+    rope element makes its rotation pair NaN; every such bf16 value is the
+    canonical 0x7FC0 in both forms of the kernel (16-byte chunks, and
+    element per lane), and no other value is NaN."""
+    say("fused write NaN rows")
+    fc = W.fused_write_case(D512, 256, seed=1250)
+    c_kv, k_pe = fc.c_kv.copy(), fc.k_pe.copy()
+    c_kv[3, 17], c_kv[50, 400] = 0x7FC1, 0xFFA5
+    k_pe[7, 5], k_pe[90, 62] = 0xFFC3, 0x7F81
+    fc.c_kv, fc.k_pe = c_kv, k_pe
+    want = np.zeros((256, D512.D), dtype=bool)
+    want[[3, 50], :D512.R] = True
+    want[7, D512.R + 4:D512.R + 6] = True    # interleaved pair (4, 5)
+    want[90, D512.R + 62:D512.R + 64] = True  # pair (62, 63)
+    ps = D512.page_size
+    for unaligned in (False, True):
+        got = bf16_host_bits(gpu_fused(mla, fc, O.KV_BF16, unaligned=unaligned).data)
+        rows = got[1].reshape(-1, D512.D)[fc.slots]
+        nan = (rows & 0x7FFF) > 0x7F80
+        assert np.array_equal(nan, want), f"unaligned={unaligned}: NaN positions differ"
+        assert np.all(rows[nan] == 0x7FC0), f"unaligned={unaligned}: a NaN is not 0x7FC0"
+
+
 def test_decode_over_a_fused_written_cache(mla):
     """End to end: the context is written with the norm and rotation folded
     in, then decoded; the oracle does the same with its own fused write."""
